@@ -1,0 +1,97 @@
+"""Pins for the LRU expert-slot cache simulation."""
+import numpy as np
+import pytest
+
+from oracle.lru import CacheTooSmall, SlotLRU
+
+
+def test_textbook_trace(golden):
+    c = SlotLRU(2)
+    names = {}
+    for r in golden("lru_textbook.txt"):
+        step, key, hit, ev, slot = r.split()
+        e = ord(key) - ord("A")
+        names[e] = key
+        (rec,) = c.lookup(0, [e])
+        assert rec[1] == bool(int(hit)) and rec[2] == int(slot)
+        assert (rec[3] is None and ev == "-") or (rec[3] == (0, ord(ev) - ord("A")))
+
+
+class TimestampLRU:
+    """Independent formulation: last-use timestamps, victim = argmin timestamp."""
+
+    def __init__(self, C):
+        self.C = C
+        self.slot = {}
+        self.ts = {}
+        self.clock = 0
+
+    def lookup(self, layer, ids):
+        out = []
+        for e in ids:
+            key = (layer, e)
+            self.clock += 1
+            if key in self.slot:
+                self.ts[key] = self.clock
+                out.append((e, True, self.slot[key], None))
+                continue
+            used = set(self.slot.values())
+            free = [s for s in range(self.C) if s not in used]
+            if free:
+                s, victim = free[0], None
+            else:
+                victim = min(self.ts, key=lambda q: self.ts[q])
+                s = self.slot.pop(victim)
+                del self.ts[victim]
+            self.slot[key] = s
+            self.ts[key] = self.clock
+            out.append((e, False, s, victim))
+        return out
+
+
+def _random_steps(n, layers, E, per, seed):
+    rng = np.random.default_rng(seed)
+    p = np.arange(1, E + 1, dtype=float) ** -1.1
+    p /= p.sum()
+    steps = []
+    for _ in range(n):
+        for l in range(layers):
+            ids = sorted(set(rng.choice(E, per, replace=False, p=p).tolist()))
+            steps.append((l, ids))
+    return steps
+
+
+@pytest.mark.parametrize("C", [4, 8, 13, 40])
+def test_matches_timestamp_lru(C):
+    steps = _random_steps(60, 3, 24, 4, C)
+    a, b = SlotLRU(C), TimestampLRU(C)
+    for l, ids in steps:
+        assert a.lookup(l, ids) == b.lookup(l, ids)
+
+
+def test_inclusion_property_and_compulsory_misses():
+    steps = _random_steps(80, 2, 20, 3, 1)
+    misses = []
+    for C in range(3, 45):
+        c = SlotLRU(C)
+        misses.append(sum(not r[1] for l, ids in steps for r in c.lookup(l, ids)))
+    assert all(a >= b for a, b in zip(misses, misses[1:]))
+    distinct = len({(l, e) for l, ids in steps for e in ids})
+    assert misses[-1] == distinct  # C >= #keys: only first touches miss
+
+
+def test_step_larger_than_cache_rejected_and_state_unchanged():
+    c = SlotLRU(2)
+    c.lookup(0, [1])
+    with pytest.raises(CacheTooSmall):
+        c.lookup(0, [2, 3, 4])
+    assert c.lookup(0, [1])[0][1] is True
+
+
+def test_never_evicts_key_of_same_step():
+    c = SlotLRU(3)
+    c.lookup(0, [0, 1, 2])
+    recs = c.lookup(1, [0, 1, 2])
+    assert [r[3] for r in recs] == [(0, 0), (0, 1), (0, 2)]
+    recs = c.lookup(0, [5, 6])  # victims must be (1,0),(1,1), never a key of this step
+    assert [r[3] for r in recs] == [(1, 0), (1, 1)]
