@@ -1,0 +1,328 @@
+"""Throughput of the sparse MoE layer on one MI355X, with its roofline and the CPU oracle beside it.
+
+Default workload (decode, A3B-like shape): hidden 2048, 128 NVFP4 experts,
+top-8 renormalised, SwiGLU intermediate 768, Zipf(1.1) router logits.  One
+step = one layer call at each of the batch sizes 1, 4 and 16 tokens (21
+tokens).  Every step uses a fresh seeded batch and the next of 8 HBM copies
+of the layer's experts, so no expert is served from the 256 MB last-level
+cache across steps.  Inputs are resident in HBM before timing starts.
+
+Other workloads (--workload):
+  prefill-mxfp4  4096 tokens, MXFP4 weights x MXFP4 activations (FP4 matrix cores)
+  prefill-bf16   4096 tokens, BF16 weights (bf16 matrix cores)
+  large-decode   hidden 7168, 256 + 1 shared MXFP4 experts, intermediate 2048, 1 token
+  large-prefill  the same layer, 2048 tokens, MXFP4 activations
+
+Prints one JSON line (see the design doc for the definitions of every field).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "bf16": 2500.0}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def routed_bytes(blob_bytes, counts):
+    return int(np.count_nonzero(counts)) * blob_bytes
+
+
+def ffn_flops(counts, H, I, shared_rows=0):
+    return 2.0 * 3 * H * I * (int(np.sum(counts)) + shared_rows)
+
+
+class Timer:
+    """HIP events recorded on the stream the library launches on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.pairs.append((s, e))
+
+    def total_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs)
+
+    def reset(self):
+        self.pairs = []
+
+
+def oracle_baseline(run_one, unit_count, budget_s=12.0):
+    """Time the oracle (as it stands) on a bounded sample; returns (value per second, sample count, threads)."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        run_one(n)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return n * unit_count / dt, n, threads, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill-mxfp4", "prefill-bf16", "large-decode", "large-prefill"])
+    ap.add_argument("--copies", type=int, default=8, help="HBM copies of the layer's experts cycled across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md, 'How the path would shard').", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    from fp4_expert_ffn_amd.layer import MoELayer, bf16_tensor, blob_of
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    wl = args.workload
+
+    if wl == "decode":
+        cfg = synth.A3B
+        fmt, amode, batches, shared = "nvfp4", "bf16", [1, 4, 16], False
+        make = lambda: synth.a3b_experts("nvfp4", config=1)
+        steps, warmup = args.steps or 300, args.warmup or 30
+        nb = 64
+        inputs = [[synth.decode_batch(T, i) for T in batches] for i in range(nb)]
+    elif wl.startswith("prefill"):
+        cfg = synth.A3B
+        fmt = "mxfp4" if wl == "prefill-mxfp4" else "bf16"
+        amode, batches, shared = fmt, [4096], False
+        make = lambda: synth.a3b_experts(fmt, config=2)
+        steps, warmup = args.steps or 30, args.warmup or 5
+        nb = 1
+        inputs = [[synth.prefill_batch(4096)]]
+    else:
+        cfg = synth.LARGE
+        fmt, shared = "mxfp4", True
+        T = 1 if wl == "large-decode" else 2048
+        amode = "bf16" if T == 1 else "mxfp4"
+        batches = [T]
+        make = None
+        steps, warmup = args.steps or (200 if T == 1 else 10), args.warmup or (20 if T == 1 else 3)
+        nb = 1
+        inputs = [[synth.large_batch(T)]]
+        args.copies = 1 if T > 1 else min(args.copies, 4)
+
+    E, k, H, I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]
+    Tmax = max(batches)
+    if wl.startswith("prefill"):
+        args.copies = min(args.copies, 2)
+    log(f"[bench] workload={wl}: generating experts")
+    t0 = time.perf_counter()
+    if make is not None:
+        experts = make()
+        shared_ex = None
+    else:
+        experts = [synth.large_expert(e) for e in range(E)]
+        shared_ex = synth.large_expert(synth.SHARED_EXPERT)
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f}s; uploading {args.copies} copies")
+    layers = []
+    blobs = [blob_of(ex) for ex in experts]
+    shared_blob = blob_of(shared_ex) if shared_ex is not None else None
+    for c in range(args.copies):
+        lay = MoELayer(E=E, k=k, H=H, I=I, fmt=fmt, max_tokens=Tmax, device=dev, shared=shared, amode=amode)
+        for e, b in enumerate(blobs):
+            lay.load_expert(e, b)
+        if shared:
+            lay.load_shared(shared_blob)
+        layers.append(lay)
+    blob_bytes = layers[0].blob_bytes
+    del blobs
+
+    # One "combo" per input batch group: its own routing/output buffers, weights copy i % copies.
+    combos = []
+    for i, group in enumerate(inputs):
+        lay = layers[i % len(layers)]
+        calls = []
+        for b in group:
+            T = b["x"].shape[0]
+            x = bf16_tensor(b["x"], dev)
+            lg = torch.from_numpy(b["logits"]).to(dev) if "logits" in b else None
+            wr = torch.from_numpy(b["w_router"]).to(dev) if "w_router" in b else None
+            st = lay.new_state(T)
+            calls.append((T, x, lg, wr, st, st.args(T, x)))
+        combos.append(calls)
+    n_per_graph = len(combos)
+    toks_per_step = sum(c[0] for c in combos[0])
+
+    def run_full():
+        for calls in combos:
+            for (T, x, lg, wr, st, a) in calls:
+                st.route(T, x=x, w_router=wr, logits=lg)
+                st.ffn(T, x, args=a)
+
+    def run_ffn():
+        for calls in combos:
+            for (T, x, lg, wr, st, a) in calls:
+                st.ffn(T, x, args=a)
+
+    # eager pass (library set-up, workspace sizing), then capture both sequences as HIP graphs
+    run_full()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    g_full, g_ffn = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_full, stream=side):
+        run_full()
+    with torch.cuda.graph(g_ffn, stream=side):
+        run_ffn()
+    torch.cuda.synchronize()
+
+    replays = max(1, -(-steps // n_per_graph))
+    steps = replays * n_per_graph
+    wreps = max(1, -(-warmup // n_per_graph))
+    warmup = wreps * n_per_graph
+    log(f"[bench] warmup {warmup} steps, timing {steps} steps ({replays} graph replays of {n_per_graph} steps)")
+    for _ in range(wreps):
+        g_full.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(replays):
+        g_full.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    value = toks_per_step * steps / wall
+
+    # FFN-only graph (routing buffers hold the last full pass): per-launch FFN duration
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g_ffn.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(replays):
+        g_ffn.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ffn_ms = e0.elapsed_time(e1)
+    n_calls = replays * sum(len(c) for c in combos)
+
+    # algorithmic bytes / flops of the FFN calls (from the routing each combo holds)
+    tot_bytes, tot_flops = 0, 0.0
+    for calls in combos:
+        for (T, x, lg, wr, st, a) in calls:
+            cn = st.counts.cpu().numpy()
+            tot_bytes += routed_bytes(blob_bytes, cn) + (blob_bytes if shared else 0) + T * H * 2 * 2
+            tot_flops += ffn_flops(cn, H, I, T if shared else 0)
+    tot_bytes *= replays
+    tot_flops *= replays
+    avg_ms = ffn_ms / n_calls
+    bytes_per_call = tot_bytes / n_calls
+    if wl in ("prefill-mxfp4", "large-prefill"):
+        ach = tot_flops / n_calls / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK_TFLOPS["fp4"], 4)}
+        roof["hbm_gbs_same_kernel"] = round(bytes_per_call / (avg_ms * 1e-3) / 1e9, 1)
+    else:
+        ach = bytes_per_call / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = None
+    roof["kernel"] = "moe_expert_ffn (all of its launches, back to back in a HIP graph)"
+    roof["avg_launch_us"] = round(avg_ms * 1e3, 3)
+    roof["algorithmic_bytes_per_launch"] = int(bytes_per_call)
+    roof["algorithmic_flops_per_launch"] = int(tot_flops / n_calls)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] timing the CPU oracle on a bounded sample")
+        b0 = inputs[0]
+        sample_tokens = sum(b["x"].shape[0] for b in b0)
+        if wl == "decode" or wl == "large-decode":
+            def run_one(n):
+                for b in inputs[n % len(inputs)]:
+                    if "logits" in b:
+                        oracle.moe.layer(b["x"], experts, k, logits=b["logits"])
+                    else:
+                        oracle.moe.layer(b["x"], experts, k, w_router=b["w_router"], shared=shared_ex)
+            val, n, thr, dt = oracle_baseline(run_one, sample_tokens, args.cpu_budget)
+            cpu = {"value": round(val, 3), "unit": "tokens/s", "cores": thr, "kind": "oracle",
+                   "sample": f"{n} oracle layer calls over batches of {[b['x'].shape[0] for b in b0]} tokens "
+                             f"({dt:.1f} s)"}
+        else:
+            b = b0[0]
+            ids, w = oracle.moe.route(b["logits"], k) if "logits" in b else (None, None)
+            if ids is None:
+                ids, w = oracle.moe.route(combos[0][0][4].logits[:b["x"].shape[0]].cpu().numpy(), k)
+            cache = {}
+
+            def wts(e):
+                if e not in cache:
+                    cache.clear()
+                    cache[e] = oracle.moe.dequant_expert(experts[e])
+                return cache[e]
+            rng = np.random.default_rng(0)
+            order = rng.permutation(b["x"].shape[0])
+            sw = oracle.moe.dequant_expert(shared_ex) if shared_ex is not None else None
+
+            def run_one(n):
+                t = int(order[n % len(order)])
+                oracle.moe.token_output(t, b["x"], ids[t], w[t], wts, shared_weights=sw, amode=amode)
+            val, n, thr, dt = oracle_baseline(run_one, 1, args.cpu_budget)
+            cpu = {"value": round(val, 3), "unit": "tokens/s", "cores": thr, "kind": "oracle",
+                   "sample": f"{n} tokens of the {b['x'].shape[0]}-token batch, one by one ({dt:.1f} s)"}
+
+    names = {"decode": "decode A3B-like NVFP4 (hidden 2048, 128 experts, top-8, inter 768), batches 1+4+16",
+             "prefill-mxfp4": "prefill A3B-like 4096 tokens, MXFP4 weights x MXFP4 activations",
+             "prefill-bf16": "prefill A3B-like 4096 tokens, BF16 weights",
+             "large-decode": "large-expert layer (hidden 7168, 256+1 shared MXFP4 experts, inter 2048), 1 token",
+             "large-prefill": "large-expert layer, 2048 tokens, MXFP4 activations"}
+    line = {
+        "metric": "MoE-layer tokens/s",
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"decode": "nvfp4xbf16->f32", "prefill-mxfp4": "mxfp4xmxfp4->f32", "prefill-bf16": "bf16->f32",
+                  "large-decode": "mxfp4xbf16->f32", "large-prefill": "mxfp4xmxfp4->f32"}[wl],
+        "data": "synthetic (seeded; weights N(0,0.02) quantised, activations N(0,1) bf16, Zipf(1.1) routing)",
+        "config": {"workload": names[wl], "tokens_per_step": toks_per_step, "experts": E, "top_k": k,
+                   "hidden": H, "intermediate": I, "weights": fmt, "hbm_copies": len(layers),
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

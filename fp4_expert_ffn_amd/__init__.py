@@ -1,0 +1,12 @@
+"""MI355X-native sparse MoE layer (route, permute, expert-slot cache, FP4 expert FFN, combine).
+
+The product is the C-ABI library ``libmoe.so`` (HIP kernels for gfx950, see
+``include/moe.h``); ``fp4_expert_ffn_amd._lib`` is its ctypes binding with the
+same names, and ``fp4_expert_ffn_amd.layer`` chains the calls for one layer.
+"""
+from ._lib import (  # noqa: F401
+    AMODE, FMT, Cache, FfnArgs, MoeError, cache_fill, cache_lookup, ffn_args, lib, moe_blob_bytes,
+    moe_cache_create, moe_cache_destroy, moe_cache_mark_used, moe_cache_pin_resident, moe_cache_reset,
+    moe_combine, moe_dequant_blob, moe_expert_ffn, moe_expert_ffn_workspace_size, moe_last_error,
+    moe_permute, moe_prepack_expert, moe_quantize_mxfp4, moe_route, moe_router_logits, moe_version,
+)

@@ -1,0 +1,268 @@
+"""ctypes binding of libmoe.so: argument marshalling only.
+
+Every function has the name of the C entry point it wraps and forwards to it;
+device tensors are passed as ``data_ptr()`` values, the stream defaults to
+torch's current HIP stream.  All arithmetic happens in the library's kernels.
+A missing library is an error (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ENOMEM, MOE_ECACHE = range(6)
+FMT = {"bf16": 0, "mxfp4": 1, "nvfp4": 2}
+AMODE = {"bf16": 0, "mxfp4": 1}
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EHIP", 4: "MOE_ENOMEM", 5: "MOE_ECACHE"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class FfnArgs(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int), ("k", ctypes.c_int), ("E", ctypes.c_int), ("H", ctypes.c_int), ("I", ctypes.c_int),
+        ("wfmt", ctypes.c_int), ("amode", ctypes.c_int),
+        ("x", ctypes.c_void_p), ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+        ("slot_of_expert", ctypes.c_void_p), ("slot_pool", ctypes.c_void_p), ("slot_stride", ctypes.c_size_t),
+        ("shared_blob", ctypes.c_void_p), ("expert_mask", ctypes.c_void_p),
+        ("y", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("inv", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class ExpertCanonical(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+        ("gate_q", ctypes.c_void_p), ("gate_s", ctypes.c_void_p), ("gate_g", ctypes.c_float),
+        ("up_q", ctypes.c_void_p), ("up_s", ctypes.c_void_p), ("up_g", ctypes.c_float),
+        ("down_q", ctypes.c_void_p), ("down_s", ctypes.c_void_p), ("down_g", ctypes.c_float),
+    ]
+
+
+# name -> (restype, argtypes); the exported C ABI (include/moe.h)
+_vp, _i, _sz, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+SIGNATURES = {
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_version": (ctypes.c_char_p, []),
+    "moe_router_logits": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
+    "moe_route": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "moe_permute": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "moe_blob_bytes": (_sz, [_i, _i, _i]),
+    "moe_prepack_expert": (_i, [ctypes.POINTER(ExpertCanonical), _vp, _sz]),
+    "moe_expert_ffn_workspace_size": (_sz, [ctypes.POINTER(FfnArgs)]),
+    "moe_expert_ffn": (_i, [ctypes.POINTER(FfnArgs), _vp]),
+    "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "moe_quantize_mxfp4": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+    "moe_dequant_blob": (_i, [_vp, _i, _vp, _vp]),
+    "moe_cache_create": (_vp, [_i, _sz, _vp, _i, _i]),
+    "moe_cache_destroy": (None, [_vp]),
+    "cache_lookup": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp]),
+    "cache_fill": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp]),
+    "moe_cache_mark_used": (_i, [_vp, _vp, _i, _vp]),
+    "moe_cache_reset": (_i, [_vp]),
+    "moe_cache_pin_resident": (_i, [_vp, _i, _i]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(python -m fp4_expert_ffn_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(st: int, what: str):
+    if st != MOE_OK:
+        raise MoeError(st, f"{what}: {lib().moe_last_error().decode()}")
+
+
+def ptr(t) -> int | None:
+    """Device/host address of a torch tensor, numpy array, int or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def stream_handle(stream=None) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_version() -> str:
+    return lib().moe_version().decode()
+
+
+def moe_router_logits(x, w_router, T, H, E, logits, stream=None):
+    _check(lib().moe_router_logits(ptr(x), ptr(w_router), T, H, E, ptr(logits), stream_handle(stream)),
+           "moe_router_logits")
+
+
+def moe_route(logits, T, E, k, renormalize, topk_ids, topk_w, stream=None):
+    _check(lib().moe_route(ptr(logits), T, E, k, int(renormalize), ptr(topk_ids), ptr(topk_w), stream_handle(stream)),
+           "moe_route")
+
+
+def moe_permute(topk_ids, T, k, E, counts, offsets, perm, inv, stream=None):
+    _check(lib().moe_permute(ptr(topk_ids), T, k, E, ptr(counts), ptr(offsets), ptr(perm), ptr(inv),
+                             stream_handle(stream)), "moe_permute")
+
+
+def moe_blob_bytes(fmt, H, I) -> int:
+    return int(lib().moe_blob_bytes(FMT.get(fmt, fmt), H, I))
+
+
+def moe_prepack_expert(fmt, H, I, gate, up, down) -> np.ndarray:
+    """gate/up/down: (codes_or_bf16, scales_or_None, g) numpy arrays in canonical layout.
+
+    Returns the blob as a host uint8 array."""
+    f = FMT.get(fmt, fmt)
+    keep = []
+
+    def arr(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        keep.append(a)
+        return a.ctypes.data
+
+    c = ExpertCanonical(f, H, I,
+                        arr(gate[0]), arr(gate[1]), float(gate[2]),
+                        arr(up[0]), arr(up[1]), float(up[2]),
+                        arr(down[0]), arr(down[1]), float(down[2]))
+    n = moe_blob_bytes(f, H, I)
+    out = np.empty(max(n, 1), np.uint8)
+    _check(lib().moe_prepack_expert(ctypes.byref(c), out.ctypes.data, n), "moe_prepack_expert")
+    return out
+
+
+def ffn_args(**kw) -> FfnArgs:
+    a = FfnArgs()
+    for name, _ in FfnArgs._fields_:
+        if name in kw:
+            v = kw.pop(name)
+            if name == "wfmt":
+                v = FMT.get(v, v)
+            elif name == "amode":
+                v = AMODE.get(v, v)
+            elif name in ("T", "k", "E", "H", "I", "slot_stride", "workspace_bytes"):
+                v = int(v)
+            else:
+                v = ptr(v)
+            setattr(a, name, v)
+    if kw:
+        raise TypeError(f"unknown moe_ffn_args fields: {sorted(kw)}")
+    return a
+
+
+def moe_expert_ffn_workspace_size(args: FfnArgs) -> int:
+    return int(lib().moe_expert_ffn_workspace_size(ctypes.byref(args)))
+
+
+def moe_expert_ffn(args: FfnArgs, stream=None):
+    _check(lib().moe_expert_ffn(ctypes.byref(args), stream_handle(stream)), "moe_expert_ffn")
+
+
+def moe_combine(y, inv, topk_w, y_shared, T, k, H, out, stream=None):
+    _check(lib().moe_combine(ptr(y), ptr(inv), ptr(topk_w), ptr(y_shared), T, k, H, ptr(out), stream_handle(stream)),
+           "moe_combine")
+
+
+def moe_quantize_mxfp4(x, rows, cols, q, s, stream=None):
+    _check(lib().moe_quantize_mxfp4(ptr(x), rows, cols, ptr(q), ptr(s), stream_handle(stream)), "moe_quantize_mxfp4")
+
+
+def moe_dequant_blob(blob, which, out, stream=None):
+    _check(lib().moe_dequant_blob(ptr(blob), which, ptr(out), stream_handle(stream)), "moe_dequant_blob")
+
+
+class Cache:
+    """Owner of a moe_cache handle (host LRU metadata + HIP events)."""
+
+    def __init__(self, num_slots, slot_bytes, slot_pool, num_layers, num_experts):
+        h = lib().moe_cache_create(num_slots, slot_bytes, ptr(slot_pool), num_layers, num_experts)
+        if not h:
+            raise MoeError(MOE_EINVAL, moe_last_error())
+        self.handle = h
+        self.num_slots = num_slots
+
+    def close(self):
+        if self.handle:
+            lib().moe_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def moe_cache_create(num_slots, slot_bytes, slot_pool, num_layers, num_experts) -> Cache:
+    return Cache(num_slots, slot_bytes, slot_pool, num_layers, num_experts)
+
+
+def moe_cache_destroy(cache: Cache):
+    cache.close()
+
+
+def cache_lookup(cache: Cache, layer: int, ids):
+    """ids: distinct ascending expert ids.  Returns (slot, hit, evicted_key) numpy arrays."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    n = ids.size
+    slot = np.empty(n, np.int32)
+    hit = np.empty(n, np.uint8)
+    ev = np.empty(n, np.int32)
+    _check(lib().cache_lookup(cache.handle, layer, ids.ctypes.data, n, slot.ctypes.data, hit.ctypes.data,
+                              ev.ctypes.data), "cache_lookup")
+    return slot, hit, ev
+
+
+def cache_fill(cache: Cache, layer, expert, slot, host_src, copy_stream=None, compute_stream=None):
+    _check(lib().cache_fill(cache.handle, layer, expert, slot, ptr(host_src), stream_handle(copy_stream),
+                            stream_handle(compute_stream)), "cache_fill")
+
+
+def moe_cache_mark_used(cache: Cache, slots, stream=None):
+    s = np.ascontiguousarray(slots, dtype=np.int32)
+    _check(lib().moe_cache_mark_used(cache.handle, s.ctypes.data, s.size, stream_handle(stream)),
+           "moe_cache_mark_used")
+
+
+def moe_cache_reset(cache: Cache):
+    _check(lib().moe_cache_reset(cache.handle), "moe_cache_reset")
+
+
+def moe_cache_pin_resident(cache: Cache, layer, s0):
+    _check(lib().moe_cache_pin_resident(cache.handle, layer, s0), "moe_cache_pin_resident")

@@ -1,0 +1,253 @@
+// moe_expert_ffn dispatcher, the weighted combine, and the debug dequantiser.
+//
+// Method: the combine weights each routed expert's output by its routing
+// weight and sums them back in token order (the sparse activation of page
+// "FreeToken量子化：MoE推論のセットアップガイド", second paragraph: every token
+// passes through a few experts); the shared expert, when present, is added
+// with weight 1 (this library's reading).
+#include <algorithm>
+
+#include "ffn_common.h"
+
+namespace moe {
+hipError_t launch_gemv(const FfnParams& P, float* h, float* y, hipStream_t s);
+hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s);
+hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st);
+}  // namespace moe
+
+namespace {
+using namespace moe;
+
+// Row count at or above which BF16 weights take the bf16 MFMA grouped GEMM.
+constexpr long long kMfmaMinRows = 512;
+
+enum Path { kPathGemv, kPathMfmaFp4, kPathMfmaBf16 };
+
+Path choose_path(const moe_ffn_args* a) {
+  if (a->amode == MOE_ACT_MXFP4) return kPathMfmaFp4;
+  if (a->wfmt == MOE_FMT_BF16 && (long long)a->T * a->k >= kMfmaMinRows) return kPathMfmaBf16;
+  return kPathGemv;
+}
+
+struct WsLayout {
+  size_t h, y, xq, xs, hq, hs, hb, total;
+};
+
+size_t al(size_t v) { return (v + 255) & ~size_t(255); }
+
+WsLayout ws_layout(const moe_ffn_args* a) {
+  const size_t R = (size_t)a->T * a->k + (a->shared_blob ? a->T : 0);
+  WsLayout w{};
+  size_t o = 0;
+  const Path p = choose_path(a);
+  if (p == kPathGemv) {
+    w.h = o; o = al(o + R * a->I * sizeof(float));
+  } else if (p == kPathMfmaFp4) {
+    w.xq = o; o = al(o + (size_t)a->T * a->H / 2);
+    w.xs = o; o = al(o + (size_t)a->T * a->H / 32);
+    w.hq = o; o = al(o + R * a->I / 2);
+    w.hs = o; o = al(o + R * a->I / 32);
+  } else {
+    w.hb = o; o = al(o + R * a->I * 2);
+  }
+  w.y = o;
+  if (!a->y) o = al(o + R * a->H * sizeof(float));
+  w.total = o;
+  return w;
+}
+
+moe_status check_args(const moe_ffn_args* a) {
+  MOE_CHECK_ARG(a, "moe_expert_ffn: null args");
+  MOE_CHECK_ARG(a->T >= 0 && a->k >= 1 && a->k <= 16 && a->E >= 1 && a->E <= 1024,
+                "moe_expert_ffn: bad sizes T=%d k=%d E=%d", a->T, a->k, a->E);
+  MOE_CHECK_ARG(a->H > 0 && a->I > 0 && a->H % 128 == 0 && a->I % 128 == 0,
+                "moe_expert_ffn: H=%d and I=%d must be positive multiples of 128", a->H, a->I);
+  MOE_CHECK_ARG(a->wfmt == MOE_FMT_BF16 || a->wfmt == MOE_FMT_MXFP4 || a->wfmt == MOE_FMT_NVFP4,
+                "moe_expert_ffn: bad weight format %d", a->wfmt);
+  MOE_CHECK_ARG(a->amode == MOE_ACT_BF16 || a->amode == MOE_ACT_MXFP4, "moe_expert_ffn: bad amode %d", a->amode);
+  if (a->amode == MOE_ACT_MXFP4 && a->wfmt != MOE_FMT_MXFP4)
+    return set_error(MOE_EUNSUPPORTED, "moe_expert_ffn: MXFP4 activations need MXFP4 weights (got format %d)",
+                     a->wfmt);
+  MOE_CHECK_ARG((long long)a->T * a->k <= (1 << 17), "moe_expert_ffn: T*k exceeds 131072");
+  MOE_CHECK_ARG(a->slot_stride % 256 == 0 && a->slot_stride >= moe_blob_bytes(a->wfmt, a->H, a->I),
+                "moe_expert_ffn: slot_stride %zu must be a multiple of 256 and >= blob bytes %zu", a->slot_stride,
+                moe_blob_bytes(a->wfmt, a->H, a->I));
+  if (a->T == 0) return MOE_OK;
+  MOE_CHECK_ARG(a->x && a->counts && a->offsets && a->perm && a->slot_of_expert && a->slot_pool,
+                "moe_expert_ffn: null input pointer");
+  MOE_CHECK_ARG(!a->out || (a->topk_w && a->inv), "moe_expert_ffn: out needs topk_w and inv");
+  const WsLayout w = ws_layout(a);
+  if (a->workspace_bytes < w.total || (w.total && !a->workspace))
+    return set_error(MOE_ENOMEM, "moe_expert_ffn: workspace %zu bytes < %zu needed", a->workspace_bytes, w.total);
+  MOE_CHECK_ARG(((uintptr_t)a->workspace & 255) == 0 && ((uintptr_t)a->slot_pool & 255) == 0 &&
+                    ((uintptr_t)a->x & 15) == 0 && (!a->y || ((uintptr_t)a->y & 15) == 0) &&
+                    (!a->shared_blob || ((uintptr_t)a->shared_blob & 255) == 0),
+                "moe_expert_ffn: misaligned pointer (workspace/slot_pool/shared_blob need 256 B, x/y 16 B)");
+  return MOE_OK;
+}
+
+// out[t, c..c+8) = bf16( sum_j w[t,j] * y[inv[t*k+j], c..] (+ y[T*k + t, c..]) )
+__global__ __launch_bounds__(128) void k_combine(const float* __restrict__ y, const int32_t* __restrict__ inv,
+                                                 const float* __restrict__ w, const float* __restrict__ ysh, int T,
+                                                 int k, int H, uint16_t* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int c = (blockIdx.x * 128 + threadIdx.x) * 8;
+  if (c >= H) return;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[(size_t)t * k + j];
+    const float4* src = reinterpret_cast<const float4*>(y + (size_t)inv[(size_t)t * k + j] * H + c);
+    const float4 a = src[0], b = src[1];
+    acc[0] = fmaf(wj, a.x, acc[0]); acc[1] = fmaf(wj, a.y, acc[1]);
+    acc[2] = fmaf(wj, a.z, acc[2]); acc[3] = fmaf(wj, a.w, acc[3]);
+    acc[4] = fmaf(wj, b.x, acc[4]); acc[5] = fmaf(wj, b.y, acc[5]);
+    acc[6] = fmaf(wj, b.z, acc[6]); acc[7] = fmaf(wj, b.w, acc[7]);
+  }
+  if (ysh) {
+    const float4* src = reinterpret_cast<const float4*>(ysh + (size_t)t * H + c);
+    const float4 a = src[0], b = src[1];
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i]) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, const float* ysh, int T, int k, int H,
+                          uint16_t* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine, dim3((H / 8 + 127) / 128, T), dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
+  return hipGetLastError();
+}
+
+// Debug dequantiser: one thread per (tile, lane) fragment.
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ blob, BlobLayout L, int fmt, int which,
+                                                 int H, int I, float* __restrict__ out) {
+  const BlobView bv = blob_view(blob, L);
+  const bool down = which == 2;
+  const int rows = down ? H : I, cols = down ? I : H;
+  const int KT = k_per_tile(fmt), nk = cols / KT;
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long nfrag = (long long)(rows / 16) * nk * 64;
+  if (gid >= nfrag) return;
+  const int lane = (int)(gid & 63);
+  const long long tl = gid >> 6;
+  const int kt = (int)(tl % nk), grp = (int)(tl / nk);
+  const int rg = down ? grp : 2 * grp + which;  // interleaved gate/up groups
+  const size_t tile = (size_t)rg * nk + kt;
+  const uint8_t* wsrc = (down ? bv.w2 : bv.w13) + tile * kTileBytes + lane * 16;
+  const uint8_t* ssrc = down ? bv.s2 : bv.s13;
+  const int row = grp * 16 + (lane & 15);
+  const uint4 q = *reinterpret_cast<const uint4*>(wsrc);
+  float* o = out + (size_t)row * cols;
+  if (fmt == MOE_FMT_BF16) {
+    const int c0 = kt * 32 + (lane >> 4) * 8;
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    for (int i = 0; i < 4; ++i) {
+      o[c0 + 2 * i] = __uint_as_float(w[i] << 16);
+      o[c0 + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    return;
+  }
+  const int c0 = kt * 128 + (lane >> 4) * 32;
+  float v[32];
+  fp4x32_to_f32(q, v);
+  if (fmt == MOE_FMT_MXFP4) {
+    const float s = e8m0_to_f32(ssrc[tile * 64 + lane]);
+    for (int i = 0; i < 32; ++i) o[c0 + i] = v[i] * s;
+  } else {
+    const float g = which == 0 ? bv.g_gate : (which == 1 ? bv.g_up : bv.g_down);
+    const float s0 = e4m3_to_f32(ssrc[tile * 128 + 2 * lane]), s1 = e4m3_to_f32(ssrc[tile * 128 + 2 * lane + 1]);
+    for (int i = 0; i < 32; ++i) o[c0 + i] = (v[i] * (i < 16 ? s0 : s1)) * g;
+  }
+}
+
+}  // namespace
+
+extern "C" size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a) {
+  if (!a) return 0;
+  return ws_layout(a).total;
+}
+
+extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream) {
+  moe_status st = check_args(a);
+  if (st != MOE_OK || a->T == 0) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  FfnParams P{};
+  P.T = a->T; P.k = a->k; P.E = a->E; P.H = a->H; P.I = a->I; P.fmt = a->wfmt;
+  P.x = a->x; P.counts = a->counts; P.offsets = a->offsets; P.perm = a->perm;
+  P.slot_of_expert = a->slot_of_expert;
+  P.slot_pool = static_cast<const uint8_t*>(a->slot_pool);
+  P.slot_stride = a->slot_stride;
+  P.shared_blob = static_cast<const uint8_t*>(a->shared_blob);
+  P.mask = a->expert_mask;
+  layout_of(a->wfmt, a->H, a->I, &P.L);
+  P.umax = (int)std::min<long long>(a->E, (long long)a->T * a->k);
+
+  const WsLayout w = ws_layout(a);
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  float* y = a->y ? a->y : reinterpret_cast<float*>(ws + w.y);
+  hipError_t e;
+  const Path path = choose_path(a);
+  if (path == kPathGemv) {
+    e = launch_gemv(P, reinterpret_cast<float*>(ws + w.h), y, s);
+  } else {
+    MfmaBufs B{};
+    B.y = y;
+    if (path == kPathMfmaFp4) {
+      B.xq = ws + w.xq; B.xs = ws + w.xs; B.hq = ws + w.hq; B.hs = ws + w.hs;
+    } else {
+      B.hb = reinterpret_cast<uint16_t*>(ws + w.hb);
+    }
+    e = launch_mfma(P, path == kPathMfmaFp4, B, s);
+  }
+  if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: launch failed: %s", hipGetErrorString(e));
+  if (a->out) {
+    const float* ysh = a->shared_blob ? y + (size_t)a->T * a->k * a->H : nullptr;
+    e = launch_combine(y, a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
+    if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_combine(const float* y, const int32_t* inv, const float* topk_w, const float* y_shared, int T,
+                                  int k, int H, uint16_t* out, moe_stream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && k >= 1 && H > 0 && H % 8 == 0, "moe_combine: bad sizes T=%d k=%d H=%d (H %% 8 == 0)", T, k, H);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(y && inv && topk_w && out, "moe_combine: null pointer");
+  MOE_CHECK_ARG(((uintptr_t)y & 15) == 0 && ((uintptr_t)out & 15) == 0 && (!y_shared || ((uintptr_t)y_shared & 15) == 0),
+                "moe_combine: y, y_shared and out must be 16-byte aligned");
+  hipError_t e = launch_combine(y, inv, topk_w, y_shared, T, k, H, out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(MOE_EHIP, "moe_combine: launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_quantize_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s,
+                                         moe_stream_t stream) {
+  MOE_CHECK_ARG(rows >= 0 && cols > 0 && cols % 32 == 0, "moe_quantize_mxfp4: bad sizes rows=%d cols=%d", rows, cols);
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK_ARG(x && q && s, "moe_quantize_mxfp4: null pointer");
+  MOE_CHECK_ARG(((uintptr_t)x & 15) == 0 && ((uintptr_t)q & 15) == 0, "moe_quantize_mxfp4: x and q need 16-byte alignment");
+  hipError_t e = launch_quant_mxfp4(x, rows, cols, q, s, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(MOE_EHIP, "moe_quantize_mxfp4: launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_dequant_blob(const void* blob, int which, float* out, moe_stream_t stream) {
+  MOE_CHECK_ARG(blob && out && which >= 0 && which <= 2, "moe_dequant_blob: bad arguments");
+  // The header lives in device memory; read it back synchronously (debug entry only).
+  BlobHeader h;
+  MOE_HIP(hipMemcpy(&h, blob, sizeof h, hipMemcpyDeviceToHost));
+  MOE_CHECK_ARG(h.magic == kBlobMagic, "moe_dequant_blob: not a blob (magic %08x)", h.magic);
+  BlobLayout L;
+  MOE_CHECK_ARG(layout_of(h.fmt, h.H, h.I, &L), "moe_dequant_blob: bad header");
+  const int rows = which == 2 ? h.H : h.I, cols = which == 2 ? h.I : h.H;
+  const long long nfrag = (long long)(rows / 16) * (cols / k_per_tile(h.fmt)) * 64;
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)((nfrag + 255) / 256)), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint8_t*>(blob), L, h.fmt, which, h.H,
+                     h.I, out);
+  MOE_LAUNCHED();
+  return MOE_OK;
+}

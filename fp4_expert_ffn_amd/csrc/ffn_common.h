@@ -1,0 +1,137 @@
+// Shared device helpers for the expert-FFN kernels (GEMV and MFMA paths).
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// Everything a FFN kernel needs to find its expert, its rows and its weights.
+struct FfnParams {
+  int T, k, E, H, I, fmt;
+  const uint16_t* x;           // [T, H] bf16
+  const int32_t* counts;       // [E]
+  const int32_t* offsets;      // [E+1]
+  const int32_t* perm;         // [T*k]
+  const int32_t* slot_of_expert;
+  const uint8_t* slot_pool;
+  size_t slot_stride;
+  const uint8_t* shared_blob;  // nullable
+  const uint8_t* mask;         // nullable [E]
+  BlobLayout L;
+  int umax;                    // routed active-expert indices covered by the grid
+};
+
+// Workspace buffers of the matrix-core path.
+struct MfmaBufs {
+  const uint8_t* xq;   // FP4 gate/up A operand: [T][H/2] codes
+  const uint8_t* xs;   //                        [T][H/32] E8M0
+  uint8_t* hq;         // FP4 SwiGLU output: [R][I/2] codes
+  uint8_t* hs;         //                    [R][I/32] E8M0
+  uint16_t* hb;        // BF16 SwiGLU output: [R][I]
+  float* y;            // expert outputs: [R][H] fp32, perm order
+};
+
+// One unit of expert work: an expert (or the shared expert) and its rows.
+struct Job {
+  const uint8_t* blob;
+  int rows;    // number of rows
+  int p0;      // first row index in the perm-ordered h / y buffers
+  int shared;  // 1 for the shared expert (row r is token r)
+};
+
+// Resolve active-expert index `a` (ascending expert id among experts with
+// rows and an enabled mask; a == umax is the shared expert).  Must be called
+// by every thread of the workgroup (uses LDS and a barrier).  rows == 0 means
+// "nothing to do".
+__device__ inline Job resolve_job(const FfnParams& P, int a) {
+  __shared__ int s_e;
+  Job j;
+  j.blob = nullptr;
+  j.rows = 0;
+  j.p0 = 0;
+  j.shared = 0;
+  if (a == P.umax) {
+    if (P.shared_blob) {
+      j.blob = P.shared_blob;
+      j.rows = P.T;
+      j.p0 = P.T * P.k;
+      j.shared = 1;
+    }
+    return j;  // uniform across the workgroup: no barrier needed
+  }
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int found = -1, seen = 0;
+    for (int base = 0; base < P.E && found < 0; base += 64) {
+      const int e = base + lane;
+      bool act = false;
+      if (e < P.E) act = P.counts[e] > 0 && (P.mask == nullptr || P.mask[e] != 0);
+      const uint64_t b = __ballot(act);
+      const int n = __popcll(b);
+      if (a < seen + n) {
+        // the (a - seen)-th set bit of b
+        uint64_t bb = b;
+        for (int i = 0; i < a - seen; ++i) bb &= bb - 1;
+        found = base + __ffsll((unsigned long long)bb) - 1;
+      }
+      seen += n;
+    }
+    if (lane == 0) s_e = found;
+  }
+  __syncthreads();
+  const int e = s_e;
+  if (e >= 0) {
+    j.rows = P.counts[e];
+    j.p0 = P.offsets[e];
+    j.blob = P.slot_pool + (size_t)P.slot_of_expert[e] * P.slot_stride;
+  }
+  return j;
+}
+
+__device__ __forceinline__ int job_token(const FfnParams& P, const Job& j, int r) {
+  return j.shared ? r : P.perm[j.p0 + r] / P.k;
+}
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// 32 E2M1 codes (16 bytes) -> 16 packed bf16 pairs (exact; scale applied later).
+__device__ __forceinline__ void fp4x32_to_bf16(const uint4 c, bf16x2_t out[16]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    out[4 * d + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 0);
+    out[4 * d + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 1);
+    out[4 * d + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 2);
+    out[4 * d + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 3);
+  }
+}
+
+// 32 E2M1 codes -> 32 floats (exact).
+__device__ __forceinline__ void fp4x32_to_f32(const uint4 c, float out[32]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 0);
+    f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 1);
+    f32x2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 2);
+    f32x2_t d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[d], 1.0f, 3);
+    out[8 * d + 0] = a.x; out[8 * d + 1] = a.y;
+    out[8 * d + 2] = b.x; out[8 * d + 3] = b.y;
+    out[8 * d + 4] = c2.x; out[8 * d + 5] = c2.y;
+    out[8 * d + 6] = d2.x; out[8 * d + 7] = d2.y;
+  }
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+}  // namespace moe

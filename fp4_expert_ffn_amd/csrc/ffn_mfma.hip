@@ -1,0 +1,410 @@
+// Prefill path of the expert FFN: a grouped GEMM over (expert, 128-row tile,
+// 128-column tile) work items on the gfx950 matrix cores.
+//
+//   FP4 : v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1 and one
+//         E8M0 scale per 32 K-values per row (MXFP4 weights x MXFP4 activations;
+//         x and the SwiGLU output are MXFP4-encoded per row, blocks of 32).
+//   BF16: v_mfma_f32_16x16x32_bf16 (BF16 weights x bf16 activations; the
+//         SwiGLU output is rounded to bf16 before the down projection).
+//
+// Method: the expert FFN of a sparse MoE layer (pages as for the GEMV path);
+// the activation precision of the FP4 path is this library's reading of a
+// 4-bit-weight GEMM on FP4 matrix cores.
+//
+// Workgroup: 256 threads = 4 waves in a 2x2 grid, each wave 64 rows x 64 cols
+// (4x4 MFMA 16x16 tiles).  K-steps of 128 (FP4) or 64 (BF16) are staged
+// global -> registers -> LDS with the next step's loads in flight during the
+// current step's MFMAs.  Tiles are listed expert by expert, column tile by
+// column tile, row tile fastest, and each XCD takes a contiguous range of the
+// list, so row tiles of a hot expert that share weights run on one L2.
+#include <algorithm>
+
+#include "ffn_common.h"
+
+namespace moe {
+
+constexpr int kBM = 128, kBN = 128;
+
+// ---------------------------------------------------------------- activation quantiser
+
+// floor(log2|v|) of a finite nonzero fp32 value (exact, from the bits).
+__device__ __forceinline__ int ilog2_f32(float v) {
+  const uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
+  const int e = (int)(u >> 23);
+  if (e) return e - 127;
+  return (31 - __clz(u)) - 149;  // subnormal: u * 2^-149
+}
+
+// |q| -> E2M1 magnitude code, round to nearest even, saturate at 6.
+__device__ __forceinline__ uint32_t e2m1_mag_rne(float a) {
+  uint32_t m;
+  if (a <= 0.25f) m = 0;
+  else if (a < 0.75f) m = 1;
+  else if (a <= 1.25f) m = 2;
+  else if (a < 1.75f) m = 3;
+  else if (a <= 2.5f) m = 4;
+  else if (a < 3.5f) m = 5;
+  else if (a <= 5.0f) m = 6;
+  else m = 7;
+  return m;
+}
+
+// Encode 32 fp32 values as MXFP4: 16 packed bytes (element 2i low nibble) + E8M0.
+__device__ __forceinline__ void mxfp4_encode32(const float* v, uint4& q, uint32_t& s) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int ex = 0;
+  if (amax != 0.f) ex = min(127, max(-127, ilog2_f32(amax) - 2));
+  s = (uint32_t)(ex + 127);
+  // 2^-ex as an exact fp32 (normal for ex in [-127, 126]; subnormal 2^-127 for ex = 127)
+  const float inv = ex == 127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(127 - ex) << 23);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float qv = v[i] * inv;
+    const uint32_t code = e2m1_mag_rne(fabsf(qv)) | ((__float_as_uint(v[i]) >> 28) & 8u);
+    w[i >> 3] |= code << (4 * (i & 7));
+  }
+  q = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// x [rows, cols] bf16 -> q [rows, cols/2], s [rows, cols/32]; one thread per 32-block.
+__global__ __launch_bounds__(256) void k_quant_mxfp4(const uint16_t* __restrict__ x, int rows, int cols,
+                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int nb = cols / 32;
+  if (b >= (long long)rows * nb) return;
+  const long long r = b / nb;
+  const int c = (int)(b % nb);
+  const uint4* src = reinterpret_cast<const uint4*>(x + r * cols + c * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = src[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+  uint4 qq;
+  uint32_t ss;
+  mxfp4_encode32(v, qq, ss);
+  *reinterpret_cast<uint4*>(q + r * (cols / 2) + c * 16) = qq;
+  s[r * nb + c] = (uint8_t)ss;
+}
+
+hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st) {
+  const long long n = (long long)rows * (cols / 32);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quant_mxfp4, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, rows, cols, q, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- tile scheduling
+
+struct TileJob {
+  const uint8_t* blob;
+  int rows;    // valid rows in this tile (0: no work)
+  int p0;      // perm-order row index of the tile's first row
+  int shared;
+  int m0;      // first row of the tile within the expert
+  int nt;      // column tile
+};
+
+// Every thread of the workgroup must call this (LDS + barriers).
+__device__ inline TileJob find_tile(const FfnParams& P, int NT) {
+  __shared__ int pre[1024 + 2];
+  __shared__ int s_info[4];
+  TileJob tj{};
+  const int tid = threadIdx.x;
+  const int E = P.E;
+  if (tid < 64) {
+    int run = 0;
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + tid;
+      int t = 0;
+      if (e < E) {
+        const int c = P.counts[e];
+        if (c > 0 && (P.mask == nullptr || P.mask[e] != 0)) t = ((c + kBM - 1) / kBM) * NT;
+      }
+      // inclusive wave scan
+      int v = t;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o);
+        if (tid >= o) v += u;
+      }
+      if (e < E) pre[e + 1] = run + v;
+      run += __shfl(v, 63);
+    }
+    if (tid == 0) pre[0] = 0;
+  }
+  __syncthreads();
+  const int routed = pre[E];
+  const int shared_tiles = P.shared_blob ? ((P.T + kBM - 1) / kBM) * NT : 0;
+  const int total = routed + shared_tiles;
+  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous range.
+  const int per = (total + 7) / 8;
+  const int b = blockIdx.x;
+  const int L = (b % 8) * per + b / 8;
+  if (b / 8 >= per || L >= total) return tj;  // rows == 0
+  if (L >= routed) {
+    const int local = L - routed, mtn = (P.T + kBM - 1) / kBM;
+    tj.blob = P.shared_blob;
+    tj.shared = 1;
+    tj.nt = local / mtn;
+    tj.m0 = (local % mtn) * kBM;
+    tj.p0 = P.T * P.k;
+    tj.rows = min(kBM, P.T - tj.m0);
+    return tj;
+  }
+  // binary search: expert e with pre[e] <= L < pre[e+1]
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= L) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const int c = P.counts[e], mt_n = (c + kBM - 1) / kBM, local = L - pre[e];
+  tj.blob = P.slot_pool + (size_t)P.slot_of_expert[e] * P.slot_stride;
+  tj.nt = local / mt_n;
+  tj.m0 = (local % mt_n) * kBM;
+  tj.p0 = P.offsets[e];
+  tj.rows = min(kBM, c - tj.m0);
+  (void)s_info;
+  return tj;
+}
+
+// ---------------------------------------------------------------- the grouped GEMM
+
+enum { kGateUp = 0, kDown = 1 };
+
+template <bool FP4, int MODE>
+__global__ __launch_bounds__(256) void k_mfma_ffn(FfnParams P, MfmaBufs B) {
+  const int K = MODE == kGateUp ? P.H : P.I;
+  const int NT = MODE == kGateUp ? (2 * P.I) / kBN : P.H / kBN;
+  const TileJob tj = find_tile(P, NT);
+  if (tj.rows == 0) return;
+
+  constexpr int KSTEP = FP4 ? 128 : 64;
+  constexpr int NCH = FP4 ? 2 : 4;  // 16-byte chunks per thread per operand per K-step
+  __shared__ __align__(16) uint8_t lds[32768 + 1024];
+  uint4* As = reinterpret_cast<uint4*>(lds);           // FP4 [8][64]; BF16 [8][2][64]
+  uint4* Bs = reinterpret_cast<uint4*>(lds + 16384);   // same shapes
+  uint8_t* Asc = lds + 32768;                          // FP4 [8][64]
+  uint8_t* Bsc = lds + 32768 + 512;                    // FP4 [8][64]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const BlobView bv = blob_view(tj.blob, P.L);
+  const uint8_t* wt = MODE == kGateUp ? bv.w13 : bv.w2;
+  const uint8_t* st = MODE == kGateUp ? bv.s13 : bv.s2;
+  const int nk_w = K / (FP4 ? 128 : 32);  // weight K-tiles per row-group
+  const int rg0 = tj.nt * 8;              // first 16-row group of the column tile
+
+  // Rows this thread stages for operand A, and their source pointers.
+  const uint8_t* arow[NCH];
+  const uint8_t* asrow[NCH];
+  bool aval[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    int row;
+    if (FP4) row = ((tid >> 6) + 4 * i) * 16 + (tid & 15);
+    else row = ((tid >> 7) + 2 * i) * 16 + (tid & 15);
+    aval[i] = row < tj.rows;
+    const int r = aval[i] ? row : 0;
+    if (MODE == kGateUp) {
+      const int t = tj.shared ? tj.m0 + r : P.perm[tj.p0 + tj.m0 + r] / P.k;
+      if (FP4) {
+        arow[i] = B.xq + (size_t)t * (P.H / 2);
+        asrow[i] = B.xs + (size_t)t * (P.H / 32);
+      } else {
+        arow[i] = reinterpret_cast<const uint8_t*>(P.x + (size_t)t * P.H);
+        asrow[i] = nullptr;
+      }
+    } else {
+      const size_t p = (size_t)tj.p0 + tj.m0 + r;
+      if (FP4) {
+        arow[i] = B.hq + p * (P.I / 2);
+        asrow[i] = B.hs + p * (P.I / 32);
+      } else {
+        arow[i] = reinterpret_cast<const uint8_t*>(B.hb + p * P.I);
+        asrow[i] = nullptr;
+      }
+    }
+  }
+
+  uint4 ra[NCH], rb[NCH];
+  uint8_t rsa[NCH], rsb[NCH];
+  auto load_stage = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + 256 * i;
+      if (FP4) {
+        const int kb = (c & 63) >> 4;  // 32-value block within the 128-wide K-tile
+        ra[i] = aval[i] ? *reinterpret_cast<const uint4*>(arow[i] + ks * 64 + kb * 16) : make_uint4(0, 0, 0, 0);
+        rsa[i] = aval[i] ? asrow[i][ks * 4 + kb] : (uint8_t)127;
+        const int j = c >> 6, l = c & 63;
+        const size_t tile = (size_t)(rg0 + j) * nk_w + ks;
+        rb[i] = *reinterpret_cast<const uint4*>(wt + tile * kTileBytes + l * 16);
+        rsb[i] = st[tile * 64 + l];
+      } else {
+        const int kts = (c >> 6) & 1, l = c & 63;
+        const int kcol = (ks * 2 + kts) * 32 + (l >> 4) * 8;  // bf16 element column
+        ra[i] = aval[i] ? *reinterpret_cast<const uint4*>(arow[i] + (size_t)kcol * 2) : make_uint4(0, 0, 0, 0);
+        const int j = c >> 7;
+        const size_t tile = (size_t)(rg0 + j) * nk_w + ks * 2 + kts;
+        rb[i] = *reinterpret_cast<const uint4*>(wt + tile * kTileBytes + l * 16);
+      }
+    }
+  };
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + 256 * i;
+      As[c] = ra[i];
+      Bs[c] = rb[i];
+      if (FP4) {
+        Asc[c] = rsa[i];
+        Bsc[c] = rsb[i];
+      }
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = K / KSTEP;
+  load_stage(0);
+  for (int ks = 0; ks < nsteps; ++ks) {
+    store_stage();
+    __syncthreads();
+    if (ks + 1 < nsteps) load_stage(ks + 1);
+    if (FP4) {
+      i32x8_t a[4], b[4];
+      int sa[4], sb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = As[(4 * wm + i) * 64 + lane];
+        a[i] = i32x8_t{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+        sa[i] = Asc[(4 * wm + i) * 64 + lane];
+        const uint4 v = Bs[(4 * wn + i) * 64 + lane];
+        b[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        sb[i] = Bsc[(4 * wn + i) * 64 + lane];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 0, sa[i], 0,
+                                                                        sb[j]);
+    } else {
+#pragma unroll
+      for (int kts = 0; kts < 2; ++kts) {
+        bf16x8_t a[4], b[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[i] = __builtin_bit_cast(bf16x8_t, As[((4 * wm + i) * 2 + kts) * 64 + lane]);
+          b[i] = __builtin_bit_cast(bf16x8_t, Bs[((4 * wn + i) * 2 + kts) * 64 + lane]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------ epilogues
+  const int col = lane & 15, rq = (lane >> 4) * 4;
+  if (MODE == kDown) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = (4 * wm + i) * 16 + rq + v;
+        if (row < tj.rows) {
+          float* yr = B.y + ((size_t)tj.p0 + tj.m0 + row) * P.H + tj.nt * kBN + (4 * wn) * 16 + col;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][v];
+        }
+      }
+    return;
+  }
+  // gate/up: column tile holds 4 (gate, up) pairs of 16 rows: pair q = 4 nt + 2 wn + jj
+  float* ht = reinterpret_cast<float*>(lds);  // [128][64] fp32 (aliases the staging buffers)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = (4 * wm + i) * 16 + rq + v;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const float g = acc[i][2 * jj][v], u = acc[i][2 * jj + 1][v];
+        ht[row * 64 + (2 * wn + jj) * 16 + col] = silu_f32(g) * u;
+      }
+    }
+  __syncthreads();
+  const int row = tid >> 1, blk = tid & 1;  // 128 rows x 2 blocks of 32 columns
+  if (row < tj.rows) {
+    const size_t p = (size_t)tj.p0 + tj.m0 + row;
+    const float* hv = ht + row * 64 + blk * 32;
+    const int c0 = tj.nt * 64 + blk * 32;  // intermediate column of the block
+    if (FP4) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = hv[i];
+      uint4 q;
+      uint32_t s;
+      mxfp4_encode32(v, q, s);
+      *reinterpret_cast<uint4*>(B.hq + p * (P.I / 2) + c0 / 2) = q;
+      B.hs[p * (P.I / 32) + c0 / 32] = (uint8_t)s;
+    } else {
+      uint16_t* dst = B.hb + p * P.I + c0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = (uint32_t)f32_to_bf16_rne(hv[8 * q + 2 * j]) | ((uint32_t)f32_to_bf16_rne(hv[8 * q + 2 * j + 1]) << 16);
+        reinterpret_cast<uint4*>(dst)[q] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+}
+
+// Upper bound on the number of work tiles of one launch.
+static int max_tiles(const FfnParams& P, int NT) {
+  const long long rows = (long long)P.T * P.k;
+  long long mt = (rows + kBM - 1) / kBM + std::min<long long>(P.E, rows);
+  if (P.shared_blob) mt += (P.T + kBM - 1) / kBM;
+  long long g = mt * NT;
+  g = (g + 7) / 8 * 8;
+  return (int)g;
+}
+
+hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s) {
+  const int nt_gu = (2 * P.I) / kBN, nt_dn = P.H / kBN;
+  if (fp4) {
+    hipError_t e = launch_quant_mxfp4(P.x, P.T, P.H, const_cast<uint8_t*>(B.xq), const_cast<uint8_t*>(B.xs), s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mfma_ffn<true, kGateUp>), dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mfma_ffn<true, kDown>), dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
+  } else {
+    hipLaunchKernelGGL((k_mfma_ffn<false, kGateUp>), dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mfma_ffn<false, kDown>), dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,350 @@
+// Router logits, top-k routing with softmax weights, and the token->expert
+// permutation (gfx950, wave64).
+//
+// Method: a routing network selects a subset of experts for every token at
+// every step (page "FreeToken qwen：ローカルQwen MoEセットアップガイド", third
+// paragraph; page "FreeToken量子化：MoE推論のセットアップガイド", second
+// paragraph).  The selection rule (fp32 logit keys, ties to the lower id, NaN
+// lowest) and the softmax over the selected logits are this library's reading.
+#include "common.h"
+
+namespace {
+
+using namespace moe;
+
+// ------------------------------------------------------------------ router logits
+
+// Small T: one workgroup per expert, 256 threads split H; tokens in registers.
+constexpr int kRouterGemvMaxT = 16;
+
+__global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                                     int T, int H, int E, float* __restrict__ out) {
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float acc[kRouterGemvMaxT];
+#pragma unroll
+  for (int t = 0; t < kRouterGemvMaxT; ++t) acc[t] = 0.f;
+  const float* wr = w + (size_t)e * H;
+  for (int h = tid * 4; h < H; h += 256 * 4) {
+    float4 wv;
+    if ((H & 3) == 0) {  // rows are 16-byte aligned: one vector load
+      wv = *reinterpret_cast<const float4*>(wr + h);
+    } else {
+      wv.x = wr[h];
+      wv.y = h + 1 < H ? wr[h + 1] : 0.f;
+      wv.z = h + 2 < H ? wr[h + 2] : 0.f;
+      wv.w = h + 3 < H ? wr[h + 3] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < kRouterGemvMaxT; ++t) {
+      if (t < T) {
+        const uint16_t* xr = x + (size_t)t * H + h;
+        float x0 = bf16_to_f32(xr[0]);
+        float x1 = h + 1 < H ? bf16_to_f32(xr[1]) : 0.f;
+        float x2 = h + 2 < H ? bf16_to_f32(xr[2]) : 0.f;
+        float x3 = h + 3 < H ? bf16_to_f32(xr[3]) : 0.f;
+        acc[t] = fmaf(x0, wv.x, acc[t]);
+        acc[t] = fmaf(x1, wv.y, acc[t]);
+        acc[t] = fmaf(x2, wv.z, acc[t]);
+        acc[t] = fmaf(x3, wv.w, acc[t]);
+      }
+    }
+  }
+  __shared__ float red[4][kRouterGemvMaxT];
+#pragma unroll
+  for (int t = 0; t < kRouterGemvMaxT; ++t) {
+    float v = acc[t];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (lane == 0) red[wave][t] = v;
+  }
+  __syncthreads();
+  if (tid < T) out[(size_t)tid * E + e] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+}
+
+// Large T: LDS-tiled fp32 GEMM, 64 tokens x 64 experts per workgroup, K step 32.
+__global__ __launch_bounds__(256) void k_router_tiled(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                                      int T, int H, int E, float* __restrict__ out) {
+  constexpr int BT = 64, BE = 64, BK = 32;
+  __shared__ float xs[BK][BT + 4];
+  __shared__ float ws[BK][BE + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int t0 = blockIdx.y * BT, e0 = blockIdx.x * BE;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < H; k0 += BK) {
+    for (int i = tid; i < BT * BK; i += 256) {
+      const int r = i / BK, c = i % BK, t = t0 + r, h = k0 + c;
+      xs[c][r] = (t < T && h < H) ? bf16_to_f32(x[(size_t)t * H + h]) : 0.f;
+    }
+    for (int i = tid; i < BE * BK; i += 256) {
+      const int r = i / BK, c = i % BK, e = e0 + r, h = k0 + c;
+      ws[c][r] = (e < E && h < H) ? w[(size_t)e * H + h] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) out[(size_t)t * E + e] = acc[i][j];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ top-k + softmax
+
+// Order-preserving map of an fp32 logit to uint32: larger value -> larger key;
+// -0 is folded onto +0; every NaN maps to 0, below -inf (0x007FFFFF).
+__device__ __forceinline__ uint32_t rank_bits(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;  // NaN
+  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;             // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_rank_bits(uint32_t r) {
+  if (r == 0u) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float((r & 0x80000000u) ? (r & 0x7FFFFFFFu) : ~r);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
+    uint64_t u = ((uint64_t)hi << 32) | lo;
+    v = u > v ? u : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float unnorm(float v, float m) {
+  if (v != v) return 0.f;
+  if (v == m) return 1.f;
+  return expf(v - m);
+}
+
+constexpr int kRouteMaxPerLane = 16;  // E <= 1024
+constexpr int kRouteMaxK = 16;
+
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k, int renorm,
+                                               int32_t* __restrict__ ids, float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  uint32_t rk[kRouteMaxPerLane];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int i = 0; i < kRouteMaxPerLane; ++i) {
+    const int e = lane + 64 * i;
+    rk[i] = 0;
+    if (e < E) {
+      rk[i] = rank_bits(row[e]);
+      avail |= 1u << i;
+    }
+  }
+  int sel_id[kRouteMaxK];
+  float sel_v[kRouteMaxK];
+#pragma unroll
+  for (int j = 0; j < kRouteMaxK; ++j) {
+    sel_id[j] = 0;
+    sel_v[j] = 0.f;
+    if (j < k) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < kRouteMaxPerLane; ++i) {
+        if (avail & (1u << i)) {
+          const uint32_t e = (uint32_t)(lane + 64 * i);
+          const uint64_t key = ((uint64_t)rk[i] << 32) | (uint32_t)~e;
+          best = key > best ? key : best;
+        }
+      }
+      best = wave_max_u64(best);
+      const int e = (int)(~(uint32_t)best);
+      if ((e & 63) == lane) avail &= ~(1u << (e >> 6));
+      sel_id[j] = e;
+      sel_v[j] = from_rank_bits((uint32_t)(best >> 32));
+    }
+  }
+  const float m = sel_v[0];
+  float num[kRouteMaxK], den = 0.f;
+#pragma unroll
+  for (int j = 0; j < kRouteMaxK; ++j) {
+    num[j] = j < k ? unnorm(sel_v[j], m) : 0.f;
+    den += num[j];
+  }
+  if (!renorm) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRouteMaxPerLane; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) s += unnorm(row[e], m);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+    den = s;
+  }
+#pragma unroll
+  for (int j = 0; j < kRouteMaxK; ++j) {
+    if (j < k && lane == j) {
+      ids[(size_t)t * k + j] = sel_id[j];
+      wts[(size_t)t * k + j] = den > 0.f ? num[j] / den : 1.0f / (float)k;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ permutation
+
+// One workgroup of 1024 threads per chunk of 1024 flat indices.  Each
+// workgroup histograms all ids (total and before its chunk) in LDS, scans
+// the totals, and places its chunk: position = offsets[e] + (# of e before
+// the chunk) + (# of e in earlier waves of the chunk) + (rank within wave).
+constexpr int kPermChunk = 1024;
+constexpr int kPermWaves = kPermChunk / 64;
+
+__global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ ids, int N, int E,
+                                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  extern __shared__ int32_t sm[];
+  int32_t* tot = sm;                   // [E]
+  int32_t* before = sm + E;            // [E]
+  int32_t* wcnt = sm + 2 * E;          // [kPermWaves][E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * kPermChunk;
+  for (int i = tid; i < E * (2 + kPermWaves); i += kPermChunk) sm[i] = 0;
+  __syncthreads();
+  for (int f = tid; f < N; f += kPermChunk) {
+    const int e = ids[f];
+    if (e >= 0 && e < E) {
+      atomicAdd(&tot[e], 1);
+      if (f < c0) atomicAdd(&before[e], 1);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of tot -> offsets (kept in `before` as base = offset + before)
+  __shared__ int32_t scan_tmp[kPermChunk];
+  {
+    // each thread owns a contiguous run of ceil(E/1024) experts
+    const int per = (E + kPermChunk - 1) / kPermChunk;
+    int run = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = tid * per + i;
+      if (e < E) run += tot[e];
+    }
+    scan_tmp[tid] = run;
+    __syncthreads();
+    for (int o = 1; o < kPermChunk; o <<= 1) {
+      const int v = tid >= o ? scan_tmp[tid - o] : 0;
+      __syncthreads();
+      scan_tmp[tid] += v;
+      __syncthreads();
+    }
+    int base = scan_tmp[tid] - run;
+    for (int i = 0; i < per; ++i) {
+      const int e = tid * per + i;
+      if (e < E) {
+        if (blockIdx.x == 0) {
+          counts[e] = tot[e];
+          offsets[e] = base;
+        }
+        before[e] += base;
+        base += tot[e];
+      }
+    }
+    if (blockIdx.x == 0 && tid == kPermChunk - 1) offsets[E] = scan_tmp[tid];
+  }
+  // rank within the wave (wave-level match of equal ids)
+  const int f = c0 + tid;
+  const int e = f < N ? ids[f] : -1;
+  const bool valid = e >= 0 && e < E;
+  uint64_t todo = __ballot(valid);
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank = 0, cnt = 0;
+  bool leader = false;
+  while (todo) {
+    const int src = __ffsll((unsigned long long)todo) - 1;
+    const int key = __shfl(e, src);
+    const uint64_t m = __ballot(valid && e == key);
+    if (valid && e == key) {
+      rank = __popcll(m & lt);
+      cnt = __popcll(m);
+      leader = lane == src;
+    }
+    todo &= ~m;
+  }
+  __syncthreads();  // before[] final
+  if (leader) wcnt[wave * E + e] = cnt;
+  __syncthreads();
+  if (valid) {
+    int pos = before[e] + rank;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
+    perm[pos] = f;
+    inv[f] = pos;
+  }
+}
+
+}  // namespace
+
+extern "C" moe_status moe_router_logits(const uint16_t* x, const float* w_router, int T, int H, int E, float* logits,
+                                        moe_stream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && H >= 1 && E >= 1, "moe_router_logits: bad sizes T=%d H=%d E=%d", T, H, E);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(x && w_router && logits, "moe_router_logits: null pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T <= kRouterGemvMaxT) {
+    hipLaunchKernelGGL(k_router_gemv, dim3(E), dim3(256), 0, s, x, w_router, T, H, E, logits);
+  } else {
+    hipLaunchKernelGGL(k_router_tiled, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x, w_router, T, H, E,
+                       logits);
+  }
+  MOE_LAUNCHED();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_route(const float* logits, int T, int E, int k, int renormalize, int32_t* topk_ids,
+                                float* topk_w, moe_stream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && E >= 1 && E <= 1024, "moe_route: bad sizes T=%d E=%d (E <= 1024)", T, E);
+  MOE_CHECK_ARG(k >= 1 && k <= E && k <= kRouteMaxK, "moe_route: k=%d must be in [1, min(E, 16)]", k);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(logits && topk_ids && topk_w, "moe_route: null pointer");
+  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), logits, T, E, k,
+                     renormalize ? 1 : 0, topk_ids, topk_w);
+  MOE_LAUNCHED();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                                  int32_t* perm, int32_t* inv, moe_stream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && k >= 1 && E >= 1 && E <= 1024, "moe_permute: bad sizes T=%d k=%d E=%d", T, k, E);
+  const long long N = (long long)T * k;
+  MOE_CHECK_ARG(N <= (1 << 17), "moe_permute: T*k = %lld exceeds 131072", N);
+  MOE_CHECK_ARG(counts && offsets && (N == 0 || (topk_ids && perm && inv)), "moe_permute: null pointer");
+  const int blocks = N == 0 ? 1 : (int)((N + kPermChunk - 1) / kPermChunk);
+  const size_t lds = sizeof(int32_t) * (size_t)E * (2 + kPermWaves);
+  static bool attr_set = false;
+  if (!attr_set) {
+    MOE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_permute),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 8 * 1024));
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_permute, dim3(blocks), dim3(kPermChunk), lds, reinterpret_cast<hipStream_t>(stream),
+                     topk_ids, (int)N, E, counts, offsets, perm, inv);
+  MOE_LAUNCHED();
+  return MOE_OK;
+}

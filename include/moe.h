@@ -1,0 +1,230 @@
+/*
+ * libmoe — the sparse MoE layer of an expert-offloading inference engine,
+ * written for AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes.
+ *
+ * The method (FreeToken, as described on five web pages):
+ *   - a routing network picks a few experts for every token at every step
+ *     [page "FreeToken qwen：ローカルQwen MoEセットアップガイド", 3rd paragraph;
+ *      page "FreeToken量子化：MoE推論のセットアップガイド", 2nd paragraph];
+ *   - host RAM holds every routed expert and the GPU keeps one expert cache
+ *     shared by all MoE layers; in decode the cache is an LRU over recently
+ *     selected experts, a hit runs on the GPU and a miss is brought over PCIe
+ *     [page "FreeToken量子化：...", paragraphs on the two-tier expert memory
+ *      hierarchy and on decode; bhrtaym-blog page, section
+ *      "MoEバックエンドは4種類から選べる", backend table, row "offload"];
+ *   - expert weights come as MXFP4, NVFP4 or BF16 checkpoints
+ *     [page "FreeToken量子化：...", 3rd paragraph; page "VRAM高騰時代の救世主? ...",
+ *      section "FreeTokenとは何か", bullet on formats].
+ * The pages give no layer-level API and no formulas; the calls below follow
+ * their statement of the problem and the standard definitions (top-k softmax
+ * router, SwiGLU expert, OCP MX / OFP8 formats).
+ *
+ * Conventions (all calls):
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns
+ *     every buffer.  No call allocates device memory except
+ *     moe_cache_create (host metadata and HIP events only).
+ *   - bf16 tensors are passed as uint16_t bit patterns; row-major.
+ *   - Every call returns moe_status.  Only host-visible arguments are
+ *     validated; device contents (ids out of range, ...) are not.  On a
+ *     non-OK status nothing was enqueued and moe_last_error() describes the
+ *     problem.  Asynchronous HIP failures surface as MOE_EHIP on a later call.
+ *   - Calls taking a hipStream_t only enqueue work on that stream (no host
+ *     synchronisation) unless stated otherwise.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* moe_stream_t; /* == hipStream_t */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* bad dimension, null pointer, bad enum          */
+  MOE_EUNSUPPORTED = 2,  /* valid but unsupported combination               */
+  MOE_EHIP = 3,          /* a HIP runtime call failed                       */
+  MOE_ENOMEM = 4,        /* workspace too small / host allocation failed     */
+  MOE_ECACHE = 5         /* a step needs more distinct experts than slots    */
+} moe_status;
+
+typedef enum { MOE_FMT_BF16 = 0, MOE_FMT_MXFP4 = 1, MOE_FMT_NVFP4 = 2 } moe_wfmt;
+typedef enum { MOE_ACT_BF16 = 0, MOE_ACT_MXFP4 = 1 } moe_amode;
+
+/* Thread-local description of the last non-OK status of this thread. */
+const char* moe_last_error(void);
+const char* moe_version(void);
+
+/* ------------------------------------------------------------------ routing */
+
+/* Router logits: logits[t,e] = sum_h x[t,h] * w_router[e,h], fp32 accumulation.
+ * [page "FreeToken qwen：...", 3rd paragraph: a routing network selects a
+ *  subset of experts per step.]
+ * x: [T,H] bf16; w_router: [E,H] fp32; logits: [T,E] fp32.
+ * Requires T >= 0, H >= 1, 1 <= E. */
+moe_status moe_router_logits(const uint16_t* x, const float* w_router, int T, int H, int E,
+                             float* logits, moe_stream_t stream);
+
+/* Top-k routing with softmax weights.
+ * [pages as for moe_router_logits; the selection rule is this library's
+ *  reading: keys are the fp32 logits, larger first, ties to the lower expert
+ *  id, NaN below -inf; ids of a row are written in rank order.]
+ * renormalize=1: w_j = exp(l_j - m) / sum over the k selected (m = top logit);
+ * renormalize=0: the softmax over all E experts, at the selected ids.
+ * exp(l - m) is taken as 1 where l == m and 0 where l is NaN; a row whose
+ * weights would all be 0 gets 1/k each.
+ * logits: [T,E] fp32; topk_ids: [T,k] int32; topk_w: [T,k] fp32.
+ * Requires 1 <= k <= min(E, 16), E <= 1024, T >= 0. */
+moe_status moe_route(const float* logits, int T, int E, int k, int renormalize,
+                     int32_t* topk_ids, float* topk_w, moe_stream_t stream);
+
+/* Token -> expert permutation: a stable counting sort of the T*k flat
+ * indices f = t*k + j by expert id (ties in ascending f).
+ * counts: [E]; offsets: [E+1] (exclusive scan, offsets[E] = T*k);
+ * perm: [T*k] (perm[p] = flat index at sorted position p);
+ * inv: [T*k] (inv[perm[p]] = p).  topk_ids values must lie in [0, E).
+ * Requires E <= 1024, T*k <= 2^24. */
+moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, int32_t* inv, moe_stream_t stream);
+
+/* ------------------------------------------------------------- expert FFN */
+
+/* Prepacked expert ("slot blob") layout, shared by the host bank and the HBM
+ * slots: a 256-byte header, then gate/up and down weights and scales in the
+ * tile order the kernels stream.  See moe_blob_bytes / moe_prepack_expert. */
+typedef struct {
+  int32_t fmt;            /* moe_wfmt                                         */
+  int32_t H, I;           /* hidden, intermediate; both multiples of 128      */
+  /* canonical row-major tensors (host): gate, up [I,H]; down [H,I]
+   *   BF16 : w_* = uint16 bf16 bits [rows, cols]
+   *   MXFP4: q_* = E2M1 codes [rows, cols/2] (element 2i in the low nibble),
+   *          s_* = E8M0 codes [rows, cols/32]
+   *   NVFP4: q_* as MXFP4, s_* = E4M3FN codes [rows, cols/16],
+   *          g_* = per-tensor dequant multiplier (w = E2M1 * E4M3 * g)     */
+  const void* gate_q; const uint8_t* gate_s; float gate_g;
+  const void* up_q;   const uint8_t* up_s;   float up_g;
+  const void* down_q; const uint8_t* down_s; float down_g;
+} moe_expert_canonical;
+
+/* Bytes of one expert blob for (fmt, H, I); 0 if the shape is unsupported. */
+size_t moe_blob_bytes(int fmt, int H, int I);
+
+/* Host-side prepack of one expert into blob_out (host, >= moe_blob_bytes).
+ * A bijection of the canonical tensors (round-trip tested). */
+moe_status moe_prepack_expert(const moe_expert_canonical* src, void* blob_out, size_t blob_bytes);
+
+/* Arguments of one expert-FFN call (SwiGLU: y = W_down (silu(W_gate x) * (W_up x))).
+ * [page "FreeToken量子化：...", decode paragraph: cached experts execute on the
+ *  GPU; the expert form is this library's reading (SwiGLU, no bias).] */
+typedef struct {
+  int T, k, E, H, I;            /* tokens, top-k, routed experts, hidden, intermediate */
+  int wfmt;                     /* moe_wfmt of every blob (routed and shared)            */
+  int amode;                    /* MOE_ACT_BF16: activations stay bf16 / fp32.
+                                   MOE_ACT_MXFP4 (wfmt MXFP4 only): x and the SwiGLU output
+                                   are MXFP4-encoded per row per 32 values and the products
+                                   run on the block-scaled FP4 matrix cores.               */
+  const uint16_t* x;            /* [T,H] bf16                                            */
+  const int32_t* counts;        /* [E]    from moe_permute                               */
+  const int32_t* offsets;       /* [E+1]  from moe_permute                               */
+  const int32_t* perm;          /* [T*k]  from moe_permute                               */
+  const int32_t* slot_of_expert;/* [E]    slot index of each routed expert's blob        */
+  const void* slot_pool;        /* base of the slots; blob of expert e at
+                                   slot_pool + slot_of_expert[e] * slot_stride           */
+  size_t slot_stride;           /* bytes, >= moe_blob_bytes, multiple of 256             */
+  const void* shared_blob;      /* nullable: always-on shared expert (same fmt, H, I),
+                                   weight 1, added after the routed sum                  */
+  const uint8_t* expert_mask;   /* nullable: [E]; if set only experts with mask[e] != 0
+                                   run (lets hits run while misses are still copying)    */
+  float* y;                     /* nullable: [T*k (+T if shared)][H] fp32 expert outputs
+                                   in perm order (shared rows last).  If null, y lives in
+                                   the workspace.                                        */
+  const float* topk_w;          /* nullable with out: [T,k] routing weights              */
+  const int32_t* inv;           /* nullable with out: [T*k] from moe_permute             */
+  uint16_t* out;                /* nullable: [T,H] bf16; if set, the combine runs too    */
+  void* workspace;              /* device scratch, >= moe_expert_ffn_workspace_size      */
+  size_t workspace_bytes;
+} moe_ffn_args;
+
+/* Bytes of device workspace a call with these dimensions needs. */
+size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a);
+
+/* Grouped expert FFN over every expert with at least one row (and the shared
+ * expert).  Small batches run a dequantising GEMV that streams each touched
+ * expert's weights once; large batches run a grouped GEMM on the matrix cores
+ * (bf16 MFMA for BF16 weights, block-scaled FP4 MFMA for MXFP4 with amode
+ * MXFP4).  Requires H, I multiples of 128, 1 <= k <= 16, E <= 1024. */
+moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream);
+
+/* Weighted combine back to token order:
+ * out[t,:] = bf16( sum_{j=0..k-1} topk_w[t,j] * y[inv[t*k+j],:]  (+ y_shared[t,:]) ).
+ * y: [T*k][H] fp32 in perm order; y_shared: nullable [T][H] fp32. */
+moe_status moe_combine(const float* y, const int32_t* inv, const float* topk_w, const float* y_shared,
+                       int T, int k, int H, uint16_t* out, moe_stream_t stream);
+
+/* MXFP4 encoding of bf16 activations, per row per 32 values (the activation
+ * quantiser of the FP4 matrix-core path): shared exponent floor(log2 amax)-2
+ * (E8M0, 127 for an all-zero block), elements round-to-nearest-even on the
+ * E2M1 grid, saturating at 6, sign from the input.
+ * x: [rows, cols] bf16; q: [rows, cols/2] bytes (element 2i low nibble);
+ * s: [rows, cols/32] E8M0.  cols % 32 == 0. */
+moe_status moe_quantize_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s,
+                              moe_stream_t stream);
+
+/* Debug: dequantise projection `which` (0 gate, 1 up, 2 down) of a device blob
+ * into out [rows, cols] fp32 (canonical order).  Used by the bit-exact tests. */
+moe_status moe_dequant_blob(const void* blob, int which, float* out, moe_stream_t stream);
+
+/* ------------------------------------------------------- expert-slot cache */
+
+/* The HBM expert cache: num_slots slots of slot_bytes each, in a device
+ * buffer owned by the caller, shared by num_layers layers of num_experts
+ * experts.  Keys are (layer, expert) = layer*num_experts + expert.
+ * [page "FreeToken量子化：...", hierarchy and decode paragraphs; bhrtaym-blog
+ *  page, backend table row "offload".]  The cache holds host metadata and
+ * HIP events only.  One cache per host thread.  Returns NULL on bad
+ * arguments (see moe_last_error). */
+typedef struct moe_cache moe_cache;
+moe_cache* moe_cache_create(int num_slots, size_t slot_bytes, void* slot_pool, int num_layers,
+                            int num_experts);
+void moe_cache_destroy(moe_cache* c);
+
+/* Look up the distinct, ascending expert ids (host) of one step of `layer`.
+ * Host-only and synchronous.  For each id: slot[i] (host), hit[i] (host,
+ * 1/0) and evicted_key[i] (host, the key whose slot a miss took, -1 if the
+ * slot was free or on a hit).  Every access makes its key most recent; a miss
+ * takes the lowest free slot, else evicts the least recently used key.  Keys
+ * of this call are never evicted by it.  n > num_slots returns MOE_ECACHE
+ * and leaves the state unchanged; unsorted / duplicate / out-of-range ids
+ * return MOE_EINVAL and leave the state unchanged. */
+moe_status cache_lookup(moe_cache* c, int layer, const int32_t* ids, int n, int32_t* slot,
+                        uint8_t* hit, int32_t* evicted_key);
+
+/* Fill `slot` with the blob of (layer, expert) from pinned host memory.
+ * Enqueues on copy_stream: wait until every compute-stream use of the slot
+ * recorded by moe_cache_mark_used has finished (write-after-read guard), then
+ * hipMemcpyAsync host->device of slot_bytes, then an event; then makes
+ * compute_stream wait on that event (read-after-write guard).  Compute work
+ * enqueued on compute_stream before this call may overlap the copy.
+ * host_src must be pinned (hipHostMalloc) and hold slot_bytes bytes. */
+moe_status cache_fill(moe_cache* c, int layer, int expert, int slot, const void* host_src,
+                      moe_stream_t copy_stream, moe_stream_t compute_stream);
+
+/* Record on compute_stream that slots[0..n) (host) are read by the work
+ * enqueued so far; a later cache_fill of one of them waits for that work. */
+moe_status moe_cache_mark_used(moe_cache* c, const int32_t* slots, int n, moe_stream_t compute_stream);
+
+/* Reset the cache to the empty state (host metadata only). */
+moe_status moe_cache_reset(moe_cache* c);
+
+/* Pre-fill bookkeeping for a fully resident layer: key (layer, e) -> slot s0 + e
+ * for e in [0, num_experts); no copy is made (the caller placed the blobs). */
+moe_status moe_cache_pin_resident(moe_cache* c, int layer, int s0);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */
