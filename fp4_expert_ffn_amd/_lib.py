@@ -56,11 +56,14 @@ SIGNATURES = {
     "moe_router_logits": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
     "moe_route": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp]),
     "moe_permute": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_permute": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_blob_bytes": (_sz, [_i, _i, _i]),
     "moe_prepack_expert": (_i, [ctypes.POINTER(ExpertCanonical), _vp, _sz]),
     "moe_expert_ffn_workspace_size": (_sz, [ctypes.POINTER(FfnArgs)]),
     "moe_expert_ffn": (_i, [ctypes.POINTER(FfnArgs), _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
+    "moe_workspace_init": (_i, [_vp, _sz, _vp]),
+    "moe_workspace_check": (_i, [_vp, _vp]),
     "moe_quantize_mxfp4": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "moe_dequant_blob": (_i, [_vp, _i, _vp, _vp]),
     "moe_cache_create": (_vp, [_i, _sz, _vp, _i, _i]),
@@ -139,6 +142,11 @@ def moe_permute(topk_ids, T, k, E, counts, offsets, perm, inv, stream=None):
                              stream_handle(stream)), "moe_permute")
 
 
+def moe_route_permute(logits, T, E, k, renormalize, topk_ids, topk_w, counts, offsets, perm, inv, stream=None):
+    _check(lib().moe_route_permute(ptr(logits), T, E, k, int(renormalize), ptr(topk_ids), ptr(topk_w), ptr(counts),
+                                   ptr(offsets), ptr(perm), ptr(inv), stream_handle(stream)), "moe_route_permute")
+
+
 def moe_blob_bytes(fmt, H, I) -> int:
     return int(lib().moe_blob_bytes(FMT.get(fmt, fmt), H, I))
 
@@ -192,6 +200,14 @@ def moe_expert_ffn_workspace_size(args: FfnArgs) -> int:
 
 def moe_expert_ffn(args: FfnArgs, stream=None):
     _check(lib().moe_expert_ffn(ctypes.byref(args), stream_handle(stream)), "moe_expert_ffn")
+
+
+def moe_workspace_init(workspace, workspace_bytes, stream=None):
+    _check(lib().moe_workspace_init(ptr(workspace), workspace_bytes, stream_handle(stream)), "moe_workspace_init")
+
+
+def moe_workspace_check(workspace, stream=None):
+    _check(lib().moe_workspace_check(ptr(workspace), stream_handle(stream)), "moe_workspace_check")
 
 
 def moe_combine(y, inv, topk_w, y_shared, T, k, H, out, stream=None):

@@ -10,7 +10,19 @@
 #include "ffn_common.h"
 
 namespace moe {
-hipError_t launch_gemv(const FfnParams& P, float* h, float* y, hipStream_t s);
+struct GemvArgs {
+  uint16_t* h;
+  float* y;
+  GemvSync* sync;
+  const float* topk_w;
+  const int32_t* inv;
+  uint16_t* out;
+  int ng, nd;
+  int rbs1, rbs2;
+  int x_all;
+  int x_bytes;
+};
+hipError_t launch_gemv(const FfnParams& P, const GemvArgs& G, hipStream_t s);
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s);
 hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st);
 }  // namespace moe
@@ -20,6 +32,10 @@ using namespace moe;
 
 // Row count at or above which BF16 weights take the bf16 MFMA grouped GEMM.
 constexpr long long kMfmaMinRows = 512;
+// Largest batch whose combine runs inside the single-launch GEMV.
+constexpr int kFusedCombineMaxT = 64;
+// Largest H and I of the GEMV path (one bf16 row of x or h per LDS stage).
+constexpr int kGemvMaxK = 28672;
 
 enum Path { kPathGemv, kPathMfmaFp4, kPathMfmaBf16 };
 
@@ -30,7 +46,7 @@ Path choose_path(const moe_ffn_args* a) {
 }
 
 struct WsLayout {
-  size_t h, y, xq, xs, hq, hs, hb, total;
+  size_t sync, h, y, xq, xs, hq, hs, hb, total;
 };
 
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
@@ -39,9 +55,10 @@ WsLayout ws_layout(const moe_ffn_args* a) {
   const size_t R = (size_t)a->T * a->k + (a->shared_blob ? a->T : 0);
   WsLayout w{};
   size_t o = 0;
+  w.sync = o; o = al(o + sizeof(GemvSync));
   const Path p = choose_path(a);
   if (p == kPathGemv) {
-    w.h = o; o = al(o + R * a->I * sizeof(float));
+    w.h = o; o = al(o + R * a->I * 2);
   } else if (p == kPathMfmaFp4) {
     w.xq = o; o = al(o + (size_t)a->T * a->H / 2);
     w.xs = o; o = al(o + (size_t)a->T * a->H / 32);
@@ -69,6 +86,10 @@ moe_status check_args(const moe_ffn_args* a) {
     return set_error(MOE_EUNSUPPORTED, "moe_expert_ffn: MXFP4 activations need MXFP4 weights (got format %d)",
                      a->wfmt);
   MOE_CHECK_ARG((long long)a->T * a->k <= (1 << 17), "moe_expert_ffn: T*k exceeds 131072");
+  MOE_CHECK_ARG(a->H / 64 <= kMaxChunks, "moe_expert_ffn: H=%d exceeds %d", a->H, 64 * kMaxChunks);
+  MOE_CHECK_ARG(choose_path(a) != kPathGemv || (a->H <= kGemvMaxK && a->I <= kGemvMaxK),
+                "moe_expert_ffn: H=%d, I=%d: the bf16-activation path stages one row of up to %d values in LDS",
+                a->H, a->I, kGemvMaxK);
   MOE_CHECK_ARG(a->slot_stride % 256 == 0 && a->slot_stride >= moe_blob_bytes(a->wfmt, a->H, a->I),
                 "moe_expert_ffn: slot_stride %zu must be a multiple of 256 and >= blob bytes %zu", a->slot_stride,
                 moe_blob_bytes(a->wfmt, a->H, a->I));
@@ -76,6 +97,7 @@ moe_status check_args(const moe_ffn_args* a) {
   MOE_CHECK_ARG(a->x && a->counts && a->offsets && a->perm && a->slot_of_expert && a->slot_pool,
                 "moe_expert_ffn: null input pointer");
   MOE_CHECK_ARG(!a->out || (a->topk_w && a->inv), "moe_expert_ffn: out needs topk_w and inv");
+  MOE_CHECK_ARG(!(a->out && a->expert_mask), "moe_expert_ffn: with expert_mask set, run moe_combine separately");
   const WsLayout w = ws_layout(a);
   if (a->workspace_bytes < w.total || (w.total && !a->workspace))
     return set_error(MOE_ENOMEM, "moe_expert_ffn: workspace %zu bytes < %zu needed", a->workspace_bytes, w.total);
@@ -191,8 +213,21 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
   float* y = a->y ? a->y : reinterpret_cast<float*>(ws + w.y);
   hipError_t e;
   const Path path = choose_path(a);
+  bool combined = false;
   if (path == kPathGemv) {
-    e = launch_gemv(P, reinterpret_cast<float*>(ws + w.h), y, s);
+    GemvArgs G{};
+    G.h = reinterpret_cast<uint16_t*>(ws + w.h);
+    G.y = y;
+    G.sync = reinterpret_cast<GemvSync*>(ws + w.sync);
+    G.ng = a->I / 32;
+    G.nd = a->H / 64;
+    if (a->out && a->T <= kFusedCombineMaxT) {
+      G.topk_w = a->topk_w;
+      G.inv = a->inv;
+      G.out = a->out;
+      combined = true;
+    }
+    e = launch_gemv(P, G, s);
   } else {
     MfmaBufs B{};
     B.y = y;
@@ -204,7 +239,7 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     e = launch_mfma(P, path == kPathMfmaFp4, B, s);
   }
   if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: launch failed: %s", hipGetErrorString(e));
-  if (a->out) {
+  if (a->out && !combined) {
     const float* ysh = a->shared_blob ? y + (size_t)a->T * a->k * a->H : nullptr;
     e = launch_combine(y, a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
     if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));
@@ -249,5 +284,34 @@ extern "C" moe_status moe_dequant_blob(const void* blob, int which, float* out, 
                      reinterpret_cast<hipStream_t>(stream), static_cast<const uint8_t*>(blob), L, h.fmt, which, h.H,
                      h.I, out);
   MOE_LAUNCHED();
+  return MOE_OK;
+}
+
+namespace {
+__global__ void k_zero_words(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+}  // namespace
+
+extern "C" moe_status moe_workspace_init(void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  MOE_CHECK_ARG(workspace && ((uintptr_t)workspace & 255) == 0 && workspace_bytes >= sizeof(GemvSync),
+                "moe_workspace_init: workspace must be 256-byte aligned and >= %zu bytes", sizeof(GemvSync));
+  hipLaunchKernelGGL(k_zero_words, dim3(16), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(workspace), sizeof(GemvSync) / 4);
+  MOE_LAUNCHED();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_workspace_check(const void* workspace, moe_stream_t stream) {
+  MOE_CHECK_ARG(workspace, "moe_workspace_check: null workspace");
+  MOE_HIP(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
+  GemvSync s;
+  MOE_HIP(hipMemcpy(&s, workspace, sizeof s, hipMemcpyDeviceToHost));
+  if (s.err) return set_error(MOE_EHIP, "moe_workspace_check: a wait inside moe_expert_ffn timed out");
+  for (int i = 0; i < kMaxActive; ++i)
+    if (s.gu_done[i] || s.dn_pass[i])
+      return set_error(MOE_EHIP, "moe_workspace_check: counters of active expert %d were left nonzero", i);
+  for (int i = 0; i < kMaxChunks; ++i)
+    if (s.dn_done[i]) return set_error(MOE_EHIP, "moe_workspace_check: chunk counter %d was left nonzero", i);
   return MOE_OK;
 }

@@ -7,6 +7,7 @@
 // paragraph).  The selection rule (fp32 logit keys, ties to the lower id, NaN
 // lowest) and the softmax over the selected logits are this library's reading.
 #include "common.h"
+#include "wave.h"
 
 namespace {
 
@@ -123,16 +124,6 @@ __device__ __forceinline__ float from_rank_bits(uint32_t r) {
   return __uint_as_float((r & 0x80000000u) ? (r & 0x7FFFFFFFu) : ~r);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
-    uint64_t u = ((uint64_t)hi << 32) | lo;
-    v = u > v ? u : v;
-  }
-  return v;
-}
-
 __device__ __forceinline__ float unnorm(float v, float m) {
   if (v != v) return 0.f;
   if (v == m) return 1.f;
@@ -142,91 +133,140 @@ __device__ __forceinline__ float unnorm(float v, float m) {
 constexpr int kRouteMaxPerLane = 16;  // E <= 1024
 constexpr int kRouteMaxK = 16;
 
-__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k, int renorm,
-                                               int32_t* __restrict__ ids, float* __restrict__ wts) {
+// Top-k of one logits row by one wave (radix select, no cross-lane reductions
+// in the critical path):
+//   1. threshold = the k-th largest rank key, found bit by bit from the top:
+//      keep a bit when at least k keys are >= the candidate (ballot + popcount);
+//   2. selected = keys above the threshold, plus the lowest-id keys equal to it;
+//   3. each selected key's output position = number of selected keys that rank
+//      above it (larger key, or equal key and lower id).
+// Writes ids[pos], w[pos] for pos in [0, k) and, if ids_lds, ids_lds[pos].
+template <int NPER>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm,
+                                          int32_t* __restrict__ ids, float* __restrict__ wout, int32_t* ids_lds) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  uint32_t rk[kRouteMaxPerLane];
-  uint32_t avail = 0;
+  constexpr int nper = NPER;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t rk[NPER];
+  float val[NPER];
 #pragma unroll
-  for (int i = 0; i < kRouteMaxPerLane; ++i) {
+  for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
-    rk[i] = 0;
-    if (e < E) {
-      rk[i] = rank_bits(row[e]);
-      avail |= 1u << i;
+    val[i] = 0.f;
+    rk[i] = 0u;
+    if (i < nper && e < E) {
+      val[i] = row[e];
+      rk[i] = rank_bits(val[i]) + 1u;  // 0 marks "no key"; NaN -> 1, below every number
     }
   }
-  int sel_id[kRouteMaxK];
-  float sel_v[kRouteMaxK];
+  // 1. threshold
+  uint32_t thr = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = thr | (1u << b);
+    int cnt = 0;
 #pragma unroll
-  for (int j = 0; j < kRouteMaxK; ++j) {
-    sel_id[j] = 0;
-    sel_v[j] = 0.f;
-    if (j < k) {
-      uint64_t best = 0;
+    for (int i = 0; i < NPER; ++i)
+      if (i < nper) cnt += __popcll(__ballot(rk[i] >= cand));
+    if (cnt >= k) thr = cand;
+  }
+  // 2. selection
+  int c_gt = 0;
 #pragma unroll
-      for (int i = 0; i < kRouteMaxPerLane; ++i) {
-        if (avail & (1u << i)) {
-          const uint32_t e = (uint32_t)(lane + 64 * i);
-          const uint64_t key = ((uint64_t)rk[i] << 32) | (uint32_t)~e;
-          best = key > best ? key : best;
+  for (int i = 0; i < NPER; ++i)
+    if (i < nper) c_gt += __popcll(__ballot(rk[i] > thr));
+  int need = k - c_gt;
+  uint32_t selmask = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    if (i < nper) {
+      const uint64_t eq = __ballot(rk[i] == thr);
+      const int take = min(__popcll(eq), need);
+      const bool mine_eq = rk[i] == thr && __popcll(eq & lt) < take;
+      if (rk[i] > thr || mine_eq) selmask |= 1u << i;
+      need -= take;
+    }
+  }
+  // 3. output positions
+  int pos[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) pos[i] = 0;
+#pragma unroll
+  for (int i2 = 0; i2 < NPER; ++i2) {
+    if (i2 < nper) {
+      uint64_t m = __ballot((selmask >> i2) & 1u);
+      while (m) {
+        const int L = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const uint32_t ok = __builtin_amdgcn_readlane(rk[i2], L);
+        const int oid = L + 64 * i2;
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+          const int myid = lane + 64 * i;
+          if ((selmask >> i) & 1u) pos[i] += (ok > rk[i] || (ok == rk[i] && oid < myid)) ? 1 : 0;
         }
       }
-      best = wave_max_u64(best);
-      const int e = (int)(~(uint32_t)best);
-      if ((e & 63) == lane) avail &= ~(1u << (e >> 6));
-      sel_id[j] = e;
-      sel_v[j] = from_rank_bits((uint32_t)(best >> 32));
     }
   }
-  const float m = sel_v[0];
-  float num[kRouteMaxK], den = 0.f;
+  // top value m (position 0) and softmax weights
+  float top = 0.f;
 #pragma unroll
-  for (int j = 0; j < kRouteMaxK; ++j) {
-    num[j] = j < k ? unnorm(sel_v[j], m) : 0.f;
-    den += num[j];
+  for (int i = 0; i < NPER; ++i)
+    if (i < nper) {
+      const uint64_t b = __ballot(((selmask >> i) & 1u) && pos[i] == 0);
+      if (b) top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[i]), __ffsll((unsigned long long)b) - 1));
+    }
+  float num[NPER], part = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    num[i] = ((selmask >> i) & 1u) ? unnorm(val[i], top) : 0.f;
+    part += num[i];
   }
   if (!renorm) {
-    float s = 0.f;
+    part = 0.f;
 #pragma unroll
-    for (int i = 0; i < kRouteMaxPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E) s += unnorm(row[e], m);
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-    den = s;
+    for (int i = 0; i < NPER; ++i)
+      if (i < nper && lane + 64 * i < E) part += unnorm(val[i], top);
   }
+  const float den = wave_sum(part);
 #pragma unroll
-  for (int j = 0; j < kRouteMaxK; ++j) {
-    if (j < k && lane == j) {
-      ids[(size_t)t * k + j] = sel_id[j];
-      wts[(size_t)t * k + j] = den > 0.f ? num[j] / den : 1.0f / (float)k;
+  for (int i = 0; i < NPER; ++i) {
+    if ((selmask >> i) & 1u) {
+      const int id = lane + 64 * i;
+      ids[pos[i]] = id;
+      wout[pos[i]] = den > 0.f ? num[i] / den : 1.0f / (float)k;
+      if (ids_lds) ids_lds[pos[i]] = id;
     }
   }
 }
 
+template <int NPER>
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k, int renorm,
+                                               int32_t* __restrict__ ids, float* __restrict__ wts) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  wave_topk<NPER>(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wts + (size_t)t * k, nullptr);
+}
+
 // ------------------------------------------------------------------ permutation
 
-// One workgroup of 1024 threads per chunk of 1024 flat indices.  Each
-// workgroup histograms all ids (total and before its chunk) in LDS, scans
-// the totals, and places its chunk: position = offsets[e] + (# of e before
-// the chunk) + (# of e in earlier waves of the chunk) + (rank within wave).
+// One workgroup of 1024 threads places a chunk of 1024 flat indices.  It
+// histograms all ids (in total and before its chunk) in LDS, scans the
+// totals, and places its chunk: position = offsets[e] + (# of e before the
+// chunk) + (# of e in earlier waves of the chunk) + (rank within the wave).
+// `ids` may point to global memory or to LDS.
 constexpr int kPermChunk = 1024;
 constexpr int kPermWaves = kPermChunk / 64;
 
-__global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ ids, int N, int E,
-                                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-  extern __shared__ int32_t sm[];
+__device__ __forceinline__ size_t permute_lds_bytes(int E) { return sizeof(int32_t) * (size_t)E * (2 + kPermWaves); }
+
+__device__ void permute_chunk(const int32_t* ids, int N, int E, int chunk, int32_t* sm, int32_t* __restrict__ counts,
+                              int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int32_t scan_tmp[kPermChunk];
   int32_t* tot = sm;                   // [E]
   int32_t* before = sm + E;            // [E]
   int32_t* wcnt = sm + 2 * E;          // [kPermWaves][E]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c0 = blockIdx.x * kPermChunk;
+  const int c0 = chunk * kPermChunk;
   for (int i = tid; i < E * (2 + kPermWaves); i += kPermChunk) sm[i] = 0;
   __syncthreads();
   for (int f = tid; f < N; f += kPermChunk) {
@@ -237,10 +277,8 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
     }
   }
   __syncthreads();
-  // exclusive scan of tot -> offsets (kept in `before` as base = offset + before)
-  __shared__ int32_t scan_tmp[kPermChunk];
   {
-    // each thread owns a contiguous run of ceil(E/1024) experts
+    // exclusive scan of the totals; each thread owns ceil(E/1024) consecutive experts
     const int per = (E + kPermChunk - 1) / kPermChunk;
     int run = 0;
     for (int i = 0; i < per; ++i) {
@@ -259,7 +297,7 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
     for (int i = 0; i < per; ++i) {
       const int e = tid * per + i;
       if (e < E) {
-        if (blockIdx.x == 0) {
+        if (chunk == 0) {
           counts[e] = tot[e];
           offsets[e] = base;
         }
@@ -267,9 +305,9 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
         base += tot[e];
       }
     }
-    if (blockIdx.x == 0 && tid == kPermChunk - 1) offsets[E] = scan_tmp[tid];
+    if (chunk == 0 && tid == kPermChunk - 1) offsets[E] = scan_tmp[tid];
   }
-  // rank within the wave (wave-level match of equal ids)
+  // rank within the wave: wave-level match of equal ids
   const int f = c0 + tid;
   const int e = f < N ? ids[f] : -1;
   const bool valid = e >= 0 && e < E;
@@ -279,7 +317,7 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
   bool leader = false;
   while (todo) {
     const int src = __ffsll((unsigned long long)todo) - 1;
-    const int key = __shfl(e, src);
+    const int key = __builtin_amdgcn_readlane(e, src);
     const uint64_t m = __ballot(valid && e == key);
     if (valid && e == key) {
       rank = __popcll(m & lt);
@@ -297,6 +335,44 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
     perm[pos] = f;
     inv[f] = pos;
   }
+}
+
+__global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ ids, int N, int E,
+                                                  int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  extern __shared__ int32_t sm[];
+  permute_chunk(ids, N, E, blockIdx.x, sm, counts, offsets, perm, inv);
+}
+
+// Routing and permutation of a small batch (T*k <= 1024) in one workgroup.
+template <int NPER>
+__global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict__ logits, int T, int E, int k,
+                                                        int renorm, int32_t* __restrict__ ids, float* __restrict__ wts,
+                                                        int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  extern __shared__ int32_t sm[];
+  __shared__ int32_t ids_s[kPermChunk];
+  const int wave = threadIdx.x >> 6;
+  for (int t = wave; t < T; t += kPermWaves)
+    wave_topk<NPER>(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wts + (size_t)t * k, ids_s + t * k);
+  __syncthreads();
+  permute_chunk(ids_s, T * k, E, 0, sm, counts, offsets, perm, inv);
+}
+
+// Kernels with more than 64 KiB of dynamic LDS must opt in once per process.
+moe_status set_lds_limits() {
+  static bool done = false;
+  if (!done) {
+    MOE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_permute), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                120 * 1024));
+    const void* fns[] = {reinterpret_cast<const void*>(k_route_permute<1>),
+                         reinterpret_cast<const void*>(k_route_permute<2>),
+                         reinterpret_cast<const void*>(k_route_permute<4>),
+                         reinterpret_cast<const void*>(k_route_permute<16>)};
+    for (const void* f : fns) MOE_HIP(hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 120 * 1024));
+    done = true;
+  }
+  return MOE_OK;
 }
 
 }  // namespace
@@ -323,8 +399,13 @@ extern "C" moe_status moe_route(const float* logits, int T, int E, int k, int re
   MOE_CHECK_ARG(k >= 1 && k <= E && k <= kRouteMaxK, "moe_route: k=%d must be in [1, min(E, 16)]", k);
   if (T == 0) return MOE_OK;
   MOE_CHECK_ARG(logits && topk_ids && topk_w, "moe_route: null pointer");
-  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), logits, T, E, k,
-                     renormalize ? 1 : 0, topk_ids, topk_w);
+  const dim3 g((T + 3) / 4);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int rn = renormalize ? 1 : 0;
+  if (E <= 64) hipLaunchKernelGGL(k_route<1>, g, dim3(256), 0, st, logits, T, E, k, rn, topk_ids, topk_w);
+  else if (E <= 128) hipLaunchKernelGGL(k_route<2>, g, dim3(256), 0, st, logits, T, E, k, rn, topk_ids, topk_w);
+  else if (E <= 256) hipLaunchKernelGGL(k_route<4>, g, dim3(256), 0, st, logits, T, E, k, rn, topk_ids, topk_w);
+  else hipLaunchKernelGGL(k_route<16>, g, dim3(256), 0, st, logits, T, E, k, rn, topk_ids, topk_w);
   MOE_LAUNCHED();
   return MOE_OK;
 }
@@ -337,14 +418,38 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, 
   MOE_CHECK_ARG(counts && offsets && (N == 0 || (topk_ids && perm && inv)), "moe_permute: null pointer");
   const int blocks = N == 0 ? 1 : (int)((N + kPermChunk - 1) / kPermChunk);
   const size_t lds = sizeof(int32_t) * (size_t)E * (2 + kPermWaves);
-  static bool attr_set = false;
-  if (!attr_set) {
-    MOE_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(k_permute),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - 8 * 1024));
-    attr_set = true;
-  }
+  moe_status st = set_lds_limits();
+  if (st != MOE_OK) return st;
   hipLaunchKernelGGL(k_permute, dim3(blocks), dim3(kPermChunk), lds, reinterpret_cast<hipStream_t>(stream),
                      topk_ids, (int)N, E, counts, offsets, perm, inv);
+  MOE_LAUNCHED();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_route_permute(const float* logits, int T, int E, int k, int renormalize, int32_t* topk_ids,
+                                        float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                        moe_stream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && E >= 1 && E <= 1024, "moe_route_permute: bad sizes T=%d E=%d (E <= 1024)", T, E);
+  MOE_CHECK_ARG(k >= 1 && k <= E && k <= kRouteMaxK, "moe_route_permute: k=%d must be in [1, min(E, 16)]", k);
+  MOE_CHECK_ARG(counts && offsets, "moe_route_permute: null pointer");
+  if ((long long)T * k > kPermChunk) {
+    moe_status st = moe_route(logits, T, E, k, renormalize, topk_ids, topk_w, stream);
+    if (st != MOE_OK) return st;
+    return moe_permute(topk_ids, T, k, E, counts, offsets, perm, inv, stream);
+  }
+  MOE_CHECK_ARG(T == 0 || (logits && topk_ids && topk_w && perm && inv), "moe_route_permute: null pointer");
+  moe_status st = set_lds_limits();
+  if (st != MOE_OK) return st;
+  const size_t lds = sizeof(int32_t) * (size_t)E * (2 + kPermWaves);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int rn = renormalize ? 1 : 0;
+#define MOE_RP(N) hipLaunchKernelGGL(k_route_permute<N>, dim3(1), dim3(kPermChunk), lds, hs, logits, T, E, k, rn, \
+                                     topk_ids, topk_w, counts, offsets, perm, inv)
+  if (E <= 64) MOE_RP(1);
+  else if (E <= 128) MOE_RP(2);
+  else if (E <= 256) MOE_RP(4);
+  else MOE_RP(16);
+#undef MOE_RP
   MOE_LAUNCHED();
   return MOE_OK;
 }

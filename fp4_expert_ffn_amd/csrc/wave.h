@@ -1,0 +1,78 @@
+// Wave64 cross-lane primitives for gfx950 without LDS round trips:
+// DPP row permutations inside each 16-lane row, then v_permlane16_swap /
+// v_permlane32_swap across rows.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// v_permlane16_swap on (v, v) returns one copy holding rows {0,0,2,2} and one
+// holding rows {1,1,3,3} of v; v_permlane32_swap likewise returns the lower and
+// the upper half of v, each duplicated.  Combining the two copies reduces over
+// row pairs (lanes l, l^16) or halves (lanes l, l^32) whichever copy is which.
+__device__ __forceinline__ float sum_rowpair(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float sum_halves(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the four lanes l, l^16, l^32, l^48 (every lane receives the sum).
+__device__ __forceinline__ float sum_rows4(float v) { return sum_halves(sum_rowpair(v)); }
+
+// Full-wave sum, result in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<kDppQuadXor1>(v);
+  v += dpp_f32<kDppQuadXor2>(v);
+  v += dpp_f32<kDppRowHalfMirror>(v);
+  v += dpp_f32<kDppRowMirror>(v);
+  return sum_rows4(v);
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+
+// Full-wave unsigned 64-bit max, result in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<kDppQuadXor1>(v));
+  v = max_u64(v, dpp_u64<kDppQuadXor2>(v));
+  v = max_u64(v, dpp_u64<kDppRowHalfMirror>(v));
+  v = max_u64(v, dpp_u64<kDppRowMirror>(v));
+  {
+    auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    auto l = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = max_u64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
+  }
+  {
+    auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    auto l = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    v = max_u64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
+  }
+  return v;
+}
+
+}  // namespace moe

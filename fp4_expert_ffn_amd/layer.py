@@ -57,20 +57,25 @@ class LayerState:
                        out=self.out if out else None)
         need = L.moe_expert_ffn_workspace_size(a)
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=lay.dev)
+            self._ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=lay.dev)
             self._args.clear()
         a.workspace = self._ws.data_ptr()
         a.workspace_bytes = self._ws.numel()
         self._args[key] = (a, x)  # keep x alive with its args
         return a
 
+    def check(self, stream=None):
+        """Verify the workspace counters (synchronises the stream)."""
+        if self._ws is not None:
+            L.moe_workspace_check(self._ws, stream)
+
     def route(self, T, x=None, w_router=None, logits=None, stream=None):
         lay = self.layer
         if logits is None:
             L.moe_router_logits(x, w_router, T, lay.H, lay.E, self.logits, stream)
             logits = self.logits
-        L.moe_route(logits, T, lay.E, lay.k, lay.renormalize, self.ids, self.w, stream)
-        L.moe_permute(self.ids, T, lay.k, lay.E, self.counts, self.offsets, self.perm, self.inv, stream)
+        L.moe_route_permute(logits, T, lay.E, lay.k, lay.renormalize, self.ids, self.w, self.counts, self.offsets,
+                            self.perm, self.inv, stream)
 
     def ffn(self, T, x, stream=None, args=None):
         L.moe_expert_ffn(args if args is not None else self.args(T, x), stream)
@@ -114,7 +119,7 @@ class MoELayer:
     # ------------------------------------------------------------ default state
     def __getattr__(self, name):
         if name in ("logits", "ids", "w", "counts", "offsets", "perm", "inv", "out", "y", "args", "route", "ffn",
-                    "forward"):
+                    "forward", "check"):
             return getattr(self.__dict__["state"], name)
         raise AttributeError(name)
 

@@ -91,6 +91,14 @@ moe_status moe_route(const float* logits, int T, int E, int k, int renormalize,
 moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts,
                        int32_t* offsets, int32_t* perm, int32_t* inv, moe_stream_t stream);
 
+/* moe_route followed by moe_permute, in a single launch when T*k <= 1024
+ * (decode batches): one workgroup selects the experts of every token and
+ * sorts the (token, slot) pairs without a round trip through a second launch.
+ * Same arguments, results and requirements as the two calls. */
+moe_status moe_route_permute(const float* logits, int T, int E, int k, int renormalize, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                             moe_stream_t stream);
+
 /* ------------------------------------------------------------- expert FFN */
 
 /* Prepacked expert ("slot blob") layout, shared by the host bank and the HBM
@@ -138,16 +146,31 @@ typedef struct {
   const void* shared_blob;      /* nullable: always-on shared expert (same fmt, H, I),
                                    weight 1, added after the routed sum                  */
   const uint8_t* expert_mask;   /* nullable: [E]; if set only experts with mask[e] != 0
-                                   run (lets hits run while misses are still copying)    */
+                                   run (lets hits run while misses are still copying);
+                                   out must then be null (combine with moe_combine)      */
   float* y;                     /* nullable: [T*k (+T if shared)][H] fp32 expert outputs
                                    in perm order (shared rows last).  If null, y lives in
                                    the workspace.                                        */
   const float* topk_w;          /* nullable with out: [T,k] routing weights              */
   const int32_t* inv;           /* nullable with out: [T*k] from moe_permute             */
   uint16_t* out;                /* nullable: [T,H] bf16; if set, the combine runs too    */
-  void* workspace;              /* device scratch, >= moe_expert_ffn_workspace_size      */
+  void* workspace;              /* device scratch, >= moe_expert_ffn_workspace_size, 256-byte
+                                   aligned.  Its first bytes hold counters that link the
+                                   workgroups of one launch: zero-fill it once after
+                                   allocating it (moe_workspace_init); every call leaves them
+                                   zero.  Calls that share a workspace must not overlap.   */
   size_t workspace_bytes;
 } moe_ffn_args;
+
+/* Zero the counter block at the start of a workspace (a small fill kernel on
+ * `stream`; safe inside stream capture). */
+moe_status moe_workspace_init(void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Synchronise `stream`, then verify that the counter block of `workspace` is
+ * back to zero and that no wait inside moe_expert_ffn gave up (a wait is
+ * bounded to a few seconds; if one expires the call's outputs are invalid and
+ * MOE_EHIP is returned here).  Debug / test entry; it blocks the host. */
+moe_status moe_workspace_check(const void* workspace, moe_stream_t stream);
 
 /* Bytes of device workspace a call with these dimensions needs. */
 size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a);

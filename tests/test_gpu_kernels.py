@@ -170,6 +170,35 @@ def test_permute_prefill_zipf_full_size():
     assert np.sum(want[0] == 0) == 8  # the masked experts receive no token
 
 
+@pytest.mark.parametrize("T,E,k", [(1, 128, 8), (4, 128, 8), (16, 128, 8), (16, 8, 2), (64, 1024, 16), (128, 128, 8),
+                                   (200, 256, 8), (0, 32, 4)])
+def test_route_permute_fused(T, E, k):
+    """moe_route_permute (one launch when T*k <= 1024, two otherwise) equals the oracle."""
+    from fp4_expert_ffn_amd import moe_route_permute
+    rng = np.random.default_rng(T * 7 + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if T > 2:
+        lg[1, :] = 0.0
+        lg[2, 3 % E] = np.nan
+    N = T * k
+    ids = torch.empty((max(T, 1), k), dtype=torch.int32, device=DEV)
+    w = torch.empty((max(T, 1), k), dtype=torch.float32, device=DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    perm = torch.empty(max(N, 1), dtype=torch.int32, device=DEV)
+    inv = torch.empty(max(N, 1), dtype=torch.int32, device=DEV)
+    say(f"route+permute T={T} E={E} k={k}")
+    moe_route_permute(_dev(lg) if T else None, T, E, k, True, ids, w, counts, offsets, perm, inv)
+    torch.cuda.synchronize()
+    rid, rw = oracle.moe.route(lg, k) if T else (np.zeros((0, k), np.int32), np.zeros((0, k), np.float32))
+    c, o, p, iv = oracle.moe.permute(rid, E)
+    if T:
+        assert np.array_equal(ids.cpu().numpy(), rid)
+        np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+    assert np.array_equal(counts.cpu().numpy(), c) and np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(perm.cpu().numpy()[:N], p) and np.array_equal(inv.cpu().numpy()[:N], iv)
+
+
 def test_permute_empty():
     say("permute empty")
     counts, offsets, perm, inv = _permute_gpu(np.zeros((0, 4), np.int32), 16)
