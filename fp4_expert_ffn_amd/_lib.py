@@ -39,6 +39,16 @@ class FfnArgs(ctypes.Structure):
     ]
 
 
+class CacheStep(ctypes.Structure):
+    _fields_ = [
+        ("layer", ctypes.c_int), ("logits", ctypes.c_void_p), ("renormalize", ctypes.c_int),
+        ("topk_ids", ctypes.c_void_p), ("host_counts", ctypes.c_void_p), ("host_map", ctypes.c_void_p),
+        ("dev_map", ctypes.c_void_p), ("host_blobs", ctypes.c_void_p), ("ffn", FfnArgs),
+        ("trace_expert", ctypes.c_void_p), ("trace_slot", ctypes.c_void_p), ("trace_hit", ctypes.c_void_p),
+        ("trace_evicted", ctypes.c_void_p), ("n_experts", ctypes.c_int),
+    ]
+
+
 class ExpertCanonical(ctypes.Structure):
     _fields_ = [
         ("fmt", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
@@ -73,6 +83,9 @@ SIGNATURES = {
     "moe_cache_mark_used": (_i, [_vp, _vp, _i, _vp]),
     "moe_cache_reset": (_i, [_vp]),
     "moe_cache_pin_resident": (_i, [_vp, _i, _i]),
+    "moe_cache_stats": (_i, [_vp, _vp, _vp, _vp]),
+    "moe_cache_map_bytes": (_sz, [_i]),
+    "moe_cache_decode_step": (_i, [_vp, ctypes.POINTER(CacheStep), _vp, _vp]),
 }
 
 _lib = None
@@ -282,3 +295,20 @@ def moe_cache_reset(cache: Cache):
 
 def moe_cache_pin_resident(cache: Cache, layer, s0):
     _check(lib().moe_cache_pin_resident(cache.handle, layer, s0), "moe_cache_pin_resident")
+
+
+def moe_cache_stats(cache: Cache):
+    """(hits, misses, bytes_filled) since creation or reset."""
+    v = (ctypes.c_longlong * 3)()
+    _check(lib().moe_cache_stats(cache.handle, ctypes.byref(v, 0), ctypes.byref(v, 8), ctypes.byref(v, 16)),
+           "moe_cache_stats")
+    return int(v[0]), int(v[1]), int(v[2])
+
+
+def moe_cache_map_bytes(E: int) -> int:
+    return int(lib().moe_cache_map_bytes(E))
+
+
+def moe_cache_decode_step(cache: Cache, step: CacheStep, copy_stream=None, compute_stream=None):
+    _check(lib().moe_cache_decode_step(cache.handle, ctypes.byref(step), stream_handle(copy_stream),
+                                       stream_handle(compute_stream)), "moe_cache_decode_step")

@@ -6,6 +6,8 @@
 // on the GPU, misses are copied over PCIe (page "FreeToken量子化：MoE推論の
 // セットアップガイド", hierarchy and decode paragraphs; bhrtaym-blog page,
 // section "MoEバックエンドは4種類から選べる", backend table row "offload").
+#include <string.h>
+
 #include <set>
 #include <vector>
 
@@ -25,6 +27,11 @@ struct moe_cache {
   std::vector<hipEvent_t> reader, filled;
   std::vector<uint8_t> has_reader;
   int device = -1;
+  // statistics
+  long long hits = 0, misses = 0, bytes_filled = 0;
+  // per-step scratch of moe_cache_decode_step
+  std::vector<int32_t> step_ids, step_slot, step_ev;
+  std::vector<uint8_t> step_hit;
 
   void unlink(int32_t k) {
     int32_t p = prev[k], n = next[k];
@@ -88,6 +95,7 @@ extern "C" moe_status moe_cache_reset(moe_cache* c) {
   MOE_CHECK_ARG(c, "moe_cache_reset: null cache");
   c->reset();
   std::fill(c->has_reader.begin(), c->has_reader.end(), 0);
+  c->hits = c->misses = c->bytes_filled = 0;
   return MOE_OK;
 }
 
@@ -130,6 +138,7 @@ extern "C" moe_status cache_lookup(moe_cache* c, int layer, const int32_t* ids, 
       slot[i] = s;
       hit[i] = 1;
       evicted_key[i] = -1;
+      ++c->hits;
       continue;
     }
     int32_t victim = -1;
@@ -148,6 +157,7 @@ extern "C" moe_status cache_lookup(moe_cache* c, int layer, const int32_t* ids, 
     slot[i] = s;
     hit[i] = 0;
     evicted_key[i] = victim;
+    ++c->misses;
   }
   return MOE_OK;
 }
@@ -164,6 +174,16 @@ static moe_status ensure_events(moe_cache* c) {
   return MOE_OK;
 }
 
+// Copy one blob into `slot` on the copy stream once the slot's last readers
+// are done; records filled[slot].
+static moe_status enqueue_fill(moe_cache* c, int slot, const void* host_src, hipStream_t cs) {
+  if (c->has_reader[slot]) MOE_HIP(hipStreamWaitEvent(cs, c->reader[slot], 0));
+  MOE_HIP(hipMemcpyAsync(c->pool + (size_t)slot * c->slot_bytes, host_src, c->slot_bytes, hipMemcpyHostToDevice, cs));
+  MOE_HIP(hipEventRecord(c->filled[slot], cs));
+  c->bytes_filled += (long long)c->slot_bytes;
+  return MOE_OK;
+}
+
 extern "C" moe_status cache_fill(moe_cache* c, int layer, int expert, int slot, const void* host_src,
                                  moe_stream_t copy_stream, moe_stream_t compute_stream) {
   MOE_CHECK_ARG(c && host_src, "cache_fill: null pointer");
@@ -177,9 +197,8 @@ extern "C" moe_status cache_fill(moe_cache* c, int layer, int expert, int slot, 
   if (st != MOE_OK) return st;
   hipStream_t cs = reinterpret_cast<hipStream_t>(copy_stream);
   hipStream_t ks = reinterpret_cast<hipStream_t>(compute_stream);
-  if (c->has_reader[slot]) MOE_HIP(hipStreamWaitEvent(cs, c->reader[slot], 0));
-  MOE_HIP(hipMemcpyAsync(c->pool + (size_t)slot * c->slot_bytes, host_src, c->slot_bytes, hipMemcpyHostToDevice, cs));
-  MOE_HIP(hipEventRecord(c->filled[slot], cs));
+  st = enqueue_fill(c, slot, host_src, cs);
+  if (st != MOE_OK) return st;
   MOE_HIP(hipStreamWaitEvent(ks, c->filled[slot], 0));
   return MOE_OK;
 }
@@ -195,5 +214,132 @@ extern "C" moe_status moe_cache_mark_used(moe_cache* c, const int32_t* slots, in
     MOE_HIP(hipEventRecord(c->reader[slots[i]], ks));
     c->has_reader[slots[i]] = 1;
   }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_stats(const moe_cache* c, long long* hits, long long* misses, long long* bytes_filled) {
+  MOE_CHECK_ARG(c && hits && misses && bytes_filled, "moe_cache_stats: null pointer");
+  *hits = c->hits;
+  *misses = c->misses;
+  *bytes_filled = c->bytes_filled;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ one decode step
+
+// dev_map / host_map layout: int32 slot_of_expert[E], uint8 hit_mask[E], uint8 miss_mask[E].
+extern "C" size_t moe_cache_map_bytes(int E) {
+  if (E <= 0) return 0;
+  return ((size_t)E * 6 + 255) & ~(size_t)255;
+}
+
+extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t copy_stream,
+                                            moe_stream_t compute_stream) {
+  MOE_CHECK_ARG(c && s, "moe_cache_decode_step: null pointer");
+  const moe_ffn_args& f = s->ffn;
+  const int E = f.E, T = f.T;
+  s->n_experts = 0;
+  MOE_CHECK_ARG(c->pool, "moe_cache_decode_step: cache has no slot pool");
+  MOE_CHECK_ARG(E == c->num_experts, "moe_cache_decode_step: E=%d but the cache has %d experts per layer", E,
+                c->num_experts);
+  MOE_CHECK_ARG(s->layer >= 0 && s->layer < c->num_layers, "moe_cache_decode_step: layer %d out of range", s->layer);
+  MOE_CHECK_ARG(T >= 0 && f.k >= 1 && f.k <= E, "moe_cache_decode_step: bad T=%d k=%d", T, f.k);
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(s->logits && s->topk_ids && s->host_counts && s->host_map && s->dev_map && s->host_blobs,
+                "moe_cache_decode_step: null step buffer");
+  MOE_CHECK_ARG(f.y && f.out && f.topk_w && f.inv && f.counts && f.offsets && f.perm,
+                "moe_cache_decode_step: ffn.y, out, topk_w, inv, counts, offsets and perm are required");
+  MOE_CHECK_ARG(((uintptr_t)s->dev_map & 255) == 0, "moe_cache_decode_step: dev_map must be 256-byte aligned");
+  MOE_CHECK_ARG(c->slot_bytes % 256 == 0, "moe_cache_decode_step: slot_bytes %zu is not a multiple of 256",
+                c->slot_bytes);
+  hipStream_t ks = reinterpret_cast<hipStream_t>(compute_stream);
+  hipStream_t cs = reinterpret_cast<hipStream_t>(copy_stream);
+  moe_status st = ensure_events(c);
+  if (st != MOE_OK) return st;
+
+  // 1-2. routing, then the step's experts on the host
+  st = moe_route_permute(s->logits, T, E, f.k, s->renormalize, s->topk_ids, const_cast<float*>(f.topk_w),
+                         const_cast<int32_t*>(f.counts), const_cast<int32_t*>(f.offsets), const_cast<int32_t*>(f.perm),
+                         const_cast<int32_t*>(f.inv), compute_stream);
+  if (st != MOE_OK) return st;
+  MOE_HIP(hipMemcpyAsync(s->host_counts, f.counts, sizeof(int32_t) * (size_t)E, hipMemcpyDeviceToHost, ks));
+  MOE_HIP(hipStreamSynchronize(ks));
+  c->step_ids.clear();
+  for (int e = 0; e < E; ++e)
+    if (s->host_counts[e] > 0) {
+      MOE_CHECK_ARG(s->host_blobs[e], "moe_cache_decode_step: host blob of expert %d is null", e);
+      c->step_ids.push_back(e);
+    }
+  const int n = (int)c->step_ids.size();
+  c->step_slot.resize(n);
+  c->step_hit.resize(n);
+  c->step_ev.resize(n);
+
+  // 3. lookup (the trace)
+  st = cache_lookup(c, s->layer, c->step_ids.data(), n, c->step_slot.data(), c->step_hit.data(), c->step_ev.data());
+  if (st != MOE_OK) return st;
+
+  // 4. miss fills on the copy stream
+  int nh = 0, nm = 0;
+  for (int i = 0; i < n; ++i) {
+    if (c->step_hit[i]) {
+      ++nh;
+      continue;
+    }
+    ++nm;
+    st = enqueue_fill(c, c->step_slot[i], s->host_blobs[c->step_ids[i]], cs);
+    if (st != MOE_OK) return st;
+  }
+
+  // 5. slot map and masks
+  const size_t mb = moe_cache_map_bytes(E);
+  int32_t* map = static_cast<int32_t*>(s->host_map);
+  uint8_t* hm = reinterpret_cast<uint8_t*>(map + E);
+  uint8_t* mm = hm + E;
+  memset(s->host_map, 0, mb);
+  for (int i = 0; i < n; ++i) {
+    map[c->step_ids[i]] = c->step_slot[i];
+    (c->step_hit[i] ? hm : mm)[c->step_ids[i]] = 1;
+  }
+  MOE_HIP(hipMemcpyAsync(s->dev_map, s->host_map, mb, hipMemcpyHostToDevice, ks));
+  const int32_t* dmap = static_cast<const int32_t*>(s->dev_map);
+  const uint8_t* dhm = reinterpret_cast<const uint8_t*>(dmap + E);
+  const uint8_t* dmm = dhm + E;
+
+  // 6. hits now, misses after their fills
+  moe_ffn_args a = f;
+  a.slot_of_expert = dmap;
+  a.slot_pool = c->pool;
+  a.slot_stride = c->slot_bytes;
+  a.out = nullptr;
+  if (nh > 0) {
+    a.expert_mask = dhm;
+    st = moe_expert_ffn(&a, compute_stream);
+    if (st != MOE_OK) return st;
+    a.shared_blob = nullptr;  // computed once
+  }
+  if (nm > 0) {
+    for (int i = 0; i < n; ++i)
+      if (!c->step_hit[i]) MOE_HIP(hipStreamWaitEvent(ks, c->filled[c->step_slot[i]], 0));
+    a.expert_mask = dmm;
+    st = moe_expert_ffn(&a, compute_stream);
+    if (st != MOE_OK) return st;
+  }
+
+  // 7. combine, then the slots' readers
+  const float* ysh = f.shared_blob ? f.y + (size_t)T * f.k * f.H : nullptr;
+  st = moe_combine(f.y, f.inv, f.topk_w, ysh, T, f.k, f.H, f.out, compute_stream);
+  if (st != MOE_OK) return st;
+  st = moe_cache_mark_used(c, c->step_slot.data(), n, compute_stream);
+  if (st != MOE_OK) return st;
+
+  if (s->trace_expert && s->trace_slot && s->trace_hit && s->trace_evicted)
+    for (int i = 0; i < n; ++i) {
+      s->trace_expert[i] = c->step_ids[i];
+      s->trace_slot[i] = c->step_slot[i];
+      s->trace_hit[i] = c->step_hit[i];
+      s->trace_evicted[i] = c->step_ev[i];
+    }
+  s->n_experts = n;
   return MOE_OK;
 }

@@ -2,10 +2,15 @@
 
     [moe_router_logits] -> moe_route -> moe_permute -> moe_expert_ffn (+ combine)
 
+and a decode stream over many layers whose experts live in pinned host memory
+behind the HBM expert-slot cache (moe_cache_decode_step per layer and token).
+
 This module only allocates torch device memory and calls the library; every
 step of the computation runs in libmoe's HIP kernels.
 """
 from __future__ import annotations
+
+import ctypes
 
 import numpy as np
 import torch
@@ -122,6 +127,103 @@ class MoELayer:
                     "forward", "check"):
             return getattr(self.__dict__["state"], name)
         raise AttributeError(name)
+
+
+class CachedDecoder:
+    """Decode through the expert-slot cache: `num_layers` layers of `num_experts`
+    experts whose blobs sit in a pinned host bank, `num_slots` HBM slots shared
+    by every layer under LRU, misses copied on a side stream.
+
+    host_blob(layer, e) -> pinned uint8 tensor holding that expert's blob.
+    """
+
+    def __init__(self, *, num_layers, num_experts, k, H, I, fmt, num_slots, host_blob, max_tokens=1,
+                 device="cuda", renormalize=True):
+        self.L, self.E, self.k, self.H, self.I, self.fmt = num_layers, num_experts, k, H, I, fmt
+        self.dev = torch.device(device)
+        self.blob_bytes = L.moe_blob_bytes(fmt, H, I)
+        self.stride = (self.blob_bytes + 255) // 256 * 256
+        self.pool = torch.empty(num_slots * self.stride, dtype=torch.uint8, device=self.dev)
+        self.cache = L.moe_cache_create(num_slots, self.stride, self.pool, num_layers, num_experts)
+        self.copy_stream = torch.cuda.Stream(device=self.dev)
+        T, E = max(max_tokens, 1), num_experts
+        self.max_tokens = T
+        # host blob table per layer (pinned blobs must hold `stride` bytes: the copy moves whole slots)
+        self._blobs = [[host_blob(l, e) for e in range(E)] for l in range(num_layers)]
+        for row in self._blobs:
+            for b in row:
+                assert b.is_pinned() and b.numel() >= self.stride
+        self._tables = [(ctypes.c_void_p * E)(*[b.data_ptr() for b in row]) for row in self._blobs]
+        mb = L.moe_cache_map_bytes(E)
+        self.host_counts = torch.empty(E, dtype=torch.int32, pin_memory=True)
+        self.host_map = torch.empty(mb, dtype=torch.uint8, pin_memory=True)
+        self.dev_map = torch.empty(mb, dtype=torch.uint8, device=self.dev)
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=self.dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=self.dev)
+        self.counts = torch.zeros(E, dtype=torch.int32, device=self.dev)
+        self.offsets = torch.zeros(E + 1, dtype=torch.int32, device=self.dev)
+        self.perm = torch.zeros(T * k, dtype=torch.int32, device=self.dev)
+        self.inv = torch.zeros(T * k, dtype=torch.int32, device=self.dev)
+        self.y = torch.empty((T * k, H), dtype=torch.float32, device=self.dev)
+        self.out = torch.empty((T, H), dtype=torch.int16, device=self.dev)
+        self.trace = [np.empty(E, np.int32), np.empty(E, np.int32), np.empty(E, np.uint8), np.empty(E, np.int32)]
+        self._steps = {}
+        self._ws = None
+
+    def _step(self, layer, T, x, logits, out):
+        key = (layer, T)
+        st = self._steps.get(key)
+        if st is None:
+            a = L.ffn_args(T=T, k=self.k, E=self.E, H=self.H, I=self.I, wfmt=self.fmt, amode="bf16", x=x,
+                           counts=self.counts, offsets=self.offsets, perm=self.perm, slot_pool=self.pool,
+                           slot_stride=self.stride, y=self.y, topk_w=self.w, inv=self.inv, out=out)
+            need = L.moe_expert_ffn_workspace_size(a)
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.dev)
+                for s in self._steps.values():
+                    s.ffn.workspace, s.ffn.workspace_bytes = self._ws.data_ptr(), self._ws.numel()
+            a.workspace, a.workspace_bytes = self._ws.data_ptr(), self._ws.numel()
+            st = L.CacheStep()
+            st.layer, st.renormalize = layer, 1
+            st.topk_ids = self.ids.data_ptr()
+            st.host_counts, st.host_map, st.dev_map = (self.host_counts.data_ptr(), self.host_map.data_ptr(),
+                                                       self.dev_map.data_ptr())
+            st.host_blobs = ctypes.cast(self._tables[layer], ctypes.c_void_p)
+            st.ffn = a
+            tr = self.trace
+            st.trace_expert, st.trace_slot, st.trace_hit, st.trace_evicted = (t.ctypes.data for t in tr)
+            self._steps[key] = st
+        st.logits = logits.data_ptr()
+        st.ffn.x = x.data_ptr()
+        st.ffn.out = out.data_ptr()
+        return st
+
+    def step(self, layer, x, logits, out=None, stream=None):
+        """One layer of one decode step: x [T,H] bf16 (int16), logits [T,E] fp32 on the device.
+        Returns the output [T,H] (bf16 bits) and the step's trace
+        (expert, slot, hit, evicted_key) as host arrays."""
+        T = x.shape[0]
+        assert T <= self.max_tokens
+        out = self.out[:T] if out is None else out
+        st = self._step(layer, T, x, logits, out)
+        L.moe_cache_decode_step(self.cache, st, self.copy_stream, stream)
+        n = st.n_experts
+        return out, tuple(t[:n].copy() for t in self.trace)
+
+    def step_fast(self, layer, x, logits, stream_handle):
+        """step() without the trace copies (stream_handle: raw hipStream_t of the compute stream)."""
+        T = x.shape[0]
+        st = self._step(layer, T, x, logits, self.out[:T])
+        L.moe_cache_decode_step(self.cache, st, self.copy_stream, stream_handle)
+
+    def stats(self):
+        return L.moe_cache_stats(self.cache)
+
+    def reset(self):
+        L.moe_cache_reset(self.cache)
+
+    def close(self):
+        self.cache.close()
 
 
 def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:

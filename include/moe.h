@@ -240,6 +240,55 @@ moe_status cache_fill(moe_cache* c, int layer, int expert, int slot, const void*
  * enqueued so far; a later cache_fill of one of them waits for that work. */
 moe_status moe_cache_mark_used(moe_cache* c, const int32_t* slots, int n, moe_stream_t compute_stream);
 
+/* Hits, misses and bytes copied by cache_fill since creation or reset (host). */
+moe_status moe_cache_stats(const moe_cache* c, long long* hits, long long* misses, long long* bytes_filled);
+
+/* One decode step of one MoE layer through the expert cache: routing, slot
+ * lookup, miss fills and the expert FFN with its combine.
+ * [page "FreeToken量子化：...", decode paragraph: the router picks experts,
+ *  hits run on the GPU at once, misses come over PCIe into LRU slots shared
+ *  by all layers; page "...", hierarchy paragraph: double buffering lets the
+ *  transfer of some experts overlap the computation of others.]
+ * The call enqueues, in this order:
+ *   1. moe_route_permute(logits) into ffn.topk_w / ffn.counts / ffn.offsets /
+ *      ffn.perm / ffn.inv and topk_ids, on compute_stream;
+ *   2. a copy of counts to host_counts, and waits for it (the host must
+ *      know the step's experts: this is the step's one host synchronisation);
+ *   3. cache_lookup of the experts with rows, in ascending id (the trace);
+ *   4. for every miss, a fill from host_blobs[expert] on copy_stream (after
+ *      the slot's previous readers);
+ *   5. the slot map and the hit / miss masks, host_map -> dev_map;
+ *   6. the FFN over the hit experts (overlapping the fills), then a wait on
+ *      each miss's fill, then the FFN over the missed experts;
+ *   7. moe_combine into ffn.out, and moe_cache_mark_used of the step's slots.
+ * ffn.slot_of_expert, ffn.expert_mask are set by the call; ffn.y is
+ * required; ffn.out, topk_w, inv receive the combine.  host_counts and
+ * host_map are pinned (hipHostMalloc) host buffers of 4E and
+ * moe_cache_map_bytes(E) bytes, dev_map a device buffer of that size; none
+ * may be reused by another step before this step's compute work finishes
+ * (a later step on the same compute_stream satisfies this).  The trace
+ * arrays (host, capacity E) receive the step's n_experts records. */
+typedef struct {
+  int layer;
+  const float* logits;          /* [T,E] fp32 router logits of the step             */
+  int renormalize;
+  int32_t* topk_ids;            /* [T,k] device                                     */
+  int32_t* host_counts;         /* pinned host [E]                                  */
+  void* host_map;               /* pinned host, moe_cache_map_bytes(E)              */
+  void* dev_map;                /* device, moe_cache_map_bytes(E), 256-byte aligned */
+  const void* const* host_blobs;/* host [E]: pinned blob of each expert of `layer`  */
+  moe_ffn_args ffn;
+  int32_t* trace_expert;        /* host [E] (nullable together)                     */
+  int32_t* trace_slot;
+  uint8_t* trace_hit;
+  int32_t* trace_evicted;
+  int n_experts;                /* out: distinct experts of the step                */
+} moe_cache_step;
+
+size_t moe_cache_map_bytes(int E);
+moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t copy_stream,
+                                 moe_stream_t compute_stream);
+
 /* Reset the cache to the empty state (host metadata only). */
 moe_status moe_cache_reset(moe_cache* c);
 

@@ -1,0 +1,126 @@
+"""The expert-slot cache on the GPU through the C ABI: slot fills from pinned
+host memory, and decode streams over several layers whose experts live in a
+pinned host bank behind an LRU cache with few slots (many misses and
+evictions).  The hit / miss / slot / eviction trace of every step must equal
+the oracle's LRU simulation exactly; each step's output must match the oracle
+layer within max |gpu - oracle| / max |oracle| <= 1e-2."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import DEV, DequantCache, need_gpu, say, torch
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    import fp4_expert_ffn_amd  # noqa: F401
+
+
+def _pinned_blob(ex, stride):
+    from fp4_expert_ffn_amd.layer import blob_of
+    b = blob_of(ex)
+    t = torch.zeros(stride, dtype=torch.uint8, pin_memory=True)
+    t[:b.size].copy_(torch.from_numpy(b))
+    return t
+
+
+def test_cache_fill_copies_the_blob_into_its_slot():
+    import fp4_expert_ffn_amd as F
+    ex = synth.expert("nvfp4", 256, 128, config=85, expert_id=3)
+    stride = (F.moe_blob_bytes("nvfp4", 256, 128) + 255) // 256 * 256
+    pool = torch.zeros(4 * stride, dtype=torch.uint8, device=DEV)
+    c = F.moe_cache_create(4, stride, pool, 1, 8)
+    src = _pinned_blob(ex, stride)
+    for e in (3, 5):
+        slot, hit, ev = F.cache_lookup(c, 0, [e])
+        say(f"cache_fill expert {e} -> slot {slot[0]}")
+        copy = torch.cuda.Stream()
+        F.cache_fill(c, 0, e, int(slot[0]), src, copy, torch.cuda.current_stream())
+        F.moe_cache_mark_used(c, slot)
+        torch.cuda.synchronize()
+        got = pool[int(slot[0]) * stride:(int(slot[0]) + 1) * stride].cpu()
+        assert torch.equal(got, src)
+    assert F.moe_cache_stats(c) == (0, 2, 2 * stride)
+    c.close()
+
+
+def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=None, config=86):
+    """Decode `tokens` single-token steps through `layers` layers; returns the
+    number of steps checked against the oracle."""
+    from fp4_expert_ffn_amd.layer import CachedDecoder, to_numpy_bf16
+    import fp4_expert_ffn_amd as F
+    stride = (F.moe_blob_bytes("nvfp4", H, I) + 255) // 256 * 256
+    bank = {}
+
+    def host_blob(l, e):
+        if (l, e) not in bank:
+            bank[(l, e)] = _pinned_blob(make_expert(l, e), stride)
+        return bank[(l, e)]
+
+    dec = CachedDecoder(num_layers=layers, num_experts=E, k=k, H=H, I=I, fmt="nvfp4", num_slots=slots,
+                        host_blob=host_blob, device=DEV)
+    logits = synth.stream_routing(tokens, layers, E, seed=config)
+    xs = np.stack([np.stack([synth.stream_activations(t, l, H, seed=config)[0] for l in range(layers)])
+                   for t in range(tokens)])
+    lg_d = torch.from_numpy(logits).to(DEV)
+    x_d = torch.from_numpy(xs.view(np.int16)).to(DEV)
+    lru = oracle.lru.SlotLRU(slots)
+    wts = {l: DequantCache(lambda e, l=l: make_expert(l, e), cap=E) for l in range(layers)}
+    checked = 0
+    misses = 0
+    for t in range(tokens):
+        for l in range(layers):
+            out, (te, ts, th, tv) = dec.step(l, x_d[t, l:l + 1], lg_d[t, l:l + 1])
+            ids, w = oracle.moe.route(logits[t, l:l + 1], k)
+            want = lru.lookup(l, sorted(set(ids[0].tolist())))
+            assert te.tolist() == [r[0] for r in want], (t, l)
+            assert th.tolist() == [int(r[1]) for r in want], (t, l)
+            assert ts.tolist() == [r[2] for r in want], (t, l)
+            assert tv.tolist() == [-1 if r[3] is None else r[3][0] * E + r[3][1] for r in want], (t, l)
+            misses += int(np.sum(th == 0))
+            if check_steps is None or (t, l) in check_steps:
+                torch.cuda.synchronize()
+                got = synth.bf16_bits_to_f32(to_numpy_bf16(out))
+                ref = oracle.moe.token_output(0, xs[t, l:l + 1], ids[0], w[0], wts[l])
+                err = oracle.moe.relative_error(got[0], ref)
+                assert err <= TOL, (t, l, err)
+                checked += 1
+    torch.cuda.synchronize()
+    hits, m, nbytes = dec.stats()
+    assert m == misses and nbytes == misses * stride
+    say(f"    {tokens} tokens x {layers} layers: {hits} hits, {m} misses, {checked} outputs checked")
+    dec.close()
+    return checked
+
+
+def test_cached_stream_small_every_step():
+    """16 experts per layer, top-4, 10 slots for 3 layers: most steps miss and evict."""
+    say("cached stream: 3 layers x 16 NVFP4 experts (hidden 256, inter 256), 10 slots, 20 tokens")
+
+    def make(l, e):
+        return synth.expert("nvfp4", 256, 256, config=86, layer=l, expert_id=e)
+
+    _run_stream(layers=3, E=16, k=4, H=256, I=256, tokens=20, slots=10, make_expert=make)
+
+
+def test_cached_stream_a3b_shape():
+    """A3B-like layers (hidden 2048, 128 NVFP4 experts, top-8, inter 768), 2 layers,
+    24 slots: the trace of every step, the output of sampled steps."""
+    say("cached stream: 2 A3B-like layers, 24 slots, 12 tokens")
+    gen = {}
+
+    def make(l, e):
+        if (l, e) not in gen:
+            gen[(l, e)] = synth.expert("nvfp4", 2048, 768, config=87, layer=l, expert_id=e)
+        return gen[(l, e)]
+
+    rng = np.random.default_rng(0)
+    steps = {(int(t), int(l)) for t, l in zip(rng.integers(0, 12, 6), rng.integers(0, 2, 6))} | {(11, 1)}
+    n = _run_stream(layers=2, E=128, k=8, H=2048, I=768, tokens=12, slots=24, make_expert=make,
+                    check_steps=steps, config=87)
+    assert n == len(steps)
