@@ -99,6 +99,7 @@ def main():
     ap.add_argument("--copies", type=int, default=8, help="HBM copies of the layer's experts cycled across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--stream-tokens", type=int, default=512, help="tokens of the stream workload")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -342,7 +343,7 @@ def bench_stream(args):
 
     cfg = synth.A3B
     E, k, H, I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]
-    LAYERS, SLOTS, TOKENS, FMT = 48, 2048, 512, "nvfp4"
+    LAYERS, SLOTS, TOKENS, FMT = 48, 2048, args.stream_tokens, "nvfp4"
     warm_tokens = args.warmup if args.warmup is not None else 4
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -407,11 +408,12 @@ def bench_stream(args):
     torch.cuda.synchronize()
     dec.reset()
     t_start = time.perf_counter()
-    run(0, 64)
+    n64 = min(64, TOKENS)
+    run(0, n64)
     torch.cuda.synchronize()
     h64, m64, _ = dec.stats()
-    log(f"[bench]   64 tokens in {time.perf_counter() - t_start:.2f} s")
-    run(64, TOKENS)
+    log(f"[bench]   {n64} tokens in {time.perf_counter() - t_start:.2f} s")
+    run(n64, TOKENS)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     hits, misses, nbytes = dec.stats()
@@ -455,7 +457,8 @@ def bench_stream(args):
         "data": "synthetic (seeded; weights N(0,0.02) quantised, activations N(0,1) bf16 per (token, layer), "
                 "Zipf(1.1) routing with 0.6 repeat of the previous token's experts)",
         "config": {"workload": "cached decode stream: 48 A3B-like NVFP4 layers (hidden 2048, 128 experts, top-8, "
-                               "inter 768) in pinned host memory, 2048 HBM slots, 512 tokens at batch 1, cold start",
+                               f"inter 768) in pinned host memory, 2048 HBM slots, {TOKENS} tokens at batch 1, "
+                               "cold start",
                    "layers": LAYERS, "slots": SLOTS, "tokens": TOKENS, "parallelism": "single GPU"},
         "roofline": {"bound": "h2d", "achieved": round(h2d, 2), "peak": round(h2d_peak, 2), "unit": "GB/s",
                      "frac": round(h2d / h2d_peak, 4), "traffic": None,

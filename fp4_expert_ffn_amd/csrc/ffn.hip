@@ -14,13 +14,11 @@ struct GemvArgs {
   uint16_t* h;
   float* y;
   GemvSync* sync;
-  const float* topk_w;
-  const int32_t* inv;
-  uint16_t* out;
   int ng, nd;
   int rbs1, rbs2;
   int x_all;
   int x_bytes;
+  float* trash;
 };
 hipError_t launch_gemv(const FfnParams& P, const GemvArgs& G, hipStream_t s);
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s);
@@ -32,8 +30,6 @@ using namespace moe;
 
 // Row count at or above which BF16 weights take the bf16 MFMA grouped GEMM.
 constexpr long long kMfmaMinRows = 512;
-// Largest batch whose combine runs inside the single-launch GEMV.
-constexpr int kFusedCombineMaxT = 64;
 // Largest H and I of the GEMV path (one bf16 row of x or h per LDS stage).
 constexpr int kGemvMaxK = 28672;
 
@@ -46,7 +42,7 @@ Path choose_path(const moe_ffn_args* a) {
 }
 
 struct WsLayout {
-  size_t sync, h, y, xq, xs, hq, hs, hb, total;
+  size_t sync, trash, h, y, xq, xs, hq, hs, hb, total;
 };
 
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
@@ -56,6 +52,7 @@ WsLayout ws_layout(const moe_ffn_args* a) {
   WsLayout w{};
   size_t o = 0;
   w.sync = o; o = al(o + sizeof(GemvSync));
+  w.trash = o; o = al(o + (1 << 20));  // 256 slots of 4 KiB
   const Path p = choose_path(a);
   if (p == kPathGemv) {
     w.h = o; o = al(o + R * a->I * 2);
@@ -213,20 +210,14 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
   float* y = a->y ? a->y : reinterpret_cast<float*>(ws + w.y);
   hipError_t e;
   const Path path = choose_path(a);
-  bool combined = false;
   if (path == kPathGemv) {
     GemvArgs G{};
     G.h = reinterpret_cast<uint16_t*>(ws + w.h);
     G.y = y;
     G.sync = reinterpret_cast<GemvSync*>(ws + w.sync);
+    G.trash = reinterpret_cast<float*>(ws + w.trash);
     G.ng = a->I / 32;
     G.nd = a->H / 64;
-    if (a->out && a->T <= kFusedCombineMaxT) {
-      G.topk_w = a->topk_w;
-      G.inv = a->inv;
-      G.out = a->out;
-      combined = true;
-    }
     e = launch_gemv(P, G, s);
   } else {
     MfmaBufs B{};
@@ -239,7 +230,7 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     e = launch_mfma(P, path == kPathMfmaFp4, B, s);
   }
   if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: launch failed: %s", hipGetErrorString(e));
-  if (a->out && !combined) {
+  if (a->out) {
     const float* ysh = a->shared_blob ? y + (size_t)a->T * a->k * a->H : nullptr;
     e = launch_combine(y, a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
     if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));
