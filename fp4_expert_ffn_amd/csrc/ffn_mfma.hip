@@ -12,9 +12,10 @@
 // 4-bit-weight GEMM on FP4 matrix cores.
 //
 // Workgroup: 256 threads = 4 waves in a 2x2 grid, each wave 64 rows x 64 cols
-// (4x4 MFMA 16x16 tiles).  K-steps of 128 (FP4) or 64 (BF16) are staged
-// global -> registers -> LDS with the next step's loads in flight during the
-// current step's MFMAs.  Tiles are listed expert by expert, column tile by
+// (4x4 MFMA 16x16 tiles).  K-steps of 256 (FP4) or 64 (BF16), i.e. 128 bytes
+// of every operand row, are staged global -> registers -> LDS
+// (double-buffered) with the next steps' loads in flight during the current
+// step's MFMAs.  Tiles are listed expert by expert, column tile by
 // column tile, row tile fastest, and each XCD takes a contiguous range of the
 // list, so row tiles of a hot expert that share weights run on one L2.
 #include <algorithm>
@@ -182,95 +183,113 @@ __device__ inline TileJob find_tile(const FfnParams& P, int NT) {
 
 enum { kGateUp = 0, kDown = 1 };
 
-template <bool FP4, int MODE>
-__global__ __launch_bounds__(256) void k_mfma_ffn(FfnParams P, MfmaBufs B) {
+template <bool FP4, int MODE, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mfma_ffn(FfnParams P, MfmaBufs B) {
   const int K = MODE == kGateUp ? P.H : P.I;
   const int NT = MODE == kGateUp ? (2 * P.I) / kBN : P.H / kBN;
   const TileJob tj = find_tile(P, NT);
   if (tj.rows == 0) return;
 
-  constexpr int KSTEP = FP4 ? 128 : 64;
-  constexpr int NCH = FP4 ? 2 : 4;  // 16-byte chunks per thread per operand per K-step
-  __shared__ __align__(16) uint8_t lds[32768 + 1024];
-  uint4* As = reinterpret_cast<uint4*>(lds);           // FP4 [8][64]; BF16 [8][2][64]
-  uint4* Bs = reinterpret_cast<uint4*>(lds + 16384);   // same shapes
-  uint8_t* Asc = lds + 32768;                          // FP4 [8][64]
-  uint8_t* Bsc = lds + 32768 + 512;                    // FP4 [8][64]
+  // One K-step = 128 bytes of every operand row (FP4: K = 256, two 128-wide
+  // K-tiles; BF16: K = 64, two 32-wide K-tiles): 16 KiB per operand.
+  constexpr int KSTEP = FP4 ? 256 : 64;
+  constexpr int kStage = 16384;
+  constexpr int kBuf = 2 * kStage + (FP4 ? 2048 : 0);  // A, B (+ A and B scale bytes)
+  __shared__ __align__(16) uint8_t lds[2 * kBuf];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const BlobView bv = blob_view(tj.blob, P.L);
-  const uint8_t* wt = MODE == kGateUp ? bv.w13 : bv.w2;
-  const uint8_t* st = MODE == kGateUp ? bv.s13 : bv.s2;
+  const uint8_t* wt = tj.blob + (MODE == kGateUp ? P.L.off_w13 : P.L.off_w2);
+  const uint8_t* st = tj.blob + (MODE == kGateUp ? P.L.off_s13 : P.L.off_s2);
   const int nk_w = K / (FP4 ? 128 : 32);  // weight K-tiles per row-group
   const int rg0 = tj.nt * 8;              // first 16-row group of the column tile
 
-  // Rows this thread stages for operand A, and their source pointers.
-  const uint8_t* arow[NCH];
-  const uint8_t* asrow[NCH];
-  bool aval[NCH];
+  // Operand A: thread t stages 16-byte segment t % 8 of rows t / 8 + 32 i
+  // (i < 4), so a wave reads eight whole 128-byte row segments per load.
+  // Rows past the tile are clamped for the address and zeroed after the load.
+  const uint8_t* arow[4];
+  int a_lds[4];
+  uint32_t akeep[4];
+  const int seg = tid & 7;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    int row;
-    if (FP4) row = ((tid >> 6) + 4 * i) * 16 + (tid & 15);
-    else row = ((tid >> 7) + 2 * i) * 16 + (tid & 15);
-    aval[i] = row < tj.rows;
-    const int r = aval[i] ? row : 0;
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid >> 3) + 32 * i;
+    akeep[i] = row < tj.rows ? 0xFFFFFFFFu : 0u;
+    const int r = row < tj.rows ? row : 0;
     if (MODE == kGateUp) {
       const int t = tj.shared ? tj.m0 + r : P.perm[tj.p0 + tj.m0 + r] / P.k;
-      if (FP4) {
-        arow[i] = B.xq + (size_t)t * (P.H / 2);
-        asrow[i] = B.xs + (size_t)t * (P.H / 32);
-      } else {
-        arow[i] = reinterpret_cast<const uint8_t*>(P.x + (size_t)t * P.H);
-        asrow[i] = nullptr;
-      }
+      arow[i] = FP4 ? B.xq + (size_t)t * (P.H / 2) : reinterpret_cast<const uint8_t*>(P.x + (size_t)t * P.H);
     } else {
-      const size_t p = (size_t)tj.p0 + tj.m0 + r;
-      if (FP4) {
-        arow[i] = B.hq + p * (P.I / 2);
-        asrow[i] = B.hs + p * (P.I / 32);
-      } else {
-        arow[i] = reinterpret_cast<const uint8_t*>(B.hb + p * P.I);
-        asrow[i] = nullptr;
-      }
+      const size_t pr = (size_t)tj.p0 + tj.m0 + r;
+      arow[i] = FP4 ? B.hq + pr * (P.I / 2) : reinterpret_cast<const uint8_t*>(B.hb + pr * P.I);
     }
+    // fragment (16-row tile mt, K-tile seg / 4), lane (seg % 4) * 16 + row % 16
+    a_lds[i] = (((row >> 4) * 2 + (seg >> 2)) * 64 + (seg & 3) * 16 + (row & 15)) * 16;
+    arow[i] += seg * 16;
   }
-
-  uint4 ra[NCH], rb[NCH];
-  uint8_t rsa[NCH], rsb[NCH];
-  auto load_stage = [&](int ks) {
+  // FP4 A scales: 8 bytes (the step's eight 32-blocks) of row tid / 2, half tid % 2.
+  const uint8_t* asrow = nullptr;
+  uint32_t askeep = 0;
+  if (FP4) {
+    const int row = tid >> 1;
+    askeep = row < tj.rows ? 0xFFFFFFFFu : 0u;
+    const int r = row < tj.rows ? row : 0;
+    if (MODE == kGateUp) {
+      const int t = tj.shared ? tj.m0 + r : P.perm[tj.p0 + tj.m0 + r] / P.k;
+      asrow = B.xs + (size_t)t * (P.H / 32);
+    } else {
+      asrow = B.hs + ((size_t)tj.p0 + tj.m0 + r) * (P.I / 32);
+    }
+    asrow += (tid & 1) * 4;
+  }
+  // Operand B: chunk c = t + 256 i is lane c % 64 of weight tile (row group
+  // c / 128, K-tile (c / 64) % 2 of the step); LDS holds it at c * 16.
+  size_t b_off[4];
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + 256 * i;
-      if (FP4) {
-        const int kb = (c & 63) >> 4;  // 32-value block within the 128-wide K-tile
-        ra[i] = aval[i] ? *reinterpret_cast<const uint4*>(arow[i] + ks * 64 + kb * 16) : make_uint4(0, 0, 0, 0);
-        rsa[i] = aval[i] ? asrow[i][ks * 4 + kb] : (uint8_t)127;
-        const int j = c >> 6, l = c & 63;
-        const size_t tile = (size_t)(rg0 + j) * nk_w + ks;
-        rb[i] = *reinterpret_cast<const uint4*>(wt + tile * kTileBytes + l * 16);
-        rsb[i] = st[tile * 64 + l];
-      } else {
-        const int kts = (c >> 6) & 1, l = c & 63;
-        const int kcol = (ks * 2 + kts) * 32 + (l >> 4) * 8;  // bf16 element column
-        ra[i] = aval[i] ? *reinterpret_cast<const uint4*>(arow[i] + (size_t)kcol * 2) : make_uint4(0, 0, 0, 0);
-        const int j = c >> 7;
-        const size_t tile = (size_t)(rg0 + j) * nk_w + ks * 2 + kts;
-        rb[i] = *reinterpret_cast<const uint4*>(wt + tile * kTileBytes + l * 16);
-      }
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + 256 * i;
+    b_off[i] = ((size_t)(rg0 + (c >> 7)) * nk_w + ((c >> 6) & 1)) * kTileBytes + (c & 63) * 16;
+  }
+  // FP4 B scales: dword t of the step's 16 scale tiles (64 bytes each).
+  const size_t bs_off = ((size_t)(rg0 + (tid >> 5)) * nk_w + ((tid >> 4) & 1)) * 64 + (tid & 15) * 4;
+
+  struct Stage {
+    uint4 a[4], b[4];
+    uint32_t sa, sb;
+  };
+  const int nsteps = (K + KSTEP - 1) / KSTEP;
+  // FP4 with K % 256 == 128: the last step holds one K-tile; its second
+  // half re-reads the first half's addresses (in bounds, finite) and is
+  // stored as zeros.
+  const bool half_tail = FP4 && (K % KSTEP) != 0;
+  auto load_stage = [&](int ks, Stage& S) {
+    const bool tail = half_tail && ks == nsteps - 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int back_a = (tail && seg >= 4) ? 64 : 0;
+      const int back_b = (tail && ((tid + 256 * i) >> 6 & 1)) ? kTileBytes : 0;
+      S.a[i] = *reinterpret_cast<const uint4*>(arow[i] + (size_t)ks * 128 - back_a);
+      S.b[i] = *reinterpret_cast<const uint4*>(wt + b_off[i] + (size_t)ks * 2 * kTileBytes - back_b);
+    }
+    if (FP4) {
+      const int back_sa = (tail && (tid & 1)) ? 4 : 0, back_sb = (tail && (tid >> 4 & 1)) ? 64 : 0;
+      S.sa = *reinterpret_cast<const uint32_t*>(asrow + (size_t)ks * 8 - back_sa);
+      S.sb = *reinterpret_cast<const uint32_t*>(st + bs_off + (size_t)ks * 2 * 64 - back_sb);
     }
   };
-  auto store_stage = [&]() {
+  auto store_stage = [&](const Stage& S, uint8_t* buf, int ks) {
+    const uint32_t lk = 0xFFFFFFFFu;
+    const bool tail = half_tail && ks == nsteps - 1;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + 256 * i;
-      As[c] = ra[i];
-      Bs[c] = rb[i];
-      if (FP4) {
-        Asc[c] = rsa[i];
-        Bsc[c] = rsb[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t k = akeep[i] & lk & ((tail && seg >= 4) ? 0u : 0xFFFFFFFFu);  // bit masks: branch-free
+      *reinterpret_cast<uint4*>(buf + a_lds[i]) = make_uint4(S.a[i].x & k, S.a[i].y & k, S.a[i].z & k, S.a[i].w & k);
+      reinterpret_cast<uint4*>(buf + kStage)[tid + 256 * i] = S.b[i];
+    }
+    if (FP4) {
+      const uint32_t k = askeep & lk & ((tail && (tid & 1)) ? 0u : 0xFFFFFFFFu);
+      reinterpret_cast<uint32_t*>(buf + 2 * kStage)[tid] = (S.sa & k) | (0x7F7F7F7Fu & ~k);
+      reinterpret_cast<uint32_t*>(buf + 2 * kStage + 1024)[tid] = S.sb;
     }
   };
 
@@ -280,38 +299,36 @@ __global__ __launch_bounds__(256) void k_mfma_ffn(FfnParams P, MfmaBufs B) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = K / KSTEP;
-  load_stage(0);
-  for (int ks = 0; ks < nsteps; ++ks) {
-    store_stage();
-    __syncthreads();
-    if (ks + 1 < nsteps) load_stage(ks + 1);
-    if (FP4) {
-      i32x8_t a[4], b[4];
-      int sa[4], sb[4];
+  auto compute = [&](const uint8_t* buf) {
+    const uint4* As = reinterpret_cast<const uint4*>(buf);
+    const uint4* Bs = reinterpret_cast<const uint4*>(buf + kStage);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 u = As[(4 * wm + i) * 64 + lane];
-        a[i] = i32x8_t{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-        sa[i] = Asc[(4 * wm + i) * 64 + lane];
-        const uint4 v = Bs[(4 * wn + i) * 64 + lane];
-        b[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        sb[i] = Bsc[(4 * wn + i) * 64 + lane];
-      }
+    for (int kt = 0; kt < 2; ++kt) {
+      if (FP4) {
+        i32x8_t a[4], b[4];
+        int sa[4], sb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const int mt = 4 * wm + i, nt = 4 * wn + i;
+          const uint4 u = As[(mt * 2 + kt) * 64 + lane];
+          a[i] = i32x8_t{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
+          sa[i] = buf[2 * kStage + (mt * 16 + (lane & 15)) * 8 + kt * 4 + (lane >> 4)];
+          const uint4 v = Bs[(nt * 2 + kt) * 64 + lane];
+          b[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          sb[i] = buf[2 * kStage + 1024 + (nt * 2 + kt) * 64 + lane];
+        }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 0, sa[i], 0,
-                                                                        sb[j]);
-    } else {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int kts = 0; kts < 2; ++kts) {
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc[i][j], 4, 4, 0, sa[i], 0,
+                                                                          sb[j]);
+      } else {
         bf16x8_t a[4], b[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          a[i] = __builtin_bit_cast(bf16x8_t, As[((4 * wm + i) * 2 + kts) * 64 + lane]);
-          b[i] = __builtin_bit_cast(bf16x8_t, Bs[((4 * wn + i) * 2 + kts) * 64 + lane]);
+          a[i] = __builtin_bit_cast(bf16x8_t, As[((4 * wm + i) * 2 + kt) * 64 + lane]);
+          b[i] = __builtin_bit_cast(bf16x8_t, Bs[((4 * wn + i) * 2 + kt) * 64 + lane]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -319,8 +336,47 @@ __global__ __launch_bounds__(256) void k_mfma_ffn(FfnParams P, MfmaBufs B) {
           for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
       }
     }
-    __syncthreads();
+  };
+
+  // Pipeline of D register stages: while step ks is stored to one LDS buffer
+  // and computed, steps ks+1 .. ks+D-1 are loading.  The stage loop is
+  // unrolled by D so every stage has fixed registers (no copies, which would
+  // force the loads to land early) and its body has no branch around memory
+  // operations (loads past the end re-read the last K-step).  The remaining
+  // nsteps % D steps run after the loop.  The other LDS buffer still serves
+  // the waves finishing step ks-1, so one barrier per step suffices, and it
+  // orders LDS only: the global loads stay in flight across it.
+  Stage S[D];
+#pragma unroll
+  for (int d = 0; d + 1 < D; ++d) {  // issued in stage order (the wait counter is in order)
+    load_stage(min(d, nsteps - 1), S[d]);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  auto step = [&](int ks, Stage& cur, Stage& next) {
+    load_stage(min(ks + D - 1, nsteps - 1), next);
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* buf = lds + (ks & 1) * kBuf;
+    store_stage(cur, buf, ks);
+    lds_barrier();
+    compute(buf);
+    // Pin this step's products here: otherwise the compiler may sink the
+    // matrix instructions past later steps' barriers and loads.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(acc[i][j]));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int ks0 = 0;
+#pragma unroll 1
+  for (; ks0 + D <= nsteps; ks0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(ks0 + d, S[d], S[(d + D - 1) % D]);
+  }
+#pragma unroll
+  for (int d = 0; d + 1 < D; ++d)
+    if (ks0 + d < nsteps) step(ks0 + d, S[d], S[(d + D - 1) % D]);
+  lds_barrier();  // the epilogue reuses the LDS
 
   // ------------------------------------------------------------ epilogues
   const int col = lane & 15, rq = (lane >> 4) * 4;
@@ -351,7 +407,7 @@ __global__ __launch_bounds__(256) void k_mfma_ffn(FfnParams P, MfmaBufs B) {
         ht[row * 64 + (2 * wn + jj) * 16 + col] = silu_f32(g) * u;
       }
     }
-  __syncthreads();
+  lds_barrier();
   const int row = tid >> 1, blk = tid & 1;  // 128 rows x 2 blocks of 32 columns
   if (row < tj.rows) {
     const size_t p = (size_t)tj.p0 + tj.m0 + row;
@@ -390,20 +446,33 @@ static int max_tiles(const FfnParams& P, int NT) {
   return (int)g;
 }
 
+typedef void (*MfmaKernel)(FfnParams, MfmaBufs);
+
+// Pipeline depth: 2 register stages for FP4 (its operands and scales leave
+// no room for a third), 3 for BF16 when the K-steps divide by 3.
+template <bool FP4, int MODE>
+static MfmaKernel mfma_kernel(int nsteps) {
+  if constexpr (!FP4)
+    if (nsteps % 3 == 0) return k_mfma_ffn<FP4, MODE, 3>;
+  return k_mfma_ffn<FP4, MODE, 2>;
+}
+
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s) {
   const int nt_gu = (2 * P.I) / kBN, nt_dn = P.H / kBN;
+  MfmaKernel k1, k2;
   if (fp4) {
     hipError_t e = launch_quant_mxfp4(P.x, P.T, P.H, const_cast<uint8_t*>(B.xq), const_cast<uint8_t*>(B.xs), s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_mfma_ffn<true, kGateUp>), dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((k_mfma_ffn<true, kDown>), dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
+    k1 = mfma_kernel<true, kGateUp>((P.H + 255) / 256);
+    k2 = mfma_kernel<true, kDown>((P.I + 255) / 256);
   } else {
-    hipLaunchKernelGGL((k_mfma_ffn<false, kGateUp>), dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_mfma_ffn<false, kDown>), dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
+    k1 = mfma_kernel<false, kGateUp>(P.H / 64);
+    k2 = mfma_kernel<false, kDown>(P.I / 64);
   }
+  hipLaunchKernelGGL(k1, dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k2, dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
   return hipGetLastError();
 }
 
