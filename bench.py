@@ -39,12 +39,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def routed_bytes(blob_bytes, counts):
-    return int(np.count_nonzero(counts)) * blob_bytes
+def moe_w13_bytes(fmt, H, I):
+    """Packed gate + up weights and scales of one expert (E2M1 + E8M0 per 32,
+    E2M1 + E4M3 per 16 + per-tensor fp32 scales, or bf16)."""
+    n = 2 * H * I
+    if fmt == "bf16":
+        return 2 * n
+    if fmt == "mxfp4":
+        return n // 2 + n // 32
+    return n // 2 + n // 16 + 8
 
 
-def ffn_flops(counts, H, I, shared_rows=0):
-    return 2.0 * 3 * H * I * (int(np.sum(counts)) + shared_rows)
+def measured_traffic(workload, root):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy's reading), or
+    None when there is none or its kernel sources have changed since."""
+    import hashlib
+    path = os.path.join(root, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    h = hashlib.sha256()
+    for src in t.get("sources", []):
+        with open(os.path.join(root, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest() != t.get("sources_sha256"):
+        return None
+    return t.get("bytes_per_launch")
 
 
 class Timer:
@@ -100,7 +122,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--stream-tokens", type=int, default=512, help="tokens of the stream workload")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="first run three plain device copies of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="no GPU work: 'stats CSV OUT CMD' writes a kernel-time summary; "
+                         "'traffic FETCH_CSV WRITE_CSV COPY_MIB OUT CMD' writes the dominant kernel's HBM bytes")
     args = ap.parse_args()
+    if args.summarize:
+        return summarize(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md, 'How the path would shard').", file=sys.stderr)
@@ -172,6 +201,15 @@ def main():
     blob_bytes = layers[0].blob_bytes
     del blobs
 
+    if args.calibration_copy:
+        n = args.calibration_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # one elementwise kernel: reads and writes MIB MiB
+        torch.cuda.synchronize()
+        del src, dst
+
     # One "combo" per input batch group: its own routing/output buffers, weights copy i % copies.
     combos = []
     for i, group in enumerate(inputs):
@@ -194,20 +232,13 @@ def main():
                 st.route(T, x=x, w_router=wr, logits=lg)
                 st.ffn(T, x, args=a)
 
-    def run_ffn():
-        for calls in combos:
-            for (T, x, lg, wr, st, a) in calls:
-                st.ffn(T, x, args=a)
-
-    # eager pass (library set-up, workspace sizing), then capture both sequences as HIP graphs
+    # eager pass (library set-up, workspace sizing), then capture the sequence as a HIP graph
     run_full()
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
-    g_full, g_ffn = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    g_full = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_full, stream=side):
         run_full()
-    with torch.cuda.graph(g_ffn, stream=side):
-        run_ffn()
     torch.cuda.synchronize()
 
     replays = max(1, -(-steps // n_per_graph))
@@ -225,43 +256,67 @@ def main():
     wall = time.perf_counter() - t_start
     value = toks_per_step * steps / wall
 
-    # FFN-only graph (routing buffers hold the last full pass): per-launch FFN duration
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g_ffn.replay()
-    torch.cuda.synchronize()
-    e0.record()
+    # Dominant kernel (the gate/up projection): its launch durations from HIP
+    # events recorded at the kernel's own start and end (moe_expert_ffn_traced),
+    # over the same calls run eagerly, the same number of steps.  Launch order:
+    # GEMV path gate/up, down, combine; FP4 path quantiser, gate/up, down,
+    # combine; BF16 matrix-core path gate/up, down, combine.
+    from fp4_expert_ffn_amd import moe_expert_ffn_traced
+    dom = 1 if amode == "mxfp4" else 0
+    stream_now = torch.cuda.current_stream()
+    pairs = []
     for _ in range(replays):
-        g_ffn.replay()
-    e1.record()
+        for calls in combos:
+            for (T, x, lg, wr, st, a) in calls:
+                st.route(T, x=x, w_router=wr, logits=lg)
+                evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+                for e in evs:
+                    e.record(stream_now)  # creates the HIP events; re-recorded by the launches
+                n = moe_expert_ffn_traced(a, evs)
+                assert n >= 2 * (dom + 1), n
+                pairs.append((evs[2 * dom], evs[2 * dom + 1]))
     torch.cuda.synchronize()
-    ffn_ms = e0.elapsed_time(e1)
-    n_calls = replays * sum(len(c) for c in combos)
+    durs = [e0.elapsed_time(e1) for e0, e1 in pairs]
+    dom_ms = sum(durs) / len(durs)
 
-    # algorithmic bytes / flops of the FFN calls (from the routing each combo holds)
-    tot_bytes, tot_flops = 0, 0.0
+    # algorithmic bytes / flops of the dominant kernel (gate/up projection + SwiGLU),
+    # per launch, from the routing each call holds
+    w13_bytes = moe_w13_bytes(fmt, H, I)
+    tot_bytes, tot_flops, n_calls = 0, 0.0, 0
     for calls in combos:
         for (T, x, lg, wr, st, a) in calls:
             cn = st.counts.cpu().numpy()
-            tot_bytes += routed_bytes(blob_bytes, cn) + (blob_bytes if shared else 0) + T * H * 2 * 2
-            tot_flops += ffn_flops(cn, H, I, T if shared else 0)
-    tot_bytes *= replays
-    tot_flops *= replays
-    avg_ms = ffn_ms / n_calls
-    bytes_per_call = tot_bytes / n_calls
-    if wl in ("prefill-mxfp4", "large-prefill"):
-        ach = tot_flops / n_calls / (avg_ms * 1e-3) / 1e12
+            rows = int(np.sum(cn)) + (T if shared else 0)
+            active = int(np.count_nonzero(cn)) + (1 if shared else 0)
+            act = 2 if amode == "bf16" else 0.53125  # bf16, or MXFP4 codes + E8M0 per 32, per value
+            tot_bytes += active * w13_bytes + T * H * act + rows * I * act
+            tot_flops += 2.0 * rows * 2 * I * H
+            n_calls += 1
+    bytes_per_launch = tot_bytes / n_calls
+    flops_per_launch = tot_flops / n_calls
+    kname = {"bf16": "k_gemv (gate/up projection + SwiGLU, bf16 operands)",
+             "mxfp4": "k_mfma_ffn (gate/up projection + SwiGLU, FP4 matrix cores)"}[amode]
+    if wl.startswith("prefill-bf16"):
+        kname = "k_mfma_ffn (gate/up projection + SwiGLU, bf16 matrix cores)"
+    elif fmt == "nvfp4":
+        kname = "k_gemv (gate/up projection + SwiGLU, NVFP4 weights on fp16 matrix cores)"
+    if amode == "mxfp4":
+        ach = flops_per_launch / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_PEAK_TFLOPS["fp4"], 4)}
-        roof["hbm_gbs_same_kernel"] = round(bytes_per_call / (avg_ms * 1e-3) / 1e9, 1)
+        roof["hbm_gbs_same_kernel"] = round(bytes_per_launch / (dom_ms * 1e-3) / 1e9, 1)
     else:
-        ach = bytes_per_call / (avg_ms * 1e-3) / 1e9
+        ach = bytes_per_launch / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
-    roof["traffic"] = None
-    roof["kernel"] = "moe_expert_ffn (all of its launches, back to back in a HIP graph)"
-    roof["avg_launch_us"] = round(avg_ms * 1e3, 3)
-    roof["algorithmic_bytes_per_launch"] = int(bytes_per_call)
-    roof["algorithmic_flops_per_launch"] = int(tot_flops / n_calls)
+        if fmt == "bf16":
+            roof["bf16_mfma_tflops_same_kernel"] = round(flops_per_launch / (dom_ms * 1e-3) / 1e12, 1)
+    roof["traffic"] = measured_traffic(wl, ROOT)
+    roof["kernel"] = kname
+    roof["avg_launch_us"] = round(dom_ms * 1e3, 3)
+    roof["launches_averaged"] = len(durs)
+    roof["algorithmic_bytes_per_launch"] = int(bytes_per_launch)
+    roof["algorithmic_flops_per_launch"] = int(flops_per_launch)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -326,9 +381,77 @@ def main():
                    "hidden": H, "intermediate": I, "weights": fmt, "hbm_copies": len(layers),
                    "parallelism": "single GPU"},
         "roofline": roof,
+        "layer_ms_per_call": round(wall / (replays * n_calls) * 1e3, 4),
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))
+
+
+# Kernel-name patterns of the dominant kernel (gate/up projection) per workload.
+DOMINANT = {"decode": "k_gemv<2, false", "large-decode": "k_gemv<1, false", "prefill-mxfp4": "k_mfma_ffn<true, 0",
+            "large-prefill": "k_mfma_ffn<true, 0", "prefill-bf16": "k_mfma_ffn<false, 0"}
+KERNEL_SOURCES = ["fp4_expert_ffn_amd/csrc/ffn_gemv.hip", "fp4_expert_ffn_amd/csrc/ffn_mfma.hip",
+                  "fp4_expert_ffn_amd/csrc/ffn_common.h", "fp4_expert_ffn_amd/csrc/common.h"]
+
+
+def _pmc_rows(path, counter):
+    import csv
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize(args):
+    """Text summaries of rocprofv3 output for profiles/ (runs no GPU work)."""
+    import csv
+    import hashlib
+    kind = args.summarize[0]
+    if kind == "stats":
+        src, out, cmd = args.summarize[1:4]
+        with open(src) as f:
+            rows = list(csv.DictReader(f))
+        lines = [f"# rocprofv3 kernel statistics", f"# command: {cmd}", "",
+                 f"{'kernel':<90} {'calls':>7} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
+        for r in rows[:12]:
+            lines.append(f"{r['Name'][:90]:<90} {int(r['Calls']):>7} {float(r['AverageNs']) / 1e3:>10.2f} "
+                         f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
+                         f"{float(r['Percentage']):>6.2f}")
+        with open(out, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(f"wrote {out}")
+        return
+    if kind == "traffic":
+        fetch_csv, write_csv, copy_mib, out, cmd = args.summarize[1:6]
+        wl = os.path.basename(out)[len("traffic_"):-len(".json")]
+        pat = DOMINANT[wl]
+        copy_bytes = int(copy_mib) << 20
+        res = {}
+        for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+            rows = _pmc_rows(path, name)
+            cal = [v for k, v in rows if "neg" in k][:3]
+            dom = [v for k, v in rows if pat in k]
+            if not cal or not dom:
+                raise SystemExit(f"{name}: no calibration copy or no {pat} dispatch in {path}")
+            res[name] = {"kib_per_dispatch": sum(dom) / len(dom), "dispatches": len(dom),
+                         "copy_kib": sum(cal) / len(cal), "bytes_per_kib": copy_bytes / (sum(cal) / len(cal))}
+        h = hashlib.sha256()
+        for src in KERNEL_SOURCES:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        fetch = res["FETCH_SIZE"]["kib_per_dispatch"] * res["FETCH_SIZE"]["bytes_per_kib"]
+        write = res["WRITE_SIZE"]["kib_per_dispatch"] * res["WRITE_SIZE"]["bytes_per_kib"]
+        t = {"workload": wl, "kernel_pattern": pat, "command": cmd, "counters": res,
+             "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
+             "bytes_per_launch": int(fetch + write), "copy_bytes": copy_bytes,
+             "sources": KERNEL_SOURCES, "sources_sha256": h.hexdigest()}
+        with open(out, "w") as f:
+            json.dump(t, f, indent=1)
+        print(f"wrote {out}: {int(fetch + write)} bytes per launch")
+        return
+    raise SystemExit(f"unknown summary kind {kind}")
 
 
 def bench_stream(args):

@@ -71,6 +71,7 @@ SIGNATURES = {
     "moe_prepack_expert": (_i, [ctypes.POINTER(ExpertCanonical), _vp, _sz]),
     "moe_expert_ffn_workspace_size": (_sz, [ctypes.POINTER(FfnArgs)]),
     "moe_expert_ffn": (_i, [ctypes.POINTER(FfnArgs), _vp]),
+    "moe_expert_ffn_traced": (_i, [ctypes.POINTER(FfnArgs), _vp, _vp, _i, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "moe_workspace_init": (_i, [_vp, _sz, _vp]),
     "moe_workspace_check": (_i, [_vp, _vp]),
@@ -213,6 +214,16 @@ def moe_expert_ffn_workspace_size(args: FfnArgs) -> int:
 
 def moe_expert_ffn(args: FfnArgs, stream=None):
     _check(lib().moe_expert_ffn(ctypes.byref(args), stream_handle(stream)), "moe_expert_ffn")
+
+
+def moe_expert_ffn_traced(args: FfnArgs, events, stream=None) -> int:
+    """moe_expert_ffn recording the given events (torch.cuda.Event, already
+    created) around its kernel launches; returns how many were recorded."""
+    arr = (ctypes.c_void_p * max(len(events), 1))(*[e.cuda_event for e in events])
+    n = ctypes.c_int(0)
+    _check(lib().moe_expert_ffn_traced(ctypes.byref(args), stream_handle(stream), arr, len(events), ctypes.byref(n)),
+           "moe_expert_ffn_traced")
+    return n.value
 
 
 def moe_workspace_init(workspace, workspace_bytes, stream=None):

@@ -1,5 +1,6 @@
 // Internal header of libmoe (not installed).  gfx950 only.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -112,6 +113,28 @@ __device__ inline BlobView blob_view(const uint8_t* b, const BlobLayout& L) {
   v.g_up = h->g[1];
   v.g_down = h->g[2];
   return v;
+}
+
+// ---------------------------------------------------------------- launch tracing
+// moe_expert_ffn_traced hands caller-created events to every kernel launch of
+// one call through this per-thread hook: launch i records events 2i and 2i+1
+// at the kernel's own start and end (hipExtLaunchKernelGGL).
+struct LaunchTrace {
+  void* const* events;  // hipEvent_t
+  int n, used;
+};
+extern thread_local LaunchTrace* g_launch_trace;
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s, Args... args) {
+  LaunchTrace* t = g_launch_trace;
+  if (t && t->used + 2 <= t->n) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, s, static_cast<hipEvent_t>(t->events[t->used]),
+                          static_cast<hipEvent_t>(t->events[t->used + 1]), 0u, args...);
+    t->used += 2;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+  }
 }
 
 // ---------------------------------------------------------------- numerics helpers

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(128) void k_combine(const float* __restrict__ y, co
 hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, const float* ysh, int T, int k, int H,
                           uint16_t* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3((H / 8 + 127) / 128, T), dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
+  launch(k_combine, dim3((H / 8 + 127) / 128, T), dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
   return hipGetLastError();
 }
 
@@ -234,8 +234,21 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     const float* ysh = a->shared_blob ? y + (size_t)a->T * a->k * a->H : nullptr;
     e = launch_combine(y, a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
     if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));
-  }
+    }
   return MOE_OK;
+}
+
+thread_local LaunchTrace* moe::g_launch_trace = nullptr;
+
+extern "C" moe_status moe_expert_ffn_traced(const moe_ffn_args* a, moe_stream_t stream, void* const* events,
+                                            int n_events, int* n_recorded) {
+  MOE_CHECK_ARG(n_events >= 0 && (n_events == 0 || events) && n_recorded, "moe_expert_ffn_traced: bad event list");
+  LaunchTrace t{events, n_events, 0};
+  g_launch_trace = &t;
+  const moe_status st = moe_expert_ffn(a, stream);
+  g_launch_trace = nullptr;
+  *n_recorded = t.used;
+  return st;
 }
 
 extern "C" moe_status moe_combine(const float* y, const int32_t* inv, const float* topk_w, const float* y_shared, int T,

@@ -532,11 +532,12 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   const long long cap2 = (long long)blocks_per_cu(reinterpret_cast<const void*>(k2), lds2) * cu_count();
   const int g1 = (int)std::max<long long>(1, std::min<long long>(nrb(G.rbs1) * G.ng, cap1));
   const int g2 = (int)std::max<long long>(1, std::min<long long>(nrb(G.rbs2) * G.nd, cap2));
-  hipLaunchKernelGGL(k1, dim3(g1), dim3(256), lds1, s, P, G);
+  launch(k1, dim3(g1), dim3(256), lds1, s, P, G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k2, dim3(g2), dim3(256), lds2, s, P, G);
-  return hipGetLastError();
+  launch(k2, dim3(g2), dim3(256), lds2, s, P, G);
+  e = hipGetLastError();
+  return e;
 }
 
 template <int FMT, bool DOWN>

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void k_quant_mxfp4(const uint16_t* __restrict_
 hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st) {
   const long long n = (long long)rows * (cols / 32);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_quant_mxfp4, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, rows, cols, q, s);
+  launch(k_quant_mxfp4, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, rows, cols, q, s);
   return hipGetLastError();
 }
 
@@ -463,17 +463,18 @@ hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStrea
   if (fp4) {
     hipError_t e = launch_quant_mxfp4(P.x, P.T, P.H, const_cast<uint8_t*>(B.xq), const_cast<uint8_t*>(B.xs), s);
     if (e != hipSuccess) return e;
-    k1 = mfma_kernel<true, kGateUp>((P.H + 255) / 256);
+      k1 = mfma_kernel<true, kGateUp>((P.H + 255) / 256);
     k2 = mfma_kernel<true, kDown>((P.I + 255) / 256);
   } else {
     k1 = mfma_kernel<false, kGateUp>(P.H / 64);
     k2 = mfma_kernel<false, kDown>(P.I / 64);
   }
-  hipLaunchKernelGGL(k1, dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
+  launch(k1, dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k2, dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
-  return hipGetLastError();
+  launch(k2, dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
+  e = hipGetLastError();
+  return e;
 }
 
 }  // namespace moe

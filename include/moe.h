@@ -182,6 +182,17 @@ size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a);
  * MXFP4).  Requires H, I multiples of 128, 1 <= k <= 16, E <= 1024. */
 moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream);
 
+/* moe_expert_ffn, timing each of its kernel launches with caller-created HIP
+ * events (hipEvent_t, passed as void*): launch i records events[2i] and
+ * events[2i + 1] at the kernel's own start and end (hipExtLaunchKernelGGL),
+ * for as many launches as n_events covers; *n_recorded (host) receives the
+ * number of events recorded.  Launch order: BF16-activation GEMV path:
+ * gate/up, down[, combine]; FP4 matrix-core path: activation quantiser,
+ * gate/up, down[, combine]; BF16 matrix-core path: gate/up, down[, combine].
+ * For measuring one kernel of the layer; not for stream capture. */
+moe_status moe_expert_ffn_traced(const moe_ffn_args* a, moe_stream_t stream, void* const* events, int n_events,
+                                 int* n_recorded);
+
 /* Weighted combine back to token order:
  * out[t,:] = bf16( sum_{j=0..k-1} topk_w[t,j] * y[inv[t*k+j],:]  (+ y_shared[t,:]) ).
  * y: [T*k][H] fp32 in perm order; y_shared: nullable [T][H] fp32. */
