@@ -300,7 +300,8 @@ def main():
         kname = "k_mfma_ffn (gate/up projection + SwiGLU, bf16 matrix cores)"
     elif fmt == "nvfp4":
         kname = "k_gemv (gate/up projection + SwiGLU, NVFP4 weights on fp16 matrix cores)"
-    if amode == "mxfp4":
+    # The large-expert prefill sits below the FP4 ridge (about 267 FLOP/B): HBM bounds it.
+    if amode == "mxfp4" and wl != "large-prefill":
         ach = flops_per_launch / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_PEAK_TFLOPS["fp4"], 4)}
@@ -311,6 +312,8 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
         if fmt == "bf16":
             roof["bf16_mfma_tflops_same_kernel"] = round(flops_per_launch / (dom_ms * 1e-3) / 1e12, 1)
+        if amode == "mxfp4":
+            roof["fp4_mfma_tflops_same_kernel"] = round(flops_per_launch / (dom_ms * 1e-3) / 1e12, 1)
     roof["traffic"] = measured_traffic(wl, ROOT)
     roof["kernel"] = kname
     roof["avg_launch_us"] = round(dom_ms * 1e3, 3)
