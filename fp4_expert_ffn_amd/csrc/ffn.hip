@@ -47,6 +47,8 @@ struct WsLayout {
 
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
+bool internal_bf16_y(const moe_ffn_args* a) { return !a->y && a->out && choose_path(a) != kPathGemv; }
+
 WsLayout ws_layout(const moe_ffn_args* a) {
   const size_t R = (size_t)a->T * a->k + (a->shared_blob ? a->T : 0);
   WsLayout w{};
@@ -64,8 +66,10 @@ WsLayout ws_layout(const moe_ffn_args* a) {
   } else {
     w.hb = o; o = al(o + R * a->I * 2);
   }
+  // Internal expert outputs: bf16 on the matrix-core paths when only the
+  // combined output is wanted (halves the y round trip), else fp32.
   w.y = o;
-  if (!a->y) o = al(o + R * a->H * sizeof(float));
+  if (!a->y) o = al(o + R * a->H * (internal_bf16_y(a) ? 2 : sizeof(float)));
   w.total = o;
   return w;
 }
@@ -105,9 +109,25 @@ moe_status check_args(const moe_ffn_args* a) {
   return MOE_OK;
 }
 
+// Eight expert outputs starting at p (fp32 or bf16) as floats.
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
 // out[t, c..c+8) = bf16( sum_j w[t,j] * y[inv[t*k+j], c..] (+ y[T*k + t, c..]) )
-__global__ __launch_bounds__(128) void k_combine(const float* __restrict__ y, const int32_t* __restrict__ inv,
-                                                 const float* __restrict__ w, const float* __restrict__ ysh, int T,
+template <typename YT>
+__global__ __launch_bounds__(128) void k_combine(const YT* __restrict__ y, const int32_t* __restrict__ inv,
+                                                 const float* __restrict__ w, const YT* __restrict__ ysh, int T,
                                                  int k, int H, uint16_t* __restrict__ out) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * 128 + threadIdx.x) * 8;
@@ -115,18 +135,16 @@ __global__ __launch_bounds__(128) void k_combine(const float* __restrict__ y, co
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int j = 0; j < k; ++j) {
     const float wj = w[(size_t)t * k + j];
-    const float4* src = reinterpret_cast<const float4*>(y + (size_t)inv[(size_t)t * k + j] * H + c);
-    const float4 a = src[0], b = src[1];
-    acc[0] = fmaf(wj, a.x, acc[0]); acc[1] = fmaf(wj, a.y, acc[1]);
-    acc[2] = fmaf(wj, a.z, acc[2]); acc[3] = fmaf(wj, a.w, acc[3]);
-    acc[4] = fmaf(wj, b.x, acc[4]); acc[5] = fmaf(wj, b.y, acc[5]);
-    acc[6] = fmaf(wj, b.z, acc[6]); acc[7] = fmaf(wj, b.w, acc[7]);
+    float v[8];
+    load8(y + (size_t)inv[(size_t)t * k + j] * H + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
   }
   if (ysh) {
-    const float4* src = reinterpret_cast<const float4*>(ysh + (size_t)t * H + c);
-    const float4 a = src[0], b = src[1];
-    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    float v[8];
+    load8(ysh + (size_t)t * H + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += v[i];
   }
   uint32_t o[4];
 #pragma unroll
@@ -134,10 +152,11 @@ __global__ __launch_bounds__(128) void k_combine(const float* __restrict__ y, co
   *reinterpret_cast<uint4*>(out + (size_t)t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-hipError_t launch_combine(const float* y, const int32_t* inv, const float* w, const float* ysh, int T, int k, int H,
+template <typename YT>
+hipError_t launch_combine(const YT* y, const int32_t* inv, const float* w, const YT* ysh, int T, int k, int H,
                           uint16_t* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  launch(k_combine, dim3((H / 8 + 127) / 128, T), dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
+  launch(k_combine<YT>, dim3((H / 8 + 127) / 128, T), dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
   return hipGetLastError();
 }
 
@@ -222,6 +241,7 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
   } else {
     MfmaBufs B{};
     B.y = y;
+    if (internal_bf16_y(a)) B.yb = reinterpret_cast<uint16_t*>(ws + w.y);
     if (path == kPathMfmaFp4) {
       B.xq = ws + w.xq; B.xs = ws + w.xs; B.hq = ws + w.hq; B.hs = ws + w.hs;
     } else {
@@ -230,7 +250,12 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     e = launch_mfma(P, path == kPathMfmaFp4, B, s);
   }
   if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: launch failed: %s", hipGetErrorString(e));
-  if (a->out) {
+  if (a->out && internal_bf16_y(a)) {
+    const uint16_t* yb = reinterpret_cast<const uint16_t*>(ws + w.y);
+    const uint16_t* ysh = a->shared_blob ? yb + (size_t)a->T * a->k * a->H : nullptr;
+    e = launch_combine(yb, a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
+    if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));
+  } else if (a->out) {
     const float* ysh = a->shared_blob ? y + (size_t)a->T * a->k * a->H : nullptr;
     e = launch_combine(y, a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
     if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));

@@ -37,6 +37,7 @@ struct MfmaBufs {
   uint8_t* hs;         //                    [R][I/32] E8M0
   uint16_t* hb;        // BF16 SwiGLU output: [R][I]
   float* y;            // expert outputs: [R][H] fp32, perm order
+  uint16_t* yb;        // if set, the expert outputs go here instead, as bf16
 };
 
 // Counters of the single-launch GEMV (first bytes of the workspace).  Zero

@@ -194,7 +194,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // K-tiles; BF16: K = 64, two 32-wide K-tiles): 16 KiB per operand.
   constexpr int KSTEP = FP4 ? 256 : 64;
   constexpr int kStage = 16384;
-  constexpr int kBuf = 2 * kStage + (FP4 ? 2048 : 0);  // A, B (+ A and B scale bytes)
+  // A rows are kept row-major with a 16-byte pad (144-byte stride): the
+  // fragment reads (16 rows at once) then hit 16 distinct bank groups.
+  constexpr int kArow = 144, kAbytes = 128 * kArow;
+  constexpr int kBoff = kAbytes, kSoff = kAbytes + kStage;
+  constexpr int kBuf = kAbytes + kStage + (FP4 ? 2048 : 0);  // A, B (+ A and B scale bytes)
   __shared__ __align__(16) uint8_t lds[2 * kBuf];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -223,8 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const size_t pr = (size_t)tj.p0 + tj.m0 + r;
       arow[i] = FP4 ? B.hq + pr * (P.I / 2) : reinterpret_cast<const uint8_t*>(B.hb + pr * P.I);
     }
-    // fragment (16-row tile mt, K-tile seg / 4), lane (seg % 4) * 16 + row % 16
-    a_lds[i] = (((row >> 4) * 2 + (seg >> 2)) * 64 + (seg & 3) * 16 + (row & 15)) * 16;
+    a_lds[i] = row * kArow + seg * 16;
     arow[i] += seg * 16;
   }
   // FP4 A scales: 8 bytes (the step's eight 32-blocks) of row tid / 2, half tid % 2.
@@ -284,12 +287,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 4; ++i) {
       const uint32_t k = akeep[i] & lk & ((tail && seg >= 4) ? 0u : 0xFFFFFFFFu);  // bit masks: branch-free
       *reinterpret_cast<uint4*>(buf + a_lds[i]) = make_uint4(S.a[i].x & k, S.a[i].y & k, S.a[i].z & k, S.a[i].w & k);
-      reinterpret_cast<uint4*>(buf + kStage)[tid + 256 * i] = S.b[i];
+      reinterpret_cast<uint4*>(buf + kBoff)[tid + 256 * i] = S.b[i];
     }
     if (FP4) {
       const uint32_t k = askeep & lk & ((tail && (tid & 1)) ? 0u : 0xFFFFFFFFu);
-      reinterpret_cast<uint32_t*>(buf + 2 * kStage)[tid] = (S.sa & k) | (0x7F7F7F7Fu & ~k);
-      reinterpret_cast<uint32_t*>(buf + 2 * kStage + 1024)[tid] = S.sb;
+      reinterpret_cast<uint32_t*>(buf + kSoff)[tid] = (S.sa & k) | (0x7F7F7F7Fu & ~k);
+      reinterpret_cast<uint32_t*>(buf + kSoff + 1024)[tid] = S.sb;
     }
   };
 
@@ -299,9 +302,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // A fragment of 16-row tile mt: lane l reads row mt*16 + l%16, bytes
+  // [kt*64 + (l/16)*16, +16) of the step (FP4: K-tile kt, 32-block l/16;
+  // BF16: 32-wide K-tile kt, 8 values l/16).
+  auto a_frag = [&](const uint8_t* buf, int mt, int kt) {
+    return *reinterpret_cast<const uint4*>(buf + (mt * 16 + (lane & 15)) * kArow + kt * 64 + (lane >> 4) * 16);
+  };
   auto compute = [&](const uint8_t* buf) {
-    const uint4* As = reinterpret_cast<const uint4*>(buf);
-    const uint4* Bs = reinterpret_cast<const uint4*>(buf + kStage);
+    const uint4* Bs = reinterpret_cast<const uint4*>(buf + kBoff);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       if (FP4) {
@@ -310,12 +318,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int mt = 4 * wm + i, nt = 4 * wn + i;
-          const uint4 u = As[(mt * 2 + kt) * 64 + lane];
+          const uint4 u = a_frag(buf, mt, kt);
           a[i] = i32x8_t{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-          sa[i] = buf[2 * kStage + (mt * 16 + (lane & 15)) * 8 + kt * 4 + (lane >> 4)];
+          sa[i] = buf[kSoff + (mt * 16 + (lane & 15)) * 8 + kt * 4 + (lane >> 4)];
           const uint4 v = Bs[(nt * 2 + kt) * 64 + lane];
           b[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          sb[i] = buf[2 * kStage + 1024 + (nt * 2 + kt) * 64 + lane];
+          sb[i] = buf[kSoff + 1024 + (nt * 2 + kt) * 64 + lane];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -327,7 +335,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bf16x8_t a[4], b[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          a[i] = __builtin_bit_cast(bf16x8_t, As[((4 * wm + i) * 2 + kt) * 64 + lane]);
+          a[i] = __builtin_bit_cast(bf16x8_t, a_frag(buf, 4 * wm + i, kt));
           b[i] = __builtin_bit_cast(bf16x8_t, Bs[((4 * wn + i) * 2 + kt) * 64 + lane]);
         }
 #pragma unroll
@@ -387,9 +395,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int v = 0; v < 4; ++v) {
         const int row = (4 * wm + i) * 16 + rq + v;
         if (row < tj.rows) {
-          float* yr = B.y + ((size_t)tj.p0 + tj.m0 + row) * P.H + tj.nt * kBN + (4 * wn) * 16 + col;
+          const size_t o = ((size_t)tj.p0 + tj.m0 + row) * P.H + tj.nt * kBN + (4 * wn) * 16 + col;
+          if (B.yb) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) yr[16 * j] = acc[i][j][v];
+            for (int j = 0; j < 4; ++j) B.yb[o + 16 * j] = f32_to_bf16_rne(acc[i][j][v]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) B.y[o + 16 * j] = acc[i][j][v];
+          }
         }
       }
     return;

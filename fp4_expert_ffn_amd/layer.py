@@ -57,7 +57,7 @@ class LayerState:
         a = L.ffn_args(T=T, k=lay.k, E=lay.E, H=lay.H, I=lay.I, wfmt=lay.fmt, amode=lay.amode, x=x,
                        counts=self.counts, offsets=self.offsets, perm=self.perm,
                        slot_of_expert=lay.slot_of_expert, slot_pool=lay.pool, slot_stride=lay.stride,
-                       shared_blob=lay.shared_blob, expert_mask=mask, y=self.y,
+                       shared_blob=lay.shared_blob, expert_mask=mask, y=None if out else self.y,
                        topk_w=self.w if out else None, inv=self.inv if out else None,
                        out=self.out if out else None)
         need = L.moe_expert_ffn_workspace_size(a)

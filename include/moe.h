@@ -150,7 +150,8 @@ typedef struct {
                                    out must then be null (combine with moe_combine)      */
   float* y;                     /* nullable: [T*k (+T if shared)][H] fp32 expert outputs
                                    in perm order (shared rows last).  If null, y lives in
-                                   the workspace.                                        */
+                                   the workspace (as bf16 on the matrix-core paths when
+                                   out is set: the combine then reads bf16 values).      */
   const float* topk_w;          /* nullable with out: [T,k] routing weights              */
   const int32_t* inv;           /* nullable with out: [T*k] from moe_permute             */
   uint16_t* out;                /* nullable: [T,H] bf16; if set, the combine runs too    */
