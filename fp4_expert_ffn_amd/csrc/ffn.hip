@@ -10,16 +10,6 @@
 #include "ffn_common.h"
 
 namespace moe {
-struct GemvArgs {
-  uint16_t* h;
-  float* y;
-  GemvSync* sync;
-  int ng, nd;
-  int rbs1, rbs2;
-  int x_all;
-  int x_bytes;
-  float* trash;
-};
 hipError_t launch_gemv(const FfnParams& P, const GemvArgs& G, hipStream_t s);
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s);
 hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st);
@@ -124,28 +114,39 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
   }
 }
 
-// out[t, c..c+8) = bf16( sum_j w[t,j] * y[inv[t*k+j], c..] (+ y[T*k + t, c..]) )
-template <typename YT>
+// out[t, c..c+8) = bf16( sum_j w[t,j] * y[inv[t*k+j], c..] (+ y[T*k + t, c..]) ).
+// KMAX >= k: the row indices and weights are loaded first, then every y row
+// (branch-free: slots past k re-read row k-1 with weight 0), so the loads
+// overlap instead of forming k dependent round trips.
+template <typename YT, int KMAX>
 __global__ __launch_bounds__(128) void k_combine(const YT* __restrict__ y, const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w, const YT* __restrict__ ysh, int T,
                                                  int k, int H, uint16_t* __restrict__ out) {
   const int t = blockIdx.y;
   const int c = (blockIdx.x * 128 + threadIdx.x) * 8;
   if (c >= H) return;
+  int row[KMAX];
+  float wj[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int jj = min(j, k - 1);
+    row[j] = inv[(size_t)t * k + jj];
+    wj[j] = w[(size_t)t * k + jj];
+  }
+  float v[KMAX][8];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) load8(y + (size_t)row[j] * H + c, v[j]);
+  float vs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (ysh) load8(ysh + (size_t)t * H + c, vs);
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[(size_t)t * k + j];
-    float v[8];
-    load8(y + (size_t)inv[(size_t)t * k + j] * H + c, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
-  }
-  if (ysh) {
-    float v[8];
-    load8(ysh + (size_t)t * H + c, v);
+  for (int j = 0; j < KMAX; ++j) {
+    const float ww = j < k ? wj[j] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(ww, v[j][i], acc[i]);
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] += vs[i];
   uint32_t o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i]) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
@@ -156,7 +157,11 @@ template <typename YT>
 hipError_t launch_combine(const YT* y, const int32_t* inv, const float* w, const YT* ysh, int T, int k, int H,
                           uint16_t* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  launch(k_combine<YT>, dim3((H / 8 + 127) / 128, T), dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
+  const dim3 g((H / 8 + 127) / 128, T);
+  if (k <= 2) launch(k_combine<YT, 2>, g, dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
+  else if (k <= 4) launch(k_combine<YT, 4>, g, dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
+  else if (k <= 8) launch(k_combine<YT, 8>, g, dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
+  else launch(k_combine<YT, 16>, g, dim3(128), 0, s, y, inv, w, ysh, T, k, H, out);
   return hipGetLastError();
 }
 
@@ -233,7 +238,6 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     GemvArgs G{};
     G.h = reinterpret_cast<uint16_t*>(ws + w.h);
     G.y = y;
-    G.sync = reinterpret_cast<GemvSync*>(ws + w.sync);
     G.trash = reinterpret_cast<float*>(ws + w.trash);
     G.ng = a->I / 32;
     G.nd = a->H / 64;

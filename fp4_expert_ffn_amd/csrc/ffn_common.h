@@ -9,6 +9,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -38,6 +39,17 @@ struct MfmaBufs {
   uint16_t* hb;        // BF16 SwiGLU output: [R][I]
   float* y;            // expert outputs: [R][H] fp32, perm order
   uint16_t* yb;        // if set, the expert outputs go here instead, as bf16
+};
+
+// Arguments of the decode (GEMV) launches beyond FfnParams.
+struct GemvArgs {
+  uint16_t* h;     // [R][I] bf16 SwiGLU output
+  float* y;        // [R][H] fp32 expert outputs
+  float* trash;    // 1 MiB of scratch: stores of padding rows land here
+  int ng, nd;      // gate/up and down column chunks per expert
+  int rbs1, rbs2;  // rows per row block (<= 16) of the two launches
+  int na;          // active-expert capacity of the LDS table
+  int act_off;     // LDS byte offset of the staged operand rows
 };
 
 // Counters of the single-launch GEMV (first bytes of the workspace).  Zero

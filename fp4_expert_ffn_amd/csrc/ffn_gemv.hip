@@ -20,6 +20,8 @@
 // dot products (with dot2 the per-row VALU work, not HBM, set the speed).
 // Lane l loads row (l % 16), K-chunk (l / 16) of each 1 KiB tile, so one
 // wave-wide 16-byte load is one contiguous tile.
+#include <type_traits>
+
 #include "ffn_common.h"
 #include "wave.h"
 
@@ -60,12 +62,16 @@ constexpr int kScaleTileBytes = FMT == MOE_FMT_MXFP4 ? 64 : FMT == MOE_FMT_NVFP4
 template <int FMT>
 constexpr int kScaleLaneBytes = FMT == MOE_FMT_MXFP4 ? 1 : FMT == MOE_FMT_NVFP4 ? 2 : 0;
 
-// A lane's scale bytes of one tile (p already offset to the lane).
+// A lane's scale bytes of one tile (p already offset to the lane), kept in
+// their loaded width: widening them right after the load would make the
+// compiler wait for it there.
 template <int FMT>
-__device__ __forceinline__ uint32_t load_scale_at(const uint8_t* p) {
+using ScaleT = typename std::conditional<FMT == MOE_FMT_NVFP4, uint16_t, uint8_t>::type;
+template <int FMT>
+__device__ __forceinline__ ScaleT<FMT> load_scale_at(const uint8_t* p) {
   if constexpr (FMT == MOE_FMT_MXFP4) return *p;
   if constexpr (FMT == MOE_FMT_NVFP4) return *reinterpret_cast<const uint16_t*>(p);
-  return 0u;
+  return 0;
 }
 
 // B operand of MFMA step s (8 values) from a lane's tile fragment, block
@@ -104,15 +110,32 @@ __device__ __forceinline__ typename Fmt<FMT>::V bfrag(const uint4 q, uint32_t sc
 // round of global loads: active expert a (ascending expert id among experts
 // with rows and an enabled mask; the shared expert last) has rows cnt[a],
 // first perm-order row p0[a], slot slot[a] (-1: shared) and row blocks of
-// `rbs` rows numbered [rb[a], rb[a+1]).  tok[p] caches perm[p] / k.
+// `rbs` rows numbered [rb[a], rb[a+1]).  tok[p] caches perm[p] / k when
+// T*k <= kTokCache.  The arrays live in dynamic LDS, sized for na active
+// experts (min(E, T*k) routed, plus the shared one).
 constexpr int kTokCache = 1024;
 struct ActiveLds {
-  int cnt[kMaxActive], p0[kMaxActive], slot[kMaxActive], rb[kMaxActive + 1];
-  int tok[kTokCache];
-  int n;
+  int *cnt, *p0, *slot, *rb, *tok;
+  int* n;
 };
 
-__device__ inline void build_active(const FfnParams& P, int rbs, ActiveLds& A) {
+__host__ __device__ inline size_t active_lds_bytes(int na, int ntok) {
+  return (size_t)(4 * na + 2 + ntok) * sizeof(int);
+}
+
+__device__ inline ActiveLds active_view(uint8_t* base, int na) {
+  int* b = reinterpret_cast<int*>(base);
+  ActiveLds A;
+  A.n = b;
+  A.cnt = b + 1;
+  A.p0 = A.cnt + na;
+  A.slot = A.p0 + na;
+  A.rb = A.slot + na;  // na + 1 entries
+  A.tok = A.rb + na + 1;
+  return A;
+}
+
+__device__ inline void build_active(const FfnParams& P, int rbs, const ActiveLds& A) {
   const int tid = threadIdx.x;
   const int N = P.T * P.k;
   if (tid >= 64) {
@@ -122,23 +145,22 @@ __device__ inline void build_active(const FfnParams& P, int rbs, ActiveLds& A) {
     // every load first (one round trip), then the compaction
     constexpr int kPer = 1024 / 64;
     int c[kPer], off[kPer], sl[kPer], mk[kPer];
+    // unconditional loads (indices clamped to E - 1), so they all issue
+    // before the first wait; lanes past E are zeroed afterwards
+    // (without a mask, the byte loads read the counts and are ignored)
+    const bool has_mask = P.mask != nullptr;
+    const uint8_t* mask = has_mask ? P.mask : reinterpret_cast<const uint8_t*>(P.counts);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int e = 64 * i + tid;
-      c[i] = 0;
-      off[i] = 0;
-      sl[i] = 0;
-      mk[i] = 1;
-      if (e < P.E) {
-        c[i] = P.counts[e];
-        off[i] = P.offsets[e];
-        sl[i] = P.slot_of_expert[e];
-        if (P.mask != nullptr) mk[i] = P.mask[e];
-      }
+      const int e = min(64 * i + tid, P.E - 1);
+      c[i] = P.counts[e];
+      off[i] = P.offsets[e];
+      sl[i] = P.slot_of_expert[e];
+      mk[i] = mask[has_mask ? e : 0];
     }
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      if (mk[i] == 0) c[i] = 0;
+      if ((has_mask && mk[i] == 0) || 64 * i + tid >= P.E) c[i] = 0;
     int seen = 0, rbrun = 0;
     const uint64_t lt = (tid == 0) ? 0ull : (~0ull >> (64 - tid));
 #pragma unroll
@@ -171,7 +193,7 @@ __device__ inline void build_active(const FfnParams& P, int rbs, ActiveLds& A) {
         A.rb[n + 1] = rbrun + (P.T + rbs - 1) / rbs;
         ++n;
       }
-      A.n = n;
+      *A.n = n;
     }
   }
   lds_barrier();
@@ -187,7 +209,7 @@ struct RowBlock {
 };
 
 __device__ inline RowBlock row_block(const FfnParams& P, const ActiveLds& A, int rbs, int rb) {
-  int lo = 0, hi = A.n - 1;  // active expert a with rb[a] <= rb < rb[a+1]
+  int lo = 0, hi = *A.n - 1;  // active expert a with rb[a] <= rb < rb[a+1]
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (A.rb[mid] <= rb) lo = mid; else hi = mid - 1;
@@ -207,77 +229,88 @@ __device__ __forceinline__ int row_token(const FfnParams& P, const ActiveLds& A,
   return P.T * P.k <= kTokCache ? A.tok[p] : P.perm[p] / P.k;
 }
 
-struct GemvArgs {
-  uint16_t* h;          // [R][I] bf16
-  float* y;             // [R][H] fp32
-  GemvSync* sync;
-  int ng, nd;           // gate/up and down column chunks per expert
-  int rbs1, rbs2;       // rows per row block (<= 16) of the two launches
-  int x_all;            // 1: every token's x row is staged once per workgroup
-  int x_bytes;          // LDS bytes of those rows (16-byte multiple)
-  float* trash;         // 1 MiB of scratch: stores of padding rows land here
-};
+// Operand rows in LDS: nr rows of K bf16 (or fp16) values, unpadded, with
+// 16-byte piece j of row r at piece r * (K/8) + (j ^ (r & swz)): the 16 rows
+// that one A-fragment read touches then fall in distinct bank groups.  They
+// arrive by direct global->LDS loads (no registers), which write 64
+// consecutive pieces per wave instruction; a last partial instruction spills
+// into kRowSlack bytes past the rows.
+constexpr int kRowSlack = 1024;
 
-constexpr int kMaxStagedRows = 256;
+__device__ __forceinline__ int row_swz(int ppr) { return (ppr % 16 == 0) ? 15 : ((ppr % 4 == 0) ? 3 : 0); }
 
-// Copy nr rows of K bf16 values (row r at rowptr(r)) into LDS with row stride
-// Kp.  For the fp16 operand path the rows are then rewritten in place as
-// fp16 of value * 2^-pexp[r], with pexp[r] >= 0 the smallest shift that keeps
-// the row's largest magnitude below 2^15 (inside fp16's range; the output
-// rows are multiplied back by 2^pexp[r]).  bf16 -> fp16 is then exact for
-// every value of magnitude >= 2^-14 * 2^pexp[r]; smaller ones round at
-// 2^-24 * 2^pexp[r], far below the row's largest product.  Ends with a barrier.
-template <bool F16, class RowPtr>
-__device__ __forceinline__ void stage_rows(uint16_t* act, int Kp, int K, int nr, RowPtr rowptr, int* pexp,
-                                           unsigned* rmax) {
-  const int tid = threadIdx.x;
-  if constexpr (F16) {
-    for (int r = tid; r < nr; r += 256) rmax[r] = 0u;
-    lds_barrier();
+template <class Src>
+__device__ __forceinline__ void dma_rows(uint8_t* act, const uint16_t* base, int K, int nr, Src src) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ppr = K / 8, total = nr * ppr, swz = row_swz(ppr);
+  const int nch = (total + 63) >> 6;
+  for (int c = wave; c < nch; c += 4) {
+    const int p = min(c * 64 + lane, total - 1);  // lanes past the rows re-read the last piece (into the slack)
+    const int r = p / ppr, j = (p % ppr) ^ (r & swz);
+    __builtin_amdgcn_global_load_lds(base + (size_t)src(r) * K + j * 8,
+                                     (__attribute__((address_space(3))) void*)(act + c * 1024), 16, 0, 0);
   }
-  for (int i = tid * 8; i < nr * K; i += 256 * 8) {
-    const int r = i / K, c = i % K;
-    const uint4 v = *reinterpret_cast<const uint4*>(rowptr(r) + c);
-    *reinterpret_cast<uint4*>(act + (size_t)r * Kp + c) = v;
-    if constexpr (F16) {
-      uint32_t m = max(max(v.x & 0x7FFFu, v.x >> 16 & 0x7FFFu), max(v.y & 0x7FFFu, v.y >> 16 & 0x7FFFu));
-      m = max(m, max(max(v.z & 0x7FFFu, v.z >> 16 & 0x7FFFu), max(v.w & 0x7FFFu, v.w >> 16 & 0x7FFFu)));
-      atomicMax(&rmax[r], m);  // |bf16| bit patterns order like the magnitudes
-    }
-  }
-  lds_barrier();
+}
+
+__device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4 v) {
+  uint32_t m = max(max(v.x & 0x7FFFu, v.x >> 16 & 0x7FFFu), max(v.y & 0x7FFFu, v.y >> 16 & 0x7FFFu));
+  return max(m, max(max(v.z & 0x7FFFu, v.z >> 16 & 0x7FFFu), max(v.w & 0x7FFFu, v.w >> 16 & 0x7FFFu)));
+}
+
+// After every wave's rows have landed (and a barrier): for the fp16 operand
+// path the rows are rewritten in place as fp16 of value * 2^-pexp[r], with
+// pexp[r] >= 0 the smallest shift that keeps the row's largest magnitude
+// below 2^15 (inside fp16's range; the output rows are multiplied back by
+// 2^pexp[r]).  bf16 -> fp16 is then exact for every value of magnitude
+// >= 2^-14 * 2^pexp[r]; smaller ones round at 2^-24 * 2^pexp[r], far below
+// the row's largest product.  The piece order does not matter here.  For
+// fp16, ends with a barrier; bf16 rows need nothing more.
+template <bool F16>
+__device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pexp, unsigned* rmax) {
   if constexpr (F16) {
-    for (int r = tid; r < nr; r += 256) {
-      const int E = (int)(rmax[r] >> 7);  // biased exponent of the row's largest |value|: it is < 2^(E-126)
-      pexp[r] = (E == 0xFF) ? 0 : max(0, E - 141);
+    const int tid = threadIdx.x, ppr = K / 8, total = nr * ppr;
+    if (tid < nr) rmax[tid] = 0u;
+    lds_barrier();
+    for (int p = tid; p < total; p += 256)
+      atomicMax(&rmax[p / ppr], bf16x8_absmax_bits(reinterpret_cast<const uint4*>(act)[p]));  // |bf16| bits order like magnitudes
+    lds_barrier();
+    if (tid < nr) {
+      const int E = (int)(rmax[tid] >> 7);  // biased exponent of the row's largest |value|: it is < 2^(E-126)
+      pexp[tid] = (E == 0xFF) ? 0 : max(0, E - 141);
     }
     lds_barrier();
-    for (int i = tid * 8; i < nr * K; i += 256 * 8) {
-      const int r = i / K, c = i % K;
-      uint4* p = reinterpret_cast<uint4*>(act + (size_t)r * Kp + c);
-      const uint4 v = *p;
-      const float sc = __uint_as_float((uint32_t)(127 - pexp[r]) << 23);
+    for (int p = tid; p < total; p += 256) {
+      uint4* q = reinterpret_cast<uint4*>(act) + p;
+      const uint4 v = *q;
+      const float sc = __uint_as_float((uint32_t)(127 - pexp[p / ppr]) << 23);
       auto cv = [&](uint32_t w) -> uint32_t {
         const f16x2_t h = {(_Float16)(bf16_to_f32((uint16_t)w) * sc), (_Float16)(bf16_to_f32((uint16_t)(w >> 16)) * sc)};
         return __builtin_bit_cast(uint32_t, h);
       };
-      *p = make_uint4(cv(v.x), cv(v.y), cv(v.z), cv(v.w));
+      *q = make_uint4(cv(v.x), cv(v.y), cv(v.z), cv(v.w));
     }
     lds_barrier();
   }
 }
 
+// Wait until at most `after` vector-memory operations are outstanding, then
+// barrier: the direct-to-LDS row loads of every wave have landed and are
+// visible, while the last `after` loads issued behind them stay in flight.
+// (The compiler does not order its own waits after these row loads; and a
+// fenced barrier would wait for every load.)
+template <int AFTER>
+__device__ __forceinline__ void rows_landed() {
+  static_assert(AFTER >= 0 && AFTER <= 63, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt [3:0] and [15:14], expcnt [6:4] (7: no wait), lgkmcnt [11:8]
+  constexpr int enc = (AFTER & 15) | ((AFTER >> 4) << 14) | (7 << 4) | (0 << 8);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(enc);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // 2^p as a float (0 <= p < 128)
 __device__ __forceinline__ float pow2i(int p) { return __uint_as_float((uint32_t)(127 + p) << 23); }
-
-// A float the compiler cannot see is uniform: loads from `p + opaque_zero()`
-// are vector-memory loads, ordered with the weight loads, rather than scalar
-// loads (whose counter the LDS reads share).
-__device__ __forceinline__ int opaque_zero() {
-  int z;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-  return z;
-}
 
 constexpr int kTrashSlots = 256;         // 4 KiB scratch slots (workgroup index modulo this)
 
@@ -289,175 +322,189 @@ constexpr int kTrashSlots = 256;         // 4 KiB scratch slots (workgroup index
 //   DOWN = true: down projection.  Item (row block, c) covers output columns
 //     [64c, 64c + 64): wave w streams row group 4c + w of W2 and writes its 16
 //     columns of y (fp32).
-// Items are numbered with c fastest; workgroup b takes the contiguous range
-// [b*items/grid, (b+1)*items/grid), so consecutive items mostly share a row
-// block and its staged operand rows.  Each wave runs all K-tiles of its row
-// group itself (no cross-wave reduction), in sub-items of SUB K-tiles (SUB
-// divides K / KT); the loads of the next sub-item are in flight while the
-// current one computes, also across items.
+// Work is split into tasks of one row block and a contiguous range of cpt
+// items (the smallest range that gives at most one task per workgroup), so a
+// workgroup stages its operand rows once: each row is read by the few
+// workgroups of its expert, not by all of them.  Each wave runs all K-tiles
+// of its row group itself (no cross-wave reduction), in sub-items of SUB
+// K-tiles (SUB divides K / KT).
+//
+// Memory pipeline: two register banks of weight tiles (plus the item's
+// per-tensor multiplier) alternate, and the loop is unrolled by two so each
+// bank keeps fixed registers: the loads of sub-item ss + 1 are in flight
+// while sub-item ss computes.  The operand rows are loaded before the first
+// weights and written to LDS while those are in flight.
 template <int FMT, bool DOWN, int SUB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemv(FfnParams P, GemvArgs G) {
   using F = Fmt<FMT>;
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ ActiveLds A;
-  __shared__ int s_pexp[DOWN ? 16 : kMaxStagedRows];
-  __shared__ unsigned s_rmax[DOWN ? 16 : kMaxStagedRows];
+  __shared__ int s_pexp[16];
+  __shared__ unsigned s_rmax[16];
   __shared__ float s_u[2][16][17];
-  __shared__ float s_g[2];  // per-tensor multipliers of the staged row block's expert
+  __shared__ int s_rows[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 15, grp = lane >> 4;
   const int H = P.H, I = P.I;
-  const int K = DOWN ? I : H, Kp = K + 8, nk = K / F::KT;
+  const int K = DOWN ? I : H, nk = K / F::KT;
   const int rbs = DOWN ? G.rbs2 : G.rbs1, nchunk = DOWN ? G.nd : G.ng;
-  const bool x_all = !DOWN && G.x_all;
-  uint16_t* act = reinterpret_cast<uint16_t*>(lds);  // [rows][K + 8] operand rows
+  const ActiveLds A = active_view(lds, G.na);
+  uint8_t* act = lds + G.act_off;  // operand rows (swizzled) + slack
   build_active(P, rbs, A);
-  const int nrb = A.rb[A.n];
-  const int items = nrb * nchunk;
-  const int i0 = (int)((long long)items * blockIdx.x / gridDim.x);
-  const int i1 = (int)((long long)items * (blockIdx.x + 1) / gridDim.x);
+  const int nrb = A.rb[*A.n];
+  const int grid = gridDim.x;
+  // items per task: at least items / grid, and few enough tasks for the grid
+  // (if even whole row blocks outnumber the workgroups, they loop over tasks)
+  int cpt = (nrb * nchunk + grid - 1) / grid;
+  while (cpt < nchunk && (long long)nrb * ((nchunk + cpt - 1) / cpt) > grid) ++cpt;
+  cpt = max(1, min(cpt, nchunk));
+  const int tpr = (nchunk + cpt - 1) / cpt;  // tasks per row block
+  const int ntasks = nrb * tpr;
   const int nsub = nk / SUB;  // SUB divides nk: every sub-item loads exactly SUB tiles
-  const int nS = (i1 - i0) * nsub;
   const size_t off_w = DOWN ? P.L.off_w2 : P.L.off_w13, off_s = DOWN ? P.L.off_s2 : P.L.off_s13;
-
-  // Loads and stores are unconditional and fixed in number per sub-item (the
-  // compiler then counts them exactly and waits only for the bank in use).
-  auto issue = [&](int ss, uint4 (&q)[SUB], uint32_t (&sc)[SUB]) {
-    const int it = i0 + ss / nsub, sub = ss % nsub;
-    const RowBlock blk = row_block(P, A, rbs, it / nchunk);
-    const int rg = 4 * (it % nchunk) + wave, kt0 = sub * SUB;
-    // 32-bit tile index (a blob holds far fewer than 2^31 tiles); per-tile
-    // addresses are then constant offsets from two base pointers, so no
-    // 64-bit arithmetic sits between the loads.
-    const uint32_t t0 = (uint32_t)rg * (uint32_t)nk + (uint32_t)kt0;
-    const uint8_t* wp = blk.blob + off_w + ((size_t)t0 << 10) + lane * 16;
-    const uint8_t* sp = blk.blob + off_s + (size_t)t0 * kScaleTileBytes<FMT> + lane * kScaleLaneBytes<FMT>;
-#pragma unroll
-    for (int j = 0; j < SUB; ++j) {
-      q[j] = ldg16(wp + j * kTileBytes);
-      sc[j] = load_scale_at<FMT>(sp + j * kScaleTileBytes<FMT>);
-    }
-  };
-
-  int staged = -1;
-  // On a new row block: its expert's per-tensor multipliers, and its operand
-  // rows (all T token rows once, if they fit).  The multipliers' load is in
-  // flight together with the rows'.
-  auto prepare = [&](int ss) {
-    const int rb = (i0 + ss / nsub) / nchunk;
-    if (rb == staged) return;  // uniform: every wave walks the same sub-items
-    const RowBlock blk = row_block(P, A, rbs, rb);
-    float gv = 0.f;
-    if (tid < (DOWN ? 1 : 2)) gv = reinterpret_cast<const BlobHeader*>(blk.blob)->g[DOWN ? 2 : tid];
-    lds_barrier();  // the previous block's rows and multipliers are no longer read
-    if (x_all) {
-      if (staged < 0)
-        stage_rows<F::F16>(act, Kp, K, P.T, [&](int t) { return P.x + (size_t)t * H; }, s_pexp, s_rmax);
-    } else if constexpr (DOWN) {
-      stage_rows<F::F16>(act, Kp, K, blk.nr, [&](int r) { return G.h + (size_t)(blk.p0 + blk.r0 + r) * I; }, s_pexp,
-                         s_rmax);
-    } else {
-      stage_rows<F::F16>(act, Kp, K, blk.nr, [&](int r) { return P.x + (size_t)row_token(P, A, blk, r) * H; },
-                         s_pexp, s_rmax);
-    }
-    if (tid < (DOWN ? 1 : 2)) s_g[tid] = gv;
-    lds_barrier();
-    staged = rb;
-  };
-
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  // The epilogue runs after every sub-item (uniform code: no branch around
-  // memory operations inside the pipelined loop); before an item's last
-  // sub-item its stores go to a scratch area, as do rows past the block and
-  // the up waves' h.
+  // per-tensor multiplier of this wave's rows: gate (even waves) / up (odd) / down
+  const int gsel = DOWN ? 2 : (wave & 1);
+  const uint16_t* rbase = DOWN ? G.h : P.x;
   // this workgroup's own 4 KiB of scratch (distinct lines: no store contention)
   float* trash = G.trash + (size_t)(blockIdx.x % kTrashSlots) * 1024;
-  auto body = [&](int ss, const uint4 (&q)[SUB], const uint32_t (&sc)[SUB]) {
-    const int it = i0 + ss / nsub, sub = ss % nsub;
-    const int chunk = it % nchunk;
-    const bool last = sub == nsub - 1;
-    const RowBlock blk = row_block(P, A, rbs, it / nchunk);
-    if (sub == 0) acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // x_all implies T*k <= kTokCache: tokens come from LDS (no global load
-    // may sit inside the pipelined loop body)
-    auto tok = [&](int r) { return blk.shared ? blk.r0 + r : A.tok[blk.p0 + blk.r0 + r]; };
-    const uint16_t* arow = nullptr;
-    if (m < blk.nr) arow = act + (size_t)(x_all ? tok(m) : m) * Kp;
-#pragma unroll
-    for (int j = 0; j < SUB; ++j) {
-      const int kt = sub * SUB + j;
-#pragma unroll
-      for (int st = 0; st < F::SPT; ++st) {
-        const int col = kt * F::KT + (F::SPT == 4 ? 32 * grp + 8 * st : 8 * grp);
-        const uint4 av = arow ? *reinterpret_cast<const uint4*>(arow + col) : make_uint4(0, 0, 0, 0);
-        typename F::V b;
-        if constexpr (F::SPT == 4) {
-          b = st == 0 ? bfrag<FMT, 0>(q[j], sc[j]) : st == 1 ? bfrag<FMT, 1>(q[j], sc[j])
-            : st == 2 ? bfrag<FMT, 2>(q[j], sc[j]) : bfrag<FMT, 3>(q[j], sc[j]);
-        } else {
-          b = bfrag<FMT, 0>(q[j], sc[j]);
-        }
-        acc = mma<FMT>(__builtin_bit_cast(typename F::V, av), b, acc);
-      }
-    }
-    // Lane: rows 4 (lane / 16) + v of the block, column lane % 16 of this
-    // wave's 16 output rows of the weight; per-tensor multiplier of those
-    // rows: gate (even waves) / up (odd) / down.
-    const float g = s_g[DOWN ? 0 : (wave & 1)];
-    float val[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = 4 * grp + v;
-      float sc2 = g;
-      if constexpr (F::F16) sc2 *= pow2i(s_pexp[r < blk.nr ? (x_all ? tok(r) : r) : 0]);
-      val[v] = acc[v] * sc2;
-    }
-    if constexpr (DOWN) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = 4 * grp + v;
-        float* dst = (last && r < blk.nr) ? G.y + (size_t)(blk.p0 + blk.r0 + r) * H + 64 * chunk + 16 * wave + m
-                                          : trash + (r * 4 + wave) * 16 + m;
-        *dst = val[v];
-      }
-    } else {
-      if (wave & 1)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) s_u[wave >> 1][4 * grp + v][m] = val[v];
-      lds_barrier();
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = 4 * grp + v;
-        const float hv = silu_f32(val[v]) * s_u[wave >> 1][r][m];
-        uint16_t* dst = (last && r < blk.nr && !(wave & 1))
-                            ? G.h + (size_t)(blk.p0 + blk.r0 + r) * I + 32 * chunk + 16 * (wave >> 1) + m
-                            : reinterpret_cast<uint16_t*>(trash) + (r * 4 + wave) * 16 + m;
-        *dst = f32_to_bf16_rne(hv);
-      }
-      lds_barrier();
-    }
+
+  struct Bank {
+    uint4 q[SUB];
+    ScaleT<FMT> sc[SUB];
+    float g;
   };
 
-  // Software pipeline: the loads of sub-item ss + 1 are issued before
-  // sub-item ss computes and are consumed in the next iteration (a
-  // loop-carried bank, so the compiler keeps them in flight).  The issue is
-  // unconditional (the last iteration re-reads its own sub-item, from cache).
-  uint4 cq[SUB], nq[SUB];
-  uint32_t cs[SUB], ns[SUB];
-  if (nS > 0) issue(0, cq, cs);
 #pragma unroll 1
-  for (int ss = 0; ss < nS; ++ss) {
-    prepare(ss);
-    issue(min(ss + 1, nS - 1), nq, ns);
-    __builtin_amdgcn_sched_barrier(0);
-    body(ss, cq, cs);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int task = blockIdx.x; task < ntasks; task += grid) {
+    const int rbi = task / tpr;
+    const int c0 = (task % tpr) * cpt, c1 = min(nchunk, c0 + cpt);
+    const RowBlock blk = row_block(P, A, rbs, rbi);
+    const int nS = (c1 - c0) * nsub;
+    const uint8_t* wbase = blk.blob + off_w;
+    const uint8_t* sbase = blk.blob + off_s;
+
+    // Loads are unconditional and fixed in number per sub-item (the compiler
+    // then counts them exactly and waits only for the bank in use).
+    auto issue = [&](int ss, Bank& b) {
+      const int chunk = c0 + ss / nsub, sub = ss % nsub;
+      const int rg = 4 * chunk + wave, kt0 = sub * SUB;
+      // 32-bit tile index (a blob holds far fewer than 2^31 tiles); per-tile
+      // addresses are then constant offsets from two base pointers, so no
+      // 64-bit arithmetic sits between the loads.
+      const uint32_t t0 = (uint32_t)rg * (uint32_t)nk + (uint32_t)kt0;
+      const uint8_t* wp = wbase + ((size_t)t0 << 10) + lane * 16;
+      const uint8_t* sp = sbase + (size_t)t0 * kScaleTileBytes<FMT> + lane * kScaleLaneBytes<FMT>;
+      // small loads first, the SUB tile loads last (the row wait below
+      // counts on at least SUB loads behind the rows)
 #pragma unroll
-    for (int j = 0; j < SUB; ++j) {
-      cq[j] = nq[j];
-      cs[j] = ns[j];
+      for (int j = 0; j < SUB; ++j) b.sc[j] = load_scale_at<FMT>(sp + j * kScaleTileBytes<FMT>);
+      b.g = reinterpret_cast<const BlobHeader*>(blk.blob)->g[gsel];
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) b.q[j] = ldg16(wp + j * kTileBytes);
+    };
+
+    // operand rows of the block (token rows of x, or rows of h), loaded ahead
+    // of the first weights; the table's barrier also ends the previous task
+    lds_barrier();
+    if (tid < blk.nr) s_rows[tid] = DOWN ? blk.p0 + blk.r0 + tid : row_token(P, A, blk, tid);
+    lds_barrier();
+    Bank b0, b1;
+    dma_rows(act, rbase, K, blk.nr, [&](int r) { return s_rows[r]; });
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    issue(0, b0);  // behind the rows: waiting for the rows leaves its SUB tile loads in flight
+    __builtin_amdgcn_sched_barrier(0);
+    rows_landed<SUB>();
+    finish_rows<F::F16>(act, K, blk.nr, s_pexp, s_rmax);
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // this lane's A row (row m of the block) and its swizzled piece offsets
+    const int ppr = K / 8, swz = row_swz(ppr);
+    const uint8_t* arow = m < blk.nr ? act + (size_t)m * ppr * 16 : nullptr;
+    // The epilogue runs after every sub-item (uniform code: no branch around
+    // memory operations inside the pipelined loop); before an item's last
+    // sub-item its stores go to a scratch area, as do rows past the block and
+    // the up waves' h.
+    auto body = [&](int ss, const Bank& b) {
+      const int chunk = c0 + ss / nsub, sub = ss % nsub;
+      const bool last = sub == nsub - 1;
+      if (sub == 0) acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) {
+        const int kt = sub * SUB + j;
+#pragma unroll
+        for (int st = 0; st < F::SPT; ++st) {
+          const int piece = (kt * F::KT + (F::SPT == 4 ? 32 * grp + 8 * st : 8 * grp)) / 8;
+          const uint4 av = arow ? *reinterpret_cast<const uint4*>(arow + ((piece ^ (m & swz)) << 4)) : make_uint4(0, 0, 0, 0);
+          typename F::V bv;
+          if constexpr (F::SPT == 4) {
+            bv = st == 0 ? bfrag<FMT, 0>(b.q[j], b.sc[j]) : st == 1 ? bfrag<FMT, 1>(b.q[j], b.sc[j])
+               : st == 2 ? bfrag<FMT, 2>(b.q[j], b.sc[j]) : bfrag<FMT, 3>(b.q[j], b.sc[j]);
+          } else {
+            bv = bfrag<FMT, 0>(b.q[j], b.sc[j]);
+          }
+          acc = mma<FMT>(__builtin_bit_cast(typename F::V, av), bv, acc);
+        }
+      }
+      // Lane: rows 4 (lane / 16) + v of the block, column lane % 16 of this
+      // wave's 16 output rows of the weight.
+      float val[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 4 * grp + v;
+        float sc2 = b.g;
+        if constexpr (F::F16) sc2 *= pow2i(s_pexp[r < blk.nr ? r : 0]);
+        val[v] = acc[v] * sc2;
+      }
+      if constexpr (DOWN) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = 4 * grp + v;
+          float* dst = (last && r < blk.nr) ? G.y + (size_t)(blk.p0 + blk.r0 + r) * H + 64 * chunk + 16 * wave + m
+                                            : trash + (r * 4 + wave) * 16 + m;
+          *dst = val[v];
+        }
+      } else {
+        if (wave & 1)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s_u[wave >> 1][4 * grp + v][m] = val[v];
+        lds_barrier();
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = 4 * grp + v;
+          const float hv = silu_f32(val[v]) * s_u[wave >> 1][r][m];
+          uint16_t* dst = (last && r < blk.nr && !(wave & 1))
+                              ? G.h + (size_t)(blk.p0 + blk.r0 + r) * I + 32 * chunk + 16 * (wave >> 1) + m
+                              : reinterpret_cast<uint16_t*>(trash) + (r * 4 + wave) * 16 + m;
+          *dst = f32_to_bf16_rne(hv);
+        }
+        lds_barrier();
+      }
+    };
+
+    // Two banks, loop unrolled by two: sub-items ss (bank b0) and ss + 1 (b1)
+    // per trip, with ss + 2 loading into b0 during ss + 1.  The last one or
+    // two sub-items run after the loop and issue nothing past the end.
+    int ss = 0;
+#pragma unroll 1
+    for (; ss + 2 < nS; ss += 2) {
+      issue(ss + 1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      body(ss, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(ss + 2, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      body(ss + 1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (ss + 1 < nS) {
+      issue(ss + 1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      body(ss, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      body(ss + 1, b1);
+    } else {
+      body(ss, b0);
     }
   }
-
 }
 
 // ---------------------------------------------------------------- launcher
@@ -475,15 +522,16 @@ static int cu_count() {
 // Resident workgroups of 256 threads per CU for a kernel and its dynamic LDS
 // (at least 1), memoised.
 static int blocks_per_cu(const void* fn, size_t lds) {
-  static const void* fns[16];
-  static size_t ldss[16];
-  static int vals[16];
+  constexpr int kMemo = 64;
+  static const void* fns[kMemo];
+  static size_t ldss[kMemo];
+  static int vals[kMemo];
   static int n = 0;
   for (int i = 0; i < n; ++i)
     if (fns[i] == fn && ldss[i] == lds) return vals[i];
   int b = 1;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, 256, lds) != hipSuccess || b < 1) b = 1;
-  if (n < 16) {
+  if (n < kMemo) {
     fns[n] = fn;
     ldss[n] = lds;
     vals[n] = b;
@@ -492,9 +540,9 @@ static int blocks_per_cu(const void* fn, size_t lds) {
   return b;
 }
 
-// Dynamic LDS per workgroup: with the static part (at most 25 KB) two
+// Dynamic LDS per workgroup: with the static part (under 5 KB) two
 // workgroups fit one CU's 160 KB.
-constexpr size_t kDynLds = 55 * 1024;
+constexpr size_t kDynLds = 75 * 1024;
 
 typedef void (*GemvKernel)(FfnParams, GemvArgs);
 
@@ -512,16 +560,22 @@ static GemvKernel gemv_kernel(int nk) {
 
 template <int FMT>
 static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
-  const size_t rowb1 = (size_t)(P.H + 8) * 2, rowb2 = (size_t)(P.I + 8) * 2;
-  G.rbs1 = (int)std::min<size_t>(16, kDynLds / rowb1);
-  G.rbs2 = (int)std::min<size_t>(16, kDynLds / rowb2);
-  G.x_bytes = (int)(((size_t)P.T * rowb1 + 15) / 16 * 16);
-  G.x_all = ((size_t)G.x_bytes <= kDynLds && P.T <= kMaxStagedRows && P.T * P.k <= kTokCache) ? 1 : 0;
-  const size_t lds1 = G.x_all ? (size_t)G.x_bytes : G.rbs1 * rowb1;
-  const size_t lds2 = G.rbs2 * rowb2;
+  const long long rows = (long long)P.T * P.k;
+  G.na = (int)std::min<long long>(P.E, rows) + (P.shared_blob ? 1 : 0);
+  const int ntok = rows <= kTokCache ? (int)rows : 0;
+  G.act_off = (int)((active_lds_bytes(G.na, ntok) + 15) / 16 * 16);
+  const size_t avail = kDynLds - (size_t)G.act_off;
+  // Rows per row block: at most 16, within the LDS left.
+  auto block_rows = [&](int K) {
+    const size_t by_lds = (avail - kRowSlack) / ((size_t)K * 2);
+    return (int)std::max<size_t>(1, std::min<size_t>(16, by_lds));
+  };
+  G.rbs1 = block_rows(P.H);
+  G.rbs2 = block_rows(P.I);
+  const size_t lds1 = G.act_off + (size_t)G.rbs1 * P.H * 2 + kRowSlack;
+  const size_t lds2 = G.act_off + (size_t)G.rbs2 * P.I * 2 + kRowSlack;
   // Row blocks: at most ceil(T*k / rbs) + min(E, T*k) routed, plus the shared expert's.
   auto nrb = [&](int rbs) {
-    const long long rows = (long long)P.T * P.k;
     long long n = (rows + rbs - 1) / rbs + std::min<long long>(P.E, rows);
     if (P.shared_blob) n += (P.T + rbs - 1) / rbs;
     return n;

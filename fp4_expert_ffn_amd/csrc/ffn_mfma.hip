@@ -211,24 +211,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Operand A: thread t stages 16-byte segment t % 8 of rows t / 8 + 32 i
   // (i < 4), so a wave reads eight whole 128-byte row segments per load.
   // Rows past the tile are clamped for the address and zeroed after the load.
-  const uint8_t* arow[4];
-  int a_lds[4];
-  uint32_t akeep[4];
+  // 32-bit byte offsets from one base pointer (the operand buffers are far
+  // below 4 GiB) keep the per-stage address state small.
+  const uint8_t* abase = MODE == kGateUp ? (FP4 ? B.xq : reinterpret_cast<const uint8_t*>(P.x))
+                                         : (FP4 ? B.hq : reinterpret_cast<const uint8_t*>(B.hb));
+  const uint32_t arow_bytes = FP4 ? K / 2 : K * 2;
+  uint32_t aoff[4];
+  uint32_t avalid = 0;  // bit i: row (tid / 8) + 32 i is inside the tile
   const int seg = tid & 7;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (tid >> 3) + 32 * i;
-    akeep[i] = row < tj.rows ? 0xFFFFFFFFu : 0u;
+    if (row < tj.rows) avalid |= 1u << i;
     const int r = row < tj.rows ? row : 0;
-    if (MODE == kGateUp) {
-      const int t = tj.shared ? tj.m0 + r : P.perm[tj.p0 + tj.m0 + r] / P.k;
-      arow[i] = FP4 ? B.xq + (size_t)t * (P.H / 2) : reinterpret_cast<const uint8_t*>(P.x + (size_t)t * P.H);
-    } else {
-      const size_t pr = (size_t)tj.p0 + tj.m0 + r;
-      arow[i] = FP4 ? B.hq + pr * (P.I / 2) : reinterpret_cast<const uint8_t*>(B.hb + pr * P.I);
-    }
-    a_lds[i] = row * kArow + seg * 16;
-    arow[i] += seg * 16;
+    uint32_t src_row;
+    if (MODE == kGateUp) src_row = tj.shared ? tj.m0 + r : P.perm[tj.p0 + tj.m0 + r] / P.k;
+    else src_row = tj.p0 + tj.m0 + r;
+    aoff[i] = src_row * arow_bytes + seg * 16;
   }
   // FP4 A scales: 8 bytes (the step's eight 32-blocks) of row tid / 2, half tid % 2.
   const uint8_t* asrow = nullptr;
@@ -247,12 +246,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   // Operand B: chunk c = t + 256 i is lane c % 64 of weight tile (row group
   // c / 128, K-tile (c / 64) % 2 of the step); LDS holds it at c * 16.
-  size_t b_off[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    b_off[i] = ((size_t)(rg0 + (c >> 7)) * nk_w + ((c >> 6) & 1)) * kTileBytes + (c & 63) * 16;
-  }
+  // (row group c / 128 and K-tile (c / 64) % 2 of chunk c = tid + 256 i)
+  const uint32_t b_off0 = ((uint32_t)(rg0 + (tid >> 7)) * nk_w + ((tid >> 6) & 1)) * kTileBytes + (tid & 63) * 16;
+  const uint32_t b_rg2 = 2u * nk_w * kTileBytes;  // chunk i adds 2 i row groups
   // FP4 B scales: dword t of the step's 16 scale tiles (64 bytes each).
   const size_t bs_off = ((size_t)(rg0 + (tid >> 5)) * nk_w + ((tid >> 4) & 1)) * 64 + (tid & 15) * 4;
 
@@ -271,8 +267,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < 4; ++i) {
       const int back_a = (tail && seg >= 4) ? 64 : 0;
       const int back_b = (tail && ((tid + 256 * i) >> 6 & 1)) ? kTileBytes : 0;
-      S.a[i] = *reinterpret_cast<const uint4*>(arow[i] + (size_t)ks * 128 - back_a);
-      S.b[i] = *reinterpret_cast<const uint4*>(wt + b_off[i] + (size_t)ks * 2 * kTileBytes - back_b);
+      S.a[i] = *reinterpret_cast<const uint4*>(abase + aoff[i] + (uint32_t)(ks * 128 - back_a));
+      S.b[i] = *reinterpret_cast<const uint4*>(wt + b_off0 + i * b_rg2 + (uint32_t)(ks * 2 * kTileBytes - back_b));
     }
     if (FP4) {
       const int back_sa = (tail && (tid & 1)) ? 4 : 0, back_sb = (tail && (tid >> 4 & 1)) ? 64 : 0;
@@ -285,8 +281,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool tail = half_tail && ks == nsteps - 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t k = akeep[i] & lk & ((tail && seg >= 4) ? 0u : 0xFFFFFFFFu);  // bit masks: branch-free
-      *reinterpret_cast<uint4*>(buf + a_lds[i]) = make_uint4(S.a[i].x & k, S.a[i].y & k, S.a[i].z & k, S.a[i].w & k);
+      const uint32_t k = (0u - ((avalid >> i) & 1u)) & lk & ((tail && seg >= 4) ? 0u : 0xFFFFFFFFu);  // bit masks
+      *reinterpret_cast<uint4*>(buf + ((tid >> 3) + 32 * i) * kArow + seg * 16) =
+          make_uint4(S.a[i].x & k, S.a[i].y & k, S.a[i].z & k, S.a[i].w & k);
       reinterpret_cast<uint4*>(buf + kBoff)[tid + 256 * i] = S.b[i];
     }
     if (FP4) {

@@ -6,6 +6,8 @@
 // paragraph; page "FreeToken量子化：MoE推論のセットアップガイド", second
 // paragraph).  The selection rule (fp32 logit keys, ties to the lower id, NaN
 // lowest) and the softmax over the selected logits are this library's reading.
+#include <algorithm>
+
 #include "common.h"
 #include "wave.h"
 
@@ -248,28 +250,25 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 }
 
 // ------------------------------------------------------------------ permutation
-
-// One workgroup of 1024 threads places a chunk of 1024 flat indices.  It
-// histograms all ids (in total and before its chunk) in LDS, scans the
+// One workgroup places a chunk of blockDim.x flat indices [c0, c0 + blockDim.x).
+// It histograms all ids (in total and before its chunk) in LDS, scans the
 // totals, and places its chunk: position = offsets[e] + (# of e before the
 // chunk) + (# of e in earlier waves of the chunk) + (rank within the wave).
-// `ids` may point to global memory or to LDS.
+// `ids` may point to global memory or to LDS.  LDS: E * (2 + waves) ints.
 constexpr int kPermChunk = 1024;
 constexpr int kPermWaves = kPermChunk / 64;
 
-__device__ __forceinline__ size_t permute_lds_bytes(int E) { return sizeof(int32_t) * (size_t)E * (2 + kPermWaves); }
-
-__device__ void permute_chunk(const int32_t* ids, int N, int E, int chunk, int32_t* sm, int32_t* __restrict__ counts,
+__device__ void permute_chunk(const int32_t* ids, int N, int E, int c0, int32_t* sm, int32_t* __restrict__ counts,
                               int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-  __shared__ int32_t scan_tmp[kPermChunk];
+  __shared__ int32_t wsum[kPermWaves];
+  const int nt = blockDim.x, nw = nt >> 6;
   int32_t* tot = sm;                   // [E]
   int32_t* before = sm + E;            // [E]
-  int32_t* wcnt = sm + 2 * E;          // [kPermWaves][E]
+  int32_t* wcnt = sm + 2 * E;          // [nw][E]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c0 = chunk * kPermChunk;
-  for (int i = tid; i < E * (2 + kPermWaves); i += kPermChunk) sm[i] = 0;
+  for (int i = tid; i < E * (2 + nw); i += nt) sm[i] = 0;
   __syncthreads();
-  for (int f = tid; f < N; f += kPermChunk) {
+  for (int f = tid; f < N; f += nt) {
     const int e = ids[f];
     if (e >= 0 && e < E) {
       atomicAdd(&tot[e], 1);
@@ -278,26 +277,29 @@ __device__ void permute_chunk(const int32_t* ids, int N, int E, int chunk, int32
   }
   __syncthreads();
   {
-    // exclusive scan of the totals; each thread owns ceil(E/1024) consecutive experts
-    const int per = (E + kPermChunk - 1) / kPermChunk;
+    // exclusive scan of the totals: thread t owns experts [t*per, t*per + per);
+    // a wave scan with shuffles, then the totals of the earlier waves
+    const int per = (E + nt - 1) / nt;
     int run = 0;
     for (int i = 0; i < per; ++i) {
       const int e = tid * per + i;
       if (e < E) run += tot[e];
     }
-    scan_tmp[tid] = run;
-    __syncthreads();
-    for (int o = 1; o < kPermChunk; o <<= 1) {
-      const int v = tid >= o ? scan_tmp[tid - o] : 0;
-      __syncthreads();
-      scan_tmp[tid] += v;
-      __syncthreads();
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
     }
-    int base = scan_tmp[tid] - run;
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int prefix = 0;
+    for (int w = 0; w < wave; ++w) prefix += wsum[w];
+    int base = prefix + incl - run;
     for (int i = 0; i < per; ++i) {
       const int e = tid * per + i;
       if (e < E) {
-        if (chunk == 0) {
+        if (c0 == 0) {
           counts[e] = tot[e];
           offsets[e] = base;
         }
@@ -305,7 +307,7 @@ __device__ void permute_chunk(const int32_t* ids, int N, int E, int chunk, int32
         base += tot[e];
       }
     }
-    if (chunk == 0 && tid == kPermChunk - 1) offsets[E] = scan_tmp[tid];
+    if (c0 == 0 && tid == nt - 1) offsets[E] = prefix + incl;
   }
   // rank within the wave: wave-level match of equal ids
   const int f = c0 + tid;
@@ -341,10 +343,11 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   extern __shared__ int32_t sm[];
-  permute_chunk(ids, N, E, blockIdx.x, sm, counts, offsets, perm, inv);
+  permute_chunk(ids, N, E, blockIdx.x * kPermChunk, sm, counts, offsets, perm, inv);
 }
 
-// Routing and permutation of a small batch (T*k <= 1024) in one workgroup.
+// Routing and permutation of a small batch (T*k <= 1024) in one workgroup of
+// at least T*k threads (one wave per token for the top-k, up to 16 waves).
 template <int NPER>
 __global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict__ logits, int T, int E, int k,
                                                         int renorm, int32_t* __restrict__ ids, float* __restrict__ wts,
@@ -352,11 +355,19 @@ __global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict_
                                                         int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   extern __shared__ int32_t sm[];
   __shared__ int32_t ids_s[kPermChunk];
-  const int wave = threadIdx.x >> 6;
-  for (int t = wave; t < T; t += kPermWaves)
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int t = wave; t < T; t += nw)
     wave_topk<NPER>(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wts + (size_t)t * k, ids_s + t * k);
   __syncthreads();
   permute_chunk(ids_s, T * k, E, 0, sm, counts, offsets, perm, inv);
+}
+
+// Threads of the one-workgroup routing + permutation: a wave per token (up to
+// 16) and at least one thread per flat index.
+static int route_permute_threads(int T, int k) {
+  const int by_tok = 64 * std::min(T, kPermWaves);
+  const int by_idx = (T * k + 63) / 64 * 64;
+  return std::max(64, std::min(kPermChunk, std::max(by_tok, by_idx)));
 }
 
 // Kernels with more than 64 KiB of dynamic LDS must opt in once per process.
@@ -440,10 +451,11 @@ extern "C" moe_status moe_route_permute(const float* logits, int T, int E, int k
   MOE_CHECK_ARG(T == 0 || (logits && topk_ids && topk_w && perm && inv), "moe_route_permute: null pointer");
   moe_status st = set_lds_limits();
   if (st != MOE_OK) return st;
-  const size_t lds = sizeof(int32_t) * (size_t)E * (2 + kPermWaves);
+  const int nt = route_permute_threads(T, k);
+  const size_t lds = sizeof(int32_t) * (size_t)E * (2 + nt / 64);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const int rn = renormalize ? 1 : 0;
-#define MOE_RP(N) hipLaunchKernelGGL(k_route_permute<N>, dim3(1), dim3(kPermChunk), lds, hs, logits, T, E, k, rn, \
+#define MOE_RP(N) hipLaunchKernelGGL(k_route_permute<N>, dim3(1), dim3(nt), lds, hs, logits, T, E, k, rn, \
                                      topk_ids, topk_w, counts, offsets, perm, inv)
   if (E <= 64) MOE_RP(1);
   else if (E <= 128) MOE_RP(2);
