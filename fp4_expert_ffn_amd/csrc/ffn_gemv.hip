@@ -266,17 +266,18 @@ __device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4 v) {
 // the row's largest product.  The piece order does not matter here.  For
 // fp16, ends with a barrier; bf16 rows need nothing more.
 template <bool F16>
-__device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pexp, unsigned* rmax) {
+__device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pexp) {
   if constexpr (F16) {
-    const int tid = threadIdx.x, ppr = K / 8, total = nr * ppr;
-    if (tid < nr) rmax[tid] = 0u;
-    lds_barrier();
-    for (int p = tid; p < total; p += 256)
-      atomicMax(&rmax[p / ppr], bf16x8_absmax_bits(reinterpret_cast<const uint4*>(act)[p]));  // |bf16| bits order like magnitudes
-    lds_barrier();
-    if (tid < nr) {
-      const int E = (int)(rmax[tid] >> 7);  // biased exponent of the row's largest |value|: it is < 2^(E-126)
-      pexp[tid] = (E == 0xFF) ? 0 : max(0, E - 141);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ppr = K / 8, total = nr * ppr;
+    const uint4* pc = reinterpret_cast<const uint4*>(act);
+    // each row's largest |value| bits (|bf16| bit patterns order like the
+    // magnitudes): wave w reduces rows w, w + 4, ...
+    for (int r = wave; r < nr; r += 4) {
+      uint32_t mx = 0;
+      for (int p = lane; p < ppr; p += 64) mx = max(mx, bf16x8_absmax_bits(pc[r * ppr + p]));
+      mx = wave_max_u32(mx);
+      const int E = (int)(mx >> 7);  // biased exponent of the row's largest |value|: it is < 2^(E-126)
+      if (lane == 0) pexp[r] = (E == 0xFF) ? 0 : max(0, E - 141);
     }
     lds_barrier();
     for (int p = tid; p < total; p += 256) {
@@ -339,7 +340,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   using F = Fmt<FMT>;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_pexp[16];
-  __shared__ unsigned s_rmax[16];
   __shared__ float s_u[2][16][17];
   __shared__ int s_rows[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 15, grp = lane >> 4;
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     issue(0, b0);  // behind the rows: waiting for the rows leaves its SUB tile loads in flight
     __builtin_amdgcn_sched_barrier(0);
     rows_landed<SUB>();
-    finish_rows<F::F16>(act, K, blk.nr, s_pexp, s_rmax);
+    finish_rows<F::F16>(act, K, blk.nr, s_pexp);
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     // this lane's A row (row m of the block) and its swizzled piece offsets
@@ -582,8 +582,10 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   };
   const auto k1 = gemv_kernel<FMT, false>(P.H / Fmt<FMT>::KT);
   const auto k2 = gemv_kernel<FMT, true>(P.I / Fmt<FMT>::KT);
-  const long long cap1 = (long long)blocks_per_cu(reinterpret_cast<const void*>(k1), lds1) * cu_count();
-  const long long cap2 = (long long)blocks_per_cu(reinterpret_cast<const void*>(k2), lds2) * cu_count();
+  // The kernels are built for two resident workgroups per CU (their register
+  // budget); more would start late, after the first ones finish.
+  const long long cap1 = (long long)std::min(2, blocks_per_cu(reinterpret_cast<const void*>(k1), lds1)) * cu_count();
+  const long long cap2 = (long long)std::min(2, blocks_per_cu(reinterpret_cast<const void*>(k2), lds2)) * cu_count();
   const int g1 = (int)std::max<long long>(1, std::min<long long>(nrb(G.rbs1) * G.ng, cap1));
   const int g2 = (int)std::max<long long>(1, std::min<long long>(nrb(G.rbs2) * G.nd, cap2));
   launch(k1, dim3(g1), dim3(256), lds1, s, P, G);

@@ -49,6 +49,18 @@ __device__ __forceinline__ float wave_sum(float v) {
   return sum_rows4(v);
 }
 
+// Full-wave unsigned 32-bit max, result in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppQuadXor1>(v));
+  v = max(v, dpp_u32<kDppQuadXor2>(v));
+  v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+  v = max(v, dpp_u32<kDppRowMirror>(v));
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
+
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 template <int CTRL>
