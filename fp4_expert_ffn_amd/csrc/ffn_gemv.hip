@@ -371,6 +371,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     ScaleT<FMT> sc[SUB];
     float g;
   };
+  // Vector-memory loads of one bank: SUB tiles, SUB scale loads (4-bit
+  // formats; 64 or 128 bytes apart, never merged) and the multiplier.
+  constexpr int kBankLoads = SUB + (FMT == MOE_FMT_BF16 ? 0 : SUB) + 1;
 
 #pragma unroll 1
   for (int task = blockIdx.x; task < ntasks; task += grid) {
@@ -392,8 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const uint32_t t0 = (uint32_t)rg * (uint32_t)nk + (uint32_t)kt0;
       const uint8_t* wp = wbase + ((size_t)t0 << 10) + lane * 16;
       const uint8_t* sp = sbase + (size_t)t0 * kScaleTileBytes<FMT> + lane * kScaleLaneBytes<FMT>;
-      // small loads first, the SUB tile loads last (the row wait below
-      // counts on at least SUB loads behind the rows)
+      // exactly kBankLoads loads: the row wait below counts them
 #pragma unroll
       for (int j = 0; j < SUB; ++j) b.sc[j] = load_scale_at<FMT>(sp + j * kScaleTileBytes<FMT>);
       b.g = reinterpret_cast<const BlobHeader*>(blk.blob)->g[gsel];
@@ -410,9 +412,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     dma_rows(act, rbase, K, blk.nr, [&](int r) { return s_rows[r]; });
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    issue(0, b0);  // behind the rows: waiting for the rows leaves its SUB tile loads in flight
+    issue(0, b0);  // behind the rows: waiting for the rows leaves all of its loads in flight
     __builtin_amdgcn_sched_barrier(0);
-    rows_landed<SUB>();
+    rows_landed<kBankLoads>();
     finish_rows<F::F16>(act, K, blk.nr, s_pexp);
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};

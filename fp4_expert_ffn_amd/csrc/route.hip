@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "topk.h"
 #include "wave.h"
 
 namespace {
@@ -110,143 +111,14 @@ __global__ __launch_bounds__(256) void k_router_tiled(const uint16_t* __restrict
   }
 }
 
-// ------------------------------------------------------------------ top-k + softmax
-
-// Order-preserving map of an fp32 logit to uint32: larger value -> larger key;
-// -0 is folded onto +0; every NaN maps to 0, below -inf (0x007FFFFF).
-__device__ __forceinline__ uint32_t rank_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;  // NaN
-  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;             // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float from_rank_bits(uint32_t r) {
-  if (r == 0u) return __uint_as_float(0x7FC00000u);
-  return __uint_as_float((r & 0x80000000u) ? (r & 0x7FFFFFFFu) : ~r);
-}
-
-__device__ __forceinline__ float unnorm(float v, float m) {
-  if (v != v) return 0.f;
-  if (v == m) return 1.f;
-  return expf(v - m);
-}
-
-constexpr int kRouteMaxPerLane = 16;  // E <= 1024
-constexpr int kRouteMaxK = 16;
-
-// Top-k of one logits row by one wave (radix select, no cross-lane reductions
-// in the critical path):
-//   1. threshold = the k-th largest rank key, found bit by bit from the top:
-//      keep a bit when at least k keys are >= the candidate (ballot + popcount);
-//   2. selected = keys above the threshold, plus the lowest-id keys equal to it;
-//   3. each selected key's output position = number of selected keys that rank
-//      above it (larger key, or equal key and lower id).
-// Writes ids[pos], w[pos] for pos in [0, k) and, if ids_lds, ids_lds[pos].
-template <int NPER>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm,
-                                          int32_t* __restrict__ ids, float* __restrict__ wout, int32_t* ids_lds) {
-  const int lane = threadIdx.x & 63;
-  constexpr int nper = NPER;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint32_t rk[NPER];
-  float val[NPER];
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int e = lane + 64 * i;
-    val[i] = 0.f;
-    rk[i] = 0u;
-    if (i < nper && e < E) {
-      val[i] = row[e];
-      rk[i] = rank_bits(val[i]) + 1u;  // 0 marks "no key"; NaN -> 1, below every number
-    }
-  }
-  // 1. threshold
-  uint32_t thr = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = thr | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (i < nper) cnt += __popcll(__ballot(rk[i] >= cand));
-    if (cnt >= k) thr = cand;
-  }
-  // 2. selection
-  int c_gt = 0;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i)
-    if (i < nper) c_gt += __popcll(__ballot(rk[i] > thr));
-  int need = k - c_gt;
-  uint32_t selmask = 0;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    if (i < nper) {
-      const uint64_t eq = __ballot(rk[i] == thr);
-      const int take = min(__popcll(eq), need);
-      const bool mine_eq = rk[i] == thr && __popcll(eq & lt) < take;
-      if (rk[i] > thr || mine_eq) selmask |= 1u << i;
-      need -= take;
-    }
-  }
-  // 3. output positions
-  int pos[NPER];
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) pos[i] = 0;
-#pragma unroll
-  for (int i2 = 0; i2 < NPER; ++i2) {
-    if (i2 < nper) {
-      uint64_t m = __ballot((selmask >> i2) & 1u);
-      while (m) {
-        const int L = __ffsll((unsigned long long)m) - 1;
-        m &= m - 1;
-        const uint32_t ok = __builtin_amdgcn_readlane(rk[i2], L);
-        const int oid = L + 64 * i2;
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-          const int myid = lane + 64 * i;
-          if ((selmask >> i) & 1u) pos[i] += (ok > rk[i] || (ok == rk[i] && oid < myid)) ? 1 : 0;
-        }
-      }
-    }
-  }
-  // top value m (position 0) and softmax weights
-  float top = 0.f;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i)
-    if (i < nper) {
-      const uint64_t b = __ballot(((selmask >> i) & 1u) && pos[i] == 0);
-      if (b) top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[i]), __ffsll((unsigned long long)b) - 1));
-    }
-  float num[NPER], part = 0.f;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    num[i] = ((selmask >> i) & 1u) ? unnorm(val[i], top) : 0.f;
-    part += num[i];
-  }
-  if (!renorm) {
-    part = 0.f;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (i < nper && lane + 64 * i < E) part += unnorm(val[i], top);
-  }
-  const float den = wave_sum(part);
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    if ((selmask >> i) & 1u) {
-      const int id = lane + 64 * i;
-      ids[pos[i]] = id;
-      wout[pos[i]] = den > 0.f ? num[i] / den : 1.0f / (float)k;
-      if (ids_lds) ids_lds[pos[i]] = id;
-    }
-  }
-}
+// ------------------------------------------------------------------ top-k + softmax (wave_topk: topk.h)
 
 template <int NPER>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E, int k, int renorm,
                                                int32_t* __restrict__ ids, float* __restrict__ wts) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  wave_topk<NPER>(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wts + (size_t)t * k, nullptr);
+  wave_topk<NPER>(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wts + (size_t)t * k);
 }
 
 // ------------------------------------------------------------------ permutation
@@ -356,9 +228,14 @@ __global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict_
   extern __shared__ int32_t sm[];
   __shared__ int32_t ids_s[kPermChunk];
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __shared__ float w_s[kPermChunk];
   for (int t = wave; t < T; t += nw)
-    wave_topk<NPER>(logits + (size_t)t * E, E, k, renorm, ids + (size_t)t * k, wts + (size_t)t * k, ids_s + t * k);
+    wave_topk<NPER>(logits + (size_t)t * E, E, k, renorm, ids_s + t * k, w_s + t * k);
   __syncthreads();
+  for (int f = threadIdx.x; f < T * k; f += blockDim.x) {
+    ids[f] = ids_s[f];
+    wts[f] = w_s[f];
+  }
   permute_chunk(ids_s, T * k, E, 0, sm, counts, offsets, perm, inv);
 }
 

@@ -1,0 +1,53 @@
+"""Static checks on the compiled decode kernel (CPU only: hipcc cross-compiles
+gfx950 assembly).
+
+The decode GEMV waits for its direct-to-LDS operand rows with an explicit
+`s_waitcnt vmcnt(N)` that counts the weight loads issued behind them (the
+vector-memory counter completes in order, so N later loads outstanding means
+the rows have landed).  That is only correct if the compiled code issues
+exactly N vector-memory loads between the last row load and the wait; this
+test checks it for every instantiation, so a compiler that merges or splits
+those loads fails here instead of racing on the GPU."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+@pytest.fixture(scope="module")
+def gemv_asm(tmp_path_factory):
+    if not (os.path.exists(HIPCC) or shutil.which("hipcc")):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "gemv.s"
+    cmd = [HIPCC, "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           os.path.join(ROOT, "fp4_expert_ffn_amd", "csrc", "ffn_gemv.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def test_row_wait_counts_the_loads_behind_the_rows(gemv_asm):
+    names = re.findall(r"^(_ZN3moe6k_gemvILi(\d)ELb(\d)ELi(\d+)EEE\w+):", gemv_asm, re.M)
+    assert len(names) == 36, len(names)  # 3 formats x 2 projections x 6 sub-item sizes
+    for full, fmt, _down, sub in names:
+        fmt, sub = int(fmt), int(sub)
+        body = gemv_asm[gemv_asm.index(full + ":"):gemv_asm.index(".Lfunc_end", gemv_asm.index(full + ":"))]
+        k = body.rfind("global_load_lds_dwordx4")
+        assert k > 0, full
+        loads, wait = 0, None
+        for line in body[k:].split("\n")[1:]:
+            t = line.strip()
+            if t.startswith(("global_load", "buffer_load", "flat_load", "scratch_load")):
+                loads += 1
+            if t.startswith("s_waitcnt") and "vmcnt" in t:
+                wait = int(t.split("vmcnt(")[1].split(")")[0])
+                break
+        # tiles, scales (4-bit formats) and the per-tensor multiplier of one bank
+        expected = sub + (sub if fmt != 0 else 0) + 1
+        assert wait == expected and loads == expected, (full, loads, wait, expected)
