@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmoe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["host.cpp", "cache.cpp", "route.hip", "ffn_gemv.hip", "ffn_mfma.hip", "ffn.hip"]
+SOURCES = ["host.cpp", "cache.cpp", "route.hip", "ffn_gemv.hip", "ffn_mfma.hip", "ffn_fp4gemm.hip", "ffn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -169,4 +169,58 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ------------------------------------------------------------ MXFP4 encoding
+// floor(log2|v|) of a finite nonzero fp32 value (exact, from the bits).
+__device__ __forceinline__ int ilog2_f32(float v) {
+  const uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
+  const int e = (int)(u >> 23);
+  if (e) return e - 127;
+  return (31 - __clz(u)) - 149;  // subnormal: u * 2^-149
+}
+
+// |q| -> E2M1 magnitude code, round to nearest even, saturate at 6.
+__device__ __forceinline__ uint32_t e2m1_mag_rne(float a) {
+  uint32_t m;
+  if (a <= 0.25f) m = 0;
+  else if (a < 0.75f) m = 1;
+  else if (a <= 1.25f) m = 2;
+  else if (a < 1.75f) m = 3;
+  else if (a <= 2.5f) m = 4;
+  else if (a < 3.5f) m = 5;
+  else if (a <= 5.0f) m = 6;
+  else m = 7;
+  return m;
+}
+
+// Encode 32 fp32 values as MXFP4: 16 packed bytes (element 2i low nibble) + E8M0.
+__device__ __forceinline__ void mxfp4_encode32(const float* v, uint4& q, uint32_t& s) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int ex = 0;
+  if (amax != 0.f) ex = min(127, max(-127, ilog2_f32(amax) - 2));
+  s = (uint32_t)(ex + 127);
+  // 2^-ex as an exact fp32 (normal for ex in [-127, 126]; subnormal 2^-127 for ex = 127)
+  const float inv = ex == 127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(127 - ex) << 23);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float qv = v[i] * inv;
+    const uint32_t code = e2m1_mag_rne(fabsf(qv)) | ((__float_as_uint(v[i]) >> 28) & 8u);
+    w[i >> 3] |= code << (4 * (i & 7));
+  }
+  q = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Barrier that orders LDS only: waits for this wave's LDS operations, not
+// for its global loads.  (A fenced barrier also waits for every global
+// load while direct-to-LDS loads are outstanding.)
+__device__ __forceinline__ void lds_sync() {
+  // gfx9 s_waitcnt: vmcnt 63 (no wait), expcnt 7 (no wait), lgkmcnt 0
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace moe

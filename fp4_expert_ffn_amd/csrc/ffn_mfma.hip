@@ -28,48 +28,6 @@ constexpr int kBM = 128, kBN = 128;
 
 // ---------------------------------------------------------------- activation quantiser
 
-// floor(log2|v|) of a finite nonzero fp32 value (exact, from the bits).
-__device__ __forceinline__ int ilog2_f32(float v) {
-  const uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
-  const int e = (int)(u >> 23);
-  if (e) return e - 127;
-  return (31 - __clz(u)) - 149;  // subnormal: u * 2^-149
-}
-
-// |q| -> E2M1 magnitude code, round to nearest even, saturate at 6.
-__device__ __forceinline__ uint32_t e2m1_mag_rne(float a) {
-  uint32_t m;
-  if (a <= 0.25f) m = 0;
-  else if (a < 0.75f) m = 1;
-  else if (a <= 1.25f) m = 2;
-  else if (a < 1.75f) m = 3;
-  else if (a <= 2.5f) m = 4;
-  else if (a < 3.5f) m = 5;
-  else if (a <= 5.0f) m = 6;
-  else m = 7;
-  return m;
-}
-
-// Encode 32 fp32 values as MXFP4: 16 packed bytes (element 2i low nibble) + E8M0.
-__device__ __forceinline__ void mxfp4_encode32(const float* v, uint4& q, uint32_t& s) {
-  float amax = 0.f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int ex = 0;
-  if (amax != 0.f) ex = min(127, max(-127, ilog2_f32(amax) - 2));
-  s = (uint32_t)(ex + 127);
-  // 2^-ex as an exact fp32 (normal for ex in [-127, 126]; subnormal 2^-127 for ex = 127)
-  const float inv = ex == 127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(127 - ex) << 23);
-  uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float qv = v[i] * inv;
-    const uint32_t code = e2m1_mag_rne(fabsf(qv)) | ((__float_as_uint(v[i]) >> 28) & 8u);
-    w[i >> 3] |= code << (4 * (i & 7));
-  }
-  q = make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // x [rows, cols] bf16 -> q [rows, cols/2], s [rows, cols/32]; one thread per 32-block.
 __global__ __launch_bounds__(256) void k_quant_mxfp4(const uint16_t* __restrict__ x, int rows, int cols,
                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
@@ -467,24 +425,35 @@ static MfmaKernel mfma_kernel(int nsteps) {
   return k_mfma_ffn<FP4, MODE, 2>;
 }
 
+bool fp4_gemm_fits(const FfnParams& P, int N, int K, bool gateup);
+hipError_t launch_fp4_gemm(const FfnParams& P, const MfmaBufs& B, bool down, hipStream_t s);
+
+// FP4: x quantised per token row; each projection runs on the persistent
+// 128 x 256 kernel where the shape allows (column count a multiple of 256;
+// gate/up: at least two K-steps), else on the 128 x 128 one.
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s) {
-  const int nt_gu = (2 * P.I) / kBN, nt_dn = P.H / kBN;
-  MfmaKernel k1, k2;
+  hipError_t e;
   if (fp4) {
-    hipError_t e = launch_quant_mxfp4(P.x, P.T, P.H, const_cast<uint8_t*>(B.xq), const_cast<uint8_t*>(B.xs), s);
+    e = launch_quant_mxfp4(P.x, P.T, P.H, const_cast<uint8_t*>(B.xq), const_cast<uint8_t*>(B.xs), s);
     if (e != hipSuccess) return e;
-      k1 = mfma_kernel<true, kGateUp>((P.H + 255) / 256);
-    k2 = mfma_kernel<true, kDown>((P.I + 255) / 256);
-  } else {
-    k1 = mfma_kernel<false, kGateUp>(P.H / 64);
-    k2 = mfma_kernel<false, kDown>(P.I / 64);
+    if (fp4_gemm_fits(P, 2 * P.I, P.H, true)) {
+      e = launch_fp4_gemm(P, B, false, s);
+    } else {
+      launch(mfma_kernel<true, kGateUp>((P.H + 255) / 256), dim3(max_tiles(P, (2 * P.I) / kBN)), dim3(256), 0, s, P,
+             B);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+    if (fp4_gemm_fits(P, P.H, P.I, false)) return launch_fp4_gemm(P, B, true, s);
+    launch(mfma_kernel<true, kDown>((P.I + 255) / 256), dim3(max_tiles(P, P.H / kBN)), dim3(256), 0, s, P, B);
+    return hipGetLastError();
   }
-  launch(k1, dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  launch(k2, dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
+  const int nt_gu = (2 * P.I) / kBN, nt_dn = P.H / kBN;
+  launch(mfma_kernel<false, kGateUp>(P.H / 64), dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
   e = hipGetLastError();
-  return e;
+  if (e != hipSuccess) return e;
+  launch(mfma_kernel<false, kDown>(P.I / 64), dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -51,3 +51,35 @@ def test_row_wait_counts_the_loads_behind_the_rows(gemv_asm):
         # tiles, scales (4-bit formats) and the per-tensor multiplier of one bank
         expected = sub + (sub if fmt != 0 else 0) + 1
         assert wait == expected and loads == expected, (full, loads, wait, expected)
+
+
+@pytest.fixture(scope="module")
+def fp4gemm_asm(tmp_path_factory):
+    if not (os.path.exists(HIPCC) or shutil.which("hipcc")):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "fp4gemm.s"
+    cmd = [HIPCC, "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           os.path.join(ROOT, "fp4_expert_ffn_amd", "csrc", "ffn_fp4gemm.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return out.read_text()
+
+
+def test_prefill_gemm_owns_m0(fp4gemm_asm):
+    """The prefill GEMM's direct-to-LDS loads set M0 in inline assembly; that is
+    only sound while the compiler itself neither reads nor writes M0 in the
+    kernel: every mention must be one of those `s_mov_b32 m0` + load pairs."""
+    names = re.findall(r"^(_ZN3moe10k_fp4_gemm\w+):", fp4gemm_asm, re.M)
+    assert len(names) == 2
+    for full in names:
+        i = fp4gemm_asm.index(full + ":")
+        body = fp4gemm_asm[i:fp4gemm_asm.index(".Lfunc_end", i)]
+        lines = [ln.strip() for ln in body.split("\n") if ln.strip() and not ln.strip().startswith(";")]
+        n = 0
+        for k, ln in enumerate(lines):
+            if re.search(r"\bm0\b", ln):
+                assert ln.startswith("s_mov_b32 m0,") and lines[k + 1] == "s_nop 0" and \
+                    lines[k + 2].startswith("global_load_lds"), (full, ln)
+                n += 1
+        assert n >= 8, (full, n)
