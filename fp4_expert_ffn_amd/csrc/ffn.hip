@@ -32,7 +32,7 @@ Path choose_path(const moe_ffn_args* a) {
 }
 
 struct WsLayout {
-  size_t sync, trash, h, y, xq, xs, hq, hs, hb, total;
+  size_t sync, trash, h, y, xq, xs, hq, hs, hb, inv, total;
 };
 
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
@@ -49,8 +49,11 @@ WsLayout ws_layout(const moe_ffn_args* a) {
   if (p == kPathGemv) {
     w.h = o; o = al(o + R * a->I * 2);
   } else if (p == kPathMfmaFp4) {
-    w.xq = o; o = al(o + (size_t)a->T * a->H / 2);
-    w.xs = o; o = al(o + (size_t)a->T * a->H / 32);
+    // x encoded per token row (128 x 128 kernel) or per routed + shared row
+    // (persistent kernel): room for the larger
+    w.xq = o; o = al(o + R * a->H / 2);
+    w.xs = o; o = al(o + R * a->H / 32);
+    w.inv = o; o = al(o + (size_t)a->T * a->k * 4);
     w.hq = o; o = al(o + R * a->I / 2);
     w.hs = o; o = al(o + R * a->I / 32);
   } else {
@@ -220,7 +223,7 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   FfnParams P{};
   P.T = a->T; P.k = a->k; P.E = a->E; P.H = a->H; P.I = a->I; P.fmt = a->wfmt;
-  P.x = a->x; P.counts = a->counts; P.offsets = a->offsets; P.perm = a->perm;
+  P.x = a->x; P.counts = a->counts; P.offsets = a->offsets; P.perm = a->perm; P.inv = a->inv;
   P.slot_of_expert = a->slot_of_expert;
   P.slot_pool = static_cast<const uint8_t*>(a->slot_pool);
   P.slot_stride = a->slot_stride;
@@ -248,6 +251,7 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     if (internal_bf16_y(a)) B.yb = reinterpret_cast<uint16_t*>(ws + w.y);
     if (path == kPathMfmaFp4) {
       B.xq = ws + w.xq; B.xs = ws + w.xs; B.hq = ws + w.hq; B.hs = ws + w.hs;
+      P.inv_ws = reinterpret_cast<int32_t*>(ws + w.inv);
     } else {
       B.hb = reinterpret_cast<uint16_t*>(ws + w.hb);
     }

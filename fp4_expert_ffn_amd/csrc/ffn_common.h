@@ -21,6 +21,8 @@ struct FfnParams {
   const int32_t* counts;       // [E]
   const int32_t* offsets;      // [E+1]
   const int32_t* perm;         // [T*k]
+  const int32_t* inv;          // [T*k] perm inverse (inv[perm[p]] = p); null: derive into inv_ws
+  int32_t* inv_ws;             // [T*k] workspace for the derived inverse
   const int32_t* slot_of_expert;
   const uint8_t* slot_pool;
   size_t slot_stride;

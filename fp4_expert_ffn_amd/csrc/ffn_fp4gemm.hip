@@ -9,25 +9,38 @@
 // cores.
 //
 // Design for gfx950:
-//  - One workgroup of 8 waves per CU, looping over a contiguous range of
-//    output tiles of 128 rows x 256 columns (XCD x takes the x-th eighth of
-//    the tile list, so an expert's tiles share one L2).  Waves form a 2 x 4
-//    grid of 64 x 64 blocks (4 x 4 MFMA tiles each).
-//  - K advances 256 values (two 128-wide K-tiles) per step.  A step's
-//    operands (A 16 KiB, B 32 KiB, their scales 3 KiB) arrive by direct
-//    global->LDS loads into a ring of NS stage buffers, issued NS - 1 steps
-//    ahead across tile boundaries: no registers hold loads in flight, so the
-//    prefetch depth is set by LDS (3 x 51 KiB).
+//  - One workgroup of 4 waves per CU loops over a contiguous range of output
+//    tiles of 128 rows x 512 columns (XCD x takes the x-th eighth of the tile
+//    list, so an expert's tiles share one L2).  Wave w computes all 128 rows
+//    x columns 128 w .. 128 w + 127: 8 x 8 MFMA tiles, 256 accumulators (the
+//    AGPRs), so every LDS fragment feeds 8 MFMAs.
+//  - K advances one 128-value K-tile per step.  A step's operands (A 8 KiB,
+//    B 32 KiB, scales 2.5 KiB) arrive by direct global->LDS loads into a ring
+//    of three stage buffers, issued three steps ahead across tile
+//    boundaries: no registers hold loads in flight.
+//  - Fragments are double-buffered in registers: step s's MFMAs run on
+//    fragments read during step s - 1, while step s + 1's fragments are read
+//    between them; the loads of step s + 3 (into the buffer step s's
+//    fragments came from) go out between the MFMA groups too, so LDS latency
+//    and waits for texture-unit slots overlap matrix-core work.
 //  - Every wave issues a fixed number of loads per step, so "stage s has
 //    landed" is an s_waitcnt vmcnt with a compile-time count; one LDS-only
-//    barrier per step then publishes the stage and frees the previous one.
+//    barrier per step publishes the stage and frees the one read before.
 //  - Each tile's expert, rows and column block come from descriptors built
-//    in LDS at the start, and the gate/up tiles' token rows from perm
-//    entries loaded (also directly into LDS) one tile ahead: the loop issues
-//    no global loads besides the ring.
-//  - The gate/up epilogue forms SwiGLU in registers (each wave holds matching
-//    gate and up columns) and MXFP4-encodes each row's 32 values with
-//    cross-lane (DPP) maxima: no LDS, so the ring keeps streaming.
+//    in LDS at the start: the loop issues no global loads besides the ring.
+//  - Both A operands are MXFP4 rows in permutation order (routed rows, then
+//    the shared expert's token rows; R in all), stored K-tile-major: codes
+//    [K/128][R][64 B], scales [K/128][R][4 B].  x arrives so from the row
+//    quantiser; the gate/up epilogue writes its SwiGLU output so.  Every
+//    direct load of an A operand or its scales then reads contiguous memory.
+//  - The weights are the MFMA's first operand, so a lane's accumulator holds
+//    four consecutive output columns of one row.  The gate/up epilogue
+//    encodes SwiGLU outputs to E2M1 in pairs with v_cvt_scalef32_pk_fp4_f32
+//    (round to nearest even, saturating at 6, as the MXFP4 encoding here
+//    requires) after a 4-lane maximum per 32-column block.
+//  - Epilogues stage their output in a dedicated LDS area and store whole
+//    row segments: a store instruction that touches 16 rows costs the
+//    texture-address unit about as much as four contiguous ones.
 #include <type_traits>
 
 #include "ffn_common.h"
@@ -37,22 +50,26 @@ namespace moe {
 
 // ---------------------------------------------------------------- the GEMM
 
-enum { kG_GateUp = 0, kG_Down = 1 };
+// down: bf16 expert outputs (yb) or fp32 (y)
+enum { kG_GateUp = 0, kG_Down = 1, kG_DownF32 = 2 };
 
-constexpr int kGBM = 128, kGBN = 256;
-constexpr int kGA = 128 * 128;           // A: 128 rows x 128 bytes (256 FP4 values)
-constexpr int kGB = 16 * 2 * 1024;       // B: 16 row groups x 2 K-tiles x 1 KiB
-constexpr int kGSA = 128 * 8;            // A scales: 8 E8M0 per row
-constexpr int kGSB = 16 * 2 * 64;        // B scales: 32 scale tiles of 64 bytes
+constexpr int kGBM = 128, kGBN = 512;
+constexpr int kGA = 128 * 64;            // A: 128 rows x 64 bytes (128 FP4 values)
+constexpr int kGB = 32 * 1024;           // B: 32 row groups x one 1 KiB tile
+constexpr int kGSA = 128 * 4;            // A scales: 4 E8M0 per row
+constexpr int kGSB = 32 * 64;            // B scales: 32 scale tiles of 64 bytes
 constexpr int kGStage = kGA + kGB + kGSA + kGSB;
 constexpr int kGStages = 3;
+// epilogue staging: gate/up codes [2][128][64 B] + scales [2][128][4 B];
+// down: four waves x 16 rows x 256 B
+constexpr int kGStaging = 2 * kGBM * 64 + 2 * kGBM * 4;
 constexpr int kGMaxTiles = 64;           // tiles per workgroup (descriptors in LDS)
+constexpr int kGThreads = 256;
 
-// The stage ring: three LDS buffers; the step loop is unrolled by three so
-// each step's buffers are known at compile time.
-__shared__ __align__(16) uint8_t g_stage0[kGStage];
-__shared__ __align__(16) uint8_t g_stage1[kGStage];
-__shared__ __align__(16) uint8_t g_stage2[kGStage];
+// The stage ring (indexed at run time: every fragment read is a per-lane
+// base plus the stage's offset plus an immediate) and the staging area.
+__shared__ __align__(16) uint8_t g_ring[kGStages * kGStage];
+__shared__ __align__(16) uint8_t g_stg[kGStaging];
 
 struct TileDesc {
   int slot;  // expert blob slot; -1: the shared expert
@@ -74,14 +91,15 @@ struct TileDesc {
 __device__ __forceinline__ uint32_t lds_off(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
 }
-__device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
+// dst: LDS byte address
+__device__ __forceinline__ void dma16(const void* src, uint32_t dst) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
-               "s"(__builtin_amdgcn_readfirstlane(lds_off(dst)))
+               "s"(__builtin_amdgcn_readfirstlane(dst))
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* src, uint8_t* dst) {
+__device__ __forceinline__ void dma4(const void* src, uint32_t dst) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src),
-               "s"(__builtin_amdgcn_readfirstlane(lds_off(dst)))
+               "s"(__builtin_amdgcn_readfirstlane(dst))
                : "memory", "m0");
 }
 
@@ -98,40 +116,35 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
-// max over the 16 lanes of a DPP row (lanes 16r .. 16r + 15), in every lane
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f32<kDppQuadXor1>(v));
-  v = fmaxf(v, dpp_f32<kDppQuadXor2>(v));
-  v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
-  v = fmaxf(v, dpp_f32<kDppRowMirror>(v));
-  return v;
+// SwiGLU gate factor z * sigmoid(z) from the hardware exp2 and reciprocal
+// (each within 1 ulp); -inf -> -0, +inf -> +inf.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
-template <int I>
-__device__ __forceinline__ uint8_t* stage_buf() {
-  if constexpr (I == 0) return g_stage0;
-  else if constexpr (I == 1) return g_stage1;
-  else return g_stage2;
+// Two E2M1 codes (a in bits 3:0, b in bits 7:4) of values already divided
+// by their block scale: round to nearest even, saturate at +-6.
+__device__ __forceinline__ uint32_t e2m1_pair(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
 }
 
 template <int MODE>
-__global__ __launch_bounds__(512) void k_fp4_gemm(FfnParams P, MfmaBufs B) {
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   __shared__ TileDesc desc[kGMaxTiles];
-  // gate/up: perm entries of the rows of tiles q (slot q % 2) and q + 1 (the
-  // other slot, loaded while tile q streams); the A row of a routed tile's
-  // row r is token plist[...] / k of the token-order activations
-  __shared__ int32_t plist[2][kGBM];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 2, wn = wave & 3;
+  // wave-uniform values in scalar registers (the compiler cannot prove it)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = MODE == kG_GateUp ? P.H : P.I;
   const int NT = (MODE == kG_GateUp ? 2 * P.I : P.H) / kGBN;
-  const int nk_w = K / 128;  // weight K-tiles per row group
-  const int nsteps = (K + 255) / 256;
-  const bool half_tail = (K % 256) != 0;  // the last step holds one K-tile
-  const uint32_t arow = K / 2, asrow = K / 32;
+  const int nsteps = K / 128;  // K-tiles per tile (K % 128 == 0 by the blob layout)
+  // rows of the K-tile-major A operands (routed rows, then shared rows)
+  const uint32_t rtot = P.T * P.k + (P.shared_blob ? P.T : 0);
+  // A operand and scale bytes between consecutive K-tiles of one row
+  const size_t a_kstride = (size_t)rtot * 64, as_kstride = (size_t)rtot * 4;
 
   // ---- the tile list: experts in id order, each expert's row tiles, each
   // row tile's column blocks (fastest); the shared expert's tiles last.
-  int* pre = reinterpret_cast<int*>(g_stage0);  // [E + 1], in the (still idle) stage area
+  int* pre = reinterpret_cast<int*>(g_ring);  // [E + 1], in the (still idle) stage area
   const int E = P.E;
   if (tid < 64) {
     int run = 0;
@@ -160,7 +173,7 @@ __global__ __launch_bounds__(512) void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   const int r = (b % 8) * (G / 8) + b / 8;  // XCD b % 8 takes the (b % 8)-th eighth of the list
   const int L0 = (int)((long long)total * r / G), L1 = (int)((long long)total * (r + 1) / G);
   const int ntile = L1 - L0;  // <= kGMaxTiles (checked by the launcher)
-  for (int q = tid; q < ntile; q += 512) {
+  for (int q = tid; q < ntile; q += kGThreads) {
     const int L = L0 + q;
     TileDesc d;
     if (L >= routed) {
@@ -187,201 +200,293 @@ __global__ __launch_bounds__(512) void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   }
   lds_barrier();
   if (ntile == 0) return;
-  if (MODE == kG_GateUp && tid < kGBM && desc[0].slot >= 0)
-    plist[0][tid] = P.perm[desc[0].row0 + min(tid, desc[0].rows - 1)];
-  lds_barrier();
   const int nsteps_total = ntile * nsteps;
 
   const uint8_t* abase = MODE == kG_GateUp ? B.xq : B.hq;
   const uint8_t* asbase = MODE == kG_GateUp ? B.xs : B.hs;
+  static_assert(MODE == kG_GateUp || MODE == kG_Down || MODE == kG_DownF32, "mode");
   const size_t off_w = MODE == kG_GateUp ? P.L.off_w13 : P.L.off_w2;
   const size_t off_s = MODE == kG_GateUp ? P.L.off_s13 : P.L.off_s2;
+  const uint32_t wstride = (uint32_t)nsteps * kTileBytes;  // weight bytes per row group
 
-  // Loads of global step s into stage buffer `buf`: waves 0-3 issue 8 (A 2,
-  // B 4, A scales 1, B scales 1), waves 4-7 issue 7 (no A scales).
-  // Issue-side tile state: the byte offsets of this lane's loads for K-step
-  // 0 of the tile being issued, recomputed at each tile's first step (the
-  // steps only add K offsets).
-  const int seg0 = (lane & 7) ^ (lane >> 3);  // logical A segment this lane loads
-  uint32_t a_off[2], as_off = 0, b_off[4], bs_off;
-  const uint8_t* blob = nullptr;
-  // row of the A operand (and its scales) for row r of tile q
-  auto a_row = [&](int q, const TileDesc& d, int r) __attribute__((always_inline)) -> uint32_t {
-    const int rr = min(r, d.rows - 1);  // rows past the tile re-read its last row
-    if (MODE == kG_Down) return d.row0 + rr;
-    if (d.slot < 0) return d.row0 - P.T * P.k + rr;  // the shared expert: token rows
-    return (uint32_t)plist[q & 1][rr] / (uint32_t)P.k;
-  };
-  auto tile_state = [&](int q) __attribute__((always_inline)) {
-    const TileDesc d = desc[q];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) a_off[i] = a_row(q, d, 8 * (2 * wave + i) + (lane >> 3)) * arow + seg0 * 16;
-    if (wave < 4) as_off = a_row(q, d, 32 * wave + (lane >> 1)) * asrow + (lane & 1) * 4;
-    blob = d.slot < 0 ? P.shared_blob : P.slot_pool + (size_t)d.slot * P.slot_stride;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int qq = 4 * wave + i;
-      b_off[i] = ((uint32_t)(d.nt * 16 + (qq >> 1)) * nk_w + (qq & 1)) * kTileBytes + lane * 16;
-    }
-    bs_off = ((uint32_t)(d.nt * 16 + 2 * wave + (lane >> 5)) * nk_w + ((lane >> 4) & 1)) * 64 + (lane & 15) * 4;
-  };
-  auto issue = [&](int s, uint8_t* st) __attribute__((always_inline)) {
-    const int q = s / nsteps, ks = s - q * nsteps;
-    if (ks == 0) {
-      tile_state(q);
-      // gate/up: the next tile's perm entries, ahead of that tile's first
-      // loads by nsteps >= 2 steps (in the other slot, whose last reader was
-      // the issue of this tile's state)
-      if (MODE == kG_GateUp && wave < 2 && q + 1 < ntile) {
-        const TileDesc dn = desc[q + 1];
-        if (dn.slot >= 0) {
-          const int r = min(64 * wave + lane, dn.rows - 1);
-          dma4(P.perm + dn.row0 + r, reinterpret_cast<uint8_t*>(&plist[(q + 1) & 1][64 * wave]));
-        }
-      }
-    }
-    // A tail step (K % 256 == 128) holds one K-tile: its second K-tile's
-    // loads re-read the first's (never used).
-    const bool tail = half_tail && ks == nsteps - 1;
-    // A: chunk c = 2 wave + i holds rows 8c .. 8c + 7; lane l writes physical
-    // segment l % 8 of row 8c + l / 8, which holds logical segment
-    // (l % 8) ^ (l / 8) (the swizzle that makes fragment reads conflict-free).
-    const uint32_t a_k = ks * 128 - ((tail && seg0 >= 4) ? 64 : 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(abase + a_off[i] + a_k, st + (2 * wave + i) * 1024);
-    // B: tile qq = 4 wave + i is row group nt * 16 + qq / 2, K-tile 2 ks + qq % 2
-    const uint8_t* wt = blob + off_w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t kk = 2 * ks * kTileBytes - ((tail && (i & 1)) ? kTileBytes : 0);
-      dma16(wt + b_off[i] + kk, st + kGA + (4 * wave + i) * 1024);
-    }
-    // A scales (waves 0-3): row 32 wave + l / 2, dword l % 2 of its 8 step bytes
-    if (wave < 4) dma4(asbase + as_off + ks * 8 - ((tail && (lane & 1)) ? 4 : 0), st + kGA + kGB + wave * 256);
-    // B scales: scale tile (row group nt * 16 + 2 wave + l / 32, K-tile
-    // 2 ks + (l / 16) % 2), dword l % 16; in LDS at (2 ntl + kt) * 64
-    dma4(blob + off_s + bs_off + 2 * ks * 64 - ((tail && ((lane >> 4) & 1)) ? 64 : 0),
-         st + kGA + kGB + kGSA + wave * 256);
+  auto uniform_desc = [&](int q) __attribute__((always_inline)) -> TileDesc {
+    TileDesc d;
+    d.slot = __builtin_amdgcn_readfirstlane(desc[q].slot);
+    d.row0 = __builtin_amdgcn_readfirstlane(desc[q].row0);
+    d.rows = __builtin_amdgcn_readfirstlane(desc[q].rows);
+    d.nt = __builtin_amdgcn_readfirstlane(desc[q].nt);
+    return d;
   };
 
-  f32x4_t acc[4][4];
+  // Loads of one step (K-tile ks of a tile) into a stage buffer, 13 slots:
+  //   0: A scales (waves 0-1): row 64 wave + l, the dword of K-tile ks
+  //   1-2: A chunk 2 wave + J - 1 (rows 16 c .. 16 c + 15, 1 KiB)
+  //   3-10: B row group nt * 32 + 8 wave + J - 3
+  //   11-12: B scale tiles of row groups nt * 32 + 8 wave + 4 (J - 11) + l / 16
+  // Waves 0-1 issue 13 loads per step, waves 2-3 issue 12.
+  // A chunk c: lane l writes physical segment l % 4 of row 16 c + l / 4,
+  // which holds logical segment (l % 4) ^ (l / 16) (row bits 3:2), the
+  // swizzle that makes fragment reads conflict-free.
+  const int aseg = (lane & 3) ^ (lane >> 4);
+  // issue-side tile state, refreshed at each tile's first K-tile
+  uint32_t a_off[2], as_off = 0;
+  const uint8_t* wt = nullptr;   // this wave's first B row group of the tile
+  const uint8_t* wst = nullptr;  // its scale tiles
+  int iss_ks = 0;
+  uint32_t iss_st = 0;
+  auto a_row = [&](const TileDesc& d, int rr) __attribute__((always_inline)) -> uint32_t {
+    return d.row0 + min(rr, d.rows - 1);  // rows past the tile re-read its last row
+  };
+  auto issue_begin = [&](int s, const uint8_t* stp) __attribute__((always_inline)) {
+    iss_st = lds_off(stp);
+    const int q = s / nsteps;
+    iss_ks = s - q * nsteps;
+    if (iss_ks == 0) {
+      const TileDesc d = uniform_desc(q);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int s, const uint8_t* st) __attribute__((always_inline)) {
-    const bool tail = half_tail && (s % nsteps) == nsteps - 1;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      if (kt == 1 && tail) break;
-      i32x8_t a[4], bb[4];
-      int sa[4], sb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (4 * wm + i) * 16 + (lane & 15), seg = kt * 4 + (lane >> 4);
-        const uint4 u = *reinterpret_cast<const uint4*>(st + row * 128 + ((seg ^ (row & 7)) << 4));
-        a[i] = i32x8_t{(int)u.x, (int)u.y, (int)u.z, (int)u.w, 0, 0, 0, 0};
-        sa[i] = st[kGA + kGB + row * 8 + kt * 4 + (lane >> 4)];
-        const int qq = (4 * wn + i) * 2 + kt;
-        const uint4 v = *reinterpret_cast<const uint4*>(st + kGA + qq * 1024 + lane * 16);
-        bb[i] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        sb[i] = st[kGA + kGB + kGSA + qq * 64 + lane];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bb[j], acc[i][j], 4, 4, 0, sa[i], 0,
-                                                                        sb[j]);
+      for (int u = 0; u < 2; ++u) a_off[u] = a_row(d, 16 * (2 * wave + u) + (lane >> 2)) * 64 + aseg * 16;
+      if (wave < 2) as_off = a_row(d, 64 * wave + lane) * 4;
+      const uint8_t* blob = d.slot < 0 ? P.shared_blob : P.slot_pool + (size_t)d.slot * P.slot_stride;
+      const uint32_t g0 = (uint32_t)(d.nt * 32 + 8 * wave);
+      wt = blob + off_w + (size_t)g0 * wstride;
+      wst = blob + off_s + (size_t)g0 * nsteps * 64;
     }
   };
+  auto issue_slot = [&](auto jc) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    if constexpr (J == 0) {
+      if (wave < 2) dma4(asbase + as_off + iss_ks * as_kstride, iss_st + kGA + kGB + wave * 256);
+    } else if constexpr (J < 3) {
+      dma16(abase + a_off[J - 1] + iss_ks * a_kstride, iss_st + (2 * wave + J - 1) * 1024);
+    } else if constexpr (J < 11) {
+      dma16(wt + (size_t)(J - 3) * wstride + (size_t)iss_ks * kTileBytes + lane * 16,
+            iss_st + kGA + (8 * wave + J - 3) * 1024);
+    } else {
+      constexpr int h = J - 11;
+      dma4(wst + ((size_t)(4 * h + (lane >> 4)) * nsteps + iss_ks) * 64 + (lane & 15) * 4,
+           iss_st + kGA + kGB + kGSA + (2 * wave + h) * 256);
+    }
+  };
+  auto issue_all = [&](int s, const uint8_t* stp) __attribute__((always_inline)) {
+    issue_begin(s, stp);
+    issue_slot(std::integral_constant<int, 0>{});
+    issue_slot(std::integral_constant<int, 1>{});
+    issue_slot(std::integral_constant<int, 2>{});
+    issue_slot(std::integral_constant<int, 3>{});
+    issue_slot(std::integral_constant<int, 4>{});
+    issue_slot(std::integral_constant<int, 5>{});
+    issue_slot(std::integral_constant<int, 6>{});
+    issue_slot(std::integral_constant<int, 7>{});
+    issue_slot(std::integral_constant<int, 8>{});
+    issue_slot(std::integral_constant<int, 9>{});
+    issue_slot(std::integral_constant<int, 10>{});
+    issue_slot(std::integral_constant<int, 11>{});
+    issue_slot(std::integral_constant<int, 12>{});
+  };
 
-  // Lane l of MFMA tile (i, j) holds column l % 16 and rows 4 (l / 16) + v.
+  // acc[i][j]: output rows 16 i + (l % 16), columns 128 wave + 16 j + 4 (l / 16) + v
+  // (the weights are the MFMA's row operand)
+  // (a tile's first K-tile starts the sums from zero: no accumulator is ever
+  // written by a plain move, which keeps them in the AGPRs)
+  f32x4_t acc[8][8];
+
+  // Fragment set: A (rows 16 i + l % 16, K-chunk l / 16) and B (row group
+  // 8 wave + j) operands and their scale bytes, for one step.
+  u32x4_t fa0[8], fb0[8], fa1[8], fb1[8];
+  int sa0[8], sb0[8], sa1[8], sb1[8];
+  // fragment u (A row tile u and B row group u) of stage buffer st: per-lane
+  // byte offsets, to which u adds only constants (A row 16 u + l % 16 keeps
+  // the swizzle bits of row l % 16)
+  const int seg = lane >> 4;
+  const uint32_t a_rd = (lane & 15) * 64 + ((seg ^ (((lane & 15) >> 2) & 3)) << 4);
+  const uint32_t sa_rd = kGA + kGB + (lane & 15) * 4 + seg;
+  const uint32_t b_rd = kGA + (8 * wave) * 1024 + lane * 16;
+  const uint32_t sb_rd = kGA + kGB + kGSA + (8 * wave) * 64 + lane;
+  auto read_frag = [&](const uint8_t* st, int u, u32x4_t* fa, u32x4_t* fb, int* sa, int* sb)
+      __attribute__((always_inline)) {
+    fa[u] = *reinterpret_cast<const u32x4_t*>(st + a_rd + u * 1024);
+    sa[u] = st[sa_rd + u * 64];
+    fb[u] = *reinterpret_cast<const u32x4_t*>(st + b_rd + u * 1024);
+    sb[u] = st[sb_rd + u * 64];
+  };
+
+  // Epilogue of tile q (reads the accumulators).
   auto epilogue = [&](int q) __attribute__((always_inline)) {
-    const TileDesc d = desc[q];
-    const int col = lane & 15;
+    const TileDesc d = uniform_desc(q);
+    const int t16 = lane & 15, g = lane >> 4;
     if constexpr (MODE == kG_Down) {
+      {
+        // per 16-row block: the wave's 16 x 128 bf16 outputs through its own
+        // 4 KiB of the staging area (16-byte granules XOR-swizzled by row),
+        // then stores of 4 rows x 256 contiguous bytes
+        uint8_t* ws = g_stg + wave * 4096;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int m = (4 * wm + i) * 16 + 4 * (lane >> 4) + v;
-          if (m < d.rows) {
-            const size_t o = (size_t)(d.row0 + m) * P.H + d.nt * kGBN + (4 * wn) * 16 + col;
-            if (B.yb) {
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16);
+            const int gr = 2 * j + (g >> 1);  // 16-byte granule of columns 16 j + 4 g
+            *reinterpret_cast<uint2*>(ws + t16 * 256 + ((gr ^ t16) << 4) + (g & 1) * 8) = make_uint2(lo, hi);
+          }
 #pragma unroll
-              for (int j = 0; j < 4; ++j) B.yb[o + 16 * j] = f32_to_bf16_rne(acc[i][j][v]);
-            } else {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) B.y[o + 16 * j] = acc[i][j][v];
-            }
+          for (int pr = 0; pr < 4; ++pr) {
+            const int rr = 4 * pr + (lane >> 4), gr = lane & 15;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ws + rr * 256 + ((gr ^ rr) << 4));
+            const int m = 16 * i + rr;
+            if (m < d.rows)
+              *reinterpret_cast<u32x4_t*>(B.yb + (size_t)(d.row0 + m) * P.H + d.nt * kGBN + 128 * wave + gr * 8) = v;
           }
         }
+      }
+    } else if constexpr (MODE == kG_DownF32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int m = 16 * i + t16;
+        if (m < d.rows) {
+          const size_t o = (size_t)(d.row0 + m) * P.H + d.nt * kGBN + 128 * wave + 4 * g;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(B.y + o + 16 * j) = acc[i][j];
+        }
+      }
     } else {
-      // W13 row groups alternate gate / up, so MFMA columns j = 0, 1 and 2, 3
-      // are (gate, up) of two 16-column pairs: 32 SwiGLU columns per row, one
-      // MXFP4 block, starting at intermediate column d.nt * 128 + 32 wn.
-      const int cb = d.nt * 128 + 32 * wn;
+      // W13 row groups alternate gate / up, so MFMA tiles j = 2p, 2p + 1 are
+      // (gate, up) of SwiGLU columns 64 wave + 16 p .. + 15 of the tile's 256
+      // (down K-tiles 2 nt and 2 nt + 1); MXFP4 block bk (32 columns) is
+      // p = 2 bk, 2 bk + 1.  Lane l holds columns 4 (l / 16) + v of each p:
+      // the block's 32 values of a row sit in lanes l % 16 + 16 g, g = 0..3.
+      // Staging: codes [K-tile][128 rows][64 B], then scales [K-tile][128][4 B].
+      const int kt = wave >> 1, half = wave & 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i) {
+        const int m = 16 * i + t16;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float h0 = silu_f32(acc[i][0][v]) * acc[i][1][v];
-          const float h1 = silu_f32(acc[i][2][v]) * acc[i][3][v];
-          const float amax = row16_max(fmaxf(fabsf(h0), fabsf(h1)));
+        for (int bk = 0; bk < 2; ++bk) {
+          float h[8];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            h[v] = silu_fast(acc[i][4 * bk][v]) * acc[i][4 * bk + 1][v];
+            h[4 + v] = silu_fast(acc[i][4 * bk + 2][v]) * acc[i][4 * bk + 3][v];
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) amax = fmaxf(amax, fabsf(h[v]));
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
           int ex = 0;
           if (amax != 0.f) ex = min(127, max(-127, ilog2_f32(amax) - 2));
+          // 2^-ex as an exact fp32 (subnormal 2^-127 for ex = 127)
           const float inv = ex == 127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(127 - ex) << 23);
-          const uint32_t c0 = e2m1_mag_rne(fabsf(h0 * inv)) | ((__float_as_uint(h0) >> 28) & 8u);
-          const uint32_t c1 = e2m1_mag_rne(fabsf(h1 * inv)) | ((__float_as_uint(h1) >> 28) & 8u);
-          // bytes of the row: byte b = codes of columns 2b (low nibble) and
-          // 2b + 1; lane 14 of each 16-lane row gathers bytes 0-7 (pair 0)
-          // and 8-15 (pair 1) by DPP row shifts and stores all 16
-          uint32_t ba = c0 | (dpp_u32<kDppQuadXor1>(c0) << 4), bb = c1 | (dpp_u32<kDppQuadXor1>(c1) << 4);
-          ba = dpp_u32<kDppRowShr2>(ba) | (ba << 8);     // lanes 4j + 2: bytes 2j, 2j + 1
-          bb = dpp_u32<kDppRowShr2>(bb) | (bb << 8);
-          ba = dpp_u32<kDppRowShr4>(ba) | (ba << 16);    // lanes 8j + 6: bytes 4j .. 4j + 3
-          bb = dpp_u32<kDppRowShr4>(bb) | (bb << 16);
-          const uint32_t la = dpp_u32<kDppRowShr8>(ba), lb = dpp_u32<kDppRowShr8>(bb);  // lane 14: bytes 0-3
-          const int m = (4 * wm + i) * 16 + 4 * (lane >> 4) + v;
-          if (m < d.rows) {
-            const size_t p = (size_t)(d.row0 + m);
-            if (col == 14) *reinterpret_cast<uint4*>(B.hq + p * (P.I / 2) + cb / 2) = make_uint4(la, ba, lb, bb);
-            if (col == 0) B.hs[p * (P.I / 32) + cb / 32] = (uint8_t)(ex + 127);
-          }
+          const uint32_t lo = e2m1_pair(h[0] * inv, h[1] * inv) | (e2m1_pair(h[2] * inv, h[3] * inv) << 8);
+          const uint32_t hi = e2m1_pair(h[4] * inv, h[5] * inv) | (e2m1_pair(h[6] * inv, h[7] * inv) << 8);
+          uint8_t* dst = g_stg + kt * (kGBM * 64) + m * 64 + 32 * half + 16 * bk + 2 * g;
+          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)lo;      // columns 4g .. 4g + 3
+          *reinterpret_cast<uint16_t*>(dst + 8) = (uint16_t)hi;  // columns 16 + 4g ..
+          if (g == 0) g_stg[2 * kGBM * 64 + kt * (kGBM * 4) + m * 4 + 2 * half + bk] = (uint8_t)(ex + 127);
         }
+      }
+      lds_sync();
+      // the tile's rows of down K-tiles 2 nt, 2 nt + 1: 16 rows x 64 B (1 KiB
+      // contiguous) per store; the scales 64 rows x 4 B per store
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = 4 * wave + u, k2 = c >> 3, row = 16 * (c & 7) + (lane >> 2);
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(g_stg + k2 * (kGBM * 64) + row * 64 + (lane & 3) * 16);
+        if (row < d.rows)
+          *reinterpret_cast<u32x4_t*>(B.hq + ((size_t)(2 * d.nt + k2) * rtot + d.row0 + row) * 64 + (lane & 3) * 16) = v;
+      }
+      {
+        const int k2 = wave >> 1, row = 64 * (wave & 1) + lane;
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(g_stg + 2 * kGBM * 64 + k2 * (kGBM * 4) + row * 4);
+        if (row < d.rows) *reinterpret_cast<uint32_t*>(B.hs + ((size_t)(2 * d.nt + k2) * rtot + d.row0 + row) * 4) = v;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   };
 
-  // ---- the pipeline: steps 0 .. NS-2 in flight before the first; step s
-  // waits for its own loads (the NS - 2 later steps' loads stay in flight),
-  // barriers, refills the buffer step s - 1 used with step s + NS - 1 (past
-  // the end: the last step again, never read), and computes.
+  // ---- the pipeline.  Prologue: stages 0-2 issued, stage 0's fragments read.
+  // Step s: wait for stage s + 1 (stage s + 2 stays in flight), barrier
+  // (stage s + 1 published; stage s's buffer, read during step s - 1, free),
+  // then 8 groups of 8 MFMAs on step s's fragments, each followed by the
+  // reads of one fragment of stage s + 1 and one or two loads of stage s + 3
+  // into stage s's buffer (past the end: the last stage again, never read).
   const int last = nsteps_total - 1;
-  issue(0, stage_buf<0>());
-  issue(min(1, last), stage_buf<1>());
-  auto step = [&](int s, auto bufc) __attribute__((always_inline)) {
-    constexpr int I = decltype(bufc)::value;
-    if (wave < 4) wait_vm<(kGStages - 2) * 8>();
-    else wait_vm<(kGStages - 2) * 7>();
+  issue_all(0, g_ring);
+  issue_all(min(1, last), g_ring + kGStage);
+  issue_all(min(2, last), g_ring + 2 * kGStage);
+  if (wave < 2) wait_vm<2 * 13>();
+  else wait_vm<2 * 12>();
+  lds_sync();
+#pragma unroll
+  for (int u = 0; u < 8; ++u) read_frag(g_ring, u, fa0, fb0, sa0, sb0);
+
+  int cur = 0, s = 0;  // global step and the stage buffer it reads
+  auto step = [&](auto zc, auto pc, u32x4_t* fa, u32x4_t* fb, int* sa, int* sb, u32x4_t* na, u32x4_t* nb, int* nsa,
+                  int* nsb) __attribute__((always_inline)) {
+    constexpr bool first = decltype(zc)::value;     // a tile's first K-tile
+    constexpr bool prefetch = decltype(pc)::value;  // read the next step's fragments
+    if (wave < 2) wait_vm<13>();
+    else wait_vm<12>();
     lds_sync();
-    issue(min(s + kGStages - 1, last), stage_buf<(I + kGStages - 1) % kGStages>());
-    compute(s, stage_buf<I>());
-    if ((s % nsteps) == nsteps - 1) epilogue(s / nsteps);
+    const int nxt = cur == kGStages - 1 ? 0 : cur + 1;
+    const uint8_t* stn = g_ring + nxt * kGStage;
+    issue_begin(min(s + kGStages, last), g_ring + cur * kGStage);
+    issue_slot(std::integral_constant<int, 0>{});
+    auto group = [&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            i32x8_t{(int)fb[j].x, (int)fb[j].y, (int)fb[j].z, (int)fb[j].w, 0, 0, 0, 0},
+            i32x8_t{(int)fa[i].x, (int)fa[i].y, (int)fa[i].z, (int)fa[i].w, 0, 0, 0, 0},
+            first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[i][j], 4, 4, 0, sb[j], 0, sa[i]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (prefetch) read_frag(stn, j, na, nb, nsa, nsb);
+      if constexpr (j < 4) {
+        issue_slot(std::integral_constant<int, 2 * j + 1>{});
+        issue_slot(std::integral_constant<int, 2 * j + 2>{});
+      } else {
+        issue_slot(std::integral_constant<int, j + 5>{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    group(std::integral_constant<int, 0>{});
+    group(std::integral_constant<int, 1>{});
+    group(std::integral_constant<int, 2>{});
+    group(std::integral_constant<int, 3>{});
+    group(std::integral_constant<int, 4>{});
+    group(std::integral_constant<int, 5>{});
+    group(std::integral_constant<int, 6>{});
+    group(std::integral_constant<int, 7>{});
+    // The step's MFMAs stay in the step: without a use here the compiler
+    // sinks side-effect-free MFMAs whose results are next read in a later
+    // block (a tile's first step into the next one, its last step into the
+    // epilogue), and they lose their place between the loads.
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      asm volatile("" ::"a"(acc[i][0]), "a"(acc[i][1]), "a"(acc[i][2]), "a"(acc[i][3]), "a"(acc[i][4]),
+                   "a"(acc[i][5]), "a"(acc[i][6]), "a"(acc[i][7]));
+    cur = nxt;
+    ++s;
   };
-  int s = 0;
-  for (; s + 3 <= nsteps_total; s += 3) {
-    step(s, std::integral_constant<int, 0>{});
-    step(s + 1, std::integral_constant<int, 1>{});
-    step(s + 2, std::integral_constant<int, 2>{});
+  // nsteps is even (checked by the launcher): a tile's steps alternate
+  // between the two fragment sets, starting with set 0.  The last step of a
+  // tile reads no fragments: the epilogue runs with only the accumulators
+  // live, and the next tile's first fragments are read after it.
+  const std::true_type yes;
+  const std::false_type no;
+  for (int q = 0; q < ntile; ++q) {
+    step(yes, yes, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
+    for (int ks = 1; ks < nsteps - 1; ks += 2) {
+      step(no, yes, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
+      step(no, yes, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
+    }
+    step(no, no, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
+    epilogue(q);
+    if (q + 1 < ntile) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) read_frag(g_ring + cur * kGStage, u, fa0, fb0, sa0, sb0);
+    }
   }
-  if (s < nsteps_total) step(s, std::integral_constant<int, 0>{});
-  if (s + 1 < nsteps_total) step(s + 1, std::integral_constant<int, 1>{});
   wait_vm<0>();  // no load into this workgroup's LDS outlives it
 }
 
@@ -393,31 +498,32 @@ static long long fp4_max_tiles(const FfnParams& P, int NT) {
   return mt * NT;
 }
 
-static int cu_count_fp4() {
+// Persistent grid: one workgroup per CU, a multiple of the 8 XCDs.
+static int fp4_grid() {
   static int n = 0;
   if (n == 0) {
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    n = cus;
+    n = cus / 8 * 8;
   }
   return n;
 }
 
-// Whether a projection of N output columns can run here (else the caller
-// uses the 128 x 128 kernel).
-bool fp4_gemm_fits(const FfnParams& P, int N, int K, bool gateup) {
-  if (N % kGBN != 0) return false;
-  if (gateup && (K + 255) / 256 < 2) return false;  // the perm entries arrive a tile ahead
-  const int G = cu_count_fp4() / 8 * 8;
+// Whether a projection of N output columns over K can run here (else the
+// caller uses the 128 x 128 kernel).
+bool fp4_gemm_fits(const FfnParams& P, int N, int K, bool /*gateup*/) {
+  if (N % kGBN != 0 || K % 256 != 0) return false;  // an even number of K-tiles
+  const int G = fp4_grid();
   if (G < 8) return false;
   const long long per = (fp4_max_tiles(P, N / kGBN) + G - 1) / G + 1;
   return per <= kGMaxTiles && (size_t)(P.E + 1) * 4 <= (size_t)kGStages * kGStage;
 }
 
 hipError_t launch_fp4_gemm(const FfnParams& P, const MfmaBufs& B, bool down, hipStream_t s) {
-  const int G = cu_count_fp4() / 8 * 8;
-  if (down) launch(k_fp4_gemm<kG_Down>, dim3(G), dim3(512), 0, s, P, B);
-  else launch(k_fp4_gemm<kG_GateUp>, dim3(G), dim3(512), 0, s, P, B);
+  const int G = fp4_grid();
+  if (down && B.yb) launch(k_fp4_gemm<kG_Down>, dim3(G), dim3(kGThreads), 0, s, P, B);
+  else if (down) launch(k_fp4_gemm<kG_DownF32>, dim3(G), dim3(kGThreads), 0, s, P, B);
+  else launch(k_fp4_gemm<kG_GateUp>, dim3(G), dim3(kGThreads), 0, s, P, B);
   return hipGetLastError();
 }
 

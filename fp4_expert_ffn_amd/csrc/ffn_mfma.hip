@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "ffn_common.h"
+#include "wave.h"
 
 namespace moe {
 
@@ -53,6 +54,61 @@ __global__ __launch_bounds__(256) void k_quant_mxfp4(const uint16_t* __restrict_
   mxfp4_encode32(v, qq, ss);
   *reinterpret_cast<uint4*>(q + r * (cols / 2) + c * 16) = qq;
   s[r * nb + c] = (uint8_t)ss;
+}
+
+// The inverse of the permutation: inv[perm[p]] = p.
+__global__ __launch_bounds__(256) void k_invert(const int32_t* __restrict__ perm, int n, int32_t* __restrict__ inv) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p < n) inv[perm[p]] = p;
+}
+
+// x -> MXFP4 for the persistent FP4 GEMM, in its A-operand layout: one wave
+// per token, one 32-value block per lane, written to the token's k routed
+// rows (inv) and, with a shared expert, to row T*k + t, K-tile-major:
+// q [cols/128][R][64 B] (block c at byte 16 (c % 4) of K-tile c / 4),
+// s [cols/128][R][4 B] (byte c % 4).  The scale dword of a K-tile is
+// gathered from its four lanes by DPP.
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ x, int T, int cols, int k,
+                                                    const int32_t* __restrict__ inv, int shared, uint32_t rtot,
+                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nb = cols / 32;  // a multiple of 4
+  for (int c0 = 0; c0 < nb; c0 += 64) {
+    const int c = c0 + lane;
+    float v[32];
+    if (c < nb) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * cols + c * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = src[i];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+          v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = 0.f;
+    }
+    uint4 qq;
+    uint32_t ss;
+    mxfp4_encode32(v, qq, ss);
+    // quad_perm broadcasts of lanes 4m + 0..3
+    const uint32_t sd = dpp_u32<0x00>(ss) | (dpp_u32<0x55>(ss) << 8) | (dpp_u32<0xAA>(ss) << 16) |
+                        (dpp_u32<0xFF>(ss) << 24);
+    if (c < nb) {
+      const size_t kt = (size_t)(c >> 2) * rtot;
+      for (int j = 0; j < k + shared; ++j) {
+        const uint32_t row = j < k ? (uint32_t)inv[(size_t)t * k + j] : (uint32_t)(T * k + t);
+        *reinterpret_cast<uint4*>(q + (kt + row) * 64 + (c & 3) * 16) = qq;
+        if ((c & 3) == 0) *reinterpret_cast<uint32_t*>(s + (kt + row) * 4) = sd;
+      }
+    }
+  }
 }
 
 hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st) {
@@ -428,23 +484,34 @@ static MfmaKernel mfma_kernel(int nsteps) {
 bool fp4_gemm_fits(const FfnParams& P, int N, int K, bool gateup);
 hipError_t launch_fp4_gemm(const FfnParams& P, const MfmaBufs& B, bool down, hipStream_t s);
 
-// FP4: x quantised per token row; each projection runs on the persistent
-// 128 x 256 kernel where the shape allows (column count a multiple of 256;
-// gate/up: at least two K-steps), else on the 128 x 128 one.
+// FP4: x quantised per token row; both projections run on the persistent
+// 128 x 256 kernel where the shapes allow (column counts multiples of 256;
+// gate/up: at least two K-tiles), else both on the 128 x 128 one (the two
+// store the SwiGLU output in different layouts).
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s) {
   hipError_t e;
   if (fp4) {
+    if (fp4_gemm_fits(P, 2 * P.I, P.H, true) && fp4_gemm_fits(P, P.H, P.I, false)) {
+      const int n = P.T * P.k;
+      const int32_t* inv = P.inv;
+      if (!inv) {
+        launch(k_invert, dim3((n + 255) / 256), dim3(256), 0, s, P.perm, n, P.inv_ws);
+        inv = P.inv_ws;
+      }
+      const uint32_t rtot = (uint32_t)n + (P.shared_blob ? P.T : 0);
+      launch(k_quant_rows, dim3((P.T + 3) / 4), dim3(256), 0, s, P.x, P.T, P.H, P.k, inv, P.shared_blob ? 1 : 0, rtot,
+             const_cast<uint8_t*>(B.xq), const_cast<uint8_t*>(B.xs));
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      e = launch_fp4_gemm(P, B, false, s);
+      if (e != hipSuccess) return e;
+      return launch_fp4_gemm(P, B, true, s);
+    }
     e = launch_quant_mxfp4(P.x, P.T, P.H, const_cast<uint8_t*>(B.xq), const_cast<uint8_t*>(B.xs), s);
     if (e != hipSuccess) return e;
-    if (fp4_gemm_fits(P, 2 * P.I, P.H, true)) {
-      e = launch_fp4_gemm(P, B, false, s);
-    } else {
-      launch(mfma_kernel<true, kGateUp>((P.H + 255) / 256), dim3(max_tiles(P, (2 * P.I) / kBN)), dim3(256), 0, s, P,
-             B);
-      e = hipGetLastError();
-    }
+    launch(mfma_kernel<true, kGateUp>((P.H + 255) / 256), dim3(max_tiles(P, (2 * P.I) / kBN)), dim3(256), 0, s, P, B);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (fp4_gemm_fits(P, P.H, P.I, false)) return launch_fp4_gemm(P, B, true, s);
     launch(mfma_kernel<true, kDown>((P.I + 255) / 256), dim3(max_tiles(P, P.H / kBN)), dim3(256), 0, s, P, B);
     return hipGetLastError();
   }
