@@ -111,6 +111,83 @@ __global__ __launch_bounds__(256) void k_router_tiled(const uint16_t* __restrict
   }
 }
 
+// Large T, H % 32 == 0: the bf16 matrix cores with the weights split into
+// three bf16 parts (w = hi + lo + lo2 exactly: each part takes the next 8
+// significant bits by truncation), each part's products summed in its own
+// fp32 accumulator, the three sums added at the end.  x is bf16, so every
+// product is exact; the error stays within fp32 summation of H terms per
+// part (plus two final additions).  One wave: 32 tokens x 16 experts, the
+// operands read straight from global memory (x rows and W rows, 64 bytes per
+// 16-lane group per K-step of 32).
+typedef __bf16 rbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float rf32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned ru32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split3(const float4& a, const float4& b, rbf16x8_t& hi, rbf16x8_t& lo,
+                                       rbf16x8_t& lo2) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  ru32x4_t h, l, l2;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t ph = 0, pl = 0, pl2 = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float x0 = v[2 * i + j];
+      const uint32_t u0 = __float_as_uint(x0) & 0xFFFF0000u;          // hi: top 16 bits
+      const float r1 = x0 - __uint_as_float(u0);                        // exact
+      const uint32_t u1 = __float_as_uint(r1) & 0xFFFF0000u;
+      const float r2 = r1 - __uint_as_float(u1);                        // exact, <= 8 significant bits
+      const uint32_t u2 = __float_as_uint(r2) & 0xFFFF0000u;            // == r2
+      ph |= (u0 >> 16) << (16 * j);
+      pl |= (u1 >> 16) << (16 * j);
+      pl2 |= (u2 >> 16) << (16 * j);
+    }
+    h[i] = ph; l[i] = pl; l2[i] = pl2;
+  }
+  hi = __builtin_bit_cast(rbf16x8_t, h);
+  lo = __builtin_bit_cast(rbf16x8_t, l);
+  lo2 = __builtin_bit_cast(rbf16x8_t, l2);
+}
+
+__global__ __launch_bounds__(64) void k_router_mfma(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                                    int T, int H, int E, float* __restrict__ out) {
+  const int lane = threadIdx.x;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 32;
+  const int r = lane & 15, kc = (lane >> 4) * 8;
+  // rows past T or E re-read the last one (results not stored)
+  const uint16_t* xa = x + (size_t)min(t0 + r, T - 1) * H + kc;
+  const uint16_t* xb = x + (size_t)min(t0 + 16 + r, T - 1) * H + kc;
+  const float* wp = w + (size_t)min(e0 + r, E - 1) * H + kc;
+  rf32x4_t acc[2][3];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int p = 0; p < 3; ++p) acc[i][p] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    const rbf16x8_t a0 = __builtin_bit_cast(rbf16x8_t, *reinterpret_cast<const ru32x4_t*>(xa + k0));
+    const rbf16x8_t a1 = __builtin_bit_cast(rbf16x8_t, *reinterpret_cast<const ru32x4_t*>(xb + k0));
+    const float4 w0 = *reinterpret_cast<const float4*>(wp + k0), w1 = *reinterpret_cast<const float4*>(wp + k0 + 4);
+    rbf16x8_t b[3];
+    split3(w0, w1, b[0], b[1], b[2]);
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      acc[0][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b[p], acc[0][p], 0, 0, 0);
+      acc[1][p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b[p], acc[1][p], 0, 0, 0);
+    }
+  }
+  // lane l: expert e0 + l % 16, tokens 4 (l / 16) + v of each 16-token tile
+  const int e = e0 + r;
+  if (e >= E) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = t0 + 16 * i + 4 * (lane >> 4) + v;
+      if (t < T) out[(size_t)t * E + e] = (acc[i][0][v] + acc[i][1][v]) + acc[i][2][v];
+    }
+}
+
 // ------------------------------------------------------------------ top-k + softmax (wave_topk: topk.h)
 
 template <int NPER>
@@ -273,6 +350,8 @@ extern "C" moe_status moe_router_logits(const uint16_t* x, const float* w_router
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T <= kRouterGemvMaxT) {
     hipLaunchKernelGGL(k_router_gemv, dim3(E), dim3(256), 0, s, x, w_router, T, H, E, logits);
+  } else if (H % 32 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)w_router & 15) == 0) {
+    hipLaunchKernelGGL(k_router_mfma, dim3((E + 15) / 16, (T + 31) / 32), dim3(64), 0, s, x, w_router, T, H, E, logits);
   } else {
     hipLaunchKernelGGL(k_router_tiled, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x, w_router, T, H, E,
                        logits);
