@@ -295,7 +295,7 @@ def main():
     bytes_per_launch = tot_bytes / n_calls
     flops_per_launch = tot_flops / n_calls
     kname = {"bf16": "k_gemv (gate/up projection + SwiGLU, bf16 operands)",
-             "mxfp4": "k_mfma_ffn (gate/up projection + SwiGLU, FP4 matrix cores)"}[amode]
+             "mxfp4": "k_fp4_gemm<0> (gate/up projection + SwiGLU, FP4 matrix cores)"}[amode]
     if wl.startswith("prefill-bf16"):
         kname = "k_mfma_ffn (gate/up projection + SwiGLU, bf16 matrix cores)"
     elif fmt == "nvfp4":
@@ -391,10 +391,11 @@ def main():
 
 
 # Kernel-name patterns of the dominant kernel (gate/up projection) per workload.
-DOMINANT = {"decode": "k_gemv<2, false", "large-decode": "k_gemv<1, false", "prefill-mxfp4": "k_mfma_ffn<true, 0",
-            "large-prefill": "k_mfma_ffn<true, 0", "prefill-bf16": "k_mfma_ffn<false, 0"}
+DOMINANT = {"decode": "k_gemv<2, false", "large-decode": "k_gemv<1, false", "prefill-mxfp4": "k_fp4_gemm<0>",
+            "large-prefill": "k_fp4_gemm<0>", "prefill-bf16": "k_mfma_ffn<false, 0"}
 KERNEL_SOURCES = ["fp4_expert_ffn_amd/csrc/ffn_gemv.hip", "fp4_expert_ffn_amd/csrc/ffn_mfma.hip",
-                  "fp4_expert_ffn_amd/csrc/ffn_common.h", "fp4_expert_ffn_amd/csrc/common.h"]
+                  "fp4_expert_ffn_amd/csrc/ffn_fp4gemm.hip", "fp4_expert_ffn_amd/csrc/ffn_common.h",
+                  "fp4_expert_ffn_amd/csrc/common.h"]
 
 
 def _pmc_rows(path, counter):

@@ -122,10 +122,11 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
-// Two E2M1 codes (a in bits 3:0, b in bits 7:4) of values already divided
-// by their block scale: round to nearest even, saturate at +-6.
-__device__ __forceinline__ uint32_t e2m1_pair(float a, float b) {
-  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+// Two E2M1 codes (a in bits 3:0, b in bits 7:4) of a / 2^e and b / 2^e,
+// where 2^e is the normal fp32 `scale` (the conversion uses its exponent
+// alone): round to nearest even, saturate at +-6.
+__device__ __forceinline__ uint32_t e2m1_pair(float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, scale, 0) & 0xFFu;
 }
 
 template <int MODE>
@@ -371,14 +372,18 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
           float amax = 0.f;
 #pragma unroll
           for (int v = 0; v < 8; ++v) amax = fmaxf(amax, fabsf(h[v]));
-          amax = fmaxf(amax, __shfl_xor(amax, 16));
-          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          amax = max_rows4(amax);  // the block's other three lanes (permlane swaps, no LDS)
           int ex = 0;
           if (amax != 0.f) ex = min(127, max(-127, ilog2_f32(amax) - 2));
-          // 2^-ex as an exact fp32 (subnormal 2^-127 for ex = 127)
-          const float inv = ex == 127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(127 - ex) << 23);
-          const uint32_t lo = e2m1_pair(h[0] * inv, h[1] * inv) | (e2m1_pair(h[2] * inv, h[3] * inv) << 8);
-          const uint32_t hi = e2m1_pair(h[4] * inv, h[5] * inv) | (e2m1_pair(h[6] * inv, h[7] * inv) << 8);
+          // the block scale 2^ex as a normal fp32; ex = -127 (every |h| <
+          // 2^-124) divides halved values by 2^-126 instead
+          const float sc = __uint_as_float((uint32_t)(max(ex, -126) + 127) << 23);
+          if (ex == -127) {
+#pragma unroll
+            for (int v = 0; v < 8; ++v) h[v] *= 0.5f;
+          }
+          const uint32_t lo = e2m1_pair(h[0], h[1], sc) | (e2m1_pair(h[2], h[3], sc) << 8);
+          const uint32_t hi = e2m1_pair(h[4], h[5], sc) | (e2m1_pair(h[6], h[7], sc) << 8);
           uint8_t* dst = g_stg + kt * (kGBM * 64) + m * 64 + 32 * half + 16 * bk + 2 * g;
           *reinterpret_cast<uint16_t*>(dst) = (uint16_t)lo;      // columns 4g .. 4g + 3
           *reinterpret_cast<uint16_t*>(dst + 8) = (uint16_t)hi;  // columns 16 + 4g ..

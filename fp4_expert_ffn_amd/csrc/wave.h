@@ -43,6 +43,14 @@ __device__ __forceinline__ float sum_halves(float v) {
 // Sum over the four lanes l, l^16, l^32, l^48 (every lane receives the sum).
 __device__ __forceinline__ float sum_rows4(float v) { return sum_halves(sum_rowpair(v)); }
 
+// Max over the four lanes l, l^16, l^32, l^48 (every lane receives it).
+__device__ __forceinline__ float max_rows4(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Full-wave sum, result in every lane.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f32<kDppQuadXor1>(v);
