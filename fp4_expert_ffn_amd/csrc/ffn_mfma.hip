@@ -493,12 +493,12 @@ hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStrea
   if (fp4) {
     if (fp4_gemm_fits(P, 2 * P.I, P.H, true) && fp4_gemm_fits(P, P.H, P.I, false)) {
       const int n = P.T * P.k;
+      const uint32_t rtot = (uint32_t)n + (P.shared_blob ? P.T : 0);
       const int32_t* inv = P.inv;
       if (!inv) {
         launch(k_invert, dim3((n + 255) / 256), dim3(256), 0, s, P.perm, n, P.inv_ws);
         inv = P.inv_ws;
       }
-      const uint32_t rtot = (uint32_t)n + (P.shared_blob ? P.T : 0);
       launch(k_quant_rows, dim3((P.T + 3) / 4), dim3(256), 0, s, P.x, P.T, P.H, P.k, inv, P.shared_blob ? 1 : 0, rtot,
              const_cast<uint8_t*>(B.xq), const_cast<uint8_t*>(B.xs));
       e = hipGetLastError();

@@ -199,25 +199,27 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 }
 
 // ------------------------------------------------------------------ permutation
-// One workgroup places a chunk of blockDim.x flat indices [c0, c0 + blockDim.x).
-// It histograms all ids (in total and before its chunk) in LDS, scans the
-// totals, and places its chunk: position = offsets[e] + (# of e before the
-// chunk) + (# of e in earlier waves of the chunk) + (rank within the wave).
-// `ids` may point to global memory or to LDS.  LDS: E * (2 + waves) ints.
+// One workgroup places a chunk of blockDim.x flat indices [c0, c0 + blockDim.x):
+// from the histogram of all ids (tot) and of the ids before its chunk
+// (before), it scans the totals and places its chunk: position = offsets[e] +
+// (# of e before the chunk) + (# of e in earlier waves of the chunk) + (rank
+// within the wave).  `ids` may point to global memory or to LDS.  LDS:
+// E * (2 + waves) ints.
 constexpr int kPermChunk = 1024;
 constexpr int kPermWaves = kPermChunk / 64;
 
-__device__ void permute_chunk(const int32_t* ids, int N, int E, int c0, int32_t* sm, int32_t* __restrict__ counts,
-                              int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
-  __shared__ int32_t wsum[kPermWaves];
+// Clears the LDS counters (tot, before, per-wave counts).
+__device__ void permute_clear(int E, int32_t* sm) {
   const int nt = blockDim.x, nw = nt >> 6;
-  int32_t* tot = sm;                   // [E]
-  int32_t* before = sm + E;            // [E]
-  int32_t* wcnt = sm + 2 * E;          // [nw][E]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < E * (2 + nw); i += nt) sm[i] = 0;
+  for (int i = threadIdx.x; i < E * (2 + nw); i += nt) sm[i] = 0;
   __syncthreads();
-  for (int f = tid; f < N; f += nt) {
+}
+
+// tot and before by counting every id (small N: one workgroup does all).
+__device__ void permute_count(const int32_t* ids, int N, int E, int c0, int32_t* sm) {
+  int32_t* tot = sm;
+  int32_t* before = sm + E;
+  for (int f = threadIdx.x; f < N; f += blockDim.x) {
     const int e = ids[f];
     if (e >= 0 && e < E) {
       atomicAdd(&tot[e], 1);
@@ -225,6 +227,18 @@ __device__ void permute_chunk(const int32_t* ids, int N, int E, int c0, int32_t*
     }
   }
   __syncthreads();
+}
+
+// Scan, counts/offsets (chunk 0), and the placement of the chunk (inv too if
+// `inv` is set).  tot and before must be complete.
+__device__ void permute_place(const int32_t* ids, int N, int E, int c0, int32_t* sm, int32_t* __restrict__ counts,
+                              int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int32_t wsum[kPermWaves];
+  const int nt = blockDim.x;
+  int32_t* tot = sm;                   // [E]
+  int32_t* before = sm + E;            // [E]
+  int32_t* wcnt = sm + 2 * E;          // [nw][E]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   {
     // exclusive scan of the totals: thread t owns experts [t*per, t*per + per);
     // a wave scan with shuffles, then the totals of the earlier waves
@@ -284,8 +298,15 @@ __device__ void permute_chunk(const int32_t* ids, int N, int E, int c0, int32_t*
     int pos = before[e] + rank;
     for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
     perm[pos] = f;
-    inv[f] = pos;
+    if (inv) inv[f] = pos;
   }
+}
+
+__device__ void permute_chunk(const int32_t* ids, int N, int E, int c0, int32_t* sm, int32_t* __restrict__ counts,
+                              int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  permute_clear(E, sm);
+  permute_count(ids, N, E, c0, sm);
+  permute_place(ids, N, E, c0, sm, counts, offsets, perm, inv);
 }
 
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ ids, int N, int E,
@@ -293,6 +314,87 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   extern __shared__ int32_t sm[];
   permute_chunk(ids, N, E, blockIdx.x * kPermChunk, sm, counts, offsets, perm, inv);
+}
+
+// Large N, E <= 256: one workgroup per expert compacts the flat indices of
+// that expert in order.  Chunk j of 1024 indices is read coalesced (thread t
+// takes index 1024 j + t); a ballot per (chunk, wave) counts the matches, a
+// workgroup scan of those counts in index order gives each match its
+// position (+ its rank among the wave's matches), and the count of (valid)
+// ids below e is the expert's offset.  Both stores of a (chunk, wave) then go
+// to consecutive positions and consecutive indices.  Every id is read by
+// every workgroup (E * N * 4 bytes, from L2), which is why E is bounded.
+constexpr int kPermExpertMaxE = 256;
+constexpr int kPermExpertMaxChunks = 32;  // N <= 32768: the ids of a thread fit in registers
+
+__global__ __launch_bounds__(1024) void k_perm_expert(const int32_t* __restrict__ ids, int N, int E,
+                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int32_t cnt[kPermExpertMaxChunks * 16];  // [chunk][wave], then its exclusive scan
+  __shared__ int32_t wlt[16], wsum[16];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nj = (N + 1023) >> 10;
+  // every id of this thread's chunks, loaded at once (one memory latency)
+  int v[kPermExpertMaxChunks];
+#pragma unroll
+  for (int j = 0; j < kPermExpertMaxChunks; ++j) {
+    const int f = (j << 10) + tid;
+    v[j] = (j < nj && f < N) ? ids[f] : -1;
+  }
+  int lt = 0;
+#pragma unroll
+  for (int j = 0; j < kPermExpertMaxChunks; ++j) {
+    if (j < nj) {
+      const uint64_t m = __ballot(v[j] == e);
+      if (lane == 0) cnt[j * 16 + wave] = __popcll(m);
+      lt += (v[j] >= 0) & (v[j] < e);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) lt += __shfl_xor(lt, o);
+  if (lane == 0) wlt[wave] = lt;
+  __syncthreads();
+  // exclusive scan of cnt[0 .. 16 nj): thread t owns entries 2t, 2t + 1
+  const int n = nj * 16;
+  const int c0 = 2 * tid < n ? cnt[2 * tid] : 0, c1 = 2 * tid + 1 < n ? cnt[2 * tid + 1] : 0;
+  int inc = c0 + c1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int pre = 0, total = 0, off = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) pre += wsum[w];
+    total += wsum[w];
+    off += wlt[w];
+  }
+  const int ex = pre + inc - c0 - c1;
+  __syncthreads();  // every count read before the scan overwrites them
+  if (2 * tid < n) cnt[2 * tid] = ex;
+  if (2 * tid + 1 < n) cnt[2 * tid + 1] = ex + c0;
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int j = 0; j < kPermExpertMaxChunks; ++j) {
+    if (j < nj) {
+      const uint64_t m = __ballot(v[j] == e);
+      if (v[j] == e) {
+        const int f = (j << 10) + tid;
+        const int pos = off + cnt[j * 16 + wave] + __popcll(m & below);
+        perm[pos] = f;
+        inv[f] = pos;
+      }
+    }
+  }
+  if (tid == 0) {
+    counts[e] = total;
+    offsets[e] = off;
+    if (e == E - 1) offsets[E] = off + total;
+  }
 }
 
 // Routing and permutation of a small batch (T*k <= 1024) in one workgroup of
@@ -387,8 +489,13 @@ extern "C" moe_status moe_permute(const int32_t* topk_ids, int T, int k, int E, 
   const size_t lds = sizeof(int32_t) * (size_t)E * (2 + kPermWaves);
   moe_status st = set_lds_limits();
   if (st != MOE_OK) return st;
-  hipLaunchKernelGGL(k_permute, dim3(blocks), dim3(kPermChunk), lds, reinterpret_cast<hipStream_t>(stream),
-                     topk_ids, (int)N, E, counts, offsets, perm, inv);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (blocks > 1 && E <= kPermExpertMaxE && blocks <= kPermExpertMaxChunks) {
+    hipLaunchKernelGGL(k_perm_expert, dim3(E), dim3(1024), 0, hs, topk_ids, (int)N, E, counts, offsets, perm, inv);
+  } else {
+    hipLaunchKernelGGL(k_permute, dim3(blocks), dim3(kPermChunk), lds, hs, topk_ids, (int)N, E, counts, offsets,
+                       perm, inv);
+  }
   MOE_LAUNCHED();
   return MOE_OK;
 }

@@ -153,7 +153,7 @@ def _permute_gpu(ids, E):
 
 
 @pytest.mark.parametrize("T,k,E", [(16, 2, 8), (1, 8, 128), (4, 8, 128), (16, 8, 128), (37, 8, 128), (129, 8, 1024),
-                                   (300, 1, 1), (2048, 8, 256)])
+                                   (300, 1, 1), (2048, 8, 256), (1100, 8, 512), (350, 3, 3), (1000, 8, 1024)])
 def test_permute_bitexact(T, k, E):
     rng = np.random.default_rng(T + k + E)
     ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
