@@ -9,9 +9,11 @@
 // cores.
 //
 // Design for gfx950:
-//  - One workgroup of 4 waves per CU loops over a contiguous range of output
-//    tiles of 128 rows x 512 columns (XCD x takes the x-th eighth of the tile
-//    list, so an expert's tiles share one L2).  Wave w computes all 128 rows
+//  - One workgroup of 4 waves per CU loops over output tiles of 128 rows x
+//    512 columns.  XCD x takes the x-th eighth of the tile list (an expert's
+//    tiles share one L2) and deals it round-robin to its workgroups, so they
+//    work on neighbouring tiles, which share a weight block, at the same
+//    time.  Wave w computes all 128 rows
 //    x columns 128 w .. 128 w + 127: 8 x 8 MFMA tiles, 256 accumulators (the
 //    AGPRs), so every LDS fragment feeds 8 MFMAs.
 //  - K advances one 128-value K-tile per step.  A step's operands (A 8 KiB,
@@ -143,8 +145,8 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   // A operand and scale bytes between consecutive K-tiles of one row
   const size_t a_kstride = (size_t)rtot * 64, as_kstride = (size_t)rtot * 4;
 
-  // ---- the tile list: experts in id order, each expert's row tiles, each
-  // row tile's column blocks (fastest); the shared expert's tiles last.
+  // ---- the tile list: experts in id order, each expert's column blocks,
+  // each column block's row tiles (fastest); the shared expert's tiles last.
   int* pre = reinterpret_cast<int*>(g_ring);  // [E + 1], in the (still idle) stage area
   const int E = P.E;
   if (tid < 64) {
@@ -170,32 +172,35 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   lds_barrier();
   const int routed = pre[E];
   const int total = routed + (P.shared_blob ? ((P.T + kGBM - 1) / kGBM) * NT : 0);
-  const int G = gridDim.x, b = blockIdx.x;
-  const int r = (b % 8) * (G / 8) + b / 8;  // XCD b % 8 takes the (b % 8)-th eighth of the list
-  const int L0 = (int)((long long)total * r / G), L1 = (int)((long long)total * (r + 1) / G);
-  const int ntile = L1 - L0;  // <= kGMaxTiles (checked by the launcher)
+  // XCD x (workgroups b with b % 8 == x) takes the x-th eighth of the list
+  // and deals it round-robin to its workgroups: at any time they work on
+  // neighbouring tiles, which share an expert's weight block (row tiles are
+  // the fastest index) in that XCD's L2.
+  const int G = gridDim.x, b = blockIdx.x, per_xcd = G / 8, x = b % 8, w = b / 8;
+  const int X0 = (int)((long long)total * x / 8), X1 = (int)((long long)total * (x + 1) / 8);
+  const int ntile = X1 - X0 > w ? (X1 - X0 - w + per_xcd - 1) / per_xcd : 0;  // <= kGMaxTiles (launcher)
   for (int q = tid; q < ntile; q += kGThreads) {
-    const int L = L0 + q;
+    const int L = X0 + w + q * per_xcd;
     TileDesc d;
     if (L >= routed) {
-      const int local = L - routed;
-      const int m0 = (local / NT) * kGBM;
+      const int local = L - routed, nrt = (P.T + kGBM - 1) / kGBM;
+      const int m0 = (local % nrt) * kGBM;
       d.slot = -1;
       d.row0 = P.T * P.k + m0;
       d.rows = min(kGBM, P.T - m0);
-      d.nt = local % NT;
+      d.nt = local / nrt;
     } else {
       int lo = 0, hi = E - 1;  // expert e with pre[e] <= L < pre[e + 1]
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (pre[mid] <= L) lo = mid; else hi = mid - 1;
       }
-      const int local = L - pre[lo];
-      const int m0 = (local / NT) * kGBM;
+      const int local = L - pre[lo], nrt = (P.counts[lo] + kGBM - 1) / kGBM;
+      const int m0 = (local % nrt) * kGBM;
       d.slot = P.slot_of_expert[lo];
       d.row0 = P.offsets[lo] + m0;
       d.rows = min(kGBM, P.counts[lo] - m0);
-      d.nt = local % NT;
+      d.nt = local / nrt;
     }
     desc[q] = d;
   }
@@ -520,7 +525,7 @@ bool fp4_gemm_fits(const FfnParams& P, int N, int K, bool /*gateup*/) {
   if (N % kGBN != 0 || K % 256 != 0) return false;  // an even number of K-tiles
   const int G = fp4_grid();
   if (G < 8) return false;
-  const long long per = (fp4_max_tiles(P, N / kGBN) + G - 1) / G + 1;
+  const long long per = (fp4_max_tiles(P, N / kGBN) + G - 1) / G + 2;
   return per <= kGMaxTiles && (size_t)(P.E + 1) * 4 <= (size_t)kGStages * kGStage;
 }
 
