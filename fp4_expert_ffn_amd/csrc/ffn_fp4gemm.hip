@@ -131,7 +131,12 @@ __device__ __forceinline__ uint32_t e2m1_pair(float a, float b, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, scale, 0) & 0xFFu;
 }
 
-template <int MODE>
+// FP4: MXFP4 weights x MXFP4 activations (K-tiles of 128, scales per 32);
+// otherwise BF16 weights x bf16 activations on v_mfma_f32_16x16x32_bf16
+// (K-tiles of 32; the same 64 bytes per A row and 1 KiB per weight row
+// group per step, no scales; A operands row-major: x token rows gathered
+// through the permutation, h in permutation order).
+template <int MODE, bool FP4>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   __shared__ TileDesc desc[kGMaxTiles];
@@ -139,11 +144,17 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = MODE == kG_GateUp ? P.H : P.I;
   const int NT = (MODE == kG_GateUp ? 2 * P.I : P.H) / kGBN;
-  const int nsteps = K / 128;  // K-tiles per tile (K % 128 == 0 by the blob layout)
-  // rows of the K-tile-major A operands (routed rows, then shared rows)
+  constexpr int kKT = FP4 ? 128 : 32;  // K values per step (one blob K-tile)
+  const int nsteps = K / kKT;          // K % 128 == 0 by the blob layout
+  // rows of the A operands (routed rows, then shared rows)
   const uint32_t rtot = P.T * P.k + (P.shared_blob ? P.T : 0);
-  // A operand and scale bytes between consecutive K-tiles of one row
-  const size_t a_kstride = (size_t)rtot * 64, as_kstride = (size_t)rtot * 4;
+  // A operand and scale bytes between consecutive K-tiles of one row (FP4:
+  // K-tile-major), and between rows (BF16: row-major)
+  const size_t a_kstride = FP4 ? (size_t)rtot * 64 : 64, as_kstride = (size_t)rtot * 4;
+  const uint32_t a_rowbytes = FP4 ? 64u : (uint32_t)K * 2;
+  // constant loads per step and wave (the vmcnt bookkeeping): waves 0-1 also
+  // load the A scales
+  constexpr int kLoadsHi = FP4 ? 13 : 10, kLoadsLo = FP4 ? 12 : 10;
 
   // ---- the tile list: experts in id order, each expert's column blocks,
   // each column block's row tiles (fastest); the shared expert's tiles last.
@@ -208,7 +219,9 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   if (ntile == 0) return;
   const int nsteps_total = ntile * nsteps;
 
-  const uint8_t* abase = MODE == kG_GateUp ? B.xq : B.hq;
+  const uint8_t* abase = FP4 ? (MODE == kG_GateUp ? B.xq : B.hq)
+                             : (MODE == kG_GateUp ? reinterpret_cast<const uint8_t*>(P.x)
+                                                  : reinterpret_cast<const uint8_t*>(B.hb));
   const uint8_t* asbase = MODE == kG_GateUp ? B.xs : B.hs;
   static_assert(MODE == kG_GateUp || MODE == kG_Down || MODE == kG_DownF32, "mode");
   const size_t off_w = MODE == kG_GateUp ? P.L.off_w13 : P.L.off_w2;
@@ -240,8 +253,15 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   const uint8_t* wst = nullptr;  // its scale tiles
   int iss_ks = 0;
   uint32_t iss_st = 0;
+  // the A row of row rr of a tile (rows past the tile re-read its last row):
+  // its permutation-order row, or for BF16 gate/up the token of that row
   auto a_row = [&](const TileDesc& d, int rr) __attribute__((always_inline)) -> uint32_t {
-    return d.row0 + min(rr, d.rows - 1);  // rows past the tile re-read its last row
+    const uint32_t r = d.row0 + min(rr, d.rows - 1);
+    if constexpr (!FP4 && MODE == kG_GateUp) {
+      if (r >= (uint32_t)(P.T * P.k)) return r - P.T * P.k;  // the shared expert: token rows
+      return (uint32_t)P.perm[r] / (uint32_t)P.k;
+    }
+    return r;
   };
   auto issue_begin = [&](int s, const uint8_t* stp) __attribute__((always_inline)) {
     iss_st = lds_off(stp);
@@ -250,8 +270,8 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
     if (iss_ks == 0) {
       const TileDesc d = uniform_desc(q);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) a_off[u] = a_row(d, 16 * (2 * wave + u) + (lane >> 2)) * 64 + aseg * 16;
-      if (wave < 2) as_off = a_row(d, 64 * wave + lane) * 4;
+      for (int u = 0; u < 2; ++u) a_off[u] = a_row(d, 16 * (2 * wave + u) + (lane >> 2)) * a_rowbytes + aseg * 16;
+      if (FP4 && wave < 2) as_off = a_row(d, 64 * wave + lane) * 4;
       const uint8_t* blob = d.slot < 0 ? P.shared_blob : P.slot_pool + (size_t)d.slot * P.slot_stride;
       const uint32_t g0 = (uint32_t)(d.nt * 32 + 8 * wave);
       wt = blob + off_w + (size_t)g0 * wstride;
@@ -261,13 +281,13 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   auto issue_slot = [&](auto jc) __attribute__((always_inline)) {
     constexpr int J = decltype(jc)::value;
     if constexpr (J == 0) {
-      if (wave < 2) dma4(asbase + as_off + iss_ks * as_kstride, iss_st + kGA + kGB + wave * 256);
+      if (FP4 && wave < 2) dma4(asbase + as_off + iss_ks * as_kstride, iss_st + kGA + kGB + wave * 256);
     } else if constexpr (J < 3) {
       dma16(abase + a_off[J - 1] + iss_ks * a_kstride, iss_st + (2 * wave + J - 1) * 1024);
     } else if constexpr (J < 11) {
       dma16(wt + (size_t)(J - 3) * wstride + (size_t)iss_ks * kTileBytes + lane * 16,
             iss_st + kGA + (8 * wave + J - 3) * 1024);
-    } else {
+    } else if constexpr (FP4) {
       constexpr int h = J - 11;
       dma4(wst + ((size_t)(4 * h + (lane >> 4)) * nsteps + iss_ks) * 64 + (lane & 15) * 4,
            iss_st + kGA + kGB + kGSA + (2 * wave + h) * 256);
@@ -311,9 +331,11 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   auto read_frag = [&](const uint8_t* st, int u, u32x4_t* fa, u32x4_t* fb, int* sa, int* sb)
       __attribute__((always_inline)) {
     fa[u] = *reinterpret_cast<const u32x4_t*>(st + a_rd + u * 1024);
-    sa[u] = st[sa_rd + u * 64];
     fb[u] = *reinterpret_cast<const u32x4_t*>(st + b_rd + u * 1024);
-    sb[u] = st[sb_rd + u * 64];
+    if constexpr (FP4) {
+      sa[u] = st[sa_rd + u * 64];
+      sb[u] = st[sb_rd + u * 64];
+    }
   };
 
   // Epilogue of tile q (reads the accumulators).
@@ -353,6 +375,37 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
           const size_t o = (size_t)(d.row0 + m) * P.H + d.nt * kGBN + 128 * wave + 4 * g;
 #pragma unroll
           for (int j = 0; j < 8; ++j) *reinterpret_cast<f32x4_t*>(B.y + o + 16 * j) = acc[i][j];
+        }
+      }
+    } else if constexpr (!FP4) {
+      // BF16: h = bf16(silu(gate) * up) for SwiGLU columns d.nt * 256 + 64 wave
+      // + 16 p + 4 g + v (MFMA tiles j = 2p gate, 2p + 1 up), row-major
+      // [R][I]: per 16-row block through the wave's own 2 KiB of staging,
+      // then stores of 8 rows x 128 contiguous bytes
+      uint8_t* ws = g_stg + wave * 4096;
+      const int cb = d.nt * 256 + 64 * wave;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          uint32_t w2[2];
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            const float h0 = silu_fast(acc[i][2 * p][2 * v]) * acc[i][2 * p + 1][2 * v];
+            const float h1 = silu_fast(acc[i][2 * p][2 * v + 1]) * acc[i][2 * p + 1][2 * v + 1];
+            w2[v] = f32_to_bf16_rne(h0) | ((uint32_t)f32_to_bf16_rne(h1) << 16);
+          }
+          // row t16, 16-byte granule 2p + g / 2 of the row's 128 bytes, XOR-swizzled by row
+          const int gr = 2 * p + (g >> 1);
+          *reinterpret_cast<uint2*>(ws + t16 * 128 + (((gr ^ t16) & 7) << 4) + (g & 1) * 8) = make_uint2(w2[0], w2[1]);
+        }
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const int rr = 8 * pr + (lane >> 3), gr = lane & 7;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ws + rr * 128 + (((gr ^ rr) & 7) << 4));
+          const int m = 16 * i + rr;
+          if (m < d.rows)
+            *reinterpret_cast<u32x4_t*>(B.hb + (size_t)(d.row0 + m) * P.I + cb + gr * 8) = v;
         }
       }
     } else {
@@ -423,8 +476,8 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   issue_all(0, g_ring);
   issue_all(min(1, last), g_ring + kGStage);
   issue_all(min(2, last), g_ring + 2 * kGStage);
-  if (wave < 2) wait_vm<2 * 13>();
-  else wait_vm<2 * 12>();
+  if (wave < 2) wait_vm<2 * kLoadsHi>();
+  else wait_vm<2 * kLoadsLo>();
   lds_sync();
 #pragma unroll
   for (int u = 0; u < 8; ++u) read_frag(g_ring, u, fa0, fb0, sa0, sb0);
@@ -434,8 +487,8 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
                   int* nsb) __attribute__((always_inline)) {
     constexpr bool first = decltype(zc)::value;     // a tile's first K-tile
     constexpr bool prefetch = decltype(pc)::value;  // read the next step's fragments
-    if (wave < 2) wait_vm<13>();
-    else wait_vm<12>();
+    if (wave < 2) wait_vm<kLoadsHi>();
+    else wait_vm<kLoadsLo>();
     lds_sync();
     const int nxt = cur == kGStages - 1 ? 0 : cur + 1;
     const uint8_t* stn = g_ring + nxt * kGStage;
@@ -444,11 +497,17 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
     auto group = [&](auto jc) __attribute__((always_inline)) {
       constexpr int j = decltype(jc)::value;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            i32x8_t{(int)fb[j].x, (int)fb[j].y, (int)fb[j].z, (int)fb[j].w, 0, 0, 0, 0},
-            i32x8_t{(int)fa[i].x, (int)fa[i].y, (int)fa[i].z, (int)fa[i].w, 0, 0, 0, 0},
-            first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[i][j], 4, 4, 0, sb[j], 0, sa[i]);
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (FP4)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              i32x8_t{(int)fb[j].x, (int)fb[j].y, (int)fb[j].z, (int)fb[j].w, 0, 0, 0, 0},
+              i32x8_t{(int)fa[i].x, (int)fa[i].y, (int)fa[i].z, (int)fa[i].w, 0, 0, 0, 0},
+              first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[i][j], 4, 4, 0, sb[j], 0, sa[i]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, fb[j]),
+                                                               __builtin_bit_cast(bf16x8_t, fa[i]),
+                                                               first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[i][j], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (prefetch) read_frag(stn, j, na, nb, nsa, nsb);
       if constexpr (j < 4) {
@@ -529,11 +588,29 @@ bool fp4_gemm_fits(const FfnParams& P, int N, int K, bool /*gateup*/) {
   return per <= kGMaxTiles && (size_t)(P.E + 1) * 4 <= (size_t)kGStages * kGStage;
 }
 
+// The same for BF16 weights (K-tiles of 32: K % 64 == 0 keeps their count even).
+bool bf16_gemm_fits(const FfnParams& P, int N, int K) {
+  if (N % kGBN != 0 || K % 64 != 0) return false;
+  const int G = fp4_grid();
+  if (G < 8) return false;
+  const long long per = (fp4_max_tiles(P, N / kGBN) + G - 1) / G + 2;
+  return per <= kGMaxTiles && (size_t)(P.E + 1) * 4 <= (size_t)kGStages * kGStage;
+}
+
 hipError_t launch_fp4_gemm(const FfnParams& P, const MfmaBufs& B, bool down, hipStream_t s) {
   const int G = fp4_grid();
-  if (down && B.yb) launch(k_fp4_gemm<kG_Down>, dim3(G), dim3(kGThreads), 0, s, P, B);
-  else if (down) launch(k_fp4_gemm<kG_DownF32>, dim3(G), dim3(kGThreads), 0, s, P, B);
-  else launch(k_fp4_gemm<kG_GateUp>, dim3(G), dim3(kGThreads), 0, s, P, B);
+  if (down && B.yb) launch(k_fp4_gemm<kG_Down, true>, dim3(G), dim3(kGThreads), 0, s, P, B);
+  else if (down) launch(k_fp4_gemm<kG_DownF32, true>, dim3(G), dim3(kGThreads), 0, s, P, B);
+  else launch(k_fp4_gemm<kG_GateUp, true>, dim3(G), dim3(kGThreads), 0, s, P, B);
+  return hipGetLastError();
+}
+
+// The BF16-weight projections on the same persistent kernel.
+hipError_t launch_bf16_gemm(const FfnParams& P, const MfmaBufs& B, bool down, hipStream_t s) {
+  const int G = fp4_grid();
+  if (down && B.yb) launch(k_fp4_gemm<kG_Down, false>, dim3(G), dim3(kGThreads), 0, s, P, B);
+  else if (down) launch(k_fp4_gemm<kG_DownF32, false>, dim3(G), dim3(kGThreads), 0, s, P, B);
+  else launch(k_fp4_gemm<kG_GateUp, false>, dim3(G), dim3(kGThreads), 0, s, P, B);
   return hipGetLastError();
 }
 

@@ -483,11 +483,14 @@ static MfmaKernel mfma_kernel(int nsteps) {
 
 bool fp4_gemm_fits(const FfnParams& P, int N, int K, bool gateup);
 hipError_t launch_fp4_gemm(const FfnParams& P, const MfmaBufs& B, bool down, hipStream_t s);
+bool bf16_gemm_fits(const FfnParams& P, int N, int K);
+hipError_t launch_bf16_gemm(const FfnParams& P, const MfmaBufs& B, bool down, hipStream_t s);
 
-// FP4: x quantised per token row; both projections run on the persistent
-// 128 x 256 kernel where the shapes allow (column counts multiples of 256;
-// gate/up: at least two K-tiles), else both on the 128 x 128 one (the two
-// store the SwiGLU output in different layouts).
+// Both projections run on the persistent 128 x 512 kernel where the shapes
+// allow (column counts multiples of 512; FP4: K a multiple of 256), else both
+// on the 128 x 128 one (on the FP4 path the two store x and the SwiGLU output
+// in different layouts).  FP4: x MXFP4-encoded first (per token, into its
+// destination rows for the persistent kernel).
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s) {
   hipError_t e;
   if (fp4) {
@@ -514,6 +517,11 @@ hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStrea
     if (e != hipSuccess) return e;
     launch(mfma_kernel<true, kDown>((P.I + 255) / 256), dim3(max_tiles(P, P.H / kBN)), dim3(256), 0, s, P, B);
     return hipGetLastError();
+  }
+  if (bf16_gemm_fits(P, 2 * P.I, P.H) && bf16_gemm_fits(P, P.H, P.I)) {
+    e = launch_bf16_gemm(P, B, false, s);
+    if (e != hipSuccess) return e;
+    return launch_bf16_gemm(P, B, true, s);
   }
   const int nt_gu = (2 * P.I) / kBN, nt_dn = P.H / kBN;
   launch(mfma_kernel<false, kGateUp>(P.H / 64), dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
