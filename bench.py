@@ -303,9 +303,9 @@ def main():
     bytes_per_launch = tot_bytes / n_calls
     flops_per_launch = tot_flops / n_calls
     kname = {"bf16": "k_gemv (gate/up projection + SwiGLU, bf16 operands)",
-             "mxfp4": "k_fp4_gemm<0> (gate/up projection + SwiGLU, FP4 matrix cores)"}[amode]
+             "mxfp4": "k_fp4_gemm<0, true> (gate/up projection + SwiGLU, FP4 matrix cores)"}[amode]
     if wl.startswith("prefill-bf16"):
-        kname = "k_mfma_ffn (gate/up projection + SwiGLU, bf16 matrix cores)"
+        kname = "k_fp4_gemm<0, false> (gate/up projection + SwiGLU, bf16 weights on bf16 matrix cores)"
     elif fmt == "nvfp4":
         kname = "k_gemv (gate/up projection + SwiGLU, NVFP4 weights on fp16 matrix cores)"
     # The large-expert prefill sits below the FP4 ridge (about 267 FLOP/B): HBM bounds it.
@@ -399,8 +399,8 @@ def main():
 
 
 # Kernel-name patterns of the dominant kernel (gate/up projection) per workload.
-DOMINANT = {"decode": "k_gemv<2, false", "large-decode": "k_gemv<1, false", "prefill-mxfp4": "k_fp4_gemm<0>",
-            "large-prefill": "k_fp4_gemm<0>", "prefill-bf16": "k_mfma_ffn<false, 0"}
+DOMINANT = {"decode": "k_gemv<2, false", "large-decode": "k_gemv<1, false", "prefill-mxfp4": "k_fp4_gemm<0, true>",
+            "large-prefill": "k_fp4_gemm<0, true>", "prefill-bf16": "k_fp4_gemm<0, false>"}
 KERNEL_SOURCES = ["fp4_expert_ffn_amd/csrc/ffn_gemv.hip", "fp4_expert_ffn_amd/csrc/ffn_mfma.hip",
                   "fp4_expert_ffn_amd/csrc/ffn_fp4gemm.hip", "fp4_expert_ffn_amd/csrc/ffn_common.h",
                   "fp4_expert_ffn_amd/csrc/common.h"]
