@@ -149,6 +149,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// SwiGLU gate factor z * sigmoid(z) from the hardware exp2 and reciprocal
+// (each within 1 ulp); -inf -> -0, +inf -> +inf.
+__device__ __forceinline__ float silu_fast(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
+
 // E4M3FN code -> float (positive scales only are produced; sign kept for generality).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t e = (c >> 3) & 15u, m = c & 7u;

@@ -118,12 +118,6 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
-// SwiGLU gate factor z * sigmoid(z) from the hardware exp2 and reciprocal
-// (each within 1 ulp); -inf -> -0, +inf -> +inf.
-__device__ __forceinline__ float silu_fast(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
-}
-
 // Two E2M1 codes (a in bits 3:0, b in bits 7:4) of a / 2^e and b / 2^e,
 // where 2^e is the normal fp32 `scale` (the conversion uses its exponent
 // alone): round to nearest even, saturate at +-6.

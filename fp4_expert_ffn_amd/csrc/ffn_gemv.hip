@@ -257,40 +257,58 @@ __device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4 v) {
   return max(m, max(max(v.z & 0x7FFFu, v.z >> 16 & 0x7FFFu), max(v.w & 0x7FFFu, v.w >> 16 & 0x7FFFu)));
 }
 
+// bf16 values of one 16-byte piece (8 values) as fp16 times 2^-p (p >= 0):
+// the power of two is applied exactly in fp32, then one rounding to fp16.
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4 v, float sc) {
+  auto cv = [&](uint32_t w) -> uint32_t {
+    const f32x2_t f = {__uint_as_float(w << 16) * sc, __uint_as_float(w & 0xFFFF0000u) * sc};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2_t));
+  };
+  return make_uint4(cv(v.x), cv(v.y), cv(v.z), cv(v.w));
+}
+
 // After every wave's rows have landed (and a barrier): for the fp16 operand
-// path the rows are rewritten in place as fp16 of value * 2^-pexp[r], with
-// pexp[r] >= 0 the smallest shift that keeps the row's largest magnitude
-// below 2^15 (inside fp16's range; the output rows are multiplied back by
-// 2^pexp[r]).  bf16 -> fp16 is then exact for every value of magnitude
-// >= 2^-14 * 2^pexp[r]; smaller ones round at 2^-24 * 2^pexp[r], far below
-// the row's largest product.  The piece order does not matter here.  For
-// fp16, ends with a barrier; bf16 rows need nothing more.
-template <bool F16>
-__device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pexp) {
+// path the rows are rewritten in place as fp16 of value * 2^-pexp[r].  A row
+// whose values are all below 2^16 in magnitude is finite in fp16 as it is:
+// pexp[r] = 0, one pass.  A row holding a larger value (or inf / NaN), which
+// the pass marks in *big, is converted again from its global copy src(r)
+// with pexp[r] >= 0 the smallest shift that keeps its largest magnitude below
+// 2^15 (the output rows are multiplied back by 2^pexp[r]).  bf16 -> fp16 is
+// exact for every value of magnitude >= 2^-14 * 2^pexp[r]; smaller ones
+// round at 2^-24 * 2^pexp[r], far below the row's largest product.  The
+// piece order does not matter for the pass.  For fp16, ends with a barrier;
+// bf16 rows need nothing more.  *big is zero on entry and on return.
+template <bool F16, class Src>
+__device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pexp, int* big, Src src) {
   if constexpr (F16) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ppr = K / 8, total = nr * ppr;
-    const uint4* pc = reinterpret_cast<const uint4*>(act);
-    // each row's largest |value| bits (|bf16| bit patterns order like the
-    // magnitudes): wave w reduces rows w, w + 4, ...
-    for (int r = wave; r < nr; r += 4) {
-      uint32_t mx = 0;
-      for (int p = lane; p < ppr; p += 64) mx = max(mx, bf16x8_absmax_bits(pc[r * ppr + p]));
-      mx = wave_max_u32(mx);
-      const int E = (int)(mx >> 7);  // biased exponent of the row's largest |value|: it is < 2^(E-126)
-      if (lane == 0) pexp[r] = (E == 0xFF) ? 0 : max(0, E - 141);
-    }
-    lds_barrier();
+    if (tid < nr) pexp[tid] = 0;
     for (int p = tid; p < total; p += 256) {
       uint4* q = reinterpret_cast<uint4*>(act) + p;
       const uint4 v = *q;
-      const float sc = __uint_as_float((uint32_t)(127 - pexp[p / ppr]) << 23);
-      auto cv = [&](uint32_t w) -> uint32_t {
-        const f16x2_t h = {(_Float16)(bf16_to_f32((uint16_t)w) * sc), (_Float16)(bf16_to_f32((uint16_t)(w >> 16)) * sc)};
-        return __builtin_bit_cast(uint32_t, h);
-      };
-      *q = make_uint4(cv(v.x), cv(v.y), cv(v.z), cv(v.w));
+      if (bf16x8_absmax_bits(v) >= 0x4780u) atomicOr(big, 1 << (p / ppr));  // |value| >= 2^16, inf or NaN
+      *q = bf16x8_to_f16x8(v, 1.0f);
     }
     lds_barrier();
+    const int bm = *big;
+    if (bm != 0) {
+      const int swz = row_swz(ppr);
+      for (int r = wave; r < nr; r += 4) {
+        if (!((bm >> r) & 1)) continue;
+        const uint4* g = reinterpret_cast<const uint4*>(src(r));
+        uint32_t mx = 0;
+        for (int j = lane; j < ppr; j += 64) mx = max(mx, bf16x8_absmax_bits(g[j]));
+        mx = wave_max_u32(mx);
+        const int E = (int)(mx >> 7);  // biased exponent of the row's largest |value|: it is < 2^(E-126)
+        const int pe = (E == 0xFF) ? 0 : max(0, E - 141);
+        if (lane == 0) pexp[r] = pe;
+        const float sc = __uint_as_float((uint32_t)(127 - pe) << 23);
+        uint4* row = reinterpret_cast<uint4*>(act) + (size_t)r * ppr;
+        for (int j = lane; j < ppr; j += 64) row[j ^ (r & swz)] = bf16x8_to_f16x8(g[j], sc);
+      }
+      lds_barrier();
+      if (tid == 0) *big = 0;
+    }
   }
 }
 
@@ -323,26 +341,36 @@ constexpr int kTrashSlots = 256;         // 4 KiB scratch slots (workgroup index
 //   DOWN = true: down projection.  Item (row block, c) covers output columns
 //     [64c, 64c + 64): wave w streams row group 4c + w of W2 and writes its 16
 //     columns of y (fp32).
-// Work is split into tasks of one row block and a contiguous range of cpt
-// items (the smallest range that gives at most one task per workgroup), so a
-// workgroup stages its operand rows once: each row is read by the few
-// workgroups of its expert, not by all of them.  Each wave runs all K-tiles
-// of its row group itself (no cross-wave reduction), in sub-items of SUB
-// K-tiles (SUB divides K / KT).
+// The items (row block major) are dealt to the workgroups in contiguous,
+// equal ranges, so every workgroup (and every CU) streams the same number of
+// weight tiles, give or take one item.  A range splits into tasks at row
+// block boundaries; a task stages its operand rows once, so each row is read
+// by the few workgroups of its expert, not by all of them.  With XALL (the
+// gate/up projection of at most kXallMaxT tokens) every token row of x is
+// staged once, in token order, by the first task, and later tasks stage
+// nothing.  Each wave runs all K-tiles of its row group itself (no
+// cross-wave reduction), in sub-items of SUB K-tiles (SUB divides K / KT).
 //
 // Memory pipeline: two register banks of weight tiles (plus the item's
 // per-tensor multiplier) alternate, and the loop is unrolled by two so each
 // bank keeps fixed registers: the loads of sub-item ss + 1 are in flight
 // while sub-item ss computes.  The operand rows are loaded before the first
-// weights and written to LDS while those are in flight.
-template <int FMT, bool DOWN, int SUB>
+// weights and written to LDS while those are in flight.  Inside a sub-item
+// the operand fragments of the next K-tile are read from LDS while the
+// current one's matrix instructions run.
+constexpr int kXallMaxT = 4;
+
+template <int FMT, bool DOWN, int SUB, bool XALL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemv(FfnParams P, GemvArgs G) {
   using F = Fmt<FMT>;
+  static_assert(!(XALL && DOWN), "the down projection stages its rows per task");
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_pexp[16];
   __shared__ float s_u[2][16][17];
   __shared__ int s_rows[16];
+  __shared__ int s_big;  // rows of the staged block that overflow fp16 (finish_rows)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 15, grp = lane >> 4;
+  if (tid == 0) s_big = 0;  // visible after the table's barrier
   const int H = P.H, I = P.I;
   const int K = DOWN ? I : H, nk = K / F::KT;
   const int rbs = DOWN ? G.rbs2 : G.rbs1, nchunk = DOWN ? G.nd : G.ng;
@@ -350,14 +378,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint8_t* act = lds + G.act_off;  // operand rows (swizzled) + slack
   build_active(P, rbs, A);
   const int nrb = A.rb[*A.n];
-  const int grid = gridDim.x;
-  // items per task: at least items / grid, and few enough tasks for the grid
-  // (if even whole row blocks outnumber the workgroups, they loop over tasks)
-  int cpt = (nrb * nchunk + grid - 1) / grid;
-  while (cpt < nchunk && (long long)nrb * ((nchunk + cpt - 1) / cpt) > grid) ++cpt;
-  cpt = max(1, min(cpt, nchunk));
-  const int tpr = (nchunk + cpt - 1) / cpt;  // tasks per row block
-  const int ntasks = nrb * tpr;
+  // this workgroup's items: [i_beg, i_end) of nrb * nchunk, row block major
+  const long long nitems = (long long)nrb * nchunk;
+  const long long i_beg = nitems * blockIdx.x / gridDim.x, i_end = nitems * (blockIdx.x + 1) / gridDim.x;
   const int nsub = nk / SUB;  // SUB divides nk: every sub-item loads exactly SUB tiles
   const size_t off_w = DOWN ? P.L.off_w2 : P.L.off_w13, off_s = DOWN ? P.L.off_s2 : P.L.off_s13;
   // per-tensor multiplier of this wave's rows: gate (even waves) / up (odd) / down
@@ -365,6 +388,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* rbase = DOWN ? G.h : P.x;
   // this workgroup's own 4 KiB of scratch (distinct lines: no store contention)
   float* trash = G.trash + (size_t)(blockIdx.x % kTrashSlots) * 1024;
+  const int ppr = K / 8, swz = row_swz(ppr);
 
   struct Bank {
     uint4 q[SUB];
@@ -375,10 +399,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // formats; 64 or 128 bytes apart, never merged) and the multiplier.
   constexpr int kBankLoads = SUB + (FMT == MOE_FMT_BF16 ? 0 : SUB) + 1;
 
+  // XALL: every token row of x, in token order, before the first task (whose
+  // first weights then go out behind them)
+  if (XALL && i_beg < i_end) dma_rows(act, P.x, K, P.T, [](int r) { return r; });
+  bool first = true;
 #pragma unroll 1
-  for (int task = blockIdx.x; task < ntasks; task += grid) {
-    const int rbi = task / tpr;
-    const int c0 = (task % tpr) * cpt, c1 = min(nchunk, c0 + cpt);
+  for (long long it = i_beg; it < i_end;) {
+    const int rbi = (int)(it / nchunk);
+    const int c0 = (int)(it % nchunk), c1 = (int)std::min<long long>(nchunk, c0 + (i_end - it));
+    it += c1 - c0;
     const RowBlock blk = row_block(P, A, rbs, rbi);
     const int nS = (c1 - c0) * nsub;
     const uint8_t* wbase = blk.blob + off_w;
@@ -403,24 +432,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int j = 0; j < SUB; ++j) b.q[j] = ldg16(wp + j * kTileBytes);
     };
 
-    // operand rows of the block (token rows of x, or rows of h), loaded ahead
-    // of the first weights; the table's barrier also ends the previous task
-    lds_barrier();
-    if (tid < blk.nr) s_rows[tid] = DOWN ? blk.p0 + blk.r0 + tid : row_token(P, A, blk, tid);
-    lds_barrier();
     Bank b0, b1;
-    dma_rows(act, rbase, K, blk.nr, [&](int r) { return s_rows[r]; });
+    if constexpr (!XALL) {
+      // operand rows of the block (token rows of x, or rows of h), loaded
+      // ahead of the first weights; the table's barrier also ends the
+      // previous task
+      lds_barrier();
+      if (tid < blk.nr) s_rows[tid] = DOWN ? blk.p0 + blk.r0 + tid : row_token(P, A, blk, tid);
+      lds_barrier();
+      dma_rows(act, rbase, K, blk.nr, [&](int r) { return s_rows[r]; });
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     issue(0, b0);  // behind the rows: waiting for the rows leaves all of its loads in flight
     __builtin_amdgcn_sched_barrier(0);
-    rows_landed<kBankLoads>();
-    finish_rows<F::F16>(act, K, blk.nr, s_pexp);
+    if (!XALL || first) {
+      rows_landed<kBankLoads>();
+      finish_rows<F::F16>(act, K, XALL ? P.T : blk.nr, s_pexp, &s_big,
+                          [&](int r) { return rbase + (size_t)(XALL ? r : s_rows[r]) * K; });
+    }
+    first = false;
 
+    // this lane's A row: row m of the block (rows past the block read its
+    // last row; their outputs are discarded), as an LDS row index
+    const int am = min(m, blk.nr - 1);
+    const int arow_i = XALL ? row_token(P, A, blk, am) : am;
+    const uint8_t* arow = act + (size_t)arow_i * ppr * 16;
+    const int aswz = arow_i & swz;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    // this lane's A row (row m of the block) and its swizzled piece offsets
-    const int ppr = K / 8, swz = row_swz(ppr);
-    const uint8_t* arow = m < blk.nr ? act + (size_t)m * ppr * 16 : nullptr;
     // The epilogue runs after every sub-item (uniform code: no branch around
     // memory operations inside the pipelined loop); before an item's last
     // sub-item its stores go to a scratch area, as do rows past the block and
@@ -429,34 +468,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int chunk = c0 + ss / nsub, sub = ss % nsub;
       const bool last = sub == nsub - 1;
       if (sub == 0) acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // Operand fragment of MFMA step u of the sub-item (K-tile u / SPT),
+      // read from LDS two steps ahead of its use (a ring of three).
+      constexpr int NU = SUB * F::SPT;
+      auto read_a = [&](int u) {
+        const int kt = sub * SUB + u / F::SPT, st = u % F::SPT;
+        const int piece = (kt * F::KT + (F::SPT == 4 ? 32 * grp + 8 * st : 8 * grp)) / 8;
+        return *reinterpret_cast<const uint4*>(arow + ((piece ^ aswz) << 4));
+      };
+      uint4 ar[3];
+      ar[0] = read_a(0);
+      if (NU > 1) ar[1] = read_a(1);
 #pragma unroll
-      for (int j = 0; j < SUB; ++j) {
-        const int kt = sub * SUB + j;
-#pragma unroll
-        for (int st = 0; st < F::SPT; ++st) {
-          const int piece = (kt * F::KT + (F::SPT == 4 ? 32 * grp + 8 * st : 8 * grp)) / 8;
-          const uint4 av = arow ? *reinterpret_cast<const uint4*>(arow + ((piece ^ (m & swz)) << 4)) : make_uint4(0, 0, 0, 0);
-          typename F::V bv;
-          if constexpr (F::SPT == 4) {
-            bv = st == 0 ? bfrag<FMT, 0>(b.q[j], b.sc[j]) : st == 1 ? bfrag<FMT, 1>(b.q[j], b.sc[j])
-               : st == 2 ? bfrag<FMT, 2>(b.q[j], b.sc[j]) : bfrag<FMT, 3>(b.q[j], b.sc[j]);
-          } else {
-            bv = bfrag<FMT, 0>(b.q[j], b.sc[j]);
-          }
-          acc = mma<FMT>(__builtin_bit_cast(typename F::V, av), bv, acc);
+      for (int u = 0; u < NU; ++u) {
+        if (u + 2 < NU) ar[(u + 2) % 3] = read_a(u + 2);
+        const int j = u / F::SPT, st = u % F::SPT;
+        typename F::V bv;
+        if constexpr (F::SPT == 4) {
+          bv = st == 0 ? bfrag<FMT, 0>(b.q[j], b.sc[j]) : st == 1 ? bfrag<FMT, 1>(b.q[j], b.sc[j])
+             : st == 2 ? bfrag<FMT, 2>(b.q[j], b.sc[j]) : bfrag<FMT, 3>(b.q[j], b.sc[j]);
+        } else {
+          bv = bfrag<FMT, 0>(b.q[j], b.sc[j]);
+        }
+        acc = mma<FMT>(__builtin_bit_cast(typename F::V, ar[u % 3]), bv, acc);
+        if (st == F::SPT - 1) {
+          // one K-tile at a time (the compiler would otherwise hoist the
+          // decode and the LDS reads of the whole sub-item)
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // Lane: rows 4 (lane / 16) + v of the block, column lane % 16 of this
       // wave's 16 output rows of the weight.
-      float val[4];
+      auto scaled = [&](float (&val)[4]) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = 4 * grp + v;
-        float sc2 = b.g;
-        if constexpr (F::F16) sc2 *= pow2i(s_pexp[r < blk.nr ? r : 0]);
-        val[v] = acc[v] * sc2;
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int r = 4 * grp + v;
+          float sc2 = b.g;
+          if constexpr (F::F16) {
+            const int rr = min(r, blk.nr - 1);
+            sc2 *= pow2i(s_pexp[XALL ? row_token(P, A, blk, rr) : rr]);
+          }
+          val[v] = acc[v] * sc2;
+        }
+      };
       if constexpr (DOWN) {
+        float val[4];
+        scaled(val);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int r = 4 * grp + v;
@@ -465,20 +523,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           *dst = val[v];
         }
       } else {
-        if (wave & 1)
+        // SwiGLU on an item's last sub-item only (a workgroup-uniform
+        // branch); the stores are issued on every sub-item all the same, to
+        // the scratch area before the last one.
+        float hv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (last) {
+          float val[4];
+          scaled(val);
+          if (wave & 1)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) s_u[wave >> 1][4 * grp + v][m] = val[v];
-        lds_barrier();
+            for (int v = 0; v < 4; ++v) s_u[wave >> 1][4 * grp + v][m] = val[v];
+          lds_barrier();
+#pragma unroll
+          for (int v = 0; v < 4; ++v) hv[v] = silu_fast(val[v]) * s_u[wave >> 1][4 * grp + v][m];
+          lds_barrier();
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int r = 4 * grp + v;
-          const float hv = silu_f32(val[v]) * s_u[wave >> 1][r][m];
           uint16_t* dst = (last && r < blk.nr && !(wave & 1))
                               ? G.h + (size_t)(blk.p0 + blk.r0 + r) * I + 32 * chunk + 16 * (wave >> 1) + m
                               : reinterpret_cast<uint16_t*>(trash) + (r * 4 + wave) * 16 + m;
-          *dst = f32_to_bf16_rne(hv);
+          *dst = f32_to_bf16_rne(hv[v]);
         }
-        lds_barrier();
       }
     };
 
@@ -548,16 +615,19 @@ constexpr size_t kDynLds = 75 * 1024;
 
 typedef void (*GemvKernel)(FfnParams, GemvArgs);
 
-// Sub-item size: the largest of 16 (only when it is all of K), 8, 6, 4, 2, 1
-// K-tiles dividing nk.
-template <int FMT, bool DOWN>
+// Sub-item size: the largest of 16 (only when it is all of K, and not for
+// NVFP4, whose decode needs more registers), 8, 6, 4, 2, 1 K-tiles dividing nk.
+template <int FMT>
+constexpr int kSubMax = FMT == MOE_FMT_NVFP4 ? 8 : 16;
+
+template <int FMT, bool DOWN, bool XALL>
 static GemvKernel gemv_kernel(int nk) {
-  if (nk == 16) return k_gemv<FMT, DOWN, 16>;
-  if (nk % 8 == 0) return k_gemv<FMT, DOWN, 8>;
-  if (nk % 6 == 0) return k_gemv<FMT, DOWN, 6>;
-  if (nk % 4 == 0) return k_gemv<FMT, DOWN, 4>;
-  if (nk % 2 == 0) return k_gemv<FMT, DOWN, 2>;
-  return k_gemv<FMT, DOWN, 1>;
+  if (nk == 16) return k_gemv<FMT, DOWN, kSubMax<FMT>, XALL>;
+  if (nk % 8 == 0) return k_gemv<FMT, DOWN, 8, XALL>;
+  if (nk % 6 == 0) return k_gemv<FMT, DOWN, 6, XALL>;
+  if (nk % 4 == 0) return k_gemv<FMT, DOWN, 4, XALL>;
+  if (nk % 2 == 0) return k_gemv<FMT, DOWN, 2, XALL>;
+  return k_gemv<FMT, DOWN, 1, XALL>;
 }
 
 template <int FMT>
@@ -574,7 +644,10 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   };
   G.rbs1 = block_rows(P.H);
   G.rbs2 = block_rows(P.I);
-  const size_t lds1 = G.act_off + (size_t)G.rbs1 * P.H * 2 + kRowSlack;
+  // Small batches stage every token row of x once per workgroup (it fits the
+  // LDS of one row block, and the token table is cached).
+  const bool xall = P.T <= kXallMaxT && P.T <= G.rbs1 && ntok > 0;
+  const size_t lds1 = G.act_off + (size_t)(xall ? P.T : G.rbs1) * P.H * 2 + kRowSlack;
   const size_t lds2 = G.act_off + (size_t)G.rbs2 * P.I * 2 + kRowSlack;
   // Row blocks: at most ceil(T*k / rbs) + min(E, T*k) routed, plus the shared expert's.
   auto nrb = [&](int rbs) {
@@ -582,8 +655,9 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
     if (P.shared_blob) n += (P.T + rbs - 1) / rbs;
     return n;
   };
-  const auto k1 = gemv_kernel<FMT, false>(P.H / Fmt<FMT>::KT);
-  const auto k2 = gemv_kernel<FMT, true>(P.I / Fmt<FMT>::KT);
+  const auto k1 = xall ? gemv_kernel<FMT, false, true>(P.H / Fmt<FMT>::KT)
+                       : gemv_kernel<FMT, false, false>(P.H / Fmt<FMT>::KT);
+  const auto k2 = gemv_kernel<FMT, true, false>(P.I / Fmt<FMT>::KT);
   // The kernels are built for two resident workgroups per CU (their register
   // budget); more would start late, after the first ones finish.
   const long long cap1 = (long long)std::min(2, blocks_per_cu(reinterpret_cast<const void*>(k1), lds1)) * cu_count();
@@ -598,10 +672,10 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   return e;
 }
 
-template <int FMT, bool DOWN>
+template <int FMT, bool DOWN, bool XALL>
 static hipError_t set_lds_limit_all() {
-  const GemvKernel ks[] = {k_gemv<FMT, DOWN, 16>, k_gemv<FMT, DOWN, 8>, k_gemv<FMT, DOWN, 6>, k_gemv<FMT, DOWN, 4>,
-                           k_gemv<FMT, DOWN, 2>, k_gemv<FMT, DOWN, 1>};
+  const GemvKernel ks[] = {k_gemv<FMT, DOWN, kSubMax<FMT>, XALL>, k_gemv<FMT, DOWN, 8, XALL>, k_gemv<FMT, DOWN, 6, XALL>,
+                           k_gemv<FMT, DOWN, 4, XALL>, k_gemv<FMT, DOWN, 2, XALL>, k_gemv<FMT, DOWN, 1, XALL>};
   for (GemvKernel f : ks) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)kDynLds);
@@ -610,16 +684,21 @@ static hipError_t set_lds_limit_all() {
   return hipSuccess;
 }
 
+template <int FMT>
+static hipError_t set_lds_limits_fmt() {
+  hipError_t e;
+  if ((e = set_lds_limit_all<FMT, false, false>()) != hipSuccess) return e;
+  if ((e = set_lds_limit_all<FMT, false, true>()) != hipSuccess) return e;
+  return set_lds_limit_all<FMT, true, false>();
+}
+
 static hipError_t set_gemv_lds_limits() {
   static bool done = false;
   if (!done) {
     hipError_t e;
-    if ((e = set_lds_limit_all<MOE_FMT_BF16, false>()) != hipSuccess) return e;
-    if ((e = set_lds_limit_all<MOE_FMT_BF16, true>()) != hipSuccess) return e;
-    if ((e = set_lds_limit_all<MOE_FMT_MXFP4, false>()) != hipSuccess) return e;
-    if ((e = set_lds_limit_all<MOE_FMT_MXFP4, true>()) != hipSuccess) return e;
-    if ((e = set_lds_limit_all<MOE_FMT_NVFP4, false>()) != hipSuccess) return e;
-    if ((e = set_lds_limit_all<MOE_FMT_NVFP4, true>()) != hipSuccess) return e;
+    if ((e = set_lds_limits_fmt<MOE_FMT_BF16>()) != hipSuccess) return e;
+    if ((e = set_lds_limits_fmt<MOE_FMT_MXFP4>()) != hipSuccess) return e;
+    if ((e = set_lds_limits_fmt<MOE_FMT_NVFP4>()) != hipSuccess) return e;
     done = true;
   }
   return hipSuccess;

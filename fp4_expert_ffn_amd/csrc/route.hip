@@ -418,6 +418,77 @@ __global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict_
   permute_chunk(ids_s, T * k, E, 0, sm, counts, offsets, perm, inv);
 }
 
+// Batches of at most 64 tokens.  The k experts of one token are distinct, so
+// the flat indices routed to expert e are ordered by token, and the stable
+// position of (t, e) is offsets[e] + (number of earlier tokens routed to e).
+// Each expert keeps a 64-bit mask of its tokens in LDS, set by the token's
+// wave right after its top-k: counts are popcounts, the rank within an
+// expert is the popcount of the mask below t.  Every wave scans the counts
+// itself (no barrier between the scan and the placement), then places its
+// own tokens.  LDS: E 64-bit masks + E ints per wave.
+template <int NPER>
+__global__ __launch_bounds__(1024) void k_route_permute_small(const float* __restrict__ logits, int T, int E, int k,
+                                                              int renorm, int32_t* __restrict__ ids,
+                                                              float* __restrict__ wts, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  extern __shared__ uint64_t tmask[];  // [E], then int off[nw][E]
+  __shared__ int32_t ids_s[64 * kRouteMaxK];
+  __shared__ float w_s[64 * kRouteMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  int32_t* off = reinterpret_cast<int32_t*>(tmask + E) + wave * E;
+  for (int e = tid; e < E; e += blockDim.x) tmask[e] = 0ull;
+  __syncthreads();
+  for (int t = wave; t < T; t += nw) {
+    wave_topk<NPER>(logits + (size_t)t * E, E, k, renorm, ids_s + t * k, w_s + t * k);
+    if (lane < k) {  // the wave reads back its own LDS writes (in order)
+      const int e = ids_s[t * k + lane];
+      ids[t * k + lane] = e;
+      wts[t * k + lane] = w_s[t * k + lane];
+      atomicOr(reinterpret_cast<unsigned long long*>(&tmask[e]), 1ull << t);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the counts: lane l owns experts [l * per, l * per + per)
+  const int per = (E + 63) / 64;
+  int run = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = lane * per + i;
+    if (e < E) run += __popcll(tmask[e]);
+  }
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  int base = incl - run;
+  for (int i = 0; i < per; ++i) {
+    const int e = lane * per + i;
+    if (e < E) {
+      const int c = __popcll(tmask[e]);
+      off[e] = base;
+      if (wave == 0) {
+        counts[e] = c;
+        offsets[e] = base;
+      }
+      base += c;
+    }
+  }
+  if (wave == 0 && lane == 63) offsets[E] = incl;
+  for (int t = wave; t < T; t += nw) {
+    if (lane < k) {
+      const int f = t * k + lane;
+      const int e = ids_s[f];
+      const int pos = off[e] + (int)__popcll(tmask[e] & ((1ull << t) - 1ull));
+      if (pos < T * k) {  // always true for a valid routing; keeps every store inside perm
+        perm[pos] = f;
+        inv[f] = pos;
+      }
+    }
+  }
+}
+
 // Threads of the one-workgroup routing + permutation: a wave per token (up to
 // 16) and at least one thread per flat index.
 static int route_permute_threads(int T, int k) {
@@ -436,7 +507,13 @@ moe_status set_lds_limits() {
                          reinterpret_cast<const void*>(k_route_permute<2>),
                          reinterpret_cast<const void*>(k_route_permute<4>),
                          reinterpret_cast<const void*>(k_route_permute<16>)};
+    const void* fns_small[] = {reinterpret_cast<const void*>(k_route_permute_small<1>),
+                               reinterpret_cast<const void*>(k_route_permute_small<2>),
+                               reinterpret_cast<const void*>(k_route_permute_small<4>),
+                               reinterpret_cast<const void*>(k_route_permute_small<16>)};
     for (const void* f : fns) MOE_HIP(hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 120 * 1024));
+    for (const void* f : fns_small)
+      MOE_HIP(hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 120 * 1024));
     done = true;
   }
   return MOE_OK;
@@ -515,16 +592,28 @@ extern "C" moe_status moe_route_permute(const float* logits, int T, int E, int k
   moe_status st = set_lds_limits();
   if (st != MOE_OK) return st;
   const int nt = route_permute_threads(T, k);
-  const size_t lds = sizeof(int32_t) * (size_t)E * (2 + nt / 64);
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const int rn = renormalize ? 1 : 0;
+  if (T >= 1 && T <= 64) {
+    const int ntw = 64 * std::min(T, kPermWaves);  // a wave per token, up to 16
+    const size_t lds = sizeof(uint64_t) * (size_t)E + sizeof(int32_t) * (size_t)E * (ntw / 64);
+#define MOE_RPS(N) hipLaunchKernelGGL(k_route_permute_small<N>, dim3(1), dim3(ntw), lds, hs, logits, T, E, k, rn, \
+                                      topk_ids, topk_w, counts, offsets, perm, inv)
+    if (E <= 64) MOE_RPS(1);
+    else if (E <= 128) MOE_RPS(2);
+    else if (E <= 256) MOE_RPS(4);
+    else MOE_RPS(16);
+#undef MOE_RPS
+  } else {
+    const size_t lds = sizeof(int32_t) * (size_t)E * (2 + nt / 64);
 #define MOE_RP(N) hipLaunchKernelGGL(k_route_permute<N>, dim3(1), dim3(nt), lds, hs, logits, T, E, k, rn, \
                                      topk_ids, topk_w, counts, offsets, perm, inv)
-  if (E <= 64) MOE_RP(1);
-  else if (E <= 128) MOE_RP(2);
-  else if (E <= 256) MOE_RP(4);
-  else MOE_RP(16);
+    if (E <= 64) MOE_RP(1);
+    else if (E <= 128) MOE_RP(2);
+    else if (E <= 256) MOE_RP(4);
+    else MOE_RP(16);
 #undef MOE_RP
+  }
   MOE_LAUNCHED();
   return MOE_OK;
 }

@@ -31,10 +31,25 @@ __device__ __forceinline__ float unnorm(float v, float m) {
   return expf(v - m);
 }
 
-// Lane l holds experts l + 64 i (i < NPER, NPER * 64 >= E).  Selection: k
-// rounds of a wave-wide max over 64-bit keys (rank key << 32 | (0xFFFF - id)),
-// so a larger logit wins and equal logits go to the lower id; the owner of
-// each winner removes it.  Round r's winner is output position r.
+// Rank of this lane among the set lanes of a wave-uniform mask m below it.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Lane l holds experts l + 64 i (i < NPER, NPER * 64 >= E), each as a 32-bit
+// rank key (0: no expert).  Selection:
+//  1. the k-th largest key value thr, counted with multiplicity, by a binary
+//     radix walk from the top bit: at bit b the keys that match the bits
+//     above b chosen so far and have bit b set are counted with ballots; if
+//     they are at least the number still needed, bit b of thr is set, else
+//     they are all selected and taken off the count;
+//  2. every key above thr is selected, and of the keys equal to thr the ones
+//     with the lowest expert ids, as many as are still needed;
+//  3. a selected key's output position is the number of selected keys that
+//     rank above it (larger key, or equal key and lower id), found by one
+//     pass over the selected keys with readlane.
+// All counts are ballots and scalar arithmetic: no cross-lane reduction
+// sits on the critical path except the softmax denominator.
 // Writes ids[pos], w[pos] for pos in [0, k) (global or LDS pointers).
 template <int NPER>
 __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm, int32_t* ids,
@@ -52,44 +67,61 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
       rk[i] = rank_bits(val[i]) + 1u;  // 0 marks "no key"; NaN -> 1, below every number
     }
   }
-  uint32_t selmask = 0;
+  // 1. threshold (wave-uniform)
+  uint32_t thr = 0u;
+  int need = k;
+#pragma unroll 4
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = thr | (1u << b);
+    const uint32_t hi = ~0u << b;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) cnt += (int)__popcll(__ballot((rk[i] & hi) == cand));
+    if (cnt >= need) thr = cand;
+    else need -= cnt;
+  }
+  // 2. selection: `need` keys equal to thr remain to be taken, lowest ids first
+  bool sel[NPER];
+  uint64_t selm[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const bool eq = rk[i] == thr && rk[i] != 0u;
+    const uint64_t eqm = __ballot(eq);
+    sel[i] = (rk[i] > thr) || (eq && lanes_below(eqm) < need);
+    selm[i] = __ballot(sel[i]);
+    need = max(0, need - (int)__popcll(eqm));  // __popcll is unsigned: keep the difference signed
+  }
+  // 3. output positions
   int pos[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) pos[i] = 0;
-  int id0 = 0;  // the largest logit's expert (wave-uniform)
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const uint64_t key = ((uint64_t)rk[i] << 32) | (uint32_t)(0xFFFF - (lane + 64 * i));
-      if (rk[i] != 0u && !((selmask >> i) & 1u)) best = max_u64(best, key);
+  for (int j = 0; j < NPER; ++j) {
+    uint64_t m = selm[j];
+    while (m) {
+      const int src = __builtin_ctzll(m);
+      m &= m - 1;
+      const uint32_t ks = (uint32_t)__builtin_amdgcn_readlane((int)rk[j], src);
+      const int id = 64 * j + src;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) pos[i] += (ks > rk[i] || (ks == rk[i] && id < lane + 64 * i)) ? 1 : 0;
     }
-    const uint64_t win = wave_max_u64(best);
-    const int id = 0xFFFF - (int)(win & 0xFFFFu);
-    if (r == 0) id0 = id;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (lane + 64 * i == id) {
-        selmask |= 1u << i;
-        pos[i] = r;
-      }
   }
-  // the top logit m, from the lane that holds it, and the softmax weights
-  float tv = 0.f;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i)
-    if (i == (id0 >> 6)) tv = val[i];
-  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tv), id0 & 63));
-  float part = 0.f;
+  // the top logit m (position 0), from the lane that holds it, and the softmax weights
+  float top = 0.f;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
-    const bool sel = (selmask >> i) & 1u;
-    if (renorm ? sel : lane + 64 * i < E) part += unnorm(val[i], top);
+    const uint64_t b = __ballot(sel[i] && pos[i] == 0);
+    if (b) top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[i]), __builtin_ctzll(b)));
   }
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i)
+    if (renorm ? sel[i] : lane + 64 * i < E) part += unnorm(val[i], top);
   const float den = wave_sum(part);
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
-    if ((selmask >> i) & 1u) {
+    if (sel[i] && pos[i] < k) {  // exactly k keys are selected; the bound keeps every store in the row
       ids[pos[i]] = lane + 64 * i;
       wout[pos[i]] = den > 0.f ? unnorm(val[i], top) / den : 1.0f / (float)k;
     }

@@ -176,7 +176,8 @@ def test_permute_prefill_zipf_full_size():
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 128, 8), (4, 128, 8), (16, 128, 8), (16, 8, 2), (64, 1024, 16), (128, 128, 8),
-                                   (200, 256, 8), (0, 32, 4)])
+                                   (200, 256, 8), (0, 32, 4), (64, 128, 8), (33, 64, 16), (5, 3, 3), (40, 300, 4),
+                                   (17, 256, 8), (64, 8, 8), (65, 128, 8), (2, 1000, 16)])
 def test_route_permute_fused(T, E, k):
     """moe_route_permute (one launch when T*k <= 1024, two otherwise) equals the oracle."""
     from fp4_expert_ffn_amd import moe_route_permute
@@ -185,6 +186,9 @@ def test_route_permute_fused(T, E, k):
     if T > 2:
         lg[1, :] = 0.0
         lg[2, 3 % E] = np.nan
+    if T > 4:
+        lg[3, :] = -np.inf
+        lg[4, ::2] = np.round(lg[4, ::2])  # ties
     N = T * k
     ids = torch.empty((max(T, 1), k), dtype=torch.int32, device=DEV)
     w = torch.empty((max(T, 1), k), dtype=torch.float32, device=DEV)

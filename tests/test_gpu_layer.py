@@ -76,16 +76,21 @@ def test_small_layers_every_path(fmt, amode, T, E, k, H, I, shared):
     _full_check(layer, x, experts, k, logits, shared=sh, amode=amode)
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
-def test_large_magnitude_activations(fmt):
-    """|x| up to about 2^21 (beyond fp16's range): the NVFP4 path stages operand
-    rows in fp16 with a per-row power-of-two shift."""
+@pytest.mark.parametrize("fmt,rows", [("nvfp4", "all"), ("mxfp4", "all"), ("nvfp4", "some")])
+def test_large_magnitude_activations(fmt, rows):
+    """|x| up to about 2^21 (beyond fp16's range) in every token row, or in
+    two of them: the NVFP4 path stages operand rows in fp16 with a per-row
+    power-of-two shift, taken again from the row's global copy for the rows
+    that overflow."""
     T, E, k, H, I = 5, 8, 2, 256, 256
     experts = [synth.expert(fmt, H, I, config=83, expert_id=e) for e in range(E)]
-    x = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(synth.activations(T, H, 83)) * np.float32(2.0 ** 19))
+    scale = np.full((T, 1), 2.0 ** 19, np.float32)
+    if rows == "some":
+        scale[[0, 2, 4]] = 1.0
+    x = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(synth.activations(T, H, 83)) * scale)
     logits = np.random.default_rng(9).standard_normal((T, E)).astype(np.float32)
     layer = resident_layer(experts, k=k, T=T)
-    say(f"large-magnitude activations {fmt}")
+    say(f"large-magnitude activations {fmt}, {rows} rows")
     layer.forward(_x(x), logits=torch.from_numpy(logits).to(DEV))
     torch.cuda.synchronize()
     _full_check(layer, x, experts, k, logits)

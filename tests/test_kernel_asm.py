@@ -5,9 +5,10 @@ The decode GEMV waits for its direct-to-LDS operand rows with an explicit
 `s_waitcnt vmcnt(N)` that counts the weight loads issued behind them (the
 vector-memory counter completes in order, so N later loads outstanding means
 the rows have landed).  That is only correct if the compiled code issues
-exactly N vector-memory loads between the last row load and the wait; this
-test checks it for every instantiation, so a compiler that merges or splits
-those loads fails here instead of racing on the GPU."""
+exactly N vector-memory loads behind the rows before the wait (the bank
+between two scheduling barriers, nothing else); this test checks it for every
+instantiation, so a compiler that merges or splits those loads fails here
+instead of racing on the GPU."""
 import os
 import re
 import shutil
@@ -32,25 +33,44 @@ def gemv_asm(tmp_path_factory):
     return out.read_text()
 
 
+def _row_waits(body):
+    """(N, loads) for every explicit row wait: an `s_waitcnt vmcnt(N)` directly
+    followed by `s_barrier`, with the number of vector-memory loads issued in
+    the block between the two scheduling barriers that precede it (the bank
+    issued behind the rows)."""
+    lines = [ln.strip() for ln in body.split("\n")]
+    code = [(i, t) for i, t in enumerate(lines) if t and not t.startswith(";;")]
+    out = []
+    for n, (i, t) in enumerate(code[:-1]):
+        if not (t.startswith("s_waitcnt") and "vmcnt(" in t and code[n + 1][1] == "s_barrier"):
+            continue
+        wait = int(t.split("vmcnt(")[1].split(")")[0])
+        marks = [j for j in range(i) if lines[j].startswith("; sched_barrier")]
+        assert len(marks) >= 2, "row wait without the bank's scheduling barriers"
+        lo, hi = marks[-2], marks[-1]
+        between = lines[hi + 1:i]
+        assert not any(x.startswith(("global_", "buffer_", "flat_", "scratch_")) for x in between), between
+        loads = sum(1 for x in lines[lo + 1:hi] if x.startswith(("global_load", "buffer_load", "flat_load")))
+        out.append((wait, loads))
+    return out
+
+
 def test_row_wait_counts_the_loads_behind_the_rows(gemv_asm):
-    names = re.findall(r"^(_ZN3moe6k_gemvILi(\d)ELb(\d)ELi(\d+)EEE\w+):", gemv_asm, re.M)
-    assert len(names) == 36, len(names)  # 3 formats x 2 projections x 6 sub-item sizes
-    for full, fmt, _down, sub in names:
+    names = re.findall(r"^(_ZN3moe6k_gemvILi(\d)ELb(\d)ELi(\d+)ELb(\d)EEE\w+):", gemv_asm, re.M)
+    # 3 formats x (gate/up, gate/up with every token row staged, down) x 6
+    # sub-item sizes, less NVFP4's 16 (its largest is 8)
+    assert len(names) == 51, len(names)
+    for full, fmt, _down, sub, _xall in names:
         fmt, sub = int(fmt), int(sub)
         body = gemv_asm[gemv_asm.index(full + ":"):gemv_asm.index(".Lfunc_end", gemv_asm.index(full + ":"))]
-        k = body.rfind("global_load_lds_dwordx4")
+        k = body.find("global_load_lds_dwordx4")
         assert k > 0, full
-        loads, wait = 0, None
-        for line in body[k:].split("\n")[1:]:
-            t = line.strip()
-            if t.startswith(("global_load", "buffer_load", "flat_load", "scratch_load")):
-                loads += 1
-            if t.startswith("s_waitcnt") and "vmcnt" in t:
-                wait = int(t.split("vmcnt(")[1].split(")")[0])
-                break
+        waits = _row_waits(body[k:])
+        assert waits, full
         # tiles, scales (4-bit formats) and the per-tensor multiplier of one bank
         expected = sub + (sub if fmt != 0 else 0) + 1
-        assert wait == expected and loads == expected, (full, loads, wait, expected)
+        for wait, loads in waits:
+            assert wait == expected and loads == expected, (full, loads, wait, expected)
 
 
 @pytest.fixture(scope="module")
