@@ -229,24 +229,26 @@ __device__ __forceinline__ int row_token(const FfnParams& P, const ActiveLds& A,
   return P.T * P.k <= kTokCache ? A.tok[p] : P.perm[p] / P.k;
 }
 
-// Operand rows in LDS: nr rows of K bf16 (or fp16) values, unpadded, with
-// 16-byte piece j of row r at piece r * (K/8) + (j ^ (r & swz)): the 16 rows
-// that one A-fragment read touches then fall in distinct bank groups.  They
-// arrive by direct global->LDS loads (no registers), which write 64
-// consecutive pieces per wave instruction; a last partial instruction spills
-// into kRowSlack bytes past the rows.
+// Operand rows in LDS: nr rows of K bf16 (or fp16) values, each followed by
+// one 16-byte pad, so 16-byte piece j of row r sits at slot r * (K/8 + 1) + j.
+// The 16 rows that one A-fragment read touches then fall 16 bytes apart in
+// the bank space (no conflicts), and a fragment's address is a per-lane base
+// plus a compile-time offset.  The rows arrive by direct global->LDS loads
+// (no registers), which write 64 consecutive slots per wave instruction (a
+// pad slot receives a copy of its row's last piece); a last partial
+// instruction spills into kRowSlack bytes past the rows.
 constexpr int kRowSlack = 1024;
 
-__device__ __forceinline__ int row_swz(int ppr) { return (ppr % 16 == 0) ? 15 : ((ppr % 4 == 0) ? 3 : 0); }
+__host__ __device__ constexpr size_t row_bytes(int K) { return (size_t)K * 2 + 16; }
 
 template <class Src>
 __device__ __forceinline__ void dma_rows(uint8_t* act, const uint16_t* base, int K, int nr, Src src) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ppr = K / 8, total = nr * ppr, swz = row_swz(ppr);
+  const int spr = K / 8 + 1, total = nr * spr;  // slots per row, slots
   const int nch = (total + 63) >> 6;
   for (int c = wave; c < nch; c += 4) {
     const int p = min(c * 64 + lane, total - 1);  // lanes past the rows re-read the last piece (into the slack)
-    const int r = p / ppr, j = (p % ppr) ^ (r & swz);
+    const int r = p / spr, j = min(p % spr, spr - 2);
     __builtin_amdgcn_global_load_lds(base + (size_t)src(r) * K + j * 8,
                                      (__attribute__((address_space(3))) void*)(act + c * 1024), 16, 0, 0);
   }
@@ -281,18 +283,18 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4 v, float sc) {
 template <bool F16, class Src>
 __device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pexp, int* big, Src src) {
   if constexpr (F16) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ppr = K / 8, total = nr * ppr;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ppr = K / 8, spr = ppr + 1;
+    const int total = nr * spr;  // pad slots hold copies of real pieces: converted alike
     if (tid < nr) pexp[tid] = 0;
     for (int p = tid; p < total; p += 256) {
       uint4* q = reinterpret_cast<uint4*>(act) + p;
       const uint4 v = *q;
-      if (bf16x8_absmax_bits(v) >= 0x4780u) atomicOr(big, 1 << (p / ppr));  // |value| >= 2^16, inf or NaN
+      if (bf16x8_absmax_bits(v) >= 0x4780u) atomicOr(big, 1 << (p / spr));  // |value| >= 2^16, inf or NaN
       *q = bf16x8_to_f16x8(v, 1.0f);
     }
     lds_barrier();
     const int bm = *big;
     if (bm != 0) {
-      const int swz = row_swz(ppr);
       for (int r = wave; r < nr; r += 4) {
         if (!((bm >> r) & 1)) continue;
         const uint4* g = reinterpret_cast<const uint4*>(src(r));
@@ -303,8 +305,8 @@ __device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pe
         const int pe = (E == 0xFF) ? 0 : max(0, E - 141);
         if (lane == 0) pexp[r] = pe;
         const float sc = __uint_as_float((uint32_t)(127 - pe) << 23);
-        uint4* row = reinterpret_cast<uint4*>(act) + (size_t)r * ppr;
-        for (int j = lane; j < ppr; j += 64) row[j ^ (r & swz)] = bf16x8_to_f16x8(g[j], sc);
+        uint4* row = reinterpret_cast<uint4*>(act) + (size_t)r * spr;
+        for (int j = lane; j < ppr; j += 64) row[j] = bf16x8_to_f16x8(g[j], sc);
       }
       lds_barrier();
       if (tid == 0) *big = 0;
@@ -388,7 +390,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* rbase = DOWN ? G.h : P.x;
   // this workgroup's own 4 KiB of scratch (distinct lines: no store contention)
   float* trash = G.trash + (size_t)(blockIdx.x % kTrashSlots) * 1024;
-  const int ppr = K / 8, swz = row_swz(ppr);
 
   struct Bank {
     uint4 q[SUB];
@@ -457,8 +458,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // last row; their outputs are discarded), as an LDS row index
     const int am = min(m, blk.nr - 1);
     const int arow_i = XALL ? row_token(P, A, blk, am) : am;
-    const uint8_t* arow = act + (size_t)arow_i * ppr * 16;
-    const int aswz = arow_i & swz;
+    // this lane's fragment base: K-group grp of its row (values 32 grp + 8 st
+    // of each 128-value K-tile, or 8 grp of each 32-value one)
+    const uint8_t* abase = act + (size_t)arow_i * row_bytes(K) + (F::SPT == 4 ? 64 : 16) * grp;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     // The epilogue runs after every sub-item (uniform code: no branch around
     // memory operations inside the pipelined loop); before an item's last
@@ -473,8 +475,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       constexpr int NU = SUB * F::SPT;
       auto read_a = [&](int u) {
         const int kt = sub * SUB + u / F::SPT, st = u % F::SPT;
-        const int piece = (kt * F::KT + (F::SPT == 4 ? 32 * grp + 8 * st : 8 * grp)) / 8;
-        return *reinterpret_cast<const uint4*>(arow + ((piece ^ aswz) << 4));
+        return *reinterpret_cast<const uint4*>(abase + kt * (F::KT * 2) + 16 * st);
       };
       uint4 ar[3];
       ar[0] = read_a(0);
@@ -639,7 +640,7 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   const size_t avail = kDynLds - (size_t)G.act_off;
   // Rows per row block: at most 16, within the LDS left.
   auto block_rows = [&](int K) {
-    const size_t by_lds = (avail - kRowSlack) / ((size_t)K * 2);
+    const size_t by_lds = (avail - kRowSlack) / row_bytes(K);
     return (int)std::max<size_t>(1, std::min<size_t>(16, by_lds));
   };
   G.rbs1 = block_rows(P.H);
@@ -647,8 +648,8 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   // Small batches stage every token row of x once per workgroup (it fits the
   // LDS of one row block, and the token table is cached).
   const bool xall = P.T <= kXallMaxT && P.T <= G.rbs1 && ntok > 0;
-  const size_t lds1 = G.act_off + (size_t)(xall ? P.T : G.rbs1) * P.H * 2 + kRowSlack;
-  const size_t lds2 = G.act_off + (size_t)G.rbs2 * P.I * 2 + kRowSlack;
+  const size_t lds1 = G.act_off + (size_t)(xall ? P.T : G.rbs1) * row_bytes(P.H) + kRowSlack;
+  const size_t lds2 = G.act_off + (size_t)G.rbs2 * row_bytes(P.I) + kRowSlack;
   // Row blocks: at most ceil(T*k / rbs) + min(E, T*k) routed, plus the shared expert's.
   auto nrb = [&](int rbs) {
     long long n = (rows + rbs - 1) / rbs + std::min<long long>(P.E, rows);

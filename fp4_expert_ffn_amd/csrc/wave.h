@@ -72,30 +72,4 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(b[0], b[1]);
 }
 
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
-}
-
-// Full-wave unsigned 64-bit max, result in every lane.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<kDppQuadXor1>(v));
-  v = max_u64(v, dpp_u64<kDppQuadXor2>(v));
-  v = max_u64(v, dpp_u64<kDppRowHalfMirror>(v));
-  v = max_u64(v, dpp_u64<kDppRowMirror>(v));
-  {
-    auto h = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-    auto l = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-    v = max_u64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
-  }
-  {
-    auto h = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-    auto l = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-    v = max_u64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
-  }
-  return v;
-}
-
 }  // namespace moe
