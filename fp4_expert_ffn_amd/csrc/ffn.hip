@@ -117,10 +117,12 @@ __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
   }
 }
 
-// out[t, c..c+8) = bf16( sum_j w[t,j] * y[inv[t*k+j], c..] (+ y[T*k + t, c..]) ).
+// out[t, c..c+8) = bf16( sum_j w[t,j] * y[inv[t*k+j], c..] (+ y[T*k + t, c..]) ),
+// or with inv null (y rows already in flat order) y[t*k+j].
 // KMAX >= k: the row indices and weights are loaded first, then every y row
 // (branch-free: slots past k re-read row k-1 with weight 0), so the loads
-// overlap instead of forming k dependent round trips.
+// overlap instead of forming k dependent round trips; flat rows need no
+// index load at all.
 template <typename YT, int KMAX>
 __global__ __launch_bounds__(128) void k_combine(const YT* __restrict__ y, const int32_t* __restrict__ inv,
                                                  const float* __restrict__ w, const YT* __restrict__ ysh, int T,
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(128) void k_combine(const YT* __restrict__ y, const
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     const int jj = min(j, k - 1);
-    row[j] = inv[(size_t)t * k + jj];
+    row[j] = inv ? inv[(size_t)t * k + jj] : t * k + jj;
     wj[j] = w[(size_t)t * k + jj];
   }
   float v[KMAX][8];
@@ -244,6 +246,9 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     G.trash = reinterpret_cast<float*>(ws + w.trash);
     G.ng = a->I / 32;
     G.nd = a->H / 64;
+    // an internal y read only by the combine below: written in flat order,
+    // so the combine needs no row-index load
+    G.yflat = (!a->y && a->out && (long long)a->T * a->k <= 1024) ? 1 : 0;
     e = launch_gemv(P, G, s);
   } else {
     MfmaBufs B{};
@@ -265,7 +270,8 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));
   } else if (a->out) {
     const float* ysh = a->shared_blob ? y + (size_t)a->T * a->k * a->H : nullptr;
-    e = launch_combine(y, a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
+    const bool yflat = path == kPathGemv && !a->y && (long long)a->T * a->k <= 1024;
+    e = launch_combine(y, yflat ? nullptr : a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
     if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));
     }
   return MOE_OK;

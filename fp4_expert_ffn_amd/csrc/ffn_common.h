@@ -52,6 +52,7 @@ struct GemvArgs {
   int rbs1, rbs2;  // rows per row block (<= 16) of the two launches
   int na;          // active-expert capacity of the LDS table
   int act_off;     // LDS byte offset of the staged operand rows
+  int yflat;       // 1: y rows in flat order t * k + j (T*k <= 1024 only), 0: perm order
 };
 
 // Counters of the single-launch GEMV (first bytes of the workspace).  Zero

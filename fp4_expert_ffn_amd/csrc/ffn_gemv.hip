@@ -110,20 +110,21 @@ __device__ __forceinline__ typename Fmt<FMT>::V bfrag(const uint4 q, uint32_t sc
 // round of global loads: active expert a (ascending expert id among experts
 // with rows and an enabled mask; the shared expert last) has rows cnt[a],
 // first perm-order row p0[a], slot slot[a] (-1: shared) and row blocks of
-// `rbs` rows numbered [rb[a], rb[a+1]).  tok[p] caches perm[p] / k when
-// T*k <= kTokCache.  The arrays live in dynamic LDS, sized for na active
-// experts (min(E, T*k) routed, plus the shared one).
+// `rbs` rows numbered [rb[a], rb[a+1]).  flat[p] caches perm[p] and tok[p]
+// perm[p] / k when T*k <= kTokCache.  The arrays live in dynamic LDS, sized
+// for na active experts (min(E, T*k) routed, plus the shared one).
 constexpr int kTokCache = 1024;
 struct ActiveLds {
-  int *cnt, *p0, *slot, *rb, *tok;
+  int *cnt, *p0, *slot, *rb, *tok, *flat;
   int* n;
 };
 
 __host__ __device__ inline size_t active_lds_bytes(int na, int ntok) {
-  return (size_t)(4 * na + 2 + ntok) * sizeof(int);
+  return (size_t)(4 * na + 2 + 2 * ntok) * sizeof(int);
 }
 
-__device__ inline ActiveLds active_view(uint8_t* base, int na) {
+// ntok: T*k if it is at most kTokCache, else 0
+__device__ inline ActiveLds active_view(uint8_t* base, int na, int ntok) {
   int* b = reinterpret_cast<int*>(base);
   ActiveLds A;
   A.n = b;
@@ -132,6 +133,7 @@ __device__ inline ActiveLds active_view(uint8_t* base, int na) {
   A.slot = A.p0 + na;
   A.rb = A.slot + na;  // na + 1 entries
   A.tok = A.rb + na + 1;
+  A.flat = A.tok + ntok;
   return A;
 }
 
@@ -140,7 +142,11 @@ __device__ inline void build_active(const FfnParams& P, int rbs, const ActiveLds
   const int N = P.T * P.k;
   if (tid >= 64) {
     if (N <= kTokCache)
-      for (int p = tid - 64; p < N; p += 192) A.tok[p] = P.perm[p] / P.k;
+      for (int p = tid - 64; p < N; p += 192) {
+        const int f = P.perm[p];
+        A.flat[p] = f;
+        A.tok[p] = f / P.k;
+      }
   } else {
     // every load first (one round trip), then the compaction
     constexpr int kPer = 1024 / 64;
@@ -376,7 +382,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int H = P.H, I = P.I;
   const int K = DOWN ? I : H, nk = K / F::KT;
   const int rbs = DOWN ? G.rbs2 : G.rbs1, nchunk = DOWN ? G.nd : G.ng;
-  const ActiveLds A = active_view(lds, G.na);
+  const ActiveLds A = active_view(lds, G.na, P.T * P.k <= kTokCache ? P.T * P.k : 0);
   uint8_t* act = lds + G.act_off;  // operand rows (swizzled) + slack
   build_active(P, rbs, A);
   const int nrb = A.rb[*A.n];
@@ -394,11 +400,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   struct Bank {
     uint4 q[SUB];
     ScaleT<FMT> sc[SUB];
-    float g;
   };
-  // Vector-memory loads of one bank: SUB tiles, SUB scale loads (4-bit
-  // formats; 64 or 128 bytes apart, never merged) and the multiplier.
-  constexpr int kBankLoads = SUB + (FMT == MOE_FMT_BF16 ? 0 : SUB) + 1;
+  // Vector-memory loads of one bank: SUB tiles and SUB scale loads (4-bit
+  // formats; 64 or 128 bytes apart, never merged).
+  constexpr int kBankLoads = SUB + (FMT == MOE_FMT_BF16 ? 0 : SUB);
 
   // XALL: every token row of x, in token order, before the first task (whose
   // first weights then go out behind them)
@@ -428,12 +433,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // exactly kBankLoads loads: the row wait below counts them
 #pragma unroll
       for (int j = 0; j < SUB; ++j) b.sc[j] = load_scale_at<FMT>(sp + j * kScaleTileBytes<FMT>);
-      b.g = reinterpret_cast<const BlobHeader*>(blk.blob)->g[gsel];
 #pragma unroll
       for (int j = 0; j < SUB; ++j) b.q[j] = ldg16(wp + j * kTileBytes);
     };
 
     Bank b0, b1;
+    // the per-tensor multiplier of this wave's rows, loaded once per task
+    // ahead of the rows (so the row wait below covers it too)
+    const float gmul = reinterpret_cast<const BlobHeader*>(blk.blob)->g[gsel];
+    asm volatile("" ::: "memory");
     if constexpr (!XALL) {
       // operand rows of the block (token rows of x, or rows of h), loaded
       // ahead of the first weights; the table's barrier also ends the
@@ -505,7 +513,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int r = 4 * grp + v;
-          float sc2 = b.g;
+          float sc2 = gmul;
           if constexpr (F::F16) {
             const int rr = min(r, blk.nr - 1);
             sc2 *= pow2i(s_pexp[XALL ? row_token(P, A, blk, rr) : rr]);
@@ -519,7 +527,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int r = 4 * grp + v;
-          float* dst = (last && r < blk.nr) ? G.y + (size_t)(blk.p0 + blk.r0 + r) * H + 64 * chunk + 16 * wave + m
+          // y row: perm order, or flat order (t * k + j) for the combine
+          // (shared rows T*k + t either way)
+          const int p = blk.p0 + blk.r0 + min(r, blk.nr - 1);
+          const int yrow = (G.yflat && !blk.shared) ? A.flat[p] : p;
+          float* dst = (last && r < blk.nr) ? G.y + (size_t)yrow * H + 64 * chunk + 16 * wave + m
                                             : trash + (r * 4 + wave) * 16 + m;
           *dst = val[v];
         }

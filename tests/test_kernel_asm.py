@@ -67,8 +67,8 @@ def test_row_wait_counts_the_loads_behind_the_rows(gemv_asm):
         assert k > 0, full
         waits = _row_waits(body[k:])
         assert waits, full
-        # tiles, scales (4-bit formats) and the per-tensor multiplier of one bank
-        expected = sub + (sub if fmt != 0 else 0) + 1
+        # tiles and scales (4-bit formats) of the bank issued behind the rows
+        expected = sub + (sub if fmt != 0 else 0)
         for wait, loads in waits:
             assert wait == expected and loads == expected, (full, loads, wait, expected)
 
