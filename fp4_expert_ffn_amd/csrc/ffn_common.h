@@ -53,6 +53,7 @@ struct GemvArgs {
   int na;          // active-expert capacity of the LDS table
   int act_off;     // LDS byte offset of the staged operand rows
   int yflat;       // 1: y rows in flat order t * k + j (T*k <= 1024 only), 0: perm order
+  int ncu;         // > 0: the grid is two workgroups per CU on ncu CUs (items dealt per CU)
 };
 
 // Counters of the single-launch GEMV (first bytes of the workspace).  Zero

@@ -386,9 +386,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint8_t* act = lds + G.act_off;  // operand rows (swizzled) + slack
   build_active(P, rbs, A);
   const int nrb = A.rb[*A.n];
-  // this workgroup's items: [i_beg, i_end) of nrb * nchunk, row block major
+  // this workgroup's items: [i_beg, i_end) of nrb * nchunk, row block major.
+  // With two workgroups per CU (workgroups b and b + ncu share a CU), each
+  // CU gets an equal contiguous range, split between its two workgroups, so
+  // CU loads differ by at most one item.
   const long long nitems = (long long)nrb * nchunk;
-  const long long i_beg = nitems * blockIdx.x / gridDim.x, i_end = nitems * (blockIdx.x + 1) / gridDim.x;
+  long long i_beg, i_end;
+  if (G.ncu > 0) {
+    const int cu = blockIdx.x % G.ncu, half = blockIdx.x / G.ncu;
+    const long long c0 = nitems * cu / G.ncu, c1 = nitems * (cu + 1) / G.ncu, mid = c0 + (c1 - c0 + 1) / 2;
+    i_beg = half ? mid : c0;
+    i_end = half ? c1 : mid;
+  } else {
+    i_beg = nitems * blockIdx.x / gridDim.x;
+    i_end = nitems * (blockIdx.x + 1) / gridDim.x;
+  }
   const int nsub = nk / SUB;  // SUB divides nk: every sub-item loads exactly SUB tiles
   const size_t off_w = DOWN ? P.L.off_w2 : P.L.off_w13, off_s = DOWN ? P.L.off_s2 : P.L.off_s13;
   // per-tensor multiplier of this wave's rows: gate (even waves) / up (odd) / down
@@ -677,9 +689,12 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   const long long cap2 = (long long)std::min(2, blocks_per_cu(reinterpret_cast<const void*>(k2), lds2)) * cu_count();
   const int g1 = (int)std::max<long long>(1, std::min<long long>(nrb(G.rbs1) * G.ng, cap1));
   const int g2 = (int)std::max<long long>(1, std::min<long long>(nrb(G.rbs2) * G.nd, cap2));
+  // a full grid of two workgroups per CU deals its items per CU
+  G.ncu = g1 == 2 * cu_count() ? cu_count() : 0;
   launch(k1, dim3(g1), dim3(256), lds1, s, P, G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  G.ncu = g2 == 2 * cu_count() ? cu_count() : 0;
   launch(k2, dim3(g2), dim3(256), lds2, s, P, G);
   e = hipGetLastError();
   return e;
