@@ -431,6 +431,15 @@ def summarize(args):
             lines.append(f"{r['Name'][:90]:<90} {int(r['Calls']):>7} {float(r['AverageNs']) / 1e3:>10.2f} "
                          f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} "
                          f"{float(r['Percentage']):>6.2f}")
+        # the dominant kernel over all its instantiations (a call-weighted average)
+        wl = os.path.basename(out)[len("kernels_"):-len(".txt")]
+        pat = DOMINANT.get(wl)
+        dom = [r for r in rows if pat and pat in r["Name"]]
+        if dom:
+            calls = sum(int(r["Calls"]) for r in dom)
+            tot = sum(float(r["TotalDurationNs"]) for r in dom)
+            lines += ["", f"dominant kernel '{pat}' ({len(dom)} instantiations): {calls} calls, "
+                          f"average {tot / calls / 1e3:.2f} us"]
         with open(out, "w") as f:
             f.write("\n".join(lines) + "\n")
         print(f"wrote {out}")
