@@ -9,5 +9,5 @@ from ._lib import (  # noqa: F401
     moe_cache_create, moe_cache_decode_step, moe_cache_destroy, moe_cache_map_bytes, moe_cache_mark_used,
     moe_cache_pin_resident, moe_cache_reset, moe_cache_stats, moe_combine, moe_dequant_blob, moe_expert_ffn,
     moe_expert_ffn_traced, moe_expert_ffn_workspace_size, moe_last_error, moe_permute, moe_prepack_expert, moe_quantize_mxfp4, moe_route,
-    moe_route_permute, moe_router_logits, moe_version, moe_workspace_check, moe_workspace_init,
+    moe_route_permute, moe_router_logits, moe_version,
 )

@@ -73,8 +73,6 @@ SIGNATURES = {
     "moe_expert_ffn": (_i, [ctypes.POINTER(FfnArgs), _vp]),
     "moe_expert_ffn_traced": (_i, [ctypes.POINTER(FfnArgs), _vp, _vp, _i, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
-    "moe_workspace_init": (_i, [_vp, _sz, _vp]),
-    "moe_workspace_check": (_i, [_vp, _vp]),
     "moe_quantize_mxfp4": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "moe_dequant_blob": (_i, [_vp, _i, _vp, _vp]),
     "moe_cache_create": (_vp, [_i, _sz, _vp, _i, _i]),
@@ -224,14 +222,6 @@ def moe_expert_ffn_traced(args: FfnArgs, events, stream=None) -> int:
     _check(lib().moe_expert_ffn_traced(ctypes.byref(args), stream_handle(stream), arr, len(events), ctypes.byref(n)),
            "moe_expert_ffn_traced")
     return n.value
-
-
-def moe_workspace_init(workspace, workspace_bytes, stream=None):
-    _check(lib().moe_workspace_init(ptr(workspace), workspace_bytes, stream_handle(stream)), "moe_workspace_init")
-
-
-def moe_workspace_check(workspace, stream=None):
-    _check(lib().moe_workspace_check(ptr(workspace), stream_handle(stream)), "moe_workspace_check")
 
 
 def moe_combine(y, inv, topk_w, y_shared, T, k, H, out, stream=None):

@@ -32,7 +32,7 @@ Path choose_path(const moe_ffn_args* a) {
 }
 
 struct WsLayout {
-  size_t sync, trash, h, y, xq, xs, hq, hs, hb, inv, total;
+  size_t trash, h, y, xq, xs, hq, hs, hb, inv, total;
 };
 
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
@@ -43,7 +43,6 @@ WsLayout ws_layout(const moe_ffn_args* a) {
   const size_t R = (size_t)a->T * a->k + (a->shared_blob ? a->T : 0);
   WsLayout w{};
   size_t o = 0;
-  w.sync = o; o = al(o + sizeof(GemvSync));
   w.trash = o; o = al(o + (1 << 20));  // 256 slots of 4 KiB
   const Path p = choose_path(a);
   if (p == kPathGemv) {
@@ -80,7 +79,6 @@ moe_status check_args(const moe_ffn_args* a) {
     return set_error(MOE_EUNSUPPORTED, "moe_expert_ffn: MXFP4 activations need MXFP4 weights (got format %d)",
                      a->wfmt);
   MOE_CHECK_ARG((long long)a->T * a->k <= (1 << 17), "moe_expert_ffn: T*k exceeds 131072");
-  MOE_CHECK_ARG(a->H / 64 <= kMaxChunks, "moe_expert_ffn: H=%d exceeds %d", a->H, 64 * kMaxChunks);
   MOE_CHECK_ARG(choose_path(a) != kPathGemv || (a->H <= kGemvMaxK && a->I <= kGemvMaxK),
                 "moe_expert_ffn: H=%d, I=%d: the bf16-activation path stages one row of up to %d values in LDS",
                 a->H, a->I, kGemvMaxK);
@@ -327,34 +325,5 @@ extern "C" moe_status moe_dequant_blob(const void* blob, int which, float* out, 
                      reinterpret_cast<hipStream_t>(stream), static_cast<const uint8_t*>(blob), L, h.fmt, which, h.H,
                      h.I, out);
   MOE_LAUNCHED();
-  return MOE_OK;
-}
-
-namespace {
-__global__ void k_zero_words(uint32_t* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
-}
-}  // namespace
-
-extern "C" moe_status moe_workspace_init(void* workspace, size_t workspace_bytes, moe_stream_t stream) {
-  MOE_CHECK_ARG(workspace && ((uintptr_t)workspace & 255) == 0 && workspace_bytes >= sizeof(GemvSync),
-                "moe_workspace_init: workspace must be 256-byte aligned and >= %zu bytes", sizeof(GemvSync));
-  hipLaunchKernelGGL(k_zero_words, dim3(16), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
-                     static_cast<uint32_t*>(workspace), sizeof(GemvSync) / 4);
-  MOE_LAUNCHED();
-  return MOE_OK;
-}
-
-extern "C" moe_status moe_workspace_check(const void* workspace, moe_stream_t stream) {
-  MOE_CHECK_ARG(workspace, "moe_workspace_check: null workspace");
-  MOE_HIP(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
-  GemvSync s;
-  MOE_HIP(hipMemcpy(&s, workspace, sizeof s, hipMemcpyDeviceToHost));
-  if (s.err) return set_error(MOE_EHIP, "moe_workspace_check: a wait inside moe_expert_ffn timed out");
-  for (int i = 0; i < kMaxActive; ++i)
-    if (s.gu_done[i] || s.dn_pass[i])
-      return set_error(MOE_EHIP, "moe_workspace_check: counters of active expert %d were left nonzero", i);
-  for (int i = 0; i < kMaxChunks; ++i)
-    if (s.dn_done[i]) return set_error(MOE_EHIP, "moe_workspace_check: chunk counter %d was left nonzero", i);
   return MOE_OK;
 }

@@ -56,18 +56,6 @@ struct GemvArgs {
   int ncu;         // > 0: the grid is two workgroups per CU on ncu CUs (items dealt per CU)
 };
 
-// Counters of the single-launch GEMV (first bytes of the workspace).  Zero
-// before the first call; every call leaves them zero again.
-constexpr int kMaxActive = 1040;  // routed experts (<= 1024) + the shared expert
-constexpr int kMaxChunks = 1024;  // 64-column chunks of H
-struct GemvSync {
-  unsigned gu_done[kMaxActive];  // gate/up workgroups finished, per active expert
-  unsigned dn_pass[kMaxActive];  // down workgroups past their wait, per active expert
-  unsigned dn_done[kMaxChunks];  // experts whose down output of a chunk is written
-  unsigned err;                  // 1: a wait timed out (results of that call are invalid)
-  unsigned pad[63];
-};
-
 // One unit of expert work: an expert (or the shared expert) and its rows.
 struct Job {
   const uint8_t* blob;

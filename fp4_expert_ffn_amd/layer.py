@@ -69,11 +69,6 @@ class LayerState:
         self._args[key] = (a, x)  # keep x alive with its args
         return a
 
-    def check(self, stream=None):
-        """Verify the workspace counters (synchronises the stream)."""
-        if self._ws is not None:
-            L.moe_workspace_check(self._ws, stream)
-
     def route(self, T, x=None, w_router=None, logits=None, stream=None):
         lay = self.layer
         if logits is None:

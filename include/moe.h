@@ -156,22 +156,10 @@ typedef struct {
   const int32_t* inv;           /* nullable with out: [T*k] from moe_permute             */
   uint16_t* out;                /* nullable: [T,H] bf16; if set, the combine runs too    */
   void* workspace;              /* device scratch, >= moe_expert_ffn_workspace_size, 256-byte
-                                   aligned.  Its first bytes hold counters that link the
-                                   workgroups of one launch: zero-fill it once after
-                                   allocating it (moe_workspace_init); every call leaves them
-                                   zero.  Calls that share a workspace must not overlap.   */
+                                   aligned; no contents carry over between calls.  Calls
+                                   that share a workspace must not overlap.                */
   size_t workspace_bytes;
 } moe_ffn_args;
-
-/* Zero the counter block at the start of a workspace (a small fill kernel on
- * `stream`; safe inside stream capture). */
-moe_status moe_workspace_init(void* workspace, size_t workspace_bytes, moe_stream_t stream);
-
-/* Synchronise `stream`, then verify that the counter block of `workspace` is
- * back to zero and that no wait inside moe_expert_ffn gave up (a wait is
- * bounded to a few seconds; if one expires the call's outputs are invalid and
- * MOE_EHIP is returned here).  Debug / test entry; it blocks the host. */
-moe_status moe_workspace_check(const void* workspace, moe_stream_t stream);
 
 /* Bytes of device workspace a call with these dimensions needs. */
 size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a);

@@ -35,7 +35,6 @@ def _full_check(layer, x_bits, experts, k, logits, shared=None, amode="bf16"):
     err = oracle.moe.relative_error(out_f32(layer, T), ref["out"])
     say(f"    rel err {err:.3e}")
     assert err <= TOL
-    layer.state.check()  # counters back to zero, no wait gave up
     return err
 
 
@@ -152,7 +151,6 @@ def _sampled_check(layer, b, make_expert, k, amode, shared=None, n_random=10):
     assert np.array_equal(layer.counts.cpu().numpy(), counts)
     out = out_f32(layer, T)
     assert np.all(np.isfinite(out))
-    layer.state.check()
     toks = sample_tokens(perm, offsets, k, T, n_random, seed=T)
     wts = DequantCache(make_expert)
     sw = oracle.moe.dequant_expert(shared) if shared is not None else None
