@@ -21,46 +21,56 @@ using namespace moe;
 // Small T: one workgroup per expert, 256 threads split H; tokens in registers.
 constexpr int kRouterGemvMaxT = 16;
 
+template <int TM>  // token capacity (T <= TM)
 __global__ __launch_bounds__(256) void k_router_gemv(const uint16_t* __restrict__ x, const float* __restrict__ w,
                                                      int T, int H, int E, float* __restrict__ out) {
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float acc[kRouterGemvMaxT];
+  float acc[TM];
 #pragma unroll
-  for (int t = 0; t < kRouterGemvMaxT; ++t) acc[t] = 0.f;
+  for (int t = 0; t < TM; ++t) acc[t] = 0.f;
   const float* wr = w + (size_t)e * H;
-  for (int h = tid * 4; h < H; h += 256 * 4) {
-    float4 wv;
-    if ((H & 3) == 0) {  // rows are 16-byte aligned: one vector load
-      wv = *reinterpret_cast<const float4*>(wr + h);
-    } else {
-      wv.x = wr[h];
-      wv.y = h + 1 < H ? wr[h + 1] : 0.f;
-      wv.z = h + 2 < H ? wr[h + 2] : 0.f;
-      wv.w = h + 3 < H ? wr[h + 3] : 0.f;
-    }
+  if ((H & 3) == 0) {
+    // rows 16-byte (weights) and 8-byte (x) aligned: 4 values per thread and
+    // chunk, kU chunks' loads issued before any of them is used
+    constexpr int kU = TM >= 16 ? 2 : TM >= 4 ? 4 : 8;
+    for (int h0 = 0; h0 < H; h0 += 1024 * kU) {
+      float4 wv[kU];
+      uint2 xv[kU][TM];
 #pragma unroll
-    for (int t = 0; t < kRouterGemvMaxT; ++t) {
-      if (t < T) {
-        const uint16_t* xr = x + (size_t)t * H + h;
-        float x0 = bf16_to_f32(xr[0]);
-        float x1 = h + 1 < H ? bf16_to_f32(xr[1]) : 0.f;
-        float x2 = h + 2 < H ? bf16_to_f32(xr[2]) : 0.f;
-        float x3 = h + 3 < H ? bf16_to_f32(xr[3]) : 0.f;
-        acc[t] = fmaf(x0, wv.x, acc[t]);
-        acc[t] = fmaf(x1, wv.y, acc[t]);
-        acc[t] = fmaf(x2, wv.z, acc[t]);
-        acc[t] = fmaf(x3, wv.w, acc[t]);
+      for (int u = 0; u < kU; ++u) {
+        const int h = min(h0 + u * 1024 + tid * 4, H - 4);  // past the end: a valid chunk, weight 0 below
+        wv[u] = *reinterpret_cast<const float4*>(wr + h);
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+          xv[u][t] = *reinterpret_cast<const uint2*>(x + (size_t)min(t, T - 1) * H + h);
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (h0 + u * 1024 + tid * 4 >= H) wv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+          acc[t] = fmaf(__uint_as_float(xv[u][t].x << 16), wv[u].x, acc[t]);
+          acc[t] = fmaf(__uint_as_float(xv[u][t].x & 0xFFFF0000u), wv[u].y, acc[t]);
+          acc[t] = fmaf(__uint_as_float(xv[u][t].y << 16), wv[u].z, acc[t]);
+          acc[t] = fmaf(__uint_as_float(xv[u][t].y & 0xFFFF0000u), wv[u].w, acc[t]);
+        }
       }
     }
+  } else {
+    for (int h = tid; h < H; h += 256) {
+      const float wv = wr[h];
+#pragma unroll
+      for (int t = 0; t < TM; ++t) acc[t] = fmaf(bf16_to_f32(x[(size_t)min(t, T - 1) * H + h]), wv, acc[t]);
+    }
   }
-  __shared__ float red[4][kRouterGemvMaxT];
+  __shared__ float red[4][TM];
 #pragma unroll
-  for (int t = 0; t < kRouterGemvMaxT; ++t) {
-    float v = acc[t];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) red[wave][t] = v;
+  for (int t = 0; t < TM; ++t) {
+    if (t < T) {
+      const float v = wave_sum(acc[t]);
+      if (lane == 0) red[wave][t] = v;
+    }
   }
   __syncthreads();
   if (tid < T) out[(size_t)tid * E + e] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
@@ -528,7 +538,9 @@ extern "C" moe_status moe_router_logits(const uint16_t* x, const float* w_router
   MOE_CHECK_ARG(x && w_router && logits, "moe_router_logits: null pointer");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (T <= kRouterGemvMaxT) {
-    hipLaunchKernelGGL(k_router_gemv, dim3(E), dim3(256), 0, s, x, w_router, T, H, E, logits);
+    if (T == 1) hipLaunchKernelGGL(k_router_gemv<1>, dim3(E), dim3(256), 0, s, x, w_router, T, H, E, logits);
+    else if (T <= 4) hipLaunchKernelGGL(k_router_gemv<4>, dim3(E), dim3(256), 0, s, x, w_router, T, H, E, logits);
+    else hipLaunchKernelGGL(k_router_gemv<16>, dim3(E), dim3(256), 0, s, x, w_router, T, H, E, logits);
   } else if (H % 32 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)w_router & 15) == 0) {
     hipLaunchKernelGGL(k_router_mfma, dim3((E + 15) / 16, (T + 31) / 32), dim3(64), 0, s, x, w_router, T, H, E, logits);
   } else {

@@ -117,7 +117,7 @@ def test_route_zipf_workloads():
 
 
 @pytest.mark.parametrize("T,H,E", [(16, 256, 8), (1, 7168, 256), (2, 2048, 128), (40, 7168, 256), (130, 384, 24),
-                                   (2048, 7168, 256), (77, 200, 10)])
+                                   (2048, 7168, 256), (77, 200, 10), (3, 202, 12), (9, 1000, 64), (4, 9000, 7)])
 def test_router_logits_error_bound(T, H, E):
     from fp4_expert_ffn_amd import moe_router_logits
     x = synth.activations(T, H, 71, T, H)
