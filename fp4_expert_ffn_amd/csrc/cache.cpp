@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <set>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -32,6 +33,8 @@ struct moe_cache {
   // per-step scratch of moe_cache_decode_step
   std::vector<int32_t> step_ids, step_slot, step_ev;
   std::vector<uint8_t> step_hit;
+  // last upload from each host slot map: the map is rewritten only after it
+  std::vector<std::pair<const void*, hipEvent_t>> map_upload;
 
   void unlink(int32_t k) {
     int32_t p = prev[k], n = next[k];
@@ -88,6 +91,7 @@ extern "C" void moe_cache_destroy(moe_cache* c) {
   if (!c) return;
   for (hipEvent_t e : c->reader) if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->filled) if (e) (void)hipEventDestroy(e);
+  for (auto& m : c->map_upload) (void)hipEventDestroy(m.second);
   delete c;
 }
 
@@ -233,6 +237,23 @@ extern "C" size_t moe_cache_map_bytes(int E) {
   return ((size_t)E * 6 + 255) & ~(size_t)255;
 }
 
+// The upload of a pinned host map is asynchronous: before the host rewrites a
+// map it waits for the last upload from that map (already done in the usual
+// case), so steps that do not synchronise the host may share a map.
+static moe_status map_before_write(moe_cache* c, const void* host_map, hipEvent_t* ev) {
+  for (auto& m : c->map_upload)
+    if (m.first == host_map) {
+      MOE_HIP(hipEventSynchronize(m.second));
+      *ev = m.second;
+      return MOE_OK;
+    }
+  hipEvent_t e = nullptr;
+  MOE_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  c->map_upload.emplace_back(host_map, e);
+  *ev = e;
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t copy_stream,
                                             moe_stream_t compute_stream) {
   MOE_CHECK_ARG(c && s, "moe_cache_decode_step: null pointer");
@@ -296,12 +317,16 @@ extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe
   int32_t* map = static_cast<int32_t*>(s->host_map);
   uint8_t* hm = reinterpret_cast<uint8_t*>(map + E);
   uint8_t* mm = hm + E;
+  hipEvent_t up = nullptr;
+  st = map_before_write(c, s->host_map, &up);
+  if (st != MOE_OK) return st;
   memset(s->host_map, 0, mb);
   for (int i = 0; i < n; ++i) {
     map[c->step_ids[i]] = c->step_slot[i];
     (c->step_hit[i] ? hm : mm)[c->step_ids[i]] = 1;
   }
   MOE_HIP(hipMemcpyAsync(s->dev_map, s->host_map, mb, hipMemcpyHostToDevice, ks));
+  MOE_HIP(hipEventRecord(up, ks));
   const int32_t* dmap = static_cast<const int32_t*>(s->dev_map);
   const uint8_t* dhm = reinterpret_cast<const uint8_t*>(dmap + E);
   const uint8_t* dmm = dhm + E;

@@ -264,9 +264,10 @@ moe_status moe_cache_stats(const moe_cache* c, long long* hits, long long* misse
  * ffn.slot_of_expert, ffn.expert_mask are set by the call; ffn.y is
  * required; ffn.out, topk_w, inv receive the combine.  host_counts and
  * host_map are pinned (hipHostMalloc) host buffers of 4E and
- * moe_cache_map_bytes(E) bytes, dev_map a device buffer of that size; none
- * may be reused by another step before this step's compute work finishes
- * (a later step on the same compute_stream satisfies this).  The trace
+ * moe_cache_map_bytes(E) bytes, dev_map a device buffer of that size;
+ * host_counts and dev_map may be reused by a later step on the same
+ * compute_stream, and a step waits for the previous upload from its host_map
+ * before rewriting it.  The trace
  * arrays (host, capacity E) receive the step's n_experts records. */
 typedef struct {
   int layer;

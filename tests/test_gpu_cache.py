@@ -124,3 +124,86 @@ def test_cached_stream_a3b_shape():
     n = _run_stream(layers=2, E=128, k=8, H=2048, I=768, tokens=12, slots=24, make_expert=make,
                     check_steps=steps, config=87)
     assert n == len(steps)
+
+
+# Prefill through the cache one layer ahead (every expert of layer l + 1
+# copied while layer l computes) is not in the library: its first GPU run, the
+# MXFP4 / MXFP4-activation case below, ended in a GPU memory fault whose cause
+# was not found by reading the code.  These tests stay skipped until the cause
+# is shown and the entry points return.
+PREFILL_SKIP = pytest.mark.skip(reason="layer-ahead prefill through the cache disabled: "
+                                "its first GPU run faulted, cause not yet shown")
+
+
+def _trace_of(want, E):
+    return ([r[0] for r in want], [int(r[1]) for r in want], [r[2] for r in want],
+            [-1 if r[3] is None else r[3][0] * E + r[3][1] for r in want])
+
+
+@PREFILL_SKIP
+@pytest.mark.parametrize("fmt,amode,T,E,k,H,I", [
+    ("mxfp4", "mxfp4", 300, 8, 2, 256, 128),
+    ("nvfp4", "bf16", 77, 16, 4, 256, 256),
+])
+def test_cached_prefill_layer_ahead(fmt, amode, T, E, k, H, I):
+    """Two prefill passes over 3 layers through a 2E-slot cache, each layer's
+    experts copied while the previous layer computes: the lookups equal the
+    oracle's LRU (the prefetch of layer l + 1 evicts layer l - 1, never l),
+    every step hits, and each layer's output matches the oracle layer."""
+    from fp4_expert_ffn_amd.layer import CachedPrefill, to_numpy_bf16
+    import fp4_expert_ffn_amd as F
+    layers, config = 3, 88
+    say(f"cached prefill {fmt}/{amode}: {layers} layers x {E} experts, T={T} k={k} H={H} I={I}, {2 * E} slots")
+    stride = (F.moe_blob_bytes(fmt, H, I) + 255) // 256 * 256
+    experts = {(l, e): synth.expert(fmt, H, I, config=config, layer=l, expert_id=e)
+               for l in range(layers) for e in range(E)}
+    pf = CachedPrefill(num_layers=layers, num_experts=E, k=k, H=H, I=I, fmt=fmt, amode=amode, max_tokens=T,
+                       host_blob=lambda l, e: _pinned_blob(experts[(l, e)], stride), device=DEV)
+    lru = oracle.lru.SlotLRU(2 * E)
+    want_misses = 0
+    for rnd in range(2):
+        xs = [synth.activations(T, H, config, rnd, l) for l in range(layers)]
+        lg = [synth.rng(config, rnd, l, 1).standard_normal((T, E), dtype=np.float32) for l in range(layers)]
+        x_d = [torch.from_numpy(x.view(np.int16)).to(DEV) for x in xs]
+        lg_d = [torch.from_numpy(a).to(DEV) for a in lg]
+        outs = [torch.empty((T, H), dtype=torch.int16, device=DEV) for _ in range(layers)]
+        traces = pf.run(x_d, lg_d, outs)
+        torch.cuda.synchronize()
+        for l in range(layers):
+            want_misses += sum(not r[1] for r in lru.lookup(l, range(E)))   # the prefetch
+            want = lru.lookup(l, range(E))          # the step: all hits
+            assert all(r[1] for r in want)
+            got = tuple(t.tolist() for t in traces[l])
+            assert got == _trace_of(want, E), (rnd, l)
+            ref = oracle.moe.layer(xs[l], [experts[(l, e)] for e in range(E)], k, logits=lg[l], amode=amode)
+            if l == layers - 1:                      # the ids buffer holds the last layer's routing
+                assert np.array_equal(pf.ids[:T].cpu().numpy(), ref["ids"])
+            err = oracle.moe.relative_error(synth.bf16_bits_to_f32(to_numpy_bf16(outs[l])), ref["out"])
+            say(f"    pass {rnd} layer {l}: rel err {err:.3e}")
+            assert err <= TOL, (rnd, l, err)
+    hits, misses, nbytes = pf.stats()
+    # 3 layers through 2 layers' slots: every prefetch misses
+    assert misses == want_misses == 6 * E and nbytes == misses * stride, (hits, misses)
+    pf.close()
+
+
+@PREFILL_SKIP
+def test_cached_prefill_step_needs_the_prefetch():
+    """A step whose layer was not prefetched fails with MOE_ECACHE and leaves the cache unchanged."""
+    from fp4_expert_ffn_amd.layer import CachedPrefill
+    import fp4_expert_ffn_amd as F
+    H, I, E, k, T = 256, 128, 8, 2, 16
+    stride = (F.moe_blob_bytes("mxfp4", H, I) + 255) // 256 * 256
+    ex = synth.expert("mxfp4", H, I, config=89)
+    blob = _pinned_blob(ex, stride)
+    pf = CachedPrefill(num_layers=2, num_experts=E, k=k, H=H, I=I, fmt="mxfp4", max_tokens=T,
+                       host_blob=lambda l, e: blob, device=DEV)
+    x = torch.zeros((T, H), dtype=torch.int16, device=DEV)
+    lg = torch.zeros((T, E), dtype=torch.float32, device=DEV)
+    out = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    pf.prefetch(0)
+    with pytest.raises(F.MoeError, match="not cached"):
+        pf.layer_step(1, x, lg, out)
+    torch.cuda.synchronize()
+    assert pf.stats() == (0, E, E * stride)
+    pf.close()
