@@ -134,7 +134,9 @@ typedef struct {
   int amode;                    /* MOE_ACT_BF16: activations stay bf16 / fp32.
                                    MOE_ACT_MXFP4 (wfmt MXFP4 only): x and the SwiGLU output
                                    are MXFP4-encoded per row per 32 values and the products
-                                   run on the block-scaled FP4 matrix cores.               */
+                                   run on the block-scaled FP4 matrix cores.  Unless
+                                   H % 512 == 0 and I % 256 == 0, it needs I >= 256, y
+                                   null and out set (MOE_EINVAL otherwise).                */
   const uint16_t* x;            /* [T,H] bf16                                            */
   const int32_t* counts;        /* [E]    from moe_permute                               */
   const int32_t* offsets;       /* [E+1]  from moe_permute                               */

@@ -169,3 +169,21 @@ def test_pin_resident(L):
     slot, hit, ev = L.cache_lookup(c, 0, [3])
     assert not hit[0] and slot[0] == 0
     c.close()
+
+
+def test_mxfp4_activations_off_the_persistent_kernel_need_the_combined_output(L):
+    """MXFP4 activations with H % 512 or I % 256 nonzero run on the 128 x 128
+    kernel, enabled there only for I >= 256 with the combined output: the
+    argument check rejects the rest before any device call (fake addresses)."""
+    base = dict(T=4, k=2, E=8, wfmt="mxfp4", amode="mxfp4", x=0x10000, counts=0x20000, offsets=0x30000,
+                perm=0x40000, slot_of_expert=0x50000, slot_pool=0x100000, topk_w=0x60000, inv=0x70000,
+                workspace=0x1000000, workspace_bytes=1 << 30)
+
+    def args(H, I, **kw):
+        stride = (L.moe_blob_bytes("mxfp4", H, I) + 255) // 256 * 256
+        return L.ffn_args(H=H, I=I, slot_stride=stride, **{**base, **kw})
+
+    for H, I, kw in [(256, 128, dict(out=0x80000)), (256, 384, dict(y=0x90000, out=0x80000)),
+                     (256, 384, dict(y=0x90000))]:
+        with pytest.raises(L.MoeError, match="MXFP4 activations"):
+            L.moe_expert_ffn(args(H, I, **kw), 0)
