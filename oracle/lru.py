@@ -15,6 +15,15 @@ Readings where the pages are silent:
   * a miss takes the lowest-numbered free slot, otherwise it evicts the least
     recently used key and reuses that key's slot;
   * a step may not look up more distinct experts than there are slots.
+
+Resizing (page "FreeToken量子化：MoE推論のセットアップガイド", the paragraph
+on resizing the expert cache at runtime at scheduler safe points; the pages
+give no placement rule, so this is a reading):
+  * the cache keeps the min(n, cached) most recently used keys and drops the
+    rest, least recent first;
+  * the kept keys move to a new set of n slots, packed from slot 0 in
+    recency order (least recent in slot 0), their relative recency unchanged;
+  * the slots above them are free, taken lowest first as before.
 """
 from __future__ import annotations
 
@@ -59,3 +68,18 @@ class SlotLRU:
             self._lru[key] = slot
             out.append((e, False, slot, victim))
         return out
+
+    def resize(self, num_slots: int):
+        """Change the slot count; returns (moves, dropped): moves lists
+        (key, old_slot, new_slot) in recency order, least recent first;
+        dropped lists the keys no longer cached, least recent first."""
+        assert num_slots > 0
+        keys = list(self._lru.items())          # least recent first
+        ndrop = max(0, len(keys) - num_slots)
+        dropped = [k for k, _ in keys[:ndrop]]
+        kept = keys[ndrop:]
+        moves = [(k, old, new) for new, (k, old) in enumerate(kept)]
+        self._lru = OrderedDict((k, new) for k, _, new in moves)
+        self._free = list(range(len(kept), num_slots))
+        self.num_slots = num_slots
+        return moves, dropped

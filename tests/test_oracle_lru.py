@@ -95,3 +95,41 @@ def test_never_evicts_key_of_same_step():
     assert [r[3] for r in recs] == [(0, 0), (0, 1), (0, 2)]
     recs = c.lookup(0, [5, 6])  # victims must be (1,0),(1,1), never a key of this step
     assert [r[3] for r in recs] == [(1, 0), (1, 1)]
+
+
+@pytest.mark.parametrize("C,n", [(12, 5), (5, 12), (9, 9), (20, 4)])
+def test_resize_keeps_what_an_lru_of_the_new_size_would_hold(C, n):
+    """Stack property of LRU: a cache of n slots that saw the whole history
+    holds exactly the n most recent keys, in recency order.  So after
+    resize(n) it holds what a fresh min(C, n)-slot cache run over the same
+    history holds, and when shrinking (n <= C) the hit / miss sequence of
+    later steps equals that of a fresh n-slot cache run over the whole
+    history."""
+    steps = _random_steps(90, 3, 16, 4, 2)
+    first, second = steps[:50], steps[50:]
+    a, b = SlotLRU(C), SlotLRU(min(C, n))
+    for l, ids in first:
+        a.lookup(l, ids)
+        b.lookup(l, ids)
+    before = [k for k in a._lru]
+    moves, dropped = a.resize(n)
+    assert dropped + [m[0] for m in moves] == before
+    assert [m[0] for m in moves] == list(b._lru)          # same keys, same recency order
+    assert [m[2] for m in moves] == list(range(len(moves)))
+    for l, ids in second:
+        ra, rb = a.lookup(l, ids), b.lookup(l, ids)
+        if n <= C:
+            assert [(r[0], r[1], r[3]) for r in ra] == [(r[0], r[1], r[3]) for r in rb]
+        slots = list(a._lru.values())
+        assert len(set(slots)) == len(slots) and all(0 <= s < n for s in slots)
+
+
+def test_resize_then_misses_take_the_slots_above_the_kept_keys():
+    c = SlotLRU(4)
+    c.lookup(0, [1, 2, 3])       # slots 0, 1, 2
+    c.lookup(1, [7])             # slot 3
+    moves, dropped = c.resize(6)
+    assert dropped == [] and [(m[0], m[2]) for m in moves] == [((0, 1), 0), ((0, 2), 1), ((0, 3), 2), ((1, 7), 3)]
+    assert [r[2] for r in c.lookup(2, [0, 1])] == [4, 5]
+    moves, dropped = c.resize(2)
+    assert dropped == [(0, 1), (0, 2), (0, 3), (1, 7)] and [m[0] for m in moves] == [(2, 0), (2, 1)]
