@@ -85,6 +85,7 @@ SIGNATURES = {
     "moe_cache_stats": (_i, [_vp, _vp, _vp, _vp]),
     "moe_cache_map_bytes": (_sz, [_i]),
     "moe_cache_decode_step": (_i, [_vp, ctypes.POINTER(CacheStep), _vp, _vp]),
+    "moe_cache_resize": (_i, [_vp, _i, _vp, _vp]),
 }
 
 _lib = None
@@ -313,3 +314,8 @@ def moe_cache_map_bytes(E: int) -> int:
 def moe_cache_decode_step(cache: Cache, step: CacheStep, copy_stream=None, compute_stream=None):
     _check(lib().moe_cache_decode_step(cache.handle, ctypes.byref(step), stream_handle(copy_stream),
                                        stream_handle(compute_stream)), "moe_cache_decode_step")
+
+
+def moe_cache_resize(cache: Cache, num_slots: int, slot_pool, stream=None):
+    _check(lib().moe_cache_resize(cache.handle, int(num_slots), ptr(slot_pool), stream_handle(stream)),
+           "moe_cache_resize")

@@ -368,3 +368,60 @@ extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe
   s->n_experts = n;
   return MOE_OK;
 }
+
+// ------------------------------------------------------------ resize at a safe point
+
+static void* slot_pool_at(void* pool, int slot, size_t slot_bytes) {
+  return static_cast<uint8_t*>(pool) + (size_t)slot * slot_bytes;
+}
+
+extern "C" moe_status moe_cache_resize(moe_cache* c, int num_slots, void* slot_pool, moe_stream_t stream) {
+  MOE_CHECK_ARG(c && slot_pool, "moe_cache_resize: null pointer");
+  MOE_CHECK_ARG(c->pool, "moe_cache_resize: cache has no slot pool");
+  MOE_CHECK_ARG(num_slots > 0, "moe_cache_resize: num_slots %d must be positive", num_slots);
+  MOE_CHECK_ARG(((uintptr_t)slot_pool & 255) == 0, "moe_cache_resize: slot_pool must be 256-byte aligned");
+  const uint8_t* np = static_cast<const uint8_t*>(slot_pool);
+  const size_t nbytes = (size_t)num_slots * c->slot_bytes, obytes = (size_t)c->num_slots * c->slot_bytes;
+  MOE_CHECK_ARG(np + nbytes <= c->pool || c->pool + obytes <= np,
+                "moe_cache_resize: the new slot pool overlaps the current one");
+  moe_status st = ensure_events(c);
+  if (st != MOE_OK) return st;
+  // keys from least to most recent; the least recent beyond num_slots are dropped
+  std::vector<int32_t> keys;
+  for (int32_t k = c->head; k >= 0; k = c->next[k]) keys.push_back(k);
+  const int nkeep = std::min<int>((int)keys.size(), num_slots), ndrop = (int)keys.size() - nkeep;
+  std::vector<hipEvent_t> filled(num_slots, nullptr), reader(num_slots, nullptr);
+  for (int s = 0; s < num_slots; ++s) {
+    MOE_HIP(hipEventCreateWithFlags(&filled[s], hipEventDisableTiming));
+    MOE_HIP(hipEventCreateWithFlags(&reader[s], hipEventDisableTiming));
+  }
+  // copy each kept blob once its fill has landed; stream order puts the
+  // copies after earlier readers of the old slots queued on `stream`
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  for (int i = 0; i < nkeep; ++i) {
+    const int32_t s = c->key_slot[keys[ndrop + i]];
+    MOE_HIP(hipStreamWaitEvent(hs, c->filled[s], 0));
+    MOE_HIP(hipMemcpyAsync(slot_pool_at(slot_pool, i, c->slot_bytes), c->pool + (size_t)s * c->slot_bytes,
+                           c->slot_bytes, hipMemcpyDeviceToDevice, hs));
+    MOE_HIP(hipEventRecord(filled[i], hs));
+  }
+  for (int i = 0; i < ndrop; ++i) {
+    c->unlink(keys[i]);
+    c->key_slot[keys[i]] = -1;
+  }
+  for (hipEvent_t e : c->reader) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->filled) (void)hipEventDestroy(e);
+  c->reader.swap(reader);
+  c->filled.swap(filled);
+  c->num_slots = num_slots;
+  c->pool = static_cast<uint8_t*>(slot_pool);
+  c->slot_key.assign(num_slots, -1);
+  c->has_reader.assign(num_slots, 0);
+  for (int i = 0; i < nkeep; ++i) {
+    c->key_slot[keys[ndrop + i]] = i;
+    c->slot_key[i] = keys[ndrop + i];
+  }
+  c->free_slots.clear();
+  for (int s = nkeep; s < num_slots; ++s) c->free_slots.insert(s);
+  return MOE_OK;
+}

@@ -214,6 +214,17 @@ class CachedDecoder:
     def stats(self):
         return L.moe_cache_stats(self.cache)
 
+    def resize(self, num_slots, stream=None):
+        """Move the cache to `num_slots` slots between steps (the most recent
+        keys kept); the old pool is released once the copies have finished."""
+        pool = torch.empty(num_slots * self.stride, dtype=torch.uint8, device=self.dev)
+        L.moe_cache_resize(self.cache, num_slots, pool, stream)
+        s = torch.cuda.current_stream(self.dev) if stream is None else stream
+        s.synchronize()
+        self.pool = pool
+        for st in self._steps.values():
+            st.ffn.slot_pool = pool.data_ptr()
+
     def reset(self):
         L.moe_cache_reset(self.cache)
 

@@ -292,6 +292,22 @@ size_t moe_cache_map_bytes(int E);
 moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t copy_stream,
                                  moe_stream_t compute_stream);
 
+/* Resize the cache at a safe point (between layer calls, no step in flight).
+ * [page "FreeToken量子化：MoE推論のセットアップガイド", paragraph on resizing
+ *  the expert cache at runtime at scheduler safe points.]
+ * The cache moves to num_slots slots in slot_pool (same slot size, 256-byte
+ * aligned, not overlapping the current pool).  It keeps the min(num_slots,
+ * cached) most recently used keys, packed into slots 0, 1, ... from least to
+ * most recent with their recency order unchanged, and drops the rest; later
+ * misses take the free slots above them, lowest first.  Each kept blob is
+ * copied device to device on `stream` after its own fill has landed; work
+ * queued on `stream` later sees the new slots, and the fill events of the new
+ * slots order other streams after the copies.  The caller may release the old
+ * pool once the copies and every earlier reader of it have finished (e.g.
+ * after synchronising `stream` when all steps ran on it).  Returns MOE_EINVAL
+ * for bad arguments (cache unchanged). */
+moe_status moe_cache_resize(moe_cache* c, int num_slots, void* slot_pool, moe_stream_t stream);
+
 /* Reset the cache to the empty state (host metadata only). */
 moe_status moe_cache_reset(moe_cache* c);
 

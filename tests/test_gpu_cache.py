@@ -49,7 +49,7 @@ def test_cache_fill_copies_the_blob_into_its_slot():
     c.close()
 
 
-def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=None, config=86):
+def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=None, config=86, resize_at=None):
     """Decode `tokens` single-token steps through `layers` layers; returns the
     number of steps checked against the oracle."""
     from fp4_expert_ffn_amd.layer import CachedDecoder, to_numpy_bf16
@@ -74,6 +74,10 @@ def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=N
     checked = 0
     misses = 0
     for t in range(tokens):
+        if resize_at and t in resize_at:
+            say(f"    resize to {resize_at[t]} slots before token {t}")
+            dec.resize(resize_at[t])
+            lru.resize(resize_at[t])
         for l in range(layers):
             out, (te, ts, th, tv) = dec.step(l, x_d[t, l:l + 1], lg_d[t, l:l + 1])
             ids, w = oracle.moe.route(logits[t, l:l + 1], k)
@@ -106,6 +110,19 @@ def test_cached_stream_small_every_step():
         return synth.expert("nvfp4", 256, 256, config=86, layer=l, expert_id=e)
 
     _run_stream(layers=3, E=16, k=4, H=256, I=256, tokens=20, slots=10, make_expert=make)
+
+
+def test_cached_stream_with_resizes():
+    """The 16-expert stream with the cache shrunk from 10 to 5 slots, then grown
+    to 14, between steps: the traces after each resize (which keys stayed, in
+    which slots) equal the oracle LRU's, and every output matches the oracle."""
+    say("cached stream with resizes: 3 layers x 16 NVFP4 experts, 10 -> 5 -> 14 slots, 24 tokens")
+
+    def make(l, e):
+        return synth.expert("nvfp4", 256, 256, config=90, layer=l, expert_id=e)
+
+    _run_stream(layers=3, E=16, k=4, H=256, I=256, tokens=24, slots=10, make_expert=make, config=90,
+                resize_at={8: 5, 16: 14})
 
 
 def test_cached_stream_a3b_shape():

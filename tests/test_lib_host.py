@@ -187,3 +187,14 @@ def test_mxfp4_activations_off_the_persistent_kernel_need_the_combined_output(L)
                      (256, 384, dict(y=0x90000))]:
         with pytest.raises(L.MoeError, match="MXFP4 activations"):
             L.moe_expert_ffn(args(H, I, **kw), 0)
+
+
+def test_cache_resize_rejects_bad_arguments(L):
+    """Argument errors return before any device call (fake pool addresses) and leave the cache unchanged."""
+    c = L.moe_cache_create(4, 1024, 0x100000, 2, 8)
+    for n, pool in [(0, 0x200000), (4, 0), (4, 0x200010), (4, 0x100400), (8, 0x0FF000)]:
+        with pytest.raises(L.MoeError):
+            L.moe_cache_resize(c, n, pool, 0)
+    slot, hit, ev = L.cache_lookup(c, 0, [1, 2, 3, 4])
+    assert list(slot) == [0, 1, 2, 3] and not any(hit)
+    c.close()
