@@ -563,6 +563,22 @@ def bench_stream(args):
     hits, misses, nbytes = dec.stats()
     value = TOKENS / wall
 
+    # a resize to half the slots between steps: the kept (most recent) blobs
+    # are copied device to device, one slot read and written each
+    from fp4_expert_ffn_amd import moe_cache_resize
+    half = SLOTS // 2
+    kept = min(half, SLOTS, misses)
+    new_pool = torch.empty(half * stride, dtype=torch.uint8, device="cuda")
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record()
+    moe_cache_resize(dec.cache, half, new_pool)
+    r1.record()
+    torch.cuda.synchronize()
+    dec.pool = new_pool
+    rs_ms = r0.elapsed_time(r1)
+    rs_gbs = 2 * kept * stride / (rs_ms * 1e-3) / 1e9
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -611,6 +627,9 @@ def bench_stream(args):
         "cache": {"hits": hits, "misses": misses, "hit_rate": round(hit_rate, 4),
                   "hit_rate_tokens_64_511": round(hit_late, 4), "misses_per_token": round(misses / TOKENS, 2),
                   "bytes_filled": nbytes},
+        "resize": {"slots": f"{SLOTS}->{half}", "kept_blobs": kept, "ms": round(rs_ms, 3),
+                   "hbm_GBps": round(rs_gbs, 1), "hbm_frac": round(rs_gbs / 8000.0, 4),
+                   "bytes_per_blob": 2 * stride, "kind": "device-to-device copies of the kept blobs"},
         "cpu_baseline": cpu,
     }
     dec.close()

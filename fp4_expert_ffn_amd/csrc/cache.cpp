@@ -33,6 +33,9 @@ struct moe_cache {
   // per-step scratch of moe_cache_decode_step
   std::vector<int32_t> step_ids, step_slot, step_ev;
   std::vector<uint8_t> step_hit;
+  // copies of the last resize, which a fill into a kept slot must follow
+  hipEvent_t resized = nullptr;
+  int has_resized = 0;
   // last upload from each host slot map: the map is rewritten only after it
   std::vector<std::pair<const void*, hipEvent_t>> map_upload;
 
@@ -92,6 +95,7 @@ extern "C" void moe_cache_destroy(moe_cache* c) {
   for (hipEvent_t e : c->reader) if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->filled) if (e) (void)hipEventDestroy(e);
   for (auto& m : c->map_upload) (void)hipEventDestroy(m.second);
+  if (c->resized) (void)hipEventDestroy(c->resized);
   delete c;
 }
 
@@ -182,6 +186,7 @@ static moe_status ensure_events(moe_cache* c) {
 // are done; records filled[slot].
 static moe_status enqueue_fill(moe_cache* c, int slot, const void* host_src, hipStream_t cs) {
   if (c->has_reader[slot]) MOE_HIP(hipStreamWaitEvent(cs, c->reader[slot], 0));
+  if (c->has_resized) MOE_HIP(hipStreamWaitEvent(cs, c->resized, 0));
   MOE_HIP(hipMemcpyAsync(c->pool + (size_t)slot * c->slot_bytes, host_src, c->slot_bytes, hipMemcpyHostToDevice, cs));
   MOE_HIP(hipEventRecord(c->filled[slot], cs));
   c->bytes_filled += (long long)c->slot_bytes;
@@ -371,8 +376,30 @@ extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe
 
 // ------------------------------------------------------------ resize at a safe point
 
-static void* slot_pool_at(void* pool, int slot, size_t slot_bytes) {
-  return static_cast<uint8_t*>(pool) + (size_t)slot * slot_bytes;
+// Blob moves of one launch: source slot of destination slot dst0 + b, passed
+// by value (the kernel argument segment holds them; no device buffer).
+constexpr int kMoveBatch = 256;
+struct SlotMoves {
+  int32_t src[kMoveBatch];
+};
+
+// Copy blob blockIdx.y of the batch (slot_vecs 16-byte vectors) from its old
+// slot to slot dst0 + blockIdx.y; the x blocks stride over the vectors, four
+// loads in flight per thread.  HBM-bound: one read and one write per byte.
+__global__ __launch_bounds__(256) void k_move_slots(SlotMoves m, int dst0, const uint4* __restrict__ src_pool,
+                                                    uint4* __restrict__ dst_pool, uint32_t slot_vecs) {
+  const uint4* src = src_pool + (size_t)m.src[blockIdx.y] * slot_vecs;
+  uint4* dst = dst_pool + (size_t)(dst0 + blockIdx.y) * slot_vecs;
+  const uint32_t step = gridDim.x * 256u;
+  for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < slot_vecs; v += 4 * step) {
+    uint4 r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (v + j * step < slot_vecs) r[j] = src[v + j * step];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (v + j * step < slot_vecs) dst[v + j * step] = r[j];
+  }
 }
 
 extern "C" moe_status moe_cache_resize(moe_cache* c, int num_slots, void* slot_pool, moe_stream_t stream) {
@@ -380,39 +407,53 @@ extern "C" moe_status moe_cache_resize(moe_cache* c, int num_slots, void* slot_p
   MOE_CHECK_ARG(c->pool, "moe_cache_resize: cache has no slot pool");
   MOE_CHECK_ARG(num_slots > 0, "moe_cache_resize: num_slots %d must be positive", num_slots);
   MOE_CHECK_ARG(((uintptr_t)slot_pool & 255) == 0, "moe_cache_resize: slot_pool must be 256-byte aligned");
+  MOE_CHECK_ARG(((uintptr_t)c->pool & 15) == 0 && c->slot_bytes % 16 == 0 && c->slot_bytes / 16 < (1ull << 31),
+                "moe_cache_resize: slot size and current pool must be multiples of 16 bytes");
   const uint8_t* np = static_cast<const uint8_t*>(slot_pool);
   const size_t nbytes = (size_t)num_slots * c->slot_bytes, obytes = (size_t)c->num_slots * c->slot_bytes;
   MOE_CHECK_ARG(np + nbytes <= c->pool || c->pool + obytes <= np,
                 "moe_cache_resize: the new slot pool overlaps the current one");
   moe_status st = ensure_events(c);
   if (st != MOE_OK) return st;
+  if (!c->resized) MOE_HIP(hipEventCreateWithFlags(&c->resized, hipEventDisableTiming));
   // keys from least to most recent; the least recent beyond num_slots are dropped
   std::vector<int32_t> keys;
   for (int32_t k = c->head; k >= 0; k = c->next[k]) keys.push_back(k);
   const int nkeep = std::min<int>((int)keys.size(), num_slots), ndrop = (int)keys.size() - nkeep;
-  std::vector<hipEvent_t> filled(num_slots, nullptr), reader(num_slots, nullptr);
-  for (int s = 0; s < num_slots; ++s) {
-    MOE_HIP(hipEventCreateWithFlags(&filled[s], hipEventDisableTiming));
-    MOE_HIP(hipEventCreateWithFlags(&reader[s], hipEventDisableTiming));
+  // the slots' events are reused (a stale record only makes a later wait
+  // stricter: readers are reset below, fills are waited for here)
+  for (int s = (int)c->filled.size(); s < num_slots; ++s) {
+    hipEvent_t f = nullptr, r = nullptr;
+    MOE_HIP(hipEventCreateWithFlags(&f, hipEventDisableTiming));
+    c->filled.push_back(f);
+    MOE_HIP(hipEventCreateWithFlags(&r, hipEventDisableTiming));
+    c->reader.push_back(r);
   }
-  // copy each kept blob once its fill has landed; stream order puts the
-  // copies after earlier readers of the old slots queued on `stream`
+  // the copies start once every kept blob's fill has landed (fills still in
+  // flight are waited for; finished ones cost nothing)
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   for (int i = 0; i < nkeep; ++i) {
-    const int32_t s = c->key_slot[keys[ndrop + i]];
-    MOE_HIP(hipStreamWaitEvent(hs, c->filled[s], 0));
-    MOE_HIP(hipMemcpyAsync(slot_pool_at(slot_pool, i, c->slot_bytes), c->pool + (size_t)s * c->slot_bytes,
-                           c->slot_bytes, hipMemcpyDeviceToDevice, hs));
-    MOE_HIP(hipEventRecord(filled[i], hs));
+    hipEvent_t f = c->filled[c->key_slot[keys[ndrop + i]]];
+    if (hipEventQuery(f) != hipSuccess) MOE_HIP(hipStreamWaitEvent(hs, f, 0));
   }
+  const uint32_t vecs = (uint32_t)(c->slot_bytes / 16);
+  const int gx = (int)std::min<uint32_t>(64, (vecs + 1023) / 1024);
+  for (int b0 = 0; b0 < nkeep; b0 += kMoveBatch) {
+    const int n = std::min(kMoveBatch, nkeep - b0);
+    SlotMoves m{};
+    for (int b = 0; b < n; ++b) m.src[b] = c->key_slot[keys[ndrop + b0 + b]];
+    moe::launch(k_move_slots, dim3(gx, n), dim3(256), 0, hs, m, b0, reinterpret_cast<const uint4*>(c->pool),
+                reinterpret_cast<uint4*>(slot_pool), vecs);
+    MOE_HIP(hipGetLastError());
+  }
+  // a later fill into a kept slot (on any stream) must follow the copies
+  MOE_HIP(hipEventRecord(c->resized, hs));
+  c->has_resized = 1;
   for (int i = 0; i < ndrop; ++i) {
     c->unlink(keys[i]);
     c->key_slot[keys[i]] = -1;
   }
-  for (hipEvent_t e : c->reader) (void)hipEventDestroy(e);
-  for (hipEvent_t e : c->filled) (void)hipEventDestroy(e);
-  c->reader.swap(reader);
-  c->filled.swap(filled);
+  // events beyond num_slots are kept for a later growth (destroyed with the cache)
   c->num_slots = num_slots;
   c->pool = static_cast<uint8_t*>(slot_pool);
   c->slot_key.assign(num_slots, -1);

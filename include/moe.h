@@ -299,13 +299,14 @@ moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t c
  * aligned, not overlapping the current pool).  It keeps the min(num_slots,
  * cached) most recently used keys, packed into slots 0, 1, ... from least to
  * most recent with their recency order unchanged, and drops the rest; later
- * misses take the free slots above them, lowest first.  Each kept blob is
- * copied device to device on `stream` after its own fill has landed; work
- * queued on `stream` later sees the new slots, and the fill events of the new
- * slots order other streams after the copies.  The caller may release the old
- * pool once the copies and every earlier reader of it have finished (e.g.
- * after synchronising `stream` when all steps ran on it).  Returns MOE_EINVAL
- * for bad arguments (cache unchanged). */
+ * misses take the free slots above them, lowest first.  The kept blobs are
+ * copied device to device on `stream` (one kernel per 256 blobs) after their
+ * fills have landed.  Later steps must run on `stream` or be ordered after it
+ * by the caller; later fills wait for the copies themselves.  The caller may
+ * release the old pool once the copies and every earlier reader of it have
+ * finished (e.g. after synchronising `stream` when all steps ran on it).  The
+ * slot size and the current pool must be multiples of 16 bytes.  Returns
+ * MOE_EINVAL for bad arguments (cache unchanged). */
 moe_status moe_cache_resize(moe_cache* c, int num_slots, void* slot_pool, moe_stream_t stream);
 
 /* Reset the cache to the empty state (host metadata only). */
