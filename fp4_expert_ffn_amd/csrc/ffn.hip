@@ -92,8 +92,8 @@ moe_status check_args(const moe_ffn_args* a) {
   MOE_CHECK_ARG(!(a->out && a->expert_mask), "moe_expert_ffn: with expert_mask set, run moe_combine separately");
   // Shapes off the persistent FP4 kernel (H % 512 or I % 256 nonzero) run on
   // the 128 x 128 kernel; there, only I >= 256 with the combined output (no
-  // fp32 y) is enabled: a call with I = 128 and fp32 y faulted the GPU and the
-  // cause is not known.
+  // fp32 y) has run on the GPU and is enabled.  The other two forms were first
+  // reached by a cached-prefill call that faulted for a cause not yet known.
   if (a->amode == MOE_ACT_MXFP4 && (a->H % 512 != 0 || a->I % 256 != 0))
     MOE_CHECK_ARG(a->I >= 256 && !a->y && a->out,
                   "moe_expert_ffn: MXFP4 activations with H=%d, I=%d need I >= 256 and the combined output "
