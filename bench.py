@@ -69,46 +69,312 @@ def measured_traffic(workload, root):
     return t.get("bytes_per_launch")
 
 
-class Timer:
-    """HIP events recorded on the stream the library launches on."""
-
-    def __init__(self, torch, stream):
-        self.torch, self.stream = torch, stream
-        self.pairs = []
-
-    def start(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record(self.stream)
-        return e
-
-    def stop(self, s):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record(self.stream)
-        self.pairs.append((s, e))
-
-    def total_ms(self):
-        return sum(a.elapsed_time(b) for a, b in self.pairs)
-
-    def reset(self):
-        self.pairs = []
+def host_cores():
+    return len(os.sched_getaffinity(0))
 
 
 def oracle_baseline(run_one, unit_count, budget_s=12.0):
-    """Time the oracle (as it stands) on a bounded sample; returns (value per second, sample count, threads)."""
+    """Time the oracle (as it stands) on a bounded sample with its BLAS threads
+    set to every host core; returns (value per second, samples, threads, seconds)."""
+    threads = host_cores()
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=threads)
     except Exception:
-        threads = len(os.sched_getaffinity(0))
+        limit = None
     t0 = time.perf_counter()
     n = 0
-    while True:
-        run_one(n)
-        n += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    try:
+        while True:
+            run_one(n)
+            n += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    finally:
+        if limit is not None:
+            limit.unregister()
     dt = time.perf_counter() - t0
     return n * unit_count / dt, n, threads, dt
+
+
+WORKLOADS = {
+    "decode": "decode A3B-like NVFP4 (hidden 2048, 128 experts, top-8, inter 768), batches 1+4+16",
+    "prefill-mxfp4": "prefill A3B-like 4096 tokens, MXFP4 weights x MXFP4 activations",
+    "prefill-bf16": "prefill A3B-like 4096 tokens, BF16 weights",
+    "large-decode": "large-expert layer (hidden 7168, 256+1 shared MXFP4 experts, inter 2048), 1 token",
+    "large-prefill": "large-expert layer, 2048 tokens, MXFP4 activations",
+}
+DTYPES = {"decode": "nvfp4xbf16->f32", "prefill-mxfp4": "mxfp4xmxfp4->f32", "prefill-bf16": "bf16->f32",
+          "large-decode": "mxfp4xbf16->f32", "large-prefill": "mxfp4xmxfp4->f32"}
+
+
+def workload_spec(wl, copies_arg):
+    """(cfg, fmt, amode, batch sizes per step, shared, input groups, weight copies, default steps, warmup).
+
+    Each step is one layer call per batch size.  Call j of unit step i reads
+    weight copy (n_calls * i + j) % copies, so consecutive calls never share a
+    copy and an expert's blob is re-read only after the other copies' calls."""
+    import synth
+    if wl == "decode":
+        inputs = [[synth.decode_batch(T, i) for T in (1, 4, 16)] for i in range(64)]
+        return synth.A3B, "nvfp4", "bf16", [1, 4, 16], False, inputs, copies_arg or 16, 300, 30
+    if wl.startswith("prefill"):
+        fmt = "mxfp4" if wl == "prefill-mxfp4" else "bf16"
+        # two weight copies alternate across calls (the experts' 320 / 1200 MB
+        # exceed the 256 MB last-level cache either way)
+        return synth.A3B, fmt, fmt, [4096], False, [[synth.prefill_batch(4096)]], copies_arg or 2, 20, 3
+    T = 1 if wl == "large-decode" else 2048
+    if T == 1:
+        inputs = [[synth.large_batch(1, batch_index=i)] for i in range(16)]
+        return synth.LARGE, "mxfp4", "bf16", [1], True, inputs, copies_arg or 4, 200, 20
+    return synth.LARGE, "mxfp4", "mxfp4", [2048], True, [[synth.large_batch(2048)]], 1, 10, 2
+
+
+def layer_workload(wl, args, torch, dev, steps=None, warmup=None, cpu_baseline=True):
+    """Set up one per-layer workload, time `steps` steps after `warmup` (one HIP
+    graph each), the dominant kernel's launches and each batch size's layer
+    call; returns the fields of its JSON line."""
+    import synth
+    from fp4_expert_ffn_amd.layer import MoELayer, bf16_tensor, blob_of
+
+    cfg, fmt, amode, batches, shared, inputs, ncopies, dsteps, dwarm = workload_spec(wl, args.copies)
+    steps = dsteps if steps is None else steps
+    warmup = dwarm if warmup is None else warmup
+    E, k, H, I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]
+    Tmax = max(batches)
+    log(f"[bench] workload={wl}: generating experts")
+    t0 = time.perf_counter()
+    if cfg is synth.LARGE:
+        experts = [synth.large_expert(e) for e in range(E)]
+        shared_ex = synth.large_expert(synth.SHARED_EXPERT)
+    else:
+        experts = synth.a3b_experts(fmt, config=1 if wl == "decode" else 2)
+        shared_ex = None
+    blobs = [blob_of(ex) for ex in experts]
+    shared_blob = blob_of(shared_ex) if shared_ex is not None else None
+    log(f"[bench] generated in {time.perf_counter() - t0:.1f}s; uploading {ncopies} weight copies")
+    layers = []
+    for c in range(ncopies):
+        lay = MoELayer(E=E, k=k, H=H, I=I, fmt=fmt, max_tokens=Tmax, device=dev, shared=shared, amode=amode)
+        for e, b in enumerate(blobs):
+            lay.load_expert(e, b)
+        if shared:
+            lay.load_shared(shared_blob)
+        layers.append(lay)
+    del blobs
+
+    # the unit: one step per input group, each call with its own buffers and copy
+    ncalls = len(batches)
+    units = []
+    for i, group in enumerate(inputs):
+        calls = []
+        for j, b in enumerate(group):
+            lay = layers[(ncalls * i + j) % ncopies]
+            T = b["x"].shape[0]
+            x = bf16_tensor(b["x"], dev)
+            lg = torch.from_numpy(b["logits"]).to(dev) if "logits" in b else None
+            wr = torch.from_numpy(b["w_router"]).to(dev) if "w_router" in b else None
+            st = lay.new_state(T)
+            calls.append((T, x, lg, wr, st, st.args(T, x)))
+        units.append(calls)
+    # copies cycle with a period of ncopies calls: extend the unit list to a whole period
+    while (len(units) * ncalls) % ncopies:
+        i = len(units)
+        calls = []
+        for j, (T, x, lg, wr, _, _) in enumerate(units[i % len(inputs)]):
+            st = layers[(ncalls * i + j) % ncopies].new_state(T)
+            calls.append((T, x, lg, wr, st, st.args(T, x)))
+        units.append(calls)
+    U = len(units)
+    toks_per_step = sum(c[0] for c in units[0])
+
+    def run_call(c):
+        T, x, lg, wr, st, a = c
+        st.route(T, x=x, w_router=wr, logits=lg)
+        st.ffn(T, x, args=a)
+
+    def capture(call_lists):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for cl in call_lists:
+                for c in cl:
+                    run_call(c)
+        return g
+
+    # eager pass (library set-up), then one graph per timed region
+    for cl in units:
+        for c in cl:
+            run_call(c)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    g_warm = capture([units[s % U] for s in range(warmup)]) if warmup > 0 else None
+    g_timed = capture([units[(warmup + s) % U] for s in range(steps)])
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {warmup} steps, timing {steps} steps ({U} distinct steps of {ncalls} calls)")
+    if g_warm is not None:
+        g_warm.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    g_timed.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    value = toks_per_step * steps / wall
+
+    # each batch size's layer call: a graph of its U calls, replayed 5 times
+    per_T = {}
+    for j, T in enumerate(batches):
+        g = capture([[cl[j]] for cl in units])
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()  # graph replays run on the current stream
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_T[T] = {"layer_us": round(e0.elapsed_time(e1) * 1e3 / (5 * U), 3)}
+        del g
+
+    # Dominant kernel (the gate/up projection): launch durations from HIP events
+    # recorded at the kernel's own start and end (moe_expert_ffn_traced), over
+    # the unit's calls run eagerly.  Launch order: GEMV path gate/up, down,
+    # combine; FP4 path quantiser, gate/up, down, combine; BF16 matrix-core
+    # path gate/up, down, combine.  The calls are enqueued in batches behind a
+    # spin kernel on the same stream, so the GPU never waits for the host
+    # inside a timed launch.
+    from fp4_expert_ffn_amd import moe_expert_ffn_traced
+    dom = 1 if amode == "mxfp4" else 0
+    stream_now = torch.cuda.current_stream()
+    reps = max(1, -(-64 // U))
+    flat = [c for _ in range(reps) for cl in units for c in cl]
+    clock_hz = 2.4e9
+    recs = []
+    for i in range(0, len(flat), 16):
+        torch.cuda._sleep(int(0.012 * clock_hz))  # about 12 ms of backlog
+        for c in flat[i:i + 16]:
+            T, x, lg, wr, st, a = c
+            st.route(T, x=x, w_router=wr, logits=lg)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+            for e in evs:
+                e.record(stream_now)  # creates the HIP events; re-recorded by the launches
+            n = moe_expert_ffn_traced(a, evs)
+            assert n >= 2 * (dom + 1), n
+            recs.append((c, evs[2 * dom], evs[2 * dom + 1]))
+    torch.cuda.synchronize()
+
+    # algorithmic bytes / flops of the gate/up launch, from the routing each call holds
+    w13 = moe_w13_bytes(fmt, H, I)
+    act = 2 if amode == "bf16" else 0.53125  # bf16, or MXFP4 codes + E8M0 per 32, per value
+    work = {}
+    for cl in units:
+        for c in cl:
+            T, st = c[0], c[4]
+            cn = st.counts.cpu().numpy()
+            rows = int(np.sum(cn)) + (T if shared else 0)
+            active = int(np.count_nonzero(cn)) + (1 if shared else 0)
+            work[id(c)] = (active * w13 + T * H * act + rows * I * act, 2.0 * rows * 2 * I * H)
+    durs, byts, flps = [], [], []
+    byT = {T: ([], [], []) for T in batches}
+    for c, e0, e1 in recs:
+        d = e0.elapsed_time(e1) * 1e-3
+        b, f = work[id(c)]
+        durs.append(d); byts.append(b); flps.append(f)
+        byT[c[0]][0].append(d); byT[c[0]][1].append(b); byT[c[0]][2].append(f)
+    dom_s = sum(durs) / len(durs)
+    bytes_per_launch, flops_per_launch = sum(byts) / len(byts), sum(flps) / len(flps)
+    for T, (d, b, f) in byT.items():
+        ds = sum(d) / len(d)
+        per_T[T]["gateup_us"] = round(ds * 1e6, 3)
+        per_T[T]["gateup_hbm_frac"] = round(sum(b) / len(b) / ds / 1e9 / HBM_PEAK_GBS, 4)
+        if amode == "mxfp4":
+            per_T[T]["gateup_fp4_frac"] = round(sum(f) / len(f) / ds / 1e12 / MFMA_PEAK_TFLOPS["fp4"], 4)
+
+    if wl == "prefill-bf16":
+        kname = "k_fp4_gemm<0, false> (gate/up projection + SwiGLU, bf16 weights on bf16 matrix cores)"
+    elif amode == "mxfp4":
+        kname = "k_fp4_gemm<0, true> (gate/up projection + SwiGLU, FP4 matrix cores)"
+    elif fmt == "nvfp4":
+        kname = "k_gemv (gate/up projection + SwiGLU, NVFP4 weights on fp16 matrix cores)"
+    else:
+        kname = "k_gemv (gate/up projection + SwiGLU, bf16 operands)"
+    # The large-expert prefill sits below the FP4 ridge (about 267 FLOP/B): HBM bounds it.
+    if amode == "mxfp4" and wl != "large-prefill":
+        ach = flops_per_launch / dom_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK_TFLOPS["fp4"], 4)}
+        roof["hbm_gbs_same_kernel"] = round(bytes_per_launch / dom_s / 1e9, 1)
+    else:
+        ach = bytes_per_launch / dom_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+        if fmt == "bf16":
+            roof["bf16_mfma_tflops_same_kernel"] = round(flops_per_launch / dom_s / 1e12, 1)
+        if amode == "mxfp4":
+            roof["fp4_mfma_tflops_same_kernel"] = round(flops_per_launch / dom_s / 1e12, 1)
+    roof["traffic"] = measured_traffic(wl, ROOT)
+    roof["kernel"] = kname
+    roof["avg_launch_us"] = round(dom_s * 1e6, 3)
+    roof["launches_averaged"] = len(durs)
+    roof["algorithmic_bytes_per_launch"] = int(bytes_per_launch)
+    roof["algorithmic_flops_per_launch"] = int(flops_per_launch)
+
+    cpu = None
+    if cpu_baseline:
+        cpu = oracle_cpu_baseline(wl, inputs, units, experts, shared_ex, k, amode, args.cpu_budget)
+    res = {
+        "value": round(value, 2), "steps": steps, "warmup": warmup, "ms_per_step": round(wall / steps * 1e3, 4),
+        "tokens_per_step": toks_per_step, "roofline": roof,
+        "per_batch": {str(T): v for T, v in per_T.items()},
+        "config": {"workload": WORKLOADS[wl], "tokens_per_step": toks_per_step, "experts": E, "top_k": k,
+                   "hidden": H, "intermediate": I, "weights": fmt, "activations": amode,
+                   "hbm_weight_copies": ncopies, "distinct_input_batches": len(inputs),
+                   "parallelism": "single GPU"},
+        "cpu_baseline": cpu,
+    }
+    del g_warm, g_timed, units, layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def oracle_cpu_baseline(wl, inputs, units, experts, shared_ex, k, amode, budget):
+    """The CPU oracle as it stands, timed on a bounded sample of the same workload."""
+    import oracle
+    log("[bench] timing the CPU oracle on a bounded sample")
+    b0 = inputs[0]
+    if wl in ("decode", "large-decode"):
+        sample_tokens = sum(b["x"].shape[0] for b in b0)
+
+        def run_one(n):
+            for b in inputs[n % len(inputs)]:
+                if "logits" in b:
+                    oracle.moe.layer(b["x"], experts, k, logits=b["logits"])
+                else:
+                    oracle.moe.layer(b["x"], experts, k, w_router=b["w_router"], shared=shared_ex)
+        val, n, thr, dt = oracle_baseline(run_one, sample_tokens, budget)
+        return {"value": round(val, 3), "unit": "tokens/s", "cores": thr, "kind": "oracle",
+                "sample": f"{n} oracle layer calls over batches of {[b['x'].shape[0] for b in b0]} tokens "
+                          f"({dt:.1f} s)"}
+    b = b0[0]
+    if "logits" in b:
+        ids, w = oracle.moe.route(b["logits"], k)
+    else:
+        ids, w = oracle.moe.route(units[0][0][4].logits[:b["x"].shape[0]].cpu().numpy(), k)
+    cache = {}
+
+    def wts(e):
+        if e not in cache:
+            cache.clear()
+            cache[e] = oracle.moe.dequant_expert(experts[e])
+        return cache[e]
+    order = np.random.default_rng(0).permutation(b["x"].shape[0])
+    sw = oracle.moe.dequant_expert(shared_ex) if shared_ex is not None else None
+
+    def run_one(n):
+        t = int(order[n % len(order)])
+        oracle.moe.token_output(t, b["x"], ids[t], w[t], wts, shared_weights=sw, amode=amode)
+    val, n, thr, dt = oracle_baseline(run_one, 1, budget)
+    return {"value": round(val, 3), "unit": "tokens/s", "cores": thr, "kind": "oracle",
+            "sample": f"{n} tokens of the {b['x'].shape[0]}-token batch, one by one ({dt:.1f} s)"}
 
 
 def main():
@@ -118,8 +384,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill-mxfp4", "prefill-bf16", "large-decode", "large-prefill", "stream"])
-    ap.add_argument("--copies", type=int, default=8, help="HBM copies of the layer's experts cycled across steps")
+    ap.add_argument("--copies", type=int, default=None, help="HBM copies of the layer's experts, rotated per call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill-leg", action="store_true", help="decode: skip the prefill_mxfp4 leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--stream-tokens", type=int, default=512, help="tokens of the stream workload")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
@@ -140,67 +407,9 @@ def main():
 
     import torch
 
-    import synth
-    from fp4_expert_ffn_amd.layer import MoELayer, bf16_tensor, blob_of
-
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream()
     wl = args.workload
-
-    if wl == "decode":
-        cfg = synth.A3B
-        fmt, amode, batches, shared = "nvfp4", "bf16", [1, 4, 16], False
-        make = lambda: synth.a3b_experts("nvfp4", config=1)
-        steps, warmup = args.steps or 300, args.warmup or 30
-        nb = 64
-        inputs = [[synth.decode_batch(T, i) for T in batches] for i in range(nb)]
-    elif wl.startswith("prefill"):
-        cfg = synth.A3B
-        fmt = "mxfp4" if wl == "prefill-mxfp4" else "bf16"
-        amode, batches, shared = fmt, [4096], False
-        make = lambda: synth.a3b_experts(fmt, config=2)
-        steps, warmup = args.steps or 30, args.warmup or 5
-        nb = 1
-        inputs = [[synth.prefill_batch(4096)]]
-    else:
-        cfg = synth.LARGE
-        fmt, shared = "mxfp4", True
-        T = 1 if wl == "large-decode" else 2048
-        amode = "bf16" if T == 1 else "mxfp4"
-        batches = [T]
-        make = None
-        steps, warmup = args.steps or (200 if T == 1 else 10), args.warmup or (20 if T == 1 else 3)
-        nb = 1
-        inputs = [[synth.large_batch(T)]]
-        args.copies = 1 if T > 1 else min(args.copies, 4)
-
-    E, k, H, I = cfg["E"], cfg["k"], cfg["H"], cfg["I"]
-    Tmax = max(batches)
-    if wl.startswith("prefill"):
-        args.copies = min(args.copies, 2)
-    log(f"[bench] workload={wl}: generating experts")
-    t0 = time.perf_counter()
-    if make is not None:
-        experts = make()
-        shared_ex = None
-    else:
-        experts = [synth.large_expert(e) for e in range(E)]
-        shared_ex = synth.large_expert(synth.SHARED_EXPERT)
-    log(f"[bench] generated in {time.perf_counter() - t0:.1f}s; uploading {args.copies} copies")
-    layers = []
-    blobs = [blob_of(ex) for ex in experts]
-    shared_blob = blob_of(shared_ex) if shared_ex is not None else None
-    for c in range(args.copies):
-        lay = MoELayer(E=E, k=k, H=H, I=I, fmt=fmt, max_tokens=Tmax, device=dev, shared=shared, amode=amode)
-        for e, b in enumerate(blobs):
-            lay.load_expert(e, b)
-        if shared:
-            lay.load_shared(shared_blob)
-        layers.append(lay)
-    blob_bytes = layers[0].blob_bytes
-    del blobs
-
     if args.calibration_copy:
         n = args.calibration_copy << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -210,191 +419,30 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # One "combo" per input batch group: its own routing/output buffers, weights copy i % copies.
-    combos = []
-    for i, group in enumerate(inputs):
-        lay = layers[i % len(layers)]
-        calls = []
-        for b in group:
-            T = b["x"].shape[0]
-            x = bf16_tensor(b["x"], dev)
-            lg = torch.from_numpy(b["logits"]).to(dev) if "logits" in b else None
-            wr = torch.from_numpy(b["w_router"]).to(dev) if "w_router" in b else None
-            st = lay.new_state(T)
-            calls.append((T, x, lg, wr, st, st.args(T, x)))
-        combos.append(calls)
-    n_per_graph = len(combos)
-    toks_per_step = sum(c[0] for c in combos[0])
-
-    def run_full():
-        for calls in combos:
-            for (T, x, lg, wr, st, a) in calls:
-                st.route(T, x=x, w_router=wr, logits=lg)
-                st.ffn(T, x, args=a)
-
-    # eager pass (library set-up, workspace sizing), then capture the sequence as a HIP graph
-    run_full()
-    torch.cuda.synchronize()
-    side = torch.cuda.Stream()
-    g_full = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_full, stream=side):
-        run_full()
-    torch.cuda.synchronize()
-
-    replays = max(1, -(-steps // n_per_graph))
-    steps = replays * n_per_graph
-    wreps = max(1, -(-warmup // n_per_graph))
-    warmup = wreps * n_per_graph
-    log(f"[bench] warmup {warmup} steps, timing {steps} steps ({replays} graph replays of {n_per_graph} steps)")
-    for _ in range(wreps):
-        g_full.replay()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for _ in range(replays):
-        g_full.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    value = toks_per_step * steps / wall
-
-    # Dominant kernel (the gate/up projection): its launch durations from HIP
-    # events recorded at the kernel's own start and end (moe_expert_ffn_traced),
-    # over the same calls run eagerly, the same number of steps.  Launch order:
-    # GEMV path gate/up, down, combine; FP4 path quantiser, gate/up, down,
-    # combine; BF16 matrix-core path gate/up, down, combine.
-    from fp4_expert_ffn_amd import moe_expert_ffn_traced
-    dom = 1 if amode == "mxfp4" else 0
-    stream_now = torch.cuda.current_stream()
-    # The calls are enqueued in batches behind a short spin kernel on the same
-    # stream, so the GPU never waits for the host inside a timed launch (an
-    # eager launch sequence is host-bound, and an idle gap between an event
-    # and its kernel would count as kernel time).
-    flat = [c for _ in range(replays) for calls in combos for c in calls]
-    clock_hz = torch.cuda.get_device_properties(0).clock_rate * 1e3 if hasattr(
-        torch.cuda.get_device_properties(0), "clock_rate") else 2.4e9
-    pairs = []
-    batch = 16
-    for i in range(0, len(flat), batch):
-        torch.cuda._sleep(int(0.012 * clock_hz))  # about 12 ms of backlog
-        for (T, x, lg, wr, st, a) in flat[i:i + batch]:
-            st.route(T, x=x, w_router=wr, logits=lg)
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
-            for e in evs:
-                e.record(stream_now)  # creates the HIP events; re-recorded by the launches
-            n = moe_expert_ffn_traced(a, evs)
-            assert n >= 2 * (dom + 1), n
-            pairs.append((evs[2 * dom], evs[2 * dom + 1]))
-    torch.cuda.synchronize()
-    durs = [e0.elapsed_time(e1) for e0, e1 in pairs]
-    dom_ms = sum(durs) / len(durs)
-
-    # algorithmic bytes / flops of the dominant kernel (gate/up projection + SwiGLU),
-    # per launch, from the routing each call holds
-    w13_bytes = moe_w13_bytes(fmt, H, I)
-    tot_bytes, tot_flops, n_calls = 0, 0.0, 0
-    for calls in combos:
-        for (T, x, lg, wr, st, a) in calls:
-            cn = st.counts.cpu().numpy()
-            rows = int(np.sum(cn)) + (T if shared else 0)
-            active = int(np.count_nonzero(cn)) + (1 if shared else 0)
-            act = 2 if amode == "bf16" else 0.53125  # bf16, or MXFP4 codes + E8M0 per 32, per value
-            tot_bytes += active * w13_bytes + T * H * act + rows * I * act
-            tot_flops += 2.0 * rows * 2 * I * H
-            n_calls += 1
-    bytes_per_launch = tot_bytes / n_calls
-    flops_per_launch = tot_flops / n_calls
-    kname = {"bf16": "k_gemv (gate/up projection + SwiGLU, bf16 operands)",
-             "mxfp4": "k_fp4_gemm<0, true> (gate/up projection + SwiGLU, FP4 matrix cores)"}[amode]
-    if wl.startswith("prefill-bf16"):
-        kname = "k_fp4_gemm<0, false> (gate/up projection + SwiGLU, bf16 weights on bf16 matrix cores)"
-    elif fmt == "nvfp4":
-        kname = "k_gemv (gate/up projection + SwiGLU, NVFP4 weights on fp16 matrix cores)"
-    # The large-expert prefill sits below the FP4 ridge (about 267 FLOP/B): HBM bounds it.
-    if amode == "mxfp4" and wl != "large-prefill":
-        ach = flops_per_launch / (dom_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_PEAK_TFLOPS["fp4"], 4)}
-        roof["hbm_gbs_same_kernel"] = round(bytes_per_launch / (dom_ms * 1e-3) / 1e9, 1)
-    else:
-        ach = bytes_per_launch / (dom_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4)}
-        if fmt == "bf16":
-            roof["bf16_mfma_tflops_same_kernel"] = round(flops_per_launch / (dom_ms * 1e-3) / 1e12, 1)
-        if amode == "mxfp4":
-            roof["fp4_mfma_tflops_same_kernel"] = round(flops_per_launch / (dom_ms * 1e-3) / 1e12, 1)
-    roof["traffic"] = measured_traffic(wl, ROOT)
-    roof["kernel"] = kname
-    roof["avg_launch_us"] = round(dom_ms * 1e3, 3)
-    roof["launches_averaged"] = len(durs)
-    roof["algorithmic_bytes_per_launch"] = int(bytes_per_launch)
-    roof["algorithmic_flops_per_launch"] = int(flops_per_launch)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        log("[bench] timing the CPU oracle on a bounded sample")
-        b0 = inputs[0]
-        sample_tokens = sum(b["x"].shape[0] for b in b0)
-        if wl == "decode" or wl == "large-decode":
-            def run_one(n):
-                for b in inputs[n % len(inputs)]:
-                    if "logits" in b:
-                        oracle.moe.layer(b["x"], experts, k, logits=b["logits"])
-                    else:
-                        oracle.moe.layer(b["x"], experts, k, w_router=b["w_router"], shared=shared_ex)
-            val, n, thr, dt = oracle_baseline(run_one, sample_tokens, args.cpu_budget)
-            cpu = {"value": round(val, 3), "unit": "tokens/s", "cores": thr, "kind": "oracle",
-                   "sample": f"{n} oracle layer calls over batches of {[b['x'].shape[0] for b in b0]} tokens "
-                             f"({dt:.1f} s)"}
-        else:
-            b = b0[0]
-            ids, w = oracle.moe.route(b["logits"], k) if "logits" in b else (None, None)
-            if ids is None:
-                ids, w = oracle.moe.route(combos[0][0][4].logits[:b["x"].shape[0]].cpu().numpy(), k)
-            cache = {}
-
-            def wts(e):
-                if e not in cache:
-                    cache.clear()
-                    cache[e] = oracle.moe.dequant_expert(experts[e])
-                return cache[e]
-            rng = np.random.default_rng(0)
-            order = rng.permutation(b["x"].shape[0])
-            sw = oracle.moe.dequant_expert(shared_ex) if shared_ex is not None else None
-
-            def run_one(n):
-                t = int(order[n % len(order)])
-                oracle.moe.token_output(t, b["x"], ids[t], w[t], wts, shared_weights=sw, amode=amode)
-            val, n, thr, dt = oracle_baseline(run_one, 1, args.cpu_budget)
-            cpu = {"value": round(val, 3), "unit": "tokens/s", "cores": thr, "kind": "oracle",
-                   "sample": f"{n} tokens of the {b['x'].shape[0]}-token batch, one by one ({dt:.1f} s)"}
-
-    names = {"decode": "decode A3B-like NVFP4 (hidden 2048, 128 experts, top-8, inter 768), batches 1+4+16",
-             "prefill-mxfp4": "prefill A3B-like 4096 tokens, MXFP4 weights x MXFP4 activations",
-             "prefill-bf16": "prefill A3B-like 4096 tokens, BF16 weights",
-             "large-decode": "large-expert layer (hidden 7168, 256+1 shared MXFP4 experts, inter 2048), 1 token",
-             "large-prefill": "large-expert layer, 2048 tokens, MXFP4 activations"}
+    r = layer_workload(wl, args, torch, dev, args.steps, args.warmup, cpu_baseline=not args.no_cpu_baseline)
     line = {
         "metric": "MoE-layer tokens/s",
-        "value": round(value, 2),
+        "value": r["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": warmup,
-        "ms_per_step": round(wall / steps * 1e3, 4),
+        "steps": r["steps"],
+        "warmup": r["warmup"],
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"decode": "nvfp4xbf16->f32", "prefill-mxfp4": "mxfp4xmxfp4->f32", "prefill-bf16": "bf16->f32",
-                  "large-decode": "mxfp4xbf16->f32", "large-prefill": "mxfp4xmxfp4->f32"}[wl],
+        "dtype": DTYPES[wl],
         "data": "synthetic (seeded; weights N(0,0.02) quantised, activations N(0,1) bf16, Zipf(1.1) routing)",
-        "config": {"workload": names[wl], "tokens_per_step": toks_per_step, "experts": E, "top_k": k,
-                   "hidden": H, "intermediate": I, "weights": fmt, "hbm_copies": len(layers),
-                   "parallelism": "single GPU"},
-        "roofline": roof,
-        "layer_ms_per_call": round(wall / (replays * n_calls) * 1e3, 4),
-        "cpu_baseline": cpu,
+        "config": r["config"],
+        "roofline": r["roofline"],
+        "per_batch": r["per_batch"],
+        "cpu_baseline": r["cpu_baseline"],
     }
+    if wl == "decode" and not args.no_prefill_leg:
+        p = layer_workload("prefill-mxfp4", args, torch, dev, cpu_baseline=False)
+        line["prefill_mxfp4"] = {"metric": "MoE-layer tokens/s", "value": p["value"], "unit": "tokens/s",
+                                 "steps": p["steps"], "warmup": p["warmup"], "ms_per_step": p["ms_per_step"],
+                                 "dtype": DTYPES["prefill-mxfp4"], "config": p["config"], "roofline": p["roofline"]}
     print(json.dumps(line))
 
 
@@ -475,6 +523,27 @@ def summarize(args):
     raise SystemExit(f"unknown summary kind {kind}")
 
 
+def stream_trace_verdict(n, e, h, s, v, E, tokens, layers, slots):
+    """SHA-256 of the stream's cache records (per step: the int32 count, then
+    (expert, hit, slot, evicted key) int32 records, little endian) and whether
+    it equals the oracle's, stored in tests/golden by make_stream_trace.py
+    for the real-size stream (48 layers, 2048 slots, 512 tokens)."""
+    import hashlib
+    dg = hashlib.sha256()
+    for i in range(n.size):
+        c = int(n[i])
+        dg.update(np.array([c], dtype="<i4").tobytes())
+        dg.update(np.stack([e[i, :c], h[i, :c].astype(np.int32), s[i, :c], v[i, :c]], axis=1).astype("<i4").tobytes())
+    out = {"sha256": dg.hexdigest(), "steps": int(n.size), "lookups": int(n.sum()), "matches_oracle": None}
+    path = os.path.join(ROOT, "tests", "golden", f"stream_trace_a3b_{layers}x{slots}x{tokens}.txt")
+    if E == 128 and os.path.exists(path):
+        with open(path) as f:
+            ref = dict(ln.split() for ln in f if ln.strip() and not ln.startswith("#"))
+        out["oracle_sha256"] = ref["sha256"]
+        out["matches_oracle"] = ref["sha256"] == out["sha256"]
+    return out
+
+
 def bench_stream(args):
     """Cached decode stream: tokens/s of 512 single-token steps through 48 layers."""
     import concurrent.futures as cf
@@ -542,26 +611,41 @@ def bench_stream(args):
     torch.cuda.synchronize()
     h2d_peak = n_cp * stride / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
 
-    def run(t0_, t1_):
+    # every step's cache records land in preallocated host arrays (row t * LAYERS + l)
+    NS = TOKENS * LAYERS
+    tr_e, tr_s, tr_v = (np.zeros((NS, E), np.int32) for _ in range(3))
+    tr_h = np.zeros((NS, E), np.uint8)
+    tr_n = np.zeros(NS, np.int32)
+    bases = (tr_e.ctypes.data, tr_s.ctypes.data, tr_h.ctypes.data, tr_v.ctypes.data)
+
+    def run(t0_, t1_, record):
         for t in range(t0_, t1_):
             for l in range(LAYERS):
-                dec.step_fast(l, x_d[t, l:l + 1], lg_d[t, l:l + 1], sh)
+                if record:
+                    i = t * LAYERS + l
+                    ptrs = (bases[0] + 4 * E * i, bases[1] + 4 * E * i, bases[2] + E * i, bases[3] + 4 * E * i)
+                    tr_n[i] = dec.step_fast(l, x_d[t, l:l + 1], lg_d[t, l:l + 1], sh, ptrs)
+                else:
+                    dec.step_fast(l, x_d[t, l:l + 1], lg_d[t, l:l + 1], sh)
 
     log(f"[bench] warmup {warm_tokens} tokens, then {TOKENS} tokens from a cold cache")
-    run(0, warm_tokens)
+    run(0, warm_tokens, False)
     torch.cuda.synchronize()
     dec.reset()
     t_start = time.perf_counter()
     n64 = min(64, TOKENS)
-    run(0, n64)
+    run(0, n64, True)
     torch.cuda.synchronize()
     h64, m64, _ = dec.stats()
     log(f"[bench]   {n64} tokens in {time.perf_counter() - t_start:.2f} s")
-    run(n64, TOKENS)
+    run(n64, TOKENS, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     hits, misses, nbytes = dec.stats()
     value = TOKENS / wall
+    trace = stream_trace_verdict(tr_n, tr_e, tr_h, tr_s, tr_v, E, TOKENS, LAYERS, SLOTS)
+    log(f"[bench] trace of {NS} steps: sha256 {trace['sha256'][:16]}..., matches the oracle's: "
+        f"{trace['matches_oracle']}")
 
     # a resize to half the slots between steps: the kept (most recent) blobs
     # are copied device to device, one slot read and written each
@@ -624,6 +708,7 @@ def bench_stream(args):
                      "frac": round(h2d / h2d_peak, 4), "traffic": None,
                      "kernel": "hipMemcpyAsync pinned host -> HBM slot (miss fills)",
                      "peak_source": f"measured: one {n_cp}-slot pinned copy on the copy stream"},
+        "trace": trace,
         "cache": {"hits": hits, "misses": misses, "hit_rate": round(hit_rate, 4),
                   "hit_rate_tokens_64_511": round(hit_late, 4), "misses_per_token": round(misses / TOKENS, 2),
                   "bytes_filled": nbytes},

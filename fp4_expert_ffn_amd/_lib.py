@@ -75,6 +75,7 @@ SIGNATURES = {
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "moe_quantize_mxfp4": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
     "moe_dequant_blob": (_i, [_vp, _i, _vp, _vp]),
+    "moe_debug_fp4_codes": (_i, [ctypes.POINTER(FfnArgs), _i, _vp, _vp, _vp]),
     "moe_cache_create": (_vp, [_i, _sz, _vp, _i, _i]),
     "moe_cache_destroy": (None, [_vp]),
     "cache_lookup": (_i, [_vp, _i, _vp, _i, _vp, _vp, _vp]),
@@ -232,6 +233,11 @@ def moe_combine(y, inv, topk_w, y_shared, T, k, H, out, stream=None):
 
 def moe_quantize_mxfp4(x, rows, cols, q, s, stream=None):
     _check(lib().moe_quantize_mxfp4(ptr(x), rows, cols, ptr(q), ptr(s), stream_handle(stream)), "moe_quantize_mxfp4")
+
+
+def moe_debug_fp4_codes(args: FfnArgs, which, q, s, stream=None):
+    _check(lib().moe_debug_fp4_codes(ctypes.byref(args), int(which), ptr(q), ptr(s), stream_handle(stream)),
+           "moe_debug_fp4_codes")
 
 
 def moe_dequant_blob(blob, which, out, stream=None):

@@ -13,6 +13,8 @@ namespace moe {
 hipError_t launch_gemv(const FfnParams& P, const GemvArgs& G, hipStream_t s);
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s);
 hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st);
+hipError_t launch_fp4_codes_canon(const FfnParams& P, const MfmaBufs& B, int which, uint8_t* q, uint8_t* s,
+                                  hipStream_t st);
 }  // namespace moe
 
 namespace {
@@ -90,14 +92,13 @@ moe_status check_args(const moe_ffn_args* a) {
                 "moe_expert_ffn: null input pointer");
   MOE_CHECK_ARG(!a->out || (a->topk_w && a->inv), "moe_expert_ffn: out needs topk_w and inv");
   MOE_CHECK_ARG(!(a->out && a->expert_mask), "moe_expert_ffn: with expert_mask set, run moe_combine separately");
-  // Shapes off the persistent FP4 kernel (H % 512 or I % 256 nonzero) run on
-  // the 128 x 128 kernel; there, only I >= 256 with the combined output (no
-  // fp32 y) has run on the GPU and is enabled.  The other two forms were first
-  // reached by a cached-prefill call that faulted for a cause not yet known.
-  if (a->amode == MOE_ACT_MXFP4 && (a->H % 512 != 0 || a->I % 256 != 0))
-    MOE_CHECK_ARG(a->I >= 256 && !a->y && a->out,
-                  "moe_expert_ffn: MXFP4 activations with H=%d, I=%d need I >= 256 and the combined output "
-                  "(y null, out set)", a->H, a->I);
+  // The matrix-core kernels address their operand rows (x, the SwiGLU
+  // output, their MXFP4 encodings) with 32-bit byte offsets.
+  if (choose_path(a) != kPathGemv) {
+    const long long R = (long long)a->T * a->k + (a->shared_blob ? a->T : 0);
+    MOE_CHECK_ARG(R * 2 * std::max(a->H, a->I) < (1LL << 32),
+                  "moe_expert_ffn: %lld rows of H=%d / I=%d bf16 values exceed 4 GiB", R, a->H, a->I);
+  }
   const WsLayout w = ws_layout(a);
   if (a->workspace_bytes < w.total || (w.total && !a->workspace))
     return set_error(MOE_ENOMEM, "moe_expert_ffn: workspace %zu bytes < %zu needed", a->workspace_bytes, w.total);
@@ -225,10 +226,8 @@ extern "C" size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a) {
   return ws_layout(a).total;
 }
 
-extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream) {
-  moe_status st = check_args(a);
-  if (st != MOE_OK || a->T == 0) return st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+namespace {
+FfnParams params_of(const moe_ffn_args* a) {
   FfnParams P{};
   P.T = a->T; P.k = a->k; P.E = a->E; P.H = a->H; P.I = a->I; P.fmt = a->wfmt;
   P.x = a->x; P.counts = a->counts; P.offsets = a->offsets; P.perm = a->perm; P.inv = a->inv;
@@ -239,6 +238,15 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
   P.mask = a->expert_mask;
   layout_of(a->wfmt, a->H, a->I, &P.L);
   P.umax = (int)std::min<long long>(a->E, (long long)a->T * a->k);
+  return P;
+}
+}  // namespace
+
+extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream) {
+  moe_status st = check_args(a);
+  if (st != MOE_OK || a->T == 0) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  FfnParams P = params_of(a);
 
   const WsLayout w = ws_layout(a);
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
@@ -280,6 +288,24 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     e = launch_combine(y, yflat ? nullptr : a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
     if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));
     }
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_debug_fp4_codes(const moe_ffn_args* a, int which, uint8_t* q, uint8_t* s,
+                                          moe_stream_t stream) {
+  moe_status st = check_args(a);
+  if (st != MOE_OK) return st;
+  MOE_CHECK_ARG(a->amode == MOE_ACT_MXFP4, "moe_debug_fp4_codes: the call has no MXFP4 activations");
+  MOE_CHECK_ARG(which == 0 || which == 1, "moe_debug_fp4_codes: which must be 0 (x) or 1 (SwiGLU output)");
+  if (a->T == 0) return MOE_OK;
+  MOE_CHECK_ARG(q && s && ((uintptr_t)q & 15) == 0, "moe_debug_fp4_codes: q (16-byte aligned) and s are required");
+  const FfnParams P = params_of(a);
+  const WsLayout w = ws_layout(a);
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  MfmaBufs B{};
+  B.xq = ws + w.xq; B.xs = ws + w.xs; B.hq = ws + w.hq; B.hs = ws + w.hs;
+  hipError_t e = launch_fp4_codes_canon(P, B, which, q, s, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return set_error(MOE_EHIP, "moe_debug_fp4_codes: launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }
 

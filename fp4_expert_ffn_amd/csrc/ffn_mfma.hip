@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "ffn_common.h"
+#include "mfma_addr.h"
 #include "wave.h"
 
 namespace moe {
@@ -225,46 +226,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Operand A: thread t stages 16-byte segment t % 8 of rows t / 8 + 32 i
   // (i < 4), so a wave reads eight whole 128-byte row segments per load.
   // Rows past the tile are clamped for the address and zeroed after the load.
-  // 32-bit byte offsets from one base pointer (the operand buffers are far
-  // below 4 GiB) keep the per-stage address state small.
+  // 32-bit byte offsets from one base pointer (the launcher bounds every
+  // operand buffer below 4 GiB) keep the per-stage address state small; the
+  // offsets come from mfma_addr.h.
   const uint8_t* abase = MODE == kGateUp ? (FP4 ? B.xq : reinterpret_cast<const uint8_t*>(P.x))
                                          : (FP4 ? B.hq : reinterpret_cast<const uint8_t*>(B.hb));
   const uint32_t arow_bytes = FP4 ? K / 2 : K * 2;
   uint32_t aoff[4];
   uint32_t avalid = 0;  // bit i: row (tid / 8) + 32 i is inside the tile
   const int seg = tid & 7;
+  // the buffer row of tile row r: the token (gate/up) or the permutation-order row (down)
+  auto src_row_of = [&](int r) -> uint32_t {
+    if (MODE == kGateUp) return tj.shared ? tj.m0 + r : P.perm[tj.p0 + tj.m0 + r] / P.k;
+    return tj.p0 + tj.m0 + r;
+  };
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (tid >> 3) + 32 * i;
     if (row < tj.rows) avalid |= 1u << i;
-    const int r = row < tj.rows ? row : 0;
-    uint32_t src_row;
-    if (MODE == kGateUp) src_row = tj.shared ? tj.m0 + r : P.perm[tj.p0 + tj.m0 + r] / P.k;
-    else src_row = tj.p0 + tj.m0 + r;
-    aoff[i] = src_row * arow_bytes + seg * 16;
+    aoff[i] = mfma_a_base(src_row_of(row < tj.rows ? row : 0), arow_bytes, tid);
   }
   // FP4 A scales: 8 bytes (the step's eight 32-blocks) of row tid / 2, half tid % 2.
-  const uint8_t* asrow = nullptr;
-  uint32_t askeep = 0;
+  const uint8_t* asbase = MODE == kGateUp ? B.xs : B.hs;
+  uint32_t as_off = 0, askeep = 0;
   if (FP4) {
     const int row = tid >> 1;
     askeep = row < tj.rows ? 0xFFFFFFFFu : 0u;
-    const int r = row < tj.rows ? row : 0;
-    if (MODE == kGateUp) {
-      const int t = tj.shared ? tj.m0 + r : P.perm[tj.p0 + tj.m0 + r] / P.k;
-      asrow = B.xs + (size_t)t * (P.H / 32);
-    } else {
-      asrow = B.hs + ((size_t)tj.p0 + tj.m0 + r) * (P.I / 32);
-    }
-    asrow += (tid & 1) * 4;
+    as_off = mfma_sa_base(src_row_of(row < tj.rows ? row : 0), (uint32_t)K / 32, tid);
   }
   // Operand B: chunk c = t + 256 i is lane c % 64 of weight tile (row group
-  // c / 128, K-tile (c / 64) % 2 of the step); LDS holds it at c * 16.
-  // (row group c / 128 and K-tile (c / 64) % 2 of chunk c = tid + 256 i)
-  const uint32_t b_off0 = ((uint32_t)(rg0 + (tid >> 7)) * nk_w + ((tid >> 6) & 1)) * kTileBytes + (tid & 63) * 16;
-  const uint32_t b_rg2 = 2u * nk_w * kTileBytes;  // chunk i adds 2 i row groups
+  // rg0 + c / 128, K-tile (c / 64) % 2 of the step); LDS holds it at c * 16.
   // FP4 B scales: dword t of the step's 16 scale tiles (64 bytes each).
-  const size_t bs_off = ((size_t)(rg0 + (tid >> 5)) * nk_w + ((tid >> 4) & 1)) * 64 + (tid & 15) * 4;
+  const uint32_t bs_off = mfma_sb_base(rg0, nk_w, tid);
 
   struct Stage {
     uint4 a[4], b[4];
@@ -279,15 +272,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool tail = half_tail && ks == nsteps - 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int back_a = (tail && seg >= 4) ? 64 : 0;
-      const int back_b = (tail && ((tid + 256 * i) >> 6 & 1)) ? kTileBytes : 0;
-      S.a[i] = *reinterpret_cast<const uint4*>(abase + aoff[i] + (uint32_t)(ks * 128 - back_a));
-      S.b[i] = *reinterpret_cast<const uint4*>(wt + b_off0 + i * b_rg2 + (uint32_t)(ks * 2 * kTileBytes - back_b));
+      S.a[i] = *reinterpret_cast<const uint4*>(abase + mfma_step_off(aoff[i], ks, 128u, mfma_a_back(tid, tail)));
+      S.b[i] = *reinterpret_cast<const uint4*>(
+          wt + mfma_step_off(mfma_b_base(rg0, nk_w, tid, i), ks, 2u * kTileBytes, mfma_b_back(tid, tail)));
     }
     if (FP4) {
-      const int back_sa = (tail && (tid & 1)) ? 4 : 0, back_sb = (tail && (tid >> 4 & 1)) ? 64 : 0;
-      S.sa = *reinterpret_cast<const uint32_t*>(asrow + (size_t)ks * 8 - back_sa);
-      S.sb = *reinterpret_cast<const uint32_t*>(st + bs_off + (size_t)ks * 2 * 64 - back_sb);
+      S.sa = *reinterpret_cast<const uint32_t*>(asbase + mfma_step_off(as_off, ks, 8u, mfma_sa_back(tid, tail)));
+      S.sb = *reinterpret_cast<const uint32_t*>(st + mfma_step_off(bs_off, ks, 128u, mfma_sb_back(tid, tail)));
     }
   };
   auto store_stage = [&](const Stage& S, uint8_t* buf, int ks) {
@@ -491,10 +482,53 @@ hipError_t launch_bf16_gemm(const FfnParams& P, const MfmaBufs& B, bool down, hi
 // on the 128 x 128 one (on the FP4 path the two store x and the SwiGLU output
 // in different layouts).  FP4: x MXFP4-encoded first (per token, into its
 // destination rows for the persistent kernel).
+bool fp4_persistent(const FfnParams& P) {
+  return fp4_gemm_fits(P, 2 * P.I, P.H, true) && fp4_gemm_fits(P, P.H, P.I, false);
+}
+
+// Copies the MXFP4 encoding of x (which = 0) or of the SwiGLU output (1) left
+// in the workspace by an FP4 call into canonical layout: q [R][K/2], s [R][K/32]
+// with row p = permutation-order row p (token perm[p] / k), rows T*k.. the
+// shared expert's tokens.  One thread per 16 code bytes (and 4 scale bytes)
+// of a row.  persistent: the workspace holds [K/128][R][64 B] and
+// [K/128][R][4 B]; else x is token-ordered [T][K/2], [T][K/32] and h is
+// already canonical.
+__global__ __launch_bounds__(256) void k_fp4_codes_canon(const uint8_t* __restrict__ wq,
+                                                         const uint8_t* __restrict__ ws, int persistent, int is_x,
+                                                         const int32_t* __restrict__ perm, int T, int k, int R,
+                                                         int K, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int chunks = K / 32;  // 16 code bytes and 1 scale byte per 32 values
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (long long)R * chunks) return;
+  const int r = (int)(g / chunks), c = (int)(g % chunks);
+  long long src_q, src_s;
+  if (persistent) {
+    const int kt = c >> 2, j = c & 3;
+    src_q = ((long long)kt * R + r) * 64 + j * 16;
+    src_s = ((long long)kt * R + r) * 4 + j;
+  } else {
+    const int row = (is_x && r < T * k) ? perm[r] / k : (is_x ? r - T * k : r);
+    src_q = (long long)row * (K / 2) + c * 16;
+    src_s = (long long)row * (K / 32) + c;
+  }
+  *reinterpret_cast<uint4*>(q + (size_t)r * (K / 2) + c * 16) = *reinterpret_cast<const uint4*>(wq + src_q);
+  s[(size_t)r * (K / 32) + c] = ws[src_s];
+}
+
+hipError_t launch_fp4_codes_canon(const FfnParams& P, const MfmaBufs& B, int which, uint8_t* q, uint8_t* s,
+                                  hipStream_t st) {
+  const int R = P.T * P.k + (P.shared_blob ? P.T : 0), K = which == 0 ? P.H : P.I;
+  const long long n = (long long)R * (K / 32);
+  if (n == 0) return hipSuccess;
+  launch(k_fp4_codes_canon, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, which == 0 ? B.xq : B.hq,
+         which == 0 ? B.xs : B.hs, fp4_persistent(P) ? 1 : 0, which == 0 ? 1 : 0, P.perm, P.T, P.k, R, K, q, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s) {
   hipError_t e;
   if (fp4) {
-    if (fp4_gemm_fits(P, 2 * P.I, P.H, true) && fp4_gemm_fits(P, P.H, P.I, false)) {
+    if (fp4_persistent(P)) {
       const int n = P.T * P.k;
       const uint32_t rtot = (uint32_t)n + (P.shared_blob ? P.T : 0);
       const int32_t* inv = P.inv;

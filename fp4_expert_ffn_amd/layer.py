@@ -85,6 +85,7 @@ class LayerState:
         assert T <= self.max_tokens
         self.route(T, x=x, w_router=w_router, logits=logits, stream=stream)
         self.ffn(T, x, stream)
+        self.last_x = x
         return self.out[:T]
 
 
@@ -162,6 +163,7 @@ class CachedDecoder:
         self.y = torch.empty((T * k, H), dtype=torch.float32, device=self.dev)
         self.out = torch.empty((T, H), dtype=torch.int16, device=self.dev)
         self.trace = [np.empty(E, np.int32), np.empty(E, np.int32), np.empty(E, np.uint8), np.empty(E, np.int32)]
+        self._trace_ptrs = tuple(t.ctypes.data for t in self.trace)
         self._steps = {}
         self._ws = None
 
@@ -201,15 +203,21 @@ class CachedDecoder:
         assert T <= self.max_tokens
         out = self.out[:T] if out is None else out
         st = self._step(layer, T, x, logits, out)
+        st.trace_expert, st.trace_slot, st.trace_hit, st.trace_evicted = self._trace_ptrs
         L.moe_cache_decode_step(self.cache, st, self.copy_stream, stream)
         n = st.n_experts
         return out, tuple(t[:n].copy() for t in self.trace)
 
-    def step_fast(self, layer, x, logits, stream_handle):
-        """step() without the trace copies (stream_handle: raw hipStream_t of the compute stream)."""
+    def step_fast(self, layer, x, logits, stream_handle, trace=None):
+        """step() without copying the trace back (stream_handle: raw hipStream_t
+        of the compute stream).  trace: None, or four host addresses (expert,
+        slot, hit, evicted-key arrays of capacity E) that receive this step's
+        records.  Returns the step's number of distinct experts."""
         T = x.shape[0]
         st = self._step(layer, T, x, logits, self.out[:T])
+        st.trace_expert, st.trace_slot, st.trace_hit, st.trace_evicted = trace or self._trace_ptrs
         L.moe_cache_decode_step(self.cache, st, self.copy_stream, stream_handle)
+        return st.n_experts
 
     def stats(self):
         return L.moe_cache_stats(self.cache)

@@ -83,7 +83,11 @@ moe_status moe_route(const float* logits, int T, int E, int k, int renormalize,
                      int32_t* topk_ids, float* topk_w, moe_stream_t stream);
 
 /* Token -> expert permutation: a stable counting sort of the T*k flat
- * indices f = t*k + j by expert id (ties in ascending f).
+ * indices f = t*k + j by expert id (ties in ascending f), so that the rows
+ * every expert processes are contiguous.
+ * [page "FreeToken量子化：MoE推論のセットアップガイド", 2nd paragraph: each
+ *  token passes through only a few of the experts, so the work of a step is
+ *  grouped per expert; the stable order is this library's reading.]
  * counts: [E]; offsets: [E+1] (exclusive scan, offsets[E] = T*k);
  * perm: [T*k] (perm[p] = flat index at sorted position p);
  * inv: [T*k] (inv[perm[p]] = p).  topk_ids values must lie in [0, E).
@@ -118,11 +122,20 @@ typedef struct {
   const void* down_q; const uint8_t* down_s; float down_g;
 } moe_expert_canonical;
 
-/* Bytes of one expert blob for (fmt, H, I); 0 if the shape is unsupported. */
+/* Bytes of one expert blob for (fmt, H, I); 0 if the shape is unsupported.
+ * [page "FreeToken量子化：...", 3rd paragraph: MXFP4, NVFP4 and BF16 expert
+ *  checkpoints; paragraph on the two-tier expert memory hierarchy: every
+ *  routed expert is held in host RAM and copied whole into a GPU cache slot,
+ *  so one expert is one fixed-size blob.]  H and I must be multiples of 128
+ *  (this library's tile width; every shape the pages name satisfies it). */
 size_t moe_blob_bytes(int fmt, int H, int I);
 
 /* Host-side prepack of one expert into blob_out (host, >= moe_blob_bytes).
- * A bijection of the canonical tensors (round-trip tested). */
+ * A bijection of the canonical tensors (round-trip tested).
+ * [pages as for moe_blob_bytes: the blob is what host RAM holds and what a
+ *  cache fill copies; the tile order inside it is this library's.]
+ * Returns MOE_EINVAL for a null pointer, a bad format or shape, or
+ * blob_bytes < moe_blob_bytes(fmt, H, I). */
 moe_status moe_prepack_expert(const moe_expert_canonical* src, void* blob_out, size_t blob_bytes);
 
 /* Arguments of one expert-FFN call (SwiGLU: y = W_down (silu(W_gate x) * (W_up x))).
@@ -134,9 +147,7 @@ typedef struct {
   int amode;                    /* MOE_ACT_BF16: activations stay bf16 / fp32.
                                    MOE_ACT_MXFP4 (wfmt MXFP4 only): x and the SwiGLU output
                                    are MXFP4-encoded per row per 32 values and the products
-                                   run on the block-scaled FP4 matrix cores.  Unless
-                                   H % 512 == 0 and I % 256 == 0, it needs I >= 256, y
-                                   null and out set (MOE_EINVAL otherwise).                */
+                                   run on the block-scaled FP4 matrix cores.             */
   const uint16_t* x;            /* [T,H] bf16                                            */
   const int32_t* counts;        /* [E]    from moe_permute                               */
   const int32_t* offsets;       /* [E+1]  from moe_permute                               */
@@ -170,7 +181,13 @@ size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a);
  * expert).  Small batches run a dequantising GEMV that streams each touched
  * expert's weights once; large batches run a grouped GEMM on the matrix cores
  * (bf16 MFMA for BF16 weights, block-scaled FP4 MFMA for MXFP4 with amode
- * MXFP4).  Requires H, I multiples of 128, 1 <= k <= 16, E <= 1024. */
+ * MXFP4).  Requires H, I multiples of 128 (this library's tile width; the
+ * formats themselves need multiples of 32), 1 <= k <= 16, E <= 1024, T*k <=
+ * 131072, and on the matrix-core paths R * max(H, I) * 2 < 2^32 bytes
+ * (R = T*k, +T with a shared expert).
+ * Errors: MOE_EINVAL (sizes, null or misaligned pointers), MOE_EUNSUPPORTED
+ * (MXFP4 activations with other weights), MOE_ENOMEM (workspace too small),
+ * MOE_EHIP (a launch failed); nothing is enqueued on an error. */
 moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream);
 
 /* moe_expert_ffn, timing each of its kernel launches with caller-created HIP
@@ -186,6 +203,11 @@ moe_status moe_expert_ffn_traced(const moe_ffn_args* a, moe_stream_t stream, voi
 
 /* Weighted combine back to token order:
  * out[t,:] = bf16( sum_{j=0..k-1} topk_w[t,j] * y[inv[t*k+j],:]  (+ y_shared[t,:]) ).
+ * [page "FreeToken量子化：MoE推論のセットアップガイド", 2nd paragraph: a token's
+ *  output is made from the few experts it passed through; page "FreeToken
+ *  qwen：...", 3rd paragraph: the router's choice per step.  Weighting by the
+ *  routing weights, j ascending, the shared expert added last with weight 1,
+ *  and bf16 rounding are this library's reading.]
  * y: [T*k][H] fp32 in perm order; y_shared: nullable [T][H] fp32. */
 moe_status moe_combine(const float* y, const int32_t* inv, const float* topk_w, const float* y_shared,
                        int T, int k, int H, uint16_t* out, moe_stream_t stream);
@@ -198,6 +220,16 @@ moe_status moe_combine(const float* y, const int32_t* inv, const float* topk_w, 
  * s: [rows, cols/32] E8M0.  cols % 32 == 0. */
 moe_status moe_quantize_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s,
                               moe_stream_t stream);
+
+/* Debug: the MXFP4 encodings an FP4 matrix-core call (amode MXFP4) left in
+ * its workspace, copied to canonical layout, for the bit-exact tests of the
+ * activation quantiser.  Enqueue on the call's stream after moe_expert_ffn
+ * with the same arguments, before the workspace is reused.
+ * which = 0: x, which = 1: the SwiGLU output h.  q: [R][K/2] bytes (element
+ * 2i in the low nibble, 16-byte aligned), s: [R][K/32] E8M0, K = H (x) or I
+ * (h), R = T*k (+T with a shared expert); row p is permutation-order row p
+ * (token perm[p] / k), rows T*k.. are the shared expert's tokens 0..T-1. */
+moe_status moe_debug_fp4_codes(const moe_ffn_args* a, int which, uint8_t* q, uint8_t* s, moe_stream_t stream);
 
 /* Debug: dequantise projection `which` (0 gate, 1 up, 2 down) of a device blob
  * into out [rows, cols] fp32 (canonical order).  Used by the bit-exact tests. */
@@ -218,6 +250,10 @@ moe_cache* moe_cache_create(int num_slots, size_t slot_bytes, void* slot_pool, i
 void moe_cache_destroy(moe_cache* c);
 
 /* Look up the distinct, ascending expert ids (host) of one step of `layer`.
+ * [page "FreeToken量子化：...", decode paragraph: the cache is an LRU over
+ *  the recently selected experts of all layers, a hit runs on the GPU, a
+ *  miss is brought in; bhrtaym-blog page, backend table row "offload".  The
+ *  key, the lookup order and the slot choice are this library's reading.]
  * Host-only and synchronous.  For each id: slot[i] (host), hit[i] (host,
  * 1/0) and evicted_key[i] (host, the key whose slot a miss took, -1 if the
  * slot was free or on a hit).  Every access makes its key most recent; a miss
@@ -229,6 +265,9 @@ moe_status cache_lookup(moe_cache* c, int layer, const int32_t* ids, int n, int3
                         uint8_t* hit, int32_t* evicted_key);
 
 /* Fill `slot` with the blob of (layer, expert) from pinned host memory.
+ * [page "FreeToken量子化：...", decode paragraph: a miss is copied over PCIe
+ *  from host RAM into the GPU cache; paragraph on double buffering: the copy
+ *  of some experts overlaps the computation of others.]
  * Enqueues on copy_stream: wait until every compute-stream use of the slot
  * recorded by moe_cache_mark_used has finished (write-after-read guard), then
  * hipMemcpyAsync host->device of slot_bytes, then an event; then makes

@@ -28,7 +28,7 @@ import math
 import numpy as np
 
 from .formats import bf16_to_f64, dequant, round_f32_to_bf16
-from .quant import quant_dequant
+from .quant import dequantize_mxfp4_codes, quant_dequant, quantize_mxfp4_rows
 
 
 def router_logits(x_bits: np.ndarray, w_router: np.ndarray) -> np.ndarray:
@@ -180,6 +180,53 @@ def layer(x_bits: np.ndarray, experts, k: int, *, logits=None, w_router=None, re
                 perm=perm, inv=inv, y_perm=y_perm, y_shared=y_shared, out=out, out_bf16=out_bf16)
 
 
+def expert_forward_rows(x_rows_bits: np.ndarray, weights, amode: str = "bf16", h_codes=None) -> np.ndarray:
+    """The SwiGLU expert of ``expert_forward`` with its n rows stacked into one
+    matrix: Y = (silu(X W_gate^T) * (X W_up^T)) W_down^T in float64, X [n, H]
+    (bf16 bits), the same definition evaluated as three matrix products.
+    amode "mxfp4" encodes X, and H rounded to float32, per row as
+    ``expert_forward`` does; then, if h_codes is a list, the encoding of H
+    (E2M1 codes [n, I], E8M0 codes [n, I/32]) is appended to it."""
+    Wg, Wu, Wd = weights
+    X = bf16_to_f64(np.asarray(x_rows_bits).reshape(-1, Wg.shape[1]))
+    if amode == "mxfp4":
+        X = quant_dequant(X.astype(np.float32))
+    Hm = silu(X @ Wg.T) * (X @ Wu.T)
+    if amode == "mxfp4":
+        codes, scales = quantize_mxfp4_rows(Hm.astype(np.float32))
+        if h_codes is not None:
+            h_codes.append((codes, scales))
+        Hm = dequantize_mxfp4_codes(codes, scales)
+    return Hm @ Wd.T
+
+
+def layer_outputs(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, E: int, expert_weights, *,
+                  shared_weights=None, amode: str = "bf16", h_codes=None) -> np.ndarray:
+    """out (float64 [T, H]) of one layer call given its routing (ids, w [T, k]):
+    the rows of each expert (the permutation of ``permute``) evaluated together
+    by ``expert_forward_rows``, then ``combine``.  expert_weights(e) returns the
+    dequantised (W_gate, W_up, W_down) of expert e; each is asked for once, in
+    ascending e.  With amode "mxfp4" and h_codes a dict, h_codes["codes"] and
+    h_codes["scales"] receive the encoding of every row's SwiGLU output in
+    permutation order (shared expert's token rows last)."""
+    T, k = ids.shape
+    H = x_bits.shape[1]
+    counts, offsets, perm, inv = permute(ids, E)
+    y_perm = np.zeros((T * k, H), np.float64)
+    hc = [] if (h_codes is not None and amode == "mxfp4") else None
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            y_perm[lo:hi] = expert_forward_rows(x_bits[perm[lo:hi] // k], expert_weights(e), amode, hc)
+    y_shared = None
+    if shared_weights is not None:
+        y_shared = expert_forward_rows(x_bits, shared_weights, amode, hc)
+    if hc is not None:
+        h_codes["codes"] = np.concatenate([c for c, _ in hc])
+        h_codes["scales"] = np.concatenate([sc for _, sc in hc])
+    return combine(y_perm, inv, w, y_shared)[0]
+
+
 def token_output(t: int, x_bits: np.ndarray, ids_row, w_row, expert_weights, *, shared_weights=None,
                  amode="bf16") -> np.ndarray:
     """out[t] alone (float64 [H]): for sampled-output checks at full size.
@@ -195,8 +242,21 @@ def token_output(t: int, x_bits: np.ndarray, ids_row, w_row, expert_weights, *, 
 
 
 def relative_error(gpu: np.ndarray, ref: np.ndarray) -> float:
-    """max |gpu - ref| / max |ref| over the whole output, in float64."""
+    """max |gpu - ref| / max |ref| over the whole output, in float64.
+
+    The two arrays must have the same shape (no broadcasting).  A non-finite
+    value in gpu gives inf; a reference that is all zeros gives 0 when gpu is
+    all zeros too, else inf."""
     g = np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
-    den = np.max(np.abs(r))
-    return float(np.max(np.abs(g - r)) / den) if den > 0 else float(np.max(np.abs(g - r)))
+    if g.shape != r.shape:
+        raise ValueError(f"shape {g.shape} != reference shape {r.shape}")
+    if g.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(g)):
+        return math.inf
+    num = float(np.max(np.abs(g - r)))
+    den = float(np.max(np.abs(r)))
+    if den == 0.0:
+        return 0.0 if num == 0.0 else math.inf
+    return num / den

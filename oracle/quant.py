@@ -44,6 +44,15 @@ def block_exponent(amax: float) -> int:
     return max(-127, min(127, (e - 1) - 2))
 
 
+def block_exponents(amax: np.ndarray) -> np.ndarray:
+    """``block_exponent`` of every element of amax (int64, same shape):
+    frexp gives amax = f * 2^e with f in [0.5, 1), so floor(log2 amax) = e - 1."""
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(amax)
+    ex = np.clip(e.astype(np.int64) - 1 - 2, -127, 127)
+    return np.where(amax == 0.0, 0, ex)
+
+
 def nearest_e2m1_codes(q: np.ndarray) -> np.ndarray:
     """Vectorised _nearest_e2m1: distance to each of the 8 magnitudes, minimum, ties -> even code."""
     q = np.asarray(q, dtype=np.float64)
@@ -64,7 +73,7 @@ def quantize_mxfp4_rows(v: np.ndarray):
     assert cols % 32 == 0
     blk = v.astype(np.float64).reshape(rows, cols // 32, 32)
     amax = np.abs(blk).max(axis=-1)
-    ex = np.array([block_exponent(float(a)) for a in amax.ravel()], dtype=np.int64).reshape(amax.shape)
+    ex = block_exponents(amax)
     scales = (ex + 127).astype(np.uint8)
     scaled = np.ldexp(blk, -ex[..., None])           # exact: power-of-two scaling in float64
     codes = nearest_e2m1_codes(scaled).reshape(rows, cols)

@@ -250,11 +250,13 @@ def prefill_batch(T: int = 4096, n_masked: int = 8, seed: int = SEED) -> dict:
                 x=activations(T, c["H"], seed, 2, 9, T), logits=logits)
 
 
-def large_batch(T: int, seed: int = SEED) -> dict:
-    """Large-expert layer input: x [T, 7168] and router weight [256, 7168] N(0, 0.02)."""
+def large_batch(T: int, seed: int = SEED, batch_index: int = 0) -> dict:
+    """Large-expert layer input: x [T, 7168] and router weight [256, 7168] N(0, 0.02).
+    batch_index > 0 draws another x (the router weight is the layer's, the same for all)."""
     c = LARGE
+    key = (seed, 3, 9, T) if batch_index == 0 else (seed, 3, 9, T, batch_index)
     return dict(cfg=3, T=T, H=c["H"], E=c["E"], k=c["k"], I=c["I"],
-                x=activations(T, c["H"], seed, 3, 9, T),
+                x=activations(T, c["H"], *key),
                 w_router=router_weight(c["E"], c["H"], seed, 3, 2))
 
 

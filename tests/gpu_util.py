@@ -57,17 +57,60 @@ class DequantCache:
         return self.d[e]
 
 
-def sample_tokens(perm, offsets, k, T, n_random, seed):
-    """Tokens to check at full size: first/last tokens, random ones, and for several
-    experts the token of the expert's last row (the ragged tail of its last tile)."""
-    rng = np.random.default_rng(seed)
-    toks = {0, T - 1}
-    toks.update(rng.choice(T, size=min(n_random, T), replace=False).tolist())
-    E = offsets.size - 1
-    nonempty = [e for e in range(E) if offsets[e + 1] > offsets[e]]
-    for e in rng.choice(nonempty, size=min(6, len(nonempty)), replace=False):
-        toks.add(int(perm[offsets[e + 1] - 1] // k))
-        toks.add(int(perm[offsets[e]] // k))
-    biggest = int(np.argmax(np.diff(offsets)))
-    toks.add(int(perm[offsets[biggest + 1] - 1] // k))
-    return sorted(toks)
+def grouped_reference(x_bits, ids, w, E, make_expert, *, shared=None, amode="bf16", h_codes=None, workers=None):
+    """Whole-output reference of one layer call: oracle.moe.layer_outputs with
+    each active expert's weights generated and dequantised ahead of use in a
+    thread pool (at most `workers` experts held at once)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    workers = workers or min(16, len(os.sched_getaffinity(0)))
+    order = sorted(set(int(e) for e in np.asarray(ids).ravel()))
+    pos = {e: i for i, e in enumerate(order)}
+    futs = {}
+    with ThreadPoolExecutor(workers) as ex:
+        def submit(i):
+            if i < len(order):
+                futs[order[i]] = ex.submit(lambda e=order[i]: oracle.moe.dequant_expert(make_expert(e)))
+        for i in range(workers):
+            submit(i)
+
+        def weights(e):
+            W = futs.pop(e).result()
+            submit(pos[e] + workers)
+            return W
+        sw = oracle.moe.dequant_expert(shared) if shared is not None else None
+        return oracle.moe.layer_outputs(x_bits, np.asarray(ids), np.asarray(w), E, weights, shared_weights=sw,
+                                        amode=amode, h_codes=h_codes)
+
+
+def gpu_fp4_codes(layer, T, x, which):
+    """The MXFP4 encoding of x (which 0) or h (1) the layer's last FP4 call left
+    in its workspace: (E2M1 codes [R, K], E8M0 [R, K/32]) in permutation order."""
+    from fp4_expert_ffn_amd import moe_debug_fp4_codes
+    a = layer.args(T, x)
+    R = T * layer.k + (T if layer.shared_blob is not None else 0)
+    K = layer.H if which == 0 else layer.I
+    q = torch.empty((R, K // 2), dtype=torch.uint8, device=DEV)
+    s = torch.empty((R, K // 32), dtype=torch.uint8, device=DEV)
+    moe_debug_fp4_codes(a, which, q, s)
+    torch.cuda.synchronize()
+    return oracle.formats.unpack_e2m1(q.cpu().numpy()), s.cpu().numpy()
+
+
+def fp4_code_report(layer, T, x_dev, x_bits, perm, k, h_ref, shared=False):
+    """R15 checks of the FP4 path: x's encoding bit-exact (per permuted row,
+    the token's row); the fraction of SwiGLU-output values whose encoding
+    (code and block scale) differs from the oracle's.  Returns that fraction."""
+    xc, xs = gpu_fp4_codes(layer, T, x_dev, 0)
+    rows = np.concatenate([np.asarray(perm) // k, np.arange(T)]) if shared else np.asarray(perm) // k
+    oc, os_ = oracle.quant.quantize_mxfp4_rows(synth.bf16_bits_to_f32(x_bits)[rows])
+    assert np.array_equal(xs, os_), "x block scales differ from the oracle's"
+    assert np.array_equal(xc, oc), "x codes differ from the oracle's"
+    hc, hs = gpu_fp4_codes(layer, T, x_dev, 1)
+    assert hc.shape == h_ref["codes"].shape and hs.shape == h_ref["scales"].shape
+    gv = oracle.quant.dequantize_mxfp4_codes(hc, hs)
+    ov = oracle.quant.dequantize_mxfp4_codes(h_ref["codes"], h_ref["scales"])
+    frac = float(np.mean(gv != ov))
+    blk = float(np.mean(hs != h_ref["scales"]))
+    say(f"    h encodings differing from the oracle's: {frac:.2e} of values, {blk:.2e} of block scales")
+    return frac

@@ -49,23 +49,29 @@ def test_cache_fill_copies_the_blob_into_its_slot():
     c.close()
 
 
-def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=None, config=86, resize_at=None):
+def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=None, config=86, resize_at=None,
+                routing_seed=None, blob_key=None):
     """Decode `tokens` single-token steps through `layers` layers; returns the
-    number of steps checked against the oracle."""
+    number of steps checked against the oracle.  blob_key(l, e) names the
+    pinned blob of an expert (experts with equal keys share one host copy;
+    make_expert must give them equal weights)."""
     from fp4_expert_ffn_amd.layer import CachedDecoder, to_numpy_bf16
     import fp4_expert_ffn_amd as F
     stride = (F.moe_blob_bytes("nvfp4", H, I) + 255) // 256 * 256
     bank = {}
+    blob_key = blob_key or (lambda l, e: (l, e))
 
     def host_blob(l, e):
-        if (l, e) not in bank:
-            bank[(l, e)] = _pinned_blob(make_expert(l, e), stride)
-        return bank[(l, e)]
+        key = blob_key(l, e)
+        if key not in bank:
+            bank[key] = _pinned_blob(make_expert(l, e), stride)
+        return bank[key]
 
     dec = CachedDecoder(num_layers=layers, num_experts=E, k=k, H=H, I=I, fmt="nvfp4", num_slots=slots,
                         host_blob=host_blob, device=DEV)
-    logits = synth.stream_routing(tokens, layers, E, seed=config)
-    xs = np.stack([np.stack([synth.stream_activations(t, l, H, seed=config)[0] for l in range(layers)])
+    seed = config if routing_seed is None else routing_seed
+    logits = synth.stream_routing(tokens, layers, E, seed=seed)
+    xs = np.stack([np.stack([synth.stream_activations(t, l, H, seed=seed)[0] for l in range(layers)])
                    for t in range(tokens)])
     lg_d = torch.from_numpy(logits).to(DEV)
     x_d = torch.from_numpy(xs.view(np.int16)).to(DEV)
@@ -140,6 +146,31 @@ def test_cached_stream_a3b_shape():
     steps = {(int(t), int(l)) for t, l in zip(rng.integers(0, 12, 6), rng.integers(0, 2, 6))} | {(11, 1)}
     n = _run_stream(layers=2, E=128, k=8, H=2048, I=768, tokens=12, slots=24, make_expert=make,
                     check_steps=steps, config=87)
+    assert n == len(steps)
+
+
+@pytest.mark.slow
+def test_cached_stream_full_size_trace():
+    """The cached decode stream at its real size: 48 A3B-like NVFP4 layers
+    (128 experts, top-8), 2048 HBM slots shared by all layers under LRU, 512
+    single-token steps from a cold cache with the stream's own routing
+    (Zipf(1.1), 0.6 repeat of the previous token's experts).  Every one of
+    the 24,576 steps' hit / miss / slot / eviction records equals the oracle
+    LRU's; sampled outputs match the oracle layer.  The LRU trace depends on
+    the routing only, so the layers share expert weights in pairs (one pinned
+    copy per (layer % 2, expert)) to keep the host bank small."""
+    say("cached stream at full size: 48 layers x 128 NVFP4 experts, 2048 slots, 512 tokens (trace of every step)")
+    gen = {}
+
+    def make(l, e):
+        key = (l % 2, e)
+        if key not in gen:
+            gen[key] = synth.expert("nvfp4", 2048, 768, config=4, layer=key[0], expert_id=e)
+        return gen[key]
+
+    steps = {(0, 0), (1, 47), (63, 5), (200, 30), (511, 47), (511, 0), (300, 17), (64, 1)}
+    n = _run_stream(layers=48, E=128, k=8, H=2048, I=768, tokens=512, slots=2048, make_expert=make,
+                    check_steps=steps, config=4, routing_seed=0, blob_key=lambda l, e: (l % 2, e))
     assert n == len(steps)
 
 

@@ -171,22 +171,17 @@ def test_pin_resident(L):
     c.close()
 
 
-def test_mxfp4_activations_off_the_persistent_kernel_need_the_combined_output(L):
-    """MXFP4 activations with H % 512 or I % 256 nonzero run on the 128 x 128
-    kernel, enabled there only for I >= 256 with the combined output: the
-    argument check rejects the rest before any device call (fake addresses)."""
-    base = dict(T=4, k=2, E=8, wfmt="mxfp4", amode="mxfp4", x=0x10000, counts=0x20000, offsets=0x30000,
-                perm=0x40000, slot_of_expert=0x50000, slot_pool=0x100000, topk_w=0x60000, inv=0x70000,
-                workspace=0x1000000, workspace_bytes=1 << 30)
-
-    def args(H, I, **kw):
-        stride = (L.moe_blob_bytes("mxfp4", H, I) + 255) // 256 * 256
-        return L.ffn_args(H=H, I=I, slot_stride=stride, **{**base, **kw})
-
-    for H, I, kw in [(256, 128, dict(out=0x80000)), (256, 384, dict(y=0x90000, out=0x80000)),
-                     (256, 384, dict(y=0x90000))]:
-        with pytest.raises(L.MoeError, match="MXFP4 activations"):
-            L.moe_expert_ffn(args(H, I, **kw), 0)
+def test_matrix_core_operands_must_fit_32_bit_offsets(L):
+    """The matrix-core kernels address x and the SwiGLU output with 32-bit
+    byte offsets: a call whose rows of max(H, I) bf16 values reach 4 GiB is
+    rejected before any device call (fake addresses)."""
+    H, I = 28672, 128
+    stride = (L.moe_blob_bytes("mxfp4", H, I) + 255) // 256 * 256
+    a = L.ffn_args(T=16384, k=8, E=8, H=H, I=I, wfmt="mxfp4", amode="mxfp4", x=0x10000, counts=0x20000,
+                   offsets=0x30000, perm=0x40000, slot_of_expert=0x50000, slot_pool=0x100000, slot_stride=stride,
+                   topk_w=0x60000, inv=0x70000, out=0x80000, workspace=0x1000000, workspace_bytes=1 << 40)
+    with pytest.raises(L.MoeError, match="exceed 4 GiB"):
+        L.moe_expert_ffn(a, 0)
 
 
 def test_cache_resize_rejects_bad_arguments(L):

@@ -125,3 +125,72 @@ def test_router_logits_fp64():
     lg = M.router_logits(L["x"], L["w_router"])
     ref = (torch.from_numpy(F.bf16_to_f64(L["x"])) @ torch.from_numpy(L["w_router"]).double().T).numpy()
     np.testing.assert_allclose(lg, ref, rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------- batched evaluation
+
+@pytest.mark.parametrize("fmt", synth.FMTS)
+@pytest.mark.parametrize("amode", ["bf16", "mxfp4"])
+def test_rows_together_equal_rows_one_by_one(fmt, amode):
+    """expert_forward_rows (three matrix products over all rows) equals the
+    per-row loop of expert_forward, which the dense-SwiGLU and scalar-loop
+    pins above fix.  float64 products in a different summation order agree to
+    rounding; in amode mxfp4 the float32 h they encode is identical here
+    except where a product lands within that rounding of an E2M1 boundary."""
+    if amode == "mxfp4" and fmt != "mxfp4":
+        pytest.skip("MXFP4 activations go with MXFP4 weights")
+    H, I, n = 256, 128, 23
+    ex = synth.expert(fmt, H, I, seed=7, config=97, expert_id=0)
+    x = synth.activations(n, H, 7, 97, 1)
+    W = M.dequant_expert(ex)
+    a = M.expert_forward(ex, x, amode)
+    b = M.expert_forward_rows(x, W, amode)
+    assert a.shape == b.shape == (n, H)
+    np.testing.assert_allclose(b, a, rtol=0, atol=1e-12 * np.abs(a).max())
+
+
+@pytest.mark.parametrize("fmt,amode,shared", [("nvfp4", "bf16", False), ("mxfp4", "mxfp4", True),
+                                              ("bf16", "bf16", True)])
+def test_grouped_layer_equals_the_per_token_layer(fmt, amode, shared):
+    """layer_outputs (each expert's rows together, given the routing) equals
+    layer() (the per-row loop) on the same routing, with a ragged row mix,
+    an expert with no rows and a shared expert."""
+    H, I, T, E, k = 128, 128, 19, 6, 2
+    exs = [synth.expert(fmt, H, I, seed=8, config=96, expert_id=e) for e in range(E)]
+    sh = synth.expert(fmt, H, I, seed=8, config=96, expert_id=synth.SHARED_EXPERT) if shared else None
+    x = synth.activations(T, H, 8, 96, 1)
+    logits = np.random.default_rng(3).standard_normal((T, E)).astype(np.float32)
+    logits[:, 4] = -1e4
+    ref = M.layer(x, exs, k, logits=logits, shared=sh, amode=amode)
+    got = M.layer_outputs(x, ref["ids"], ref["w"], E, lambda e: M.dequant_expert(exs[e]),
+                          shared_weights=M.dequant_expert(sh) if shared else None, amode=amode)
+    np.testing.assert_allclose(got, ref["out"], rtol=0, atol=1e-12 * np.abs(ref["out"]).max())
+
+
+# ---------------------------------------------------------------- the tolerance metric
+
+def test_relative_error_hand_cases():
+    """max |gpu - ref| / max |ref|, on values built by hand."""
+    ref = np.array([[1.0, -4.0], [2.0, 0.0]])
+    # a known ratio: the largest difference 0.04 over the largest |ref| 4
+    assert M.relative_error(ref + np.array([[0.0, 0.04], [-0.01, 0.0]]), ref) == pytest.approx(0.01, rel=1e-12)
+    # the denominator is max |ref|, not max |gpu|: 18 / 2, not 18 / 20
+    assert M.relative_error(np.array([1.0, 20.0]), np.array([1.0, 2.0])) == pytest.approx(9.0)
+    # ... and not the signed maximum of ref (which is 1 here): 0.5 / 10
+    assert M.relative_error(np.array([-10.0, 1.5]), np.array([-10.0, 1.0])) == pytest.approx(0.05)
+    # the numerator is the largest absolute difference, whatever its sign
+    assert M.relative_error(np.array([3.0, -1.0]), np.array([3.0, 2.0])) == pytest.approx(1.0)
+    # identical arrays, and an all-zero reference
+    assert M.relative_error(ref, ref) == 0.0
+    assert M.relative_error(np.zeros(3), np.zeros(3)) == 0.0
+    assert M.relative_error(np.array([0.0, 1e-3, 0.0]), np.zeros(3)) == math.inf
+    # a NaN or inf anywhere in the GPU output fails any tolerance
+    for bad in (math.nan, math.inf, -math.inf):
+        assert not M.relative_error(np.array([1.0, bad]), np.array([1.0, 1.0])) <= 1e-2
+
+
+def test_relative_error_refuses_broadcasting():
+    ref = np.ones((3, 4))
+    for shape in ((4,), (1, 4), (3, 1), (4, 3)):
+        with pytest.raises(ValueError):
+            M.relative_error(np.ones(shape), ref)

@@ -133,3 +133,46 @@ def test_resize_then_misses_take_the_slots_above_the_kept_keys():
     assert [r[2] for r in c.lookup(2, [0, 1])] == [4, 5]
     moves, dropped = c.resize(2)
     assert dropped == [(0, 1), (0, 2), (0, 3), (1, 7)] and [m[0] for m in moves] == [(2, 0), (2, 1)]
+
+
+def test_stream_trace_golden_is_current():
+    """The stored oracle trace of the real-size cached stream (used by the
+    stream benchmark's trace verdict) equals the oracle's trace today."""
+    import importlib.util
+    import os
+    from tests.conftest import GOLDEN
+    spec = importlib.util.spec_from_file_location("mk", os.path.join(GOLDEN, "make_stream_trace.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    digest, hits, misses = mk.oracle_trace()
+    with open(os.path.join(GOLDEN, "stream_trace_a3b_48x2048x512.txt")) as f:
+        ref = dict(ln.split() for ln in f if ln.strip() and not ln.startswith("#"))
+    assert ref["sha256"] == digest and int(ref["hits"]) == hits and int(ref["misses"]) == misses
+
+
+def test_bench_trace_verdict_reads_the_oracle_encoding():
+    """bench.py's stream trace verdict, fed the oracle's own records in the
+    layout the library writes them (per step: expert, slot, hit, evicted-key
+    rows), reports a match; one changed slot makes it report a mismatch."""
+    import numpy as np
+    import bench
+    import oracle
+    import synth
+    L_, E, K, S, T = 48, 128, 8, 2048, 512
+    logits = synth.stream_routing(T, L_, E)
+    lru = oracle.lru.SlotLRU(S)
+    NS = T * L_
+    e, s, v = (np.zeros((NS, E), np.int32) for _ in range(3))
+    h = np.zeros((NS, E), np.uint8)
+    n = np.zeros(NS, np.int32)
+    for t in range(T):
+        ids, _ = oracle.moe.route(logits[t], K)
+        for l in range(L_):
+            i = t * L_ + l
+            recs = lru.lookup(l, sorted(set(ids[l].tolist())))
+            n[i] = len(recs)
+            for j, (ex, hit, slot, ev) in enumerate(recs):
+                e[i, j], h[i, j], s[i, j], v[i, j] = ex, int(hit), slot, -1 if ev is None else ev[0] * E + ev[1]
+    assert bench.stream_trace_verdict(n, e, h, s, v, E, T, L_, S)["matches_oracle"] is True
+    s[NS // 2, 0] += 1
+    assert bench.stream_trace_verdict(n, e, h, s, v, E, T, L_, S)["matches_oracle"] is False

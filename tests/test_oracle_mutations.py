@@ -117,3 +117,52 @@ def test_lru_evicting_most_recent_caught(monkeypatch):
         return out
     monkeypatch.setattr(LRU.SlotLRU, "lookup", bad_lookup)
     _fails(tlru.test_textbook_trace, golden_rows)
+
+
+def test_metric_dividing_by_max_gpu_caught(monkeypatch):
+    def bad(gpu, ref):
+        g, r = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+        return float(np.max(np.abs(g - r)) / np.max(np.abs(g)))
+    monkeypatch.setattr(M, "relative_error", bad)
+    _fails(tffn.test_relative_error_hand_cases)
+
+
+def test_metric_dividing_by_signed_max_caught(monkeypatch):
+    def bad(gpu, ref):
+        g, r = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+        return float(np.max(np.abs(g - r)) / np.max(r))
+    monkeypatch.setattr(M, "relative_error", bad)
+    _fails(tffn.test_relative_error_hand_cases)
+
+
+def test_metric_broadcasting_caught(monkeypatch):
+    def bad(gpu, ref):
+        g, r = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+        return float(np.max(np.abs(g - r)) / np.max(np.abs(r)))
+    monkeypatch.setattr(M, "relative_error", bad)
+    with pytest.raises(pytest.fail.Exception, match="DID NOT RAISE"):
+        tffn.test_relative_error_refuses_broadcasting()
+
+
+def test_batched_expert_with_gate_and_up_swapped_caught(monkeypatch):
+    orig = M.expert_forward_rows
+    monkeypatch.setattr(M, "expert_forward_rows", lambda x, w, amode="bf16": orig(x, (w[1], w[0], w[2]), amode))
+    _fails(tffn.test_rows_together_equal_rows_one_by_one, "mxfp4", "bf16")
+
+
+def test_grouped_layer_with_rows_off_by_one_expert_caught(monkeypatch):
+    orig_perm = M.permute
+
+    def bad(ids, E):
+        counts, offsets, perm, inv = orig_perm(ids, E)
+        return counts, offsets, np.roll(perm, 1), inv
+    orig_layer_outputs = M.layer_outputs
+
+    def layer_outputs(*a, **kw):
+        monkeypatch.setattr(M, "permute", bad)
+        try:
+            return orig_layer_outputs(*a, **kw)
+        finally:
+            monkeypatch.setattr(M, "permute", orig_perm)
+    monkeypatch.setattr(M, "layer_outputs", layer_outputs)
+    _fails(tffn.test_grouped_layer_equals_the_per_token_layer, "nvfp4", "bf16", False)

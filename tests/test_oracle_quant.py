@@ -67,3 +67,18 @@ def test_zero_block_and_pack():
     packed = Q.pack_codes(c)
     assert packed.shape == (1, 32)
     assert packed[0, 16] == (c[0, 32] | (c[0, 33] << 4))
+
+
+def test_vectorised_block_exponents_equal_the_scalar_definition():
+    """block_exponents (frexp over an array) equals block_exponent element by
+    element: powers of two and their neighbours, subnormals, zero, the clamp
+    at both ends and a random sweep."""
+    vals = [0.0, 5.877471754111438e-39, 1.401298464324817e-45, 2.0 ** -149, 2.0 ** -127, 2.0 ** 127, 3.0e38]
+    for e in range(-140, 128, 3):
+        p = 2.0 ** e
+        vals += [p, np.nextafter(p, 0.0), np.nextafter(p, np.inf), 1.5 * p]
+    vals += list(np.abs(np.random.default_rng(0).standard_normal(2000)) * 10.0 ** np.random.default_rng(1).integers(-30, 30, 2000))
+    a = np.array(vals, np.float64)
+    got = Q.block_exponents(a)
+    want = np.array([Q.block_exponent(float(v)) for v in a])
+    assert np.array_equal(got, want)
