@@ -71,6 +71,7 @@ SIGNATURES = {
     "moe_prepack_expert": (_i, [ctypes.POINTER(ExpertCanonical), _vp, _sz]),
     "moe_expert_ffn_workspace_size": (_sz, [ctypes.POINTER(FfnArgs)]),
     "moe_expert_ffn": (_i, [ctypes.POINTER(FfnArgs), _vp]),
+    "moe_expert_ffn_noalloc": (_i, [ctypes.POINTER(FfnArgs), _vp]),
     "moe_expert_ffn_traced": (_i, [ctypes.POINTER(FfnArgs), _vp, _vp, _i, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "moe_quantize_mxfp4": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
@@ -214,6 +215,11 @@ def moe_expert_ffn_workspace_size(args: FfnArgs) -> int:
 
 def moe_expert_ffn(args: FfnArgs, stream=None):
     _check(lib().moe_expert_ffn(ctypes.byref(args), stream_handle(stream)), "moe_expert_ffn")
+
+
+def moe_expert_ffn_noalloc(args: FfnArgs, stream=None):
+    """moe_expert_ffn on the library's static device scratch (args.workspace is ignored)."""
+    _check(lib().moe_expert_ffn_noalloc(ctypes.byref(args), stream_handle(stream)), "moe_expert_ffn_noalloc")
 
 
 def moe_expert_ffn_traced(args: FfnArgs, events, stream=None) -> int:

@@ -6,6 +6,7 @@
 // passes through a few experts); the shared expert, when present, is added
 // with weight 1 (this library's reading).
 #include <algorithm>
+#include <mutex>
 
 #include "ffn_common.h"
 
@@ -307,6 +308,52 @@ extern "C" moe_status moe_debug_fp4_codes(const moe_ffn_args* a, int which, uint
   hipError_t e = launch_fp4_codes_canon(P, B, which, q, s, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return set_error(MOE_EHIP, "moe_debug_fp4_codes: launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
+}
+
+// ------------------------------------------------- allocation-free entry point
+// The workspace of moe_expert_ffn_noalloc: a static device array, one copy
+// per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in; its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device on the first call there.
+// Nothing in it needs clearing: every kernel reads only workspace bytes the
+// same call wrote first.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each device
+
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  MOE_HIP(hipGetDevice(&dev));
+  MOE_CHECK_ARG(dev >= 0 && dev < kMaxDevices, "moe_expert_ffn_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    MOE_CHECK_ARG(ptr && ((uintptr_t)ptr & 255) == 0, "moe_expert_ffn_noalloc: bad scratch address %p", ptr);
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+extern "C" moe_status moe_expert_ffn_noalloc(const moe_ffn_args* a, moe_stream_t stream) {
+  MOE_CHECK_ARG(a, "moe_expert_ffn_noalloc: null args");
+  moe_ffn_args b = *a;
+  const size_t need = moe_expert_ffn_workspace_size(&b);
+  if (need > kNoallocScratchBytes)
+    return set_error(MOE_ENOMEM, "moe_expert_ffn_noalloc: the call needs %zu bytes of workspace, more than the "
+                     "%zu of static scratch (use moe_expert_ffn with a workspace)", need, kNoallocScratchBytes);
+  void* ptr = nullptr;
+  moe_status st = scratch_address(&ptr);
+  if (st != MOE_OK) return st;
+  b.workspace = ptr;
+  b.workspace_bytes = kNoallocScratchBytes;
+  return moe_expert_ffn(&b, stream);
 }
 
 thread_local LaunchTrace* moe::g_launch_trace = nullptr;

@@ -190,6 +190,19 @@ size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a);
  * MOE_EHIP (a launch failed); nothing is enqueued on an error. */
 moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream);
 
+/* moe_expert_ffn without a caller workspace and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  a->workspace and
+ * a->workspace_bytes are ignored: the kernels use a static device scratch
+ * array of 32 MiB (one per GPU, held until the process ends; its address is
+ * looked up on the first call on each device).  Calls whose
+ * moe_expert_ffn_workspace_size exceeds 32 MiB return MOE_ENOMEM before any
+ * device work (decode batches need a few MiB; large prefills do not fit).
+ * Every call on a GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (on different streams, or from several host threads) race and must be
+ * ordered by the caller.  Otherwise as moe_expert_ffn. */
+moe_status moe_expert_ffn_noalloc(const moe_ffn_args* a, moe_stream_t stream);
+
 /* moe_expert_ffn, timing each of its kernel launches with caller-created HIP
  * events (hipEvent_t, passed as void*): launch i records events[2i] and
  * events[2i + 1] at the kernel's own start and end (hipExtLaunchKernelGGL),

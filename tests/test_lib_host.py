@@ -193,3 +193,18 @@ def test_cache_resize_rejects_bad_arguments(L):
     slot, hit, ev = L.cache_lookup(c, 0, [1, 2, 3, 4])
     assert list(slot) == [0, 1, 2, 3] and not any(hit)
     c.close()
+
+
+def test_noalloc_refuses_calls_beyond_its_scratch(L):
+    """moe_expert_ffn_noalloc checks the call's workspace need against its
+    32 MiB static scratch before any device call (fake addresses): a
+    4096-token FP4 prefill needs far more and gets MOE_ENOMEM."""
+    H, I = 2048, 768
+    stride = (L.moe_blob_bytes("mxfp4", H, I) + 255) // 256 * 256
+    a = L.ffn_args(T=4096, k=8, E=128, H=H, I=I, wfmt="mxfp4", amode="mxfp4", x=0x10000, counts=0x20000,
+                   offsets=0x30000, perm=0x40000, slot_of_expert=0x50000, slot_pool=0x100000, slot_stride=stride,
+                   topk_w=0x60000, inv=0x70000, out=0x80000)
+    assert L.moe_expert_ffn_workspace_size(a) > 32 << 20
+    with pytest.raises(L.MoeError, match="static scratch") as e:
+        L.moe_expert_ffn_noalloc(a, 0)
+    assert e.value.status == L.MOE_ENOMEM
