@@ -49,6 +49,14 @@ class CacheStep(ctypes.Structure):
     ]
 
 
+class CachePrefill(ctypes.Structure):
+    _fields_ = [
+        ("layer", ctypes.c_int), ("logits", ctypes.c_void_p), ("renormalize", ctypes.c_int),
+        ("topk_ids", ctypes.c_void_p), ("dev_map", ctypes.c_void_p), ("ffn", FfnArgs),
+        ("trace_slot", ctypes.c_void_p), ("trace_hit", ctypes.c_void_p), ("trace_evicted", ctypes.c_void_p),
+    ]
+
+
 class ExpertCanonical(ctypes.Structure):
     _fields_ = [
         ("fmt", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
@@ -88,6 +96,8 @@ SIGNATURES = {
     "moe_cache_map_bytes": (_sz, [_i]),
     "moe_cache_decode_step": (_i, [_vp, ctypes.POINTER(CacheStep), _vp, _vp]),
     "moe_cache_resize": (_i, [_vp, _i, _vp, _vp]),
+    "moe_cache_prefetch_layer": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_cache_prefill_step": (_i, [_vp, ctypes.POINTER(CachePrefill), _vp]),
 }
 
 _lib = None
@@ -331,3 +341,18 @@ def moe_cache_decode_step(cache: Cache, step: CacheStep, copy_stream=None, compu
 def moe_cache_resize(cache: Cache, num_slots: int, slot_pool, stream=None):
     _check(lib().moe_cache_resize(cache.handle, int(num_slots), ptr(slot_pool), stream_handle(stream)),
            "moe_cache_resize")
+
+
+def moe_cache_prefetch_layer(cache: Cache, layer, host_blobs, host_map, dev_map, trace=None, copy_stream=None,
+                             compute_stream=None):
+    """host_blobs: ctypes array of E pinned blob addresses; trace: None or
+    (slot int32 [E], hit uint8 [E], evicted int32 [E]) numpy arrays."""
+    t = (None, None, None) if trace is None else tuple(a.ctypes.data for a in trace)
+    _check(lib().moe_cache_prefetch_layer(cache.handle, int(layer), ctypes.cast(host_blobs, ctypes.c_void_p),
+                                          ptr(host_map), ptr(dev_map), *t, stream_handle(copy_stream),
+                                          stream_handle(compute_stream)), "moe_cache_prefetch_layer")
+
+
+def moe_cache_prefill_step(cache: Cache, step: CachePrefill, compute_stream=None):
+    _check(lib().moe_cache_prefill_step(cache.handle, ctypes.byref(step), stream_handle(compute_stream)),
+           "moe_cache_prefill_step")

@@ -1,20 +1,43 @@
 // The HBM expert-slot cache: host-side LRU over (layer, expert) keys plus the
-// stream/event protocol for filling slots from pinned host memory.
+// stream/event protocol for filling slots from pinned host memory.  Host code
+// only (the HIP runtime API); the blob moves of a resize are launched through
+// launch_move_slots (cache_kernels.hip).
 //
 // Method: host RAM holds every routed expert; one GPU cache is shared by all
 // MoE layers; in decode it is an LRU over recently selected experts, hits run
 // on the GPU, misses are copied over PCIe (page "FreeToken量子化：MoE推論の
 // セットアップガイド", hierarchy and decode paragraphs; bhrtaym-blog page,
 // section "MoEバックエンドは4種類から選べる", backend table row "offload").
+// In prefill the next layer's experts are copied while the current layer
+// computes (the same page, paragraph on prefill double buffering).
+//
+// Ordering protocol (one compute stream per cache; fills on copy streams):
+//  - write after read: a fill waits for the last readers of its slot.  Each
+//    marking of readers records one event from a ring of kRing events on the
+//    compute stream; a slot keeps the generation of its last marking.  A
+//    ring event is re-recorded only after the host has waited for its
+//    previous record, so a slot whose marking is older than kRing needs no
+//    wait at all.
+//  - read after write: a fill records filled[slot]; the step that first
+//    reads the slot makes the compute stream wait for it (pending flag).
+//  - a resize copies kept blobs after every fill enqueued so far, through a
+//    tail event per copy stream recorded after its last fill.
 #include <string.h>
 
+#include <algorithm>
 #include <set>
 #include <utility>
 #include <vector>
 
-#include "common.h"
+#include "host_common.h"
+
+namespace moe {
+hipError_t launch_move_slots(const int32_t* src_slots, int n, int dst0, const void* src_pool, void* dst_pool,
+                             size_t slot_bytes, hipStream_t s);
+}
 
 struct moe_cache {
+  static constexpr int kRing = 256;
   int num_slots = 0, num_layers = 0, num_experts = 0;
   size_t slot_bytes = 0;
   uint8_t* pool = nullptr;
@@ -24,13 +47,18 @@ struct moe_cache {
   std::vector<int32_t> prev, next; // per key
   int32_t head = -1, tail = -1;
   std::set<int32_t> free_slots;
-  // events (created on first use)
-  std::vector<hipEvent_t> reader, filled;
-  std::vector<uint8_t> has_reader;
-  int device = -1;
+  // fills: per-slot completion events and pending flags; per copy stream the
+  // event recorded after its last fill
+  std::vector<hipEvent_t> filled;
+  std::vector<uint8_t> fill_pending;
+  std::vector<std::pair<hipStream_t, hipEvent_t>> fill_tail;
+  // readers: the ring of marking events and each slot's last marking
+  std::vector<hipEvent_t> ring;
+  long long gen = 0;
+  std::vector<long long> reader_gen;  // -1: no reader recorded
   // statistics
   long long hits = 0, misses = 0, bytes_filled = 0;
-  // per-step scratch of moe_cache_decode_step
+  // per-step scratch
   std::vector<int32_t> step_ids, step_slot, step_ev;
   std::vector<uint8_t> step_hit;
   // copies of the last resize, which a fill into a kept slot must follow
@@ -85,15 +113,17 @@ extern "C" moe_cache* moe_cache_create(int num_slots, size_t slot_bytes, void* s
   c->prev.assign(nk, -1);
   c->next.assign(nk, -1);
   c->slot_key.assign(num_slots, -1);
-  c->has_reader.assign(num_slots, 0);
+  c->fill_pending.assign(num_slots, 0);
+  c->reader_gen.assign(num_slots, -1);
   c->reset();
   return c;
 }
 
 extern "C" void moe_cache_destroy(moe_cache* c) {
   if (!c) return;
-  for (hipEvent_t e : c->reader) if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->ring) if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : c->filled) if (e) (void)hipEventDestroy(e);
+  for (auto& t : c->fill_tail) (void)hipEventDestroy(t.second);
   for (auto& m : c->map_upload) (void)hipEventDestroy(m.second);
   if (c->resized) (void)hipEventDestroy(c->resized);
   delete c;
@@ -102,7 +132,6 @@ extern "C" void moe_cache_destroy(moe_cache* c) {
 extern "C" moe_status moe_cache_reset(moe_cache* c) {
   MOE_CHECK_ARG(c, "moe_cache_reset: null cache");
   c->reset();
-  std::fill(c->has_reader.begin(), c->has_reader.end(), 0);
   c->hits = c->misses = c->bytes_filled = 0;
   return MOE_OK;
 }
@@ -170,26 +199,123 @@ extern "C" moe_status cache_lookup(moe_cache* c, int layer, const int32_t* ids, 
   return MOE_OK;
 }
 
+// ------------------------------------------------------------ the ordering protocol
+
+// Per-slot fill events and the reader ring, created on first use.
+// (On a failure the events created so far are released or kept complete:
+// the ring is adopted only whole.)
 static moe_status ensure_events(moe_cache* c) {
-  if (!c->reader.empty()) return MOE_OK;
-  MOE_HIP(hipGetDevice(&c->device));
-  c->reader.assign(c->num_slots, nullptr);
-  c->filled.assign(c->num_slots, nullptr);
-  for (int s = 0; s < c->num_slots; ++s) {
-    MOE_HIP(hipEventCreateWithFlags(&c->reader[s], hipEventDisableTiming));
-    MOE_HIP(hipEventCreateWithFlags(&c->filled[s], hipEventDisableTiming));
+  if (c->ring.empty()) {
+    std::vector<hipEvent_t> ring(moe_cache::kRing, nullptr);
+    for (auto& e : ring) {
+      const hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      if (err != hipSuccess) {
+        for (hipEvent_t x : ring) if (x) (void)hipEventDestroy(x);
+        return moe::set_error(MOE_EHIP, "hipEventCreateWithFlags failed: %s", hipGetErrorString(err));
+      }
+    }
+    c->ring.swap(ring);
+  }
+  while ((int)c->filled.size() < c->num_slots) {
+    hipEvent_t f = nullptr;
+    MOE_HIP(hipEventCreateWithFlags(&f, hipEventDisableTiming));
+    c->filled.push_back(f);
   }
   return MOE_OK;
 }
 
+// The copy stream waits for the last readers of `slot` (write after read).
+static moe_status wait_readers(moe_cache* c, int slot, hipStream_t cs) {
+  const long long g = c->reader_gen[slot];
+  // the ring entry of generation g is re-recorded at g + kRing, after the
+  // host waited for this record: then the readers have finished
+  if (g < 0 || c->gen > g + moe_cache::kRing) return MOE_OK;
+  MOE_HIP(hipStreamWaitEvent(cs, c->ring[g % moe_cache::kRing], 0));
+  return MOE_OK;
+}
+
+// Record that slots[0..n) are read by the work enqueued on ks so far.
+static moe_status mark_readers(moe_cache* c, const int32_t* slots, int n, hipStream_t ks) {
+  if (n == 0) return MOE_OK;
+  const long long g = c->gen;
+  hipEvent_t e = c->ring[g % moe_cache::kRing];
+  if (g >= moe_cache::kRing) MOE_HIP(hipEventSynchronize(e));  // its record of kRing markings ago
+  MOE_HIP(hipEventRecord(e, ks));
+  for (int i = 0; i < n; ++i) c->reader_gen[slots[i]] = g;
+  ++c->gen;
+  return MOE_OK;
+}
+
 // Copy one blob into `slot` on the copy stream once the slot's last readers
-// are done; records filled[slot].
+// (and any resize copy) are done; records filled[slot].
 static moe_status enqueue_fill(moe_cache* c, int slot, const void* host_src, hipStream_t cs) {
-  if (c->has_reader[slot]) MOE_HIP(hipStreamWaitEvent(cs, c->reader[slot], 0));
+  moe_status st = wait_readers(c, slot, cs);
+  if (st != MOE_OK) return st;
   if (c->has_resized) MOE_HIP(hipStreamWaitEvent(cs, c->resized, 0));
   MOE_HIP(hipMemcpyAsync(c->pool + (size_t)slot * c->slot_bytes, host_src, c->slot_bytes, hipMemcpyHostToDevice, cs));
   MOE_HIP(hipEventRecord(c->filled[slot], cs));
+  c->fill_pending[slot] = 1;
   c->bytes_filled += (long long)c->slot_bytes;
+  return MOE_OK;
+}
+
+static moe_status note_fill_tail(moe_cache* c, hipStream_t cs);
+
+// After a fill of the step's lookups failed to enqueue: the misses from
+// index i0 on (whose blobs will not arrive) leave the cache and their slots
+// become free, so no key maps to a slot without its blob.  Keys they evicted
+// stay evicted.
+static void drop_unfilled(moe_cache* c, int layer, int i0, int n) {
+  for (int i = i0; i < n; ++i) {
+    if (c->step_hit[i]) continue;
+    const int32_t k = layer * c->num_experts + c->step_ids[i];
+    const int32_t s = c->key_slot[k];
+    if (s < 0) continue;
+    c->unlink(k);
+    c->key_slot[k] = -1;
+    c->slot_key[s] = -1;
+    c->free_slots.insert(s);
+  }
+}
+
+// Fills of the step's misses (the lookups in step_ids / step_slot /
+// step_hit) on cs; on a failure the unfilled misses are dropped.
+static moe_status fill_misses(moe_cache* c, int layer, int n, const void* const* host_blobs, hipStream_t cs,
+                              int* n_miss) {
+  int nm = 0;
+  for (int i = 0; i < n; ++i) {
+    if (c->step_hit[i]) continue;
+    const moe_status st = enqueue_fill(c, c->step_slot[i], host_blobs[c->step_ids[i]], cs);
+    if (st != MOE_OK) {
+      drop_unfilled(c, layer, i, n);
+      return st;
+    }
+    ++nm;
+  }
+  *n_miss = nm;
+  if (nm > 0) return note_fill_tail(c, cs);
+  return MOE_OK;
+}
+
+// The compute stream waits for the fill of `slot` if no earlier wait covers it.
+static moe_status wait_fill(moe_cache* c, int slot, hipStream_t ks) {
+  if (!c->fill_pending[slot]) return MOE_OK;
+  MOE_HIP(hipStreamWaitEvent(ks, c->filled[slot], 0));
+  c->fill_pending[slot] = 0;
+  return MOE_OK;
+}
+
+// Records the copy stream's tail event after its latest fills.
+static moe_status note_fill_tail(moe_cache* c, hipStream_t cs) {
+  for (auto& t : c->fill_tail)
+    if (t.first == cs) {
+      MOE_HIP(hipEventRecord(t.second, cs));
+      return MOE_OK;
+    }
+  hipEvent_t e = nullptr;
+  MOE_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  c->fill_tail.emplace_back(cs, e);
+  MOE_HIP(hipEventRecord(e, cs));
   return MOE_OK;
 }
 
@@ -208,8 +334,9 @@ extern "C" moe_status cache_fill(moe_cache* c, int layer, int expert, int slot, 
   hipStream_t ks = reinterpret_cast<hipStream_t>(compute_stream);
   st = enqueue_fill(c, slot, host_src, cs);
   if (st != MOE_OK) return st;
-  MOE_HIP(hipStreamWaitEvent(ks, c->filled[slot], 0));
-  return MOE_OK;
+  st = note_fill_tail(c, cs);
+  if (st != MOE_OK) return st;
+  return wait_fill(c, slot, ks);
 }
 
 extern "C" moe_status moe_cache_mark_used(moe_cache* c, const int32_t* slots, int n, moe_stream_t compute_stream) {
@@ -218,12 +345,7 @@ extern "C" moe_status moe_cache_mark_used(moe_cache* c, const int32_t* slots, in
     MOE_CHECK_ARG(slots[i] >= 0 && slots[i] < c->num_slots, "moe_cache_mark_used: slot %d out of range", slots[i]);
   moe_status st = ensure_events(c);
   if (st != MOE_OK) return st;
-  hipStream_t ks = reinterpret_cast<hipStream_t>(compute_stream);
-  for (int i = 0; i < n; ++i) {
-    MOE_HIP(hipEventRecord(c->reader[slots[i]], ks));
-    c->has_reader[slots[i]] = 1;
-  }
-  return MOE_OK;
+  return mark_readers(c, slots, n, reinterpret_cast<hipStream_t>(compute_stream));
 }
 
 extern "C" moe_status moe_cache_stats(const moe_cache* c, long long* hits, long long* misses, long long* bytes_filled) {
@@ -234,7 +356,7 @@ extern "C" moe_status moe_cache_stats(const moe_cache* c, long long* hits, long 
   return MOE_OK;
 }
 
-// ------------------------------------------------------------ one decode step
+// ------------------------------------------------------------ slot maps
 
 // dev_map / host_map layout: int32 slot_of_expert[E], uint8 hit_mask[E], uint8 miss_mask[E].
 extern "C" size_t moe_cache_map_bytes(int E) {
@@ -258,6 +380,37 @@ static moe_status map_before_write(moe_cache* c, const void* host_map, hipEvent_
   *ev = e;
   return MOE_OK;
 }
+
+// Writes the step's map into host_map (slots and the hit / miss masks of
+// step_ids) and uploads it to dev_map on ks.
+static moe_status upload_map(moe_cache* c, void* host_map, void* dev_map, int E, int n, hipStream_t ks) {
+  hipEvent_t up = nullptr;
+  moe_status st = map_before_write(c, host_map, &up);
+  if (st != MOE_OK) return st;
+  const size_t mb = moe_cache_map_bytes(E);
+  int32_t* map = static_cast<int32_t*>(host_map);
+  uint8_t* hm = reinterpret_cast<uint8_t*>(map + E);
+  uint8_t* mm = hm + E;
+  memset(host_map, 0, mb);
+  for (int i = 0; i < n; ++i) {
+    map[c->step_ids[i]] = c->step_slot[i];
+    (c->step_hit[i] ? hm : mm)[c->step_ids[i]] = 1;
+  }
+  MOE_HIP(hipMemcpyAsync(dev_map, host_map, mb, hipMemcpyHostToDevice, ks));
+  MOE_HIP(hipEventRecord(up, ks));
+  return MOE_OK;
+}
+
+static void copy_trace(const moe_cache* c, int n, int32_t* te, int32_t* ts, uint8_t* th, int32_t* tv) {
+  for (int i = 0; i < n; ++i) {
+    if (te) te[i] = c->step_ids[i];
+    ts[i] = c->step_slot[i];
+    th[i] = c->step_hit[i];
+    tv[i] = c->step_ev[i];
+  }
+}
+
+// ------------------------------------------------------------ one decode step
 
 extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t copy_stream,
                                             moe_stream_t compute_stream) {
@@ -306,43 +459,27 @@ extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe
   if (st != MOE_OK) return st;
 
   // 4. miss fills on the copy stream
-  int nh = 0, nm = 0;
-  for (int i = 0; i < n; ++i) {
-    if (c->step_hit[i]) {
-      ++nh;
-      continue;
-    }
-    ++nm;
-    st = enqueue_fill(c, c->step_slot[i], s->host_blobs[c->step_ids[i]], cs);
-    if (st != MOE_OK) return st;
-  }
+  int nm = 0;
+  st = fill_misses(c, s->layer, n, s->host_blobs, cs, &nm);
+  if (st != MOE_OK) return st;
+  const int nh = n - nm;
 
   // 5. slot map and masks
-  const size_t mb = moe_cache_map_bytes(E);
-  int32_t* map = static_cast<int32_t*>(s->host_map);
-  uint8_t* hm = reinterpret_cast<uint8_t*>(map + E);
-  uint8_t* mm = hm + E;
-  hipEvent_t up = nullptr;
-  st = map_before_write(c, s->host_map, &up);
+  st = upload_map(c, s->host_map, s->dev_map, E, n, ks);
   if (st != MOE_OK) return st;
-  memset(s->host_map, 0, mb);
-  for (int i = 0; i < n; ++i) {
-    map[c->step_ids[i]] = c->step_slot[i];
-    (c->step_hit[i] ? hm : mm)[c->step_ids[i]] = 1;
-  }
-  MOE_HIP(hipMemcpyAsync(s->dev_map, s->host_map, mb, hipMemcpyHostToDevice, ks));
-  MOE_HIP(hipEventRecord(up, ks));
   const int32_t* dmap = static_cast<const int32_t*>(s->dev_map);
   const uint8_t* dhm = reinterpret_cast<const uint8_t*>(dmap + E);
   const uint8_t* dmm = dhm + E;
 
-  // 6. hits now, misses after their fills
+  // 6. hits now (after any fill of theirs still pending), misses after their fills
   moe_ffn_args a = f;
   a.slot_of_expert = dmap;
   a.slot_pool = c->pool;
   a.slot_stride = c->slot_bytes;
   a.out = nullptr;
   if (nh > 0) {
+    for (int i = 0; i < n; ++i)
+      if (c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], ks)) != MOE_OK) return st;
     a.expert_mask = dhm;
     st = moe_expert_ffn(&a, compute_stream);
     if (st != MOE_OK) return st;
@@ -350,57 +487,119 @@ extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe
   }
   if (nm > 0) {
     for (int i = 0; i < n; ++i)
-      if (!c->step_hit[i]) MOE_HIP(hipStreamWaitEvent(ks, c->filled[c->step_slot[i]], 0));
+      if (!c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], ks)) != MOE_OK) return st;
     a.expert_mask = dmm;
     st = moe_expert_ffn(&a, compute_stream);
     if (st != MOE_OK) return st;
   }
 
-  // 7. combine, then the slots' readers
+  // 7. combine, then the slots' readers (one marking for the step)
   const float* ysh = f.shared_blob ? f.y + (size_t)T * f.k * f.H : nullptr;
   st = moe_combine(f.y, f.inv, f.topk_w, ysh, T, f.k, f.H, f.out, compute_stream);
   if (st != MOE_OK) return st;
-  st = moe_cache_mark_used(c, c->step_slot.data(), n, compute_stream);
+  st = mark_readers(c, c->step_slot.data(), n, ks);
   if (st != MOE_OK) return st;
 
-  if (s->trace_expert && s->trace_slot && s->trace_hit && s->trace_evicted)
-    for (int i = 0; i < n; ++i) {
-      s->trace_expert[i] = c->step_ids[i];
-      s->trace_slot[i] = c->step_slot[i];
-      s->trace_hit[i] = c->step_hit[i];
-      s->trace_evicted[i] = c->step_ev[i];
-    }
+  if (s->trace_slot && s->trace_hit && s->trace_evicted)
+    copy_trace(c, n, s->trace_expert, s->trace_slot, s->trace_hit, s->trace_evicted);
   s->n_experts = n;
   return MOE_OK;
 }
 
-// ------------------------------------------------------------ resize at a safe point
+// ------------------------------------------------------------ layer-ahead prefill
 
-// Blob moves of one launch: source slot of destination slot dst0 + b, passed
-// by value (the kernel argument segment holds them; no device buffer).
-constexpr int kMoveBatch = 256;
-struct SlotMoves {
-  int32_t src[kMoveBatch];
-};
-
-// Copy blob blockIdx.y of the batch (slot_vecs 16-byte vectors) from its old
-// slot to slot dst0 + blockIdx.y; the x blocks stride over the vectors, four
-// loads in flight per thread.  HBM-bound: one read and one write per byte.
-__global__ __launch_bounds__(256) void k_move_slots(SlotMoves m, int dst0, const uint4* __restrict__ src_pool,
-                                                    uint4* __restrict__ dst_pool, uint32_t slot_vecs) {
-  const uint4* src = src_pool + (size_t)m.src[blockIdx.y] * slot_vecs;
-  uint4* dst = dst_pool + (size_t)(dst0 + blockIdx.y) * slot_vecs;
-  const uint32_t step = gridDim.x * 256u;
-  for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < slot_vecs; v += 4 * step) {
-    uint4 r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (v + j * step < slot_vecs) r[j] = src[v + j * step];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (v + j * step < slot_vecs) dst[v + j * step] = r[j];
-  }
+extern "C" moe_status moe_cache_prefetch_layer(moe_cache* c, int layer, const void* const* host_blobs,
+                                               void* host_map, void* dev_map, int32_t* trace_slot,
+                                               uint8_t* trace_hit, int32_t* trace_evicted, moe_stream_t copy_stream,
+                                               moe_stream_t compute_stream) {
+  MOE_CHECK_ARG(c, "moe_cache_prefetch_layer: null cache");
+  MOE_CHECK_ARG(c->pool, "moe_cache_prefetch_layer: cache has no slot pool");
+  MOE_CHECK_ARG(layer >= 0 && layer < c->num_layers, "moe_cache_prefetch_layer: layer %d out of range", layer);
+  MOE_CHECK_ARG(host_blobs && host_map && dev_map, "moe_cache_prefetch_layer: null pointer");
+  MOE_CHECK_ARG(((uintptr_t)dev_map & 255) == 0, "moe_cache_prefetch_layer: dev_map must be 256-byte aligned");
+  const int E = c->num_experts;
+  for (int e = 0; e < E; ++e) MOE_CHECK_ARG(host_blobs[e], "moe_cache_prefetch_layer: host blob of expert %d is null", e);
+  if (E > c->num_slots)
+    return moe::set_error(MOE_ECACHE, "moe_cache_prefetch_layer: %d experts of a layer > %d slots", E, c->num_slots);
+  moe_status st = ensure_events(c);
+  if (st != MOE_OK) return st;
+  hipStream_t ks = reinterpret_cast<hipStream_t>(compute_stream);
+  hipStream_t cs = reinterpret_cast<hipStream_t>(copy_stream);
+  c->step_ids.resize(E);
+  for (int e = 0; e < E; ++e) c->step_ids[e] = e;
+  c->step_slot.resize(E);
+  c->step_hit.resize(E);
+  c->step_ev.resize(E);
+  st = cache_lookup(c, layer, c->step_ids.data(), E, c->step_slot.data(), c->step_hit.data(), c->step_ev.data());
+  if (st != MOE_OK) return st;
+  int nm = 0;
+  st = fill_misses(c, layer, E, host_blobs, cs, &nm);
+  if (st != MOE_OK) return st;
+  st = upload_map(c, host_map, dev_map, E, E, ks);
+  if (st != MOE_OK) return st;
+  if (trace_slot && trace_hit && trace_evicted) copy_trace(c, E, nullptr, trace_slot, trace_hit, trace_evicted);
+  return MOE_OK;
 }
+
+extern "C" moe_status moe_cache_prefill_step(moe_cache* c, moe_cache_prefill* s, moe_stream_t compute_stream) {
+  MOE_CHECK_ARG(c && s, "moe_cache_prefill_step: null pointer");
+  const moe_ffn_args& f = s->ffn;
+  const int E = f.E, T = f.T;
+  MOE_CHECK_ARG(c->pool, "moe_cache_prefill_step: cache has no slot pool");
+  MOE_CHECK_ARG(E == c->num_experts, "moe_cache_prefill_step: E=%d but the cache has %d experts per layer", E,
+                c->num_experts);
+  MOE_CHECK_ARG(s->layer >= 0 && s->layer < c->num_layers, "moe_cache_prefill_step: layer %d out of range", s->layer);
+  MOE_CHECK_ARG(T >= 0 && f.k >= 1 && f.k <= E, "moe_cache_prefill_step: bad T=%d k=%d", T, f.k);
+  MOE_CHECK_ARG(s->logits && s->topk_ids && s->dev_map && f.out && f.topk_w && f.inv && f.counts && f.offsets &&
+                    f.perm,
+                "moe_cache_prefill_step: logits, topk_ids, dev_map and ffn.out, topk_w, inv, counts, offsets, perm "
+                "are required");
+  // every expert of the layer must be cached (its prefetch came first);
+  // checked before any state changes
+  for (int e = 0; e < E; ++e)
+    if (c->key_slot[(size_t)s->layer * E + e] < 0)
+      return moe::set_error(MOE_ECACHE, "moe_cache_prefill_step: expert (%d, %d) is not cached: prefetch the layer "
+                            "first", s->layer, e);
+  moe_status st = ensure_events(c);
+  if (st != MOE_OK) return st;
+  hipStream_t ks = reinterpret_cast<hipStream_t>(compute_stream);
+  c->step_ids.resize(E);
+  for (int e = 0; e < E; ++e) c->step_ids[e] = e;
+  c->step_slot.resize(E);
+  c->step_hit.resize(E);
+  c->step_ev.resize(E);
+  st = cache_lookup(c, s->layer, c->step_ids.data(), E, c->step_slot.data(), c->step_hit.data(), c->step_ev.data());
+  if (st != MOE_OK) return st;
+  for (int e = 0; e < E; ++e)
+    if ((st = wait_fill(c, c->step_slot[e], ks)) != MOE_OK) return st;
+  if (T > 0) {
+    if ((long long)T * f.k <= 1024) {
+      st = moe_route_permute(s->logits, T, E, f.k, s->renormalize, s->topk_ids, const_cast<float*>(f.topk_w),
+                             const_cast<int32_t*>(f.counts), const_cast<int32_t*>(f.offsets),
+                             const_cast<int32_t*>(f.perm), const_cast<int32_t*>(f.inv), compute_stream);
+    } else {
+      st = moe_route(s->logits, T, E, f.k, s->renormalize, s->topk_ids, const_cast<float*>(f.topk_w), compute_stream);
+      if (st == MOE_OK)
+        st = moe_permute(s->topk_ids, T, f.k, E, const_cast<int32_t*>(f.counts), const_cast<int32_t*>(f.offsets),
+                         const_cast<int32_t*>(f.perm), const_cast<int32_t*>(f.inv), compute_stream);
+    }
+    if (st != MOE_OK) return st;
+    moe_ffn_args a = f;
+    a.slot_of_expert = static_cast<const int32_t*>(s->dev_map);
+    a.slot_pool = c->pool;
+    a.slot_stride = c->slot_bytes;
+    a.expert_mask = nullptr;
+    st = moe_expert_ffn(&a, compute_stream);
+    if (st != MOE_OK) return st;
+  }
+  st = mark_readers(c, c->step_slot.data(), E, ks);
+  if (st != MOE_OK) return st;
+  if (s->trace_slot && s->trace_hit && s->trace_evicted)
+    copy_trace(c, E, nullptr, s->trace_slot, s->trace_hit, s->trace_evicted);
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ resize at a safe point
 
 extern "C" moe_status moe_cache_resize(moe_cache* c, int num_slots, void* slot_pool, moe_stream_t stream) {
   MOE_CHECK_ARG(c && slot_pool, "moe_cache_resize: null pointer");
@@ -420,32 +619,13 @@ extern "C" moe_status moe_cache_resize(moe_cache* c, int num_slots, void* slot_p
   std::vector<int32_t> keys;
   for (int32_t k = c->head; k >= 0; k = c->next[k]) keys.push_back(k);
   const int nkeep = std::min<int>((int)keys.size(), num_slots), ndrop = (int)keys.size() - nkeep;
-  // the slots' events are reused (a stale record only makes a later wait
-  // stricter: readers are reset below, fills are waited for here)
-  for (int s = (int)c->filled.size(); s < num_slots; ++s) {
-    hipEvent_t f = nullptr, r = nullptr;
-    MOE_HIP(hipEventCreateWithFlags(&f, hipEventDisableTiming));
-    c->filled.push_back(f);
-    MOE_HIP(hipEventCreateWithFlags(&r, hipEventDisableTiming));
-    c->reader.push_back(r);
-  }
-  // the copies start once every kept blob's fill has landed (fills still in
-  // flight are waited for; finished ones cost nothing)
+  // the copies start after every fill enqueued so far (one wait per copy stream)
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  for (int i = 0; i < nkeep; ++i) {
-    hipEvent_t f = c->filled[c->key_slot[keys[ndrop + i]]];
-    if (hipEventQuery(f) != hipSuccess) MOE_HIP(hipStreamWaitEvent(hs, f, 0));
-  }
-  const uint32_t vecs = (uint32_t)(c->slot_bytes / 16);
-  const int gx = (int)std::min<uint32_t>(64, (vecs + 1023) / 1024);
-  for (int b0 = 0; b0 < nkeep; b0 += kMoveBatch) {
-    const int n = std::min(kMoveBatch, nkeep - b0);
-    SlotMoves m{};
-    for (int b = 0; b < n; ++b) m.src[b] = c->key_slot[keys[ndrop + b0 + b]];
-    moe::launch(k_move_slots, dim3(gx, n), dim3(256), 0, hs, m, b0, reinterpret_cast<const uint4*>(c->pool),
-                reinterpret_cast<uint4*>(slot_pool), vecs);
-    MOE_HIP(hipGetLastError());
-  }
+  for (auto& t : c->fill_tail) MOE_HIP(hipStreamWaitEvent(hs, t.second, 0));
+  std::vector<int32_t> src(nkeep);
+  for (int i = 0; i < nkeep; ++i) src[i] = c->key_slot[keys[ndrop + i]];
+  const hipError_t e = moe::launch_move_slots(src.data(), nkeep, 0, c->pool, slot_pool, c->slot_bytes, hs);
+  if (e != hipSuccess) return moe::set_error(MOE_EHIP, "moe_cache_resize: copy launch failed: %s", hipGetErrorString(e));
   // a later fill into a kept slot (on any stream) must follow the copies
   MOE_HIP(hipEventRecord(c->resized, hs));
   c->has_resized = 1;
@@ -453,16 +633,18 @@ extern "C" moe_status moe_cache_resize(moe_cache* c, int num_slots, void* slot_p
     c->unlink(keys[i]);
     c->key_slot[keys[i]] = -1;
   }
-  // events beyond num_slots are kept for a later growth (destroyed with the cache)
   c->num_slots = num_slots;
   c->pool = static_cast<uint8_t*>(slot_pool);
   c->slot_key.assign(num_slots, -1);
-  c->has_reader.assign(num_slots, 0);
+  // the new slots were written by the copies on `stream` (ordered before later
+  // steps, which run on it); their readers start afresh
+  c->fill_pending.assign(num_slots, 0);
+  c->reader_gen.assign(num_slots, -1);
   for (int i = 0; i < nkeep; ++i) {
     c->key_slot[keys[ndrop + i]] = i;
     c->slot_key[i] = keys[ndrop + i];
   }
   c->free_slots.clear();
   for (int s = nkeep; s < num_slots; ++s) c->free_slots.insert(s);
-  return MOE_OK;
+  return ensure_events(c);
 }

@@ -3,7 +3,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "common.h"
+#include "host_common.h"
 
 namespace moe {
 static thread_local char g_err[512] = "";

@@ -240,6 +240,96 @@ class CachedDecoder:
         self.cache.close()
 
 
+class CachedPrefill:
+    """Prefill through the expert-slot cache, one layer ahead: while layer l
+    computes, every expert of layer l + 1 is copied from the pinned host bank
+    on a side stream into a cache of `num_slots` slots (default 2E: the layer
+    computing and the layer arriving).
+
+    host_blob(layer, e) -> pinned uint8 tensor holding that expert's blob.
+    """
+
+    def __init__(self, *, num_layers, num_experts, k, H, I, fmt, max_tokens, host_blob, amode="bf16",
+                 num_slots=None, device="cuda", renormalize=True):
+        self.L, self.E, self.k, self.H, self.I, self.fmt, self.amode = num_layers, num_experts, k, H, I, fmt, amode
+        self.renormalize = 1 if renormalize else 0
+        self.dev = torch.device(device)
+        self.blob_bytes = L.moe_blob_bytes(fmt, H, I)
+        self.stride = (self.blob_bytes + 255) // 256 * 256
+        self.num_slots = num_slots or 2 * num_experts
+        self.pool = torch.empty(self.num_slots * self.stride, dtype=torch.uint8, device=self.dev)
+        self.cache = L.moe_cache_create(self.num_slots, self.stride, self.pool, num_layers, num_experts)
+        self.copy_stream = torch.cuda.Stream(device=self.dev)
+        E, T = num_experts, max(max_tokens, 1)
+        self.max_tokens = T
+        self._blobs = [[host_blob(l, e) for e in range(E)] for l in range(num_layers)]
+        for row in self._blobs:
+            for b in row:
+                assert b.is_pinned() and b.numel() >= self.stride
+        self._tables = [(ctypes.c_void_p * E)(*[b.data_ptr() for b in row]) for row in self._blobs]
+        mb = L.moe_cache_map_bytes(E)
+        # one slot map per layer: layer l's step reads its map while layer l + 1's is uploaded
+        self.host_maps = [torch.empty(mb, dtype=torch.uint8, pin_memory=True) for _ in range(num_layers)]
+        self.dev_maps = [torch.empty(mb, dtype=torch.uint8, device=self.dev) for _ in range(num_layers)]
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=self.dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=self.dev)
+        self.counts = torch.zeros(E, dtype=torch.int32, device=self.dev)
+        self.offsets = torch.zeros(E + 1, dtype=torch.int32, device=self.dev)
+        self.perm = torch.zeros(T * k, dtype=torch.int32, device=self.dev)
+        self.inv = torch.zeros(T * k, dtype=torch.int32, device=self.dev)
+        a = self._args(T, None, None)
+        need = L.moe_expert_ffn_workspace_size(a)
+        self._ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=self.dev)
+        self.trace = (np.empty(E, np.int32), np.empty(E, np.uint8), np.empty(E, np.int32))
+
+    def _args(self, T, x, out):
+        a = L.ffn_args(T=T, k=self.k, E=self.E, H=self.H, I=self.I, wfmt=self.fmt, amode=self.amode, x=x,
+                       counts=self.counts, offsets=self.offsets, perm=self.perm, topk_w=self.w, inv=self.inv, out=out,
+                       slot_stride=self.stride)
+        if getattr(self, "_ws", None) is not None:
+            a.workspace, a.workspace_bytes = self._ws.data_ptr(), self._ws.numel()
+        return a
+
+    def prefetch(self, layer, stream=None):
+        """Queue the copies of every expert of `layer` not cached yet; returns
+        the lookups (slot, hit, evicted key) of experts 0..E-1."""
+        L.moe_cache_prefetch_layer(self.cache, layer, self._tables[layer], self.host_maps[layer],
+                                   self.dev_maps[layer], self.trace, self.copy_stream, stream)
+        return tuple(t.copy() for t in self.trace)
+
+    def layer_step(self, layer, x, logits, out, stream=None):
+        """One prefill step of a prefetched layer: x [T,H] bf16 (int16), logits
+        [T,E] fp32, out [T,H] (int16) on the device.  Returns the step's lookups
+        (expert, hit, slot, evicted key) of experts 0..E-1."""
+        T = x.shape[0]
+        assert T <= self.max_tokens
+        st = L.CachePrefill()
+        st.layer, st.renormalize = layer, self.renormalize
+        st.logits, st.topk_ids, st.dev_map = logits.data_ptr(), self.ids.data_ptr(), self.dev_maps[layer].data_ptr()
+        st.ffn = self._args(T, x, out)
+        slot, hit, ev = self.trace
+        st.trace_slot, st.trace_hit, st.trace_evicted = slot.ctypes.data, hit.ctypes.data, ev.ctypes.data
+        L.moe_cache_prefill_step(self.cache, st, stream)
+        return np.arange(self.E, dtype=np.int32), hit.copy(), slot.copy(), ev.copy()
+
+    def run(self, xs, logits, outs, stream=None):
+        """Every layer in order, each layer's experts prefetched while the
+        previous layer computes; returns each step's lookups."""
+        traces = []
+        self.prefetch(0, stream)
+        for l in range(self.L):
+            traces.append(self.layer_step(l, xs[l], logits[l], outs[l], stream))
+            if l + 1 < self.L:
+                self.prefetch(l + 1, stream)
+        return traces
+
+    def stats(self):
+        return L.moe_cache_stats(self.cache)
+
+    def close(self):
+        self.cache.close()
+
+
 def bf16_tensor(bits: np.ndarray, device="cuda") -> torch.Tensor:
     """Upload bf16 bit patterns (uint16 numpy) as an int16 device tensor."""
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device)

@@ -344,6 +344,54 @@ size_t moe_cache_map_bytes(int E);
 moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t copy_stream,
                                  moe_stream_t compute_stream);
 
+/* ------------------------------------------------- layer-ahead prefill
+ * [page "FreeToken量子化：MoE推論のセットアップガイド", paragraph on prefill:
+ *  the experts of the next layer are copied over PCIe while the current
+ *  layer computes, double buffering whole layers.]  A prefill batch routes
+ * its tokens to nearly every expert, so a layer's step needs all of its
+ * experts: moe_cache_prefetch_layer(l + 1) is called right after
+ * moe_cache_prefill_step(l), and its copies overlap that step's compute.  A
+ * cache of 2E slots holds the layer computing and the layer arriving.
+ * Neither call synchronises the host.  All steps of a cache run on one
+ * compute stream. */
+
+/* Look up every expert of `layer` in ascending id (misses take the lowest
+ * free slot, else evict the least recently used key), fill each miss from
+ * host_blobs[e] (pinned, slot_bytes each) on copy_stream after its slot's
+ * last readers, and upload the layer's slot map (moe_cache_map_bytes(E):
+ * int32 slot of every expert first) from host_map (pinned; rewritten only
+ * after its previous upload) to dev_map (device, 256-byte aligned) on
+ * compute_stream.  trace_slot / trace_hit / trace_evicted (host [E],
+ * nullable together) receive the lookups of experts 0..E-1.  Returns
+ * MOE_ECACHE (cache unchanged) if E > num_slots. */
+moe_status moe_cache_prefetch_layer(moe_cache* c, int layer, const void* const* host_blobs, void* host_map,
+                                    void* dev_map, int32_t* trace_slot, uint8_t* trace_hit, int32_t* trace_evicted,
+                                    moe_stream_t copy_stream, moe_stream_t compute_stream);
+
+/* One prefill step of a layer whose experts were prefetched. */
+typedef struct {
+  int layer;
+  const float* logits;          /* [T,E] fp32 router logits                          */
+  int renormalize;
+  int32_t* topk_ids;            /* [T,k] device                                      */
+  const void* dev_map;          /* the layer's map from moe_cache_prefetch_layer     */
+  moe_ffn_args ffn;             /* T, k, E, H, I, wfmt, amode, x, counts, offsets,
+                                   perm, inv, topk_w, out (required), y (nullable),
+                                   shared_blob, workspace; slot_of_expert, slot_pool,
+                                   slot_stride and expert_mask are set by the call    */
+  int32_t* trace_slot;          /* host [E] (nullable together): the lookups         */
+  uint8_t* trace_hit;
+  int32_t* trace_evicted;
+} moe_cache_prefill;
+
+/* Looks up every expert of s->layer (all hits, ascending id: the step's
+ * trace), makes compute_stream wait for the layer's fills, then enqueues
+ * routing, permutation, the expert FFN and the combine into ffn.out on
+ * compute_stream, and records the layer's slots as read by them.  Returns
+ * MOE_ECACHE with the cache unchanged if an expert of the layer is not
+ * cached (its prefetch did not run, or a later one evicted it). */
+moe_status moe_cache_prefill_step(moe_cache* c, moe_cache_prefill* s, moe_stream_t compute_stream);
+
 /* Resize the cache at a safe point (between layer calls, no step in flight).
  * [page "FreeToken量子化：MoE推論のセットアップガイド", paragraph on resizing
  *  the expert cache at runtime at scheduler safe points.]
@@ -352,8 +400,8 @@ moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t c
  * cached) most recently used keys, packed into slots 0, 1, ... from least to
  * most recent with their recency order unchanged, and drops the rest; later
  * misses take the free slots above them, lowest first.  The kept blobs are
- * copied device to device on `stream` (one kernel per 256 blobs) after their
- * fills have landed.  Later steps must run on `stream` or be ordered after it
+ * copied device to device on `stream` (one kernel per 256 blobs) after every
+ * fill enqueued so far has landed.  Later steps must run on `stream` or be ordered after it
  * by the caller; later fills wait for the copies themselves.  The caller may
  * release the old pool once the copies and every earlier reader of it have
  * finished (e.g. after synchronising `stream` when all steps ran on it).  The

@@ -175,12 +175,7 @@ def test_cached_stream_full_size_trace():
 
 
 # Prefill through the cache one layer ahead (every expert of layer l + 1
-# copied while layer l computes) is not in the library: its first GPU run, the
-# MXFP4 / MXFP4-activation case below, ended in a GPU memory fault whose cause
-# was not found by reading the code.  These tests stay skipped until the cause
-# is shown and the entry points return.
-PREFILL_SKIP = pytest.mark.skip(reason="layer-ahead prefill through the cache disabled: "
-                                "its first GPU run faulted, cause not yet shown")
+# copied while layer l computes).
 
 
 def _trace_of(want, E):
@@ -188,7 +183,6 @@ def _trace_of(want, E):
             [-1 if r[3] is None else r[3][0] * E + r[3][1] for r in want])
 
 
-@PREFILL_SKIP
 @pytest.mark.parametrize("fmt,amode,T,E,k,H,I", [
     ("mxfp4", "mxfp4", 300, 8, 2, 256, 128),
     ("nvfp4", "bf16", 77, 16, 4, 256, 256),
@@ -235,7 +229,6 @@ def test_cached_prefill_layer_ahead(fmt, amode, T, E, k, H, I):
     pf.close()
 
 
-@PREFILL_SKIP
 def test_cached_prefill_step_needs_the_prefetch():
     """A step whose layer was not prefetched fails with MOE_ECACHE and leaves the cache unchanged."""
     from fp4_expert_ffn_amd.layer import CachedPrefill
