@@ -45,6 +45,8 @@ def moe_w13_bytes(fmt, H, I):
     n = 2 * H * I
     if fmt == "bf16":
         return 2 * n
+    if fmt == "fp8":
+        return n + 8
     if fmt == "mxfp4":
         return n // 2 + n // 32
     return n // 2 + n // 16 + 8
@@ -101,10 +103,13 @@ WORKLOADS = {
     "decode": "decode A3B-like NVFP4 (hidden 2048, 128 experts, top-8, inter 768), batches 1+4+16",
     "prefill-mxfp4": "prefill A3B-like 4096 tokens, MXFP4 weights x MXFP4 activations",
     "prefill-bf16": "prefill A3B-like 4096 tokens, BF16 weights",
+    "prefill-nvfp4": "prefill A3B-like 4096 tokens, NVFP4 weights decoded to bf16, bf16 activations",
+    "prefill-fp8": "prefill A3B-like 4096 tokens, FP8 weights decoded to bf16, bf16 activations",
     "large-decode": "large-expert layer (hidden 7168, 256+1 shared MXFP4 experts, inter 2048), 1 token",
     "large-prefill": "large-expert layer, 2048 tokens, MXFP4 activations",
 }
 DTYPES = {"decode": "nvfp4xbf16->f32", "prefill-mxfp4": "mxfp4xmxfp4->f32", "prefill-bf16": "bf16->f32",
+          "prefill-nvfp4": "nvfp4->bf16xbf16->f32", "prefill-fp8": "fp8->bf16xbf16->f32",
           "large-decode": "mxfp4xbf16->f32", "large-prefill": "mxfp4xmxfp4->f32"}
 
 
@@ -119,10 +124,11 @@ def workload_spec(wl, copies_arg):
         inputs = [[synth.decode_batch(T, i) for T in (1, 4, 16)] for i in range(64)]
         return synth.A3B, "nvfp4", "bf16", [1, 4, 16], False, inputs, copies_arg or 16, 300, 30
     if wl.startswith("prefill"):
-        fmt = "mxfp4" if wl == "prefill-mxfp4" else "bf16"
-        # two weight copies alternate across calls (the experts' 320 / 1200 MB
-        # exceed the 256 MB last-level cache either way)
-        return synth.A3B, fmt, fmt, [4096], False, [[synth.prefill_batch(4096)]], copies_arg or 2, 20, 3
+        fmt = wl[len("prefill-"):]
+        amode = "mxfp4" if fmt == "mxfp4" else "bf16"
+        # two weight copies alternate across calls (the experts' 320 MB and
+        # more exceed the 256 MB last-level cache either way)
+        return synth.A3B, fmt, amode, [4096], False, [[synth.prefill_batch(4096)]], copies_arg or 2, 20, 3
     T = 1 if wl == "large-decode" else 2048
     if T == 1:
         inputs = [[synth.large_batch(1, batch_index=i)] for i in range(16)]
@@ -290,6 +296,9 @@ def layer_workload(wl, args, torch, dev, steps=None, warmup=None, cpu_baseline=T
 
     if wl == "prefill-bf16":
         kname = "k_fp4_gemm<0, false> (gate/up projection + SwiGLU, bf16 weights on bf16 matrix cores)"
+    elif wl in ("prefill-nvfp4", "prefill-fp8"):
+        kname = f"k_mfma_ffn<false, 0, *, {fmt}> (gate/up projection + SwiGLU, {fmt} weights decoded to bf16 " \
+                "in LDS, bf16 matrix cores)"
     elif amode == "mxfp4":
         kname = "k_fp4_gemm<0, true> (gate/up projection + SwiGLU, FP4 matrix cores)"
     elif fmt == "nvfp4":
@@ -297,7 +306,13 @@ def layer_workload(wl, args, torch, dev, steps=None, warmup=None, cpu_baseline=T
     else:
         kname = "k_gemv (gate/up projection + SwiGLU, bf16 operands)"
     # The large-expert prefill sits below the FP4 ridge (about 267 FLOP/B): HBM bounds it.
-    if amode == "mxfp4" and wl != "large-prefill":
+    if wl in ("prefill-nvfp4", "prefill-fp8"):
+        # 4.5 / 8.5 bits per weight: compute-bound on the bf16 matrix cores
+        ach = flops_per_launch / dom_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_PEAK_TFLOPS["bf16"], 4)}
+        roof["hbm_gbs_same_kernel"] = round(bytes_per_launch / dom_s / 1e9, 1)
+    elif amode == "mxfp4" and wl != "large-prefill":
         ach = flops_per_launch / dom_s / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS["fp4"], "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_PEAK_TFLOPS["fp4"], 4)}
@@ -383,7 +398,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill-mxfp4", "prefill-bf16", "large-decode", "large-prefill", "stream"])
+                    choices=["decode", "prefill-mxfp4", "prefill-bf16", "prefill-nvfp4", "prefill-fp8", "large-decode",
+                             "large-prefill", "stream"])
     ap.add_argument("--copies", type=int, default=None, help="HBM copies of the layer's experts, rotated per call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill-leg", action="store_true", help="decode: skip the prefill_mxfp4 leg")

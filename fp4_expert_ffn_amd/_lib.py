@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ENOMEM, MOE_ECACHE = range(6)
-FMT = {"bf16": 0, "mxfp4": 1, "nvfp4": 2}
+FMT = {"bf16": 0, "mxfp4": 1, "nvfp4": 2, "fp8": 3}
 AMODE = {"bf16": 0, "mxfp4": 1}
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_EUNSUPPORTED", 3: "MOE_EHIP", 4: "MOE_ENOMEM", 5: "MOE_ECACHE"}
 

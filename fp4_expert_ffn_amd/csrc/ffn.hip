@@ -21,7 +21,9 @@ hipError_t launch_fp4_codes_canon(const FfnParams& P, const MfmaBufs& B, int whi
 namespace {
 using namespace moe;
 
-// Row count at or above which BF16 weights take the bf16 MFMA grouped GEMM.
+// Row count at or above which bf16-activation calls take the bf16 MFMA
+// grouped GEMM (BF16 weights as they are; NVFP4, MXFP4 and FP8 weights
+// decoded to bf16 on the way into LDS).
 constexpr long long kMfmaMinRows = 512;
 // Largest H and I of the GEMV path (one bf16 row of x or h per LDS stage).
 constexpr int kGemvMaxK = 28672;
@@ -30,7 +32,7 @@ enum Path { kPathGemv, kPathMfmaFp4, kPathMfmaBf16 };
 
 Path choose_path(const moe_ffn_args* a) {
   if (a->amode == MOE_ACT_MXFP4) return kPathMfmaFp4;
-  if (a->wfmt == MOE_FMT_BF16 && (long long)a->T * a->k >= kMfmaMinRows) return kPathMfmaBf16;
+  if ((long long)a->T * a->k >= kMfmaMinRows) return kPathMfmaBf16;
   return kPathGemv;
 }
 
@@ -75,7 +77,8 @@ moe_status check_args(const moe_ffn_args* a) {
                 "moe_expert_ffn: bad sizes T=%d k=%d E=%d", a->T, a->k, a->E);
   MOE_CHECK_ARG(a->H > 0 && a->I > 0 && a->H % 128 == 0 && a->I % 128 == 0,
                 "moe_expert_ffn: H=%d and I=%d must be positive multiples of 128", a->H, a->I);
-  MOE_CHECK_ARG(a->wfmt == MOE_FMT_BF16 || a->wfmt == MOE_FMT_MXFP4 || a->wfmt == MOE_FMT_NVFP4,
+  MOE_CHECK_ARG(a->wfmt == MOE_FMT_BF16 || a->wfmt == MOE_FMT_MXFP4 || a->wfmt == MOE_FMT_NVFP4 ||
+                    a->wfmt == MOE_FMT_FP8,
                 "moe_expert_ffn: bad weight format %d", a->wfmt);
   MOE_CHECK_ARG(a->amode == MOE_ACT_BF16 || a->amode == MOE_ACT_MXFP4, "moe_expert_ffn: bad amode %d", a->amode);
   if (a->amode == MOE_ACT_MXFP4 && a->wfmt != MOE_FMT_MXFP4)
@@ -204,6 +207,18 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ blo
     for (int i = 0; i < 4; ++i) {
       o[c0 + 2 * i] = __uint_as_float(w[i] << 16);
       o[c0 + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+    return;
+  }
+  if (fmt == MOE_FMT_FP8) {
+    const int c0 = kt * 64 + (lane >> 4) * 16;
+    const float g = which == 0 ? bv.g_gate : (which == 1 ? bv.g_up : bv.g_down);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    for (int i = 0; i < 4; ++i) {
+      o[c0 + 4 * i + 0] = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 0) * g;
+      o[c0 + 4 * i + 1] = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 1) * g;
+      o[c0 + 4 * i + 2] = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 2) * g;
+      o[c0 + 4 * i + 3] = __builtin_amdgcn_cvt_f32_fp8((int)w[i], 3) * g;
     }
     return;
   }

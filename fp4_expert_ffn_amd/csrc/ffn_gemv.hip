@@ -49,6 +49,12 @@ struct Fmt<MOE_FMT_NVFP4> {
   static constexpr bool F16 = true;
   using V = f16x8_t;
 };
+template <>
+struct Fmt<MOE_FMT_FP8> {
+  static constexpr int KT = 64, SPT = 2;
+  static constexpr bool F16 = true;
+  using V = f16x8_t;
+};
 
 template <int FMT>
 __device__ __forceinline__ f32x4_t mma(typename Fmt<FMT>::V a, typename Fmt<FMT>::V b, f32x4_t c) {
@@ -78,12 +84,20 @@ __device__ __forceinline__ ScaleT<FMT> load_scale_at(const uint8_t* p) {
 // scale applied exactly: E2M1 x E8M0 in bf16 (the conversion applies the
 // power of two); E2M1 x E4M3 in fp16, where the product (at most 5
 // significant bits, magnitude in [2^-10, 2688]) is exact, so one packed
-// fp16 multiply applies the scale.  For the 4-bit formats step s takes the
-// lane's values 8s..8s+7 (its 32 values cover 4 steps).
+// fp16 multiply applies the scale; E4M3 (FP8) in fp16 as it is.  For the
+// 4-bit formats step s takes the lane's values 8s..8s+7 (its 32 values
+// cover 4 steps), for FP8 its 16 values cover 2 steps.
 template <int FMT, int S>
 __device__ __forceinline__ typename Fmt<FMT>::V bfrag(const uint4 q, uint32_t sc) {
   if constexpr (FMT == MOE_FMT_BF16) {
     return __builtin_bit_cast(bf16x8_t, q);
+  } else if constexpr (FMT == MOE_FMT_FP8) {
+    const uint32_t lo = S == 0 ? q.x : q.z, hi = S == 0 ? q.y : q.w;
+    const f16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+    const f16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+    const f16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+    const f16x2_t e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+    return f16x8_t{a.x, a.y, b.x, b.y, c.x, c.y, e.x, e.y};
   } else {
     const uint32_t d = S == 0 ? q.x : S == 1 ? q.y : S == 2 ? q.z : q.w;
     if constexpr (FMT == MOE_FMT_MXFP4) {
@@ -415,7 +429,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   // Vector-memory loads of one bank: SUB tiles and SUB scale loads (4-bit
   // formats; 64 or 128 bytes apart, never merged).
-  constexpr int kBankLoads = SUB + (FMT == MOE_FMT_BF16 ? 0 : SUB);
+  constexpr int kBankLoads = SUB + (kScaleTileBytes<FMT> ? SUB : 0);
 
   // XALL: every token row of x, in token order, before the first task (whose
   // first weights then go out behind them)
@@ -480,7 +494,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int arow_i = XALL ? row_token(P, A, blk, am) : am;
     // this lane's fragment base: K-group grp of its row (values 32 grp + 8 st
     // of each 128-value K-tile, or 8 grp of each 32-value one)
-    const uint8_t* abase = act + (size_t)arow_i * row_bytes(K) + (F::SPT == 4 ? 64 : 16) * grp;
+    const uint8_t* abase = act + (size_t)arow_i * row_bytes(K) + (F::KT / 2) * grp;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     // The epilogue runs after every sub-item (uniform code: no branch around
     // memory operations inside the pipelined loop); before an item's last
@@ -508,6 +522,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if constexpr (F::SPT == 4) {
           bv = st == 0 ? bfrag<FMT, 0>(b.q[j], b.sc[j]) : st == 1 ? bfrag<FMT, 1>(b.q[j], b.sc[j])
              : st == 2 ? bfrag<FMT, 2>(b.q[j], b.sc[j]) : bfrag<FMT, 3>(b.q[j], b.sc[j]);
+        } else if constexpr (F::SPT == 2) {
+          bv = st == 0 ? bfrag<FMT, 0>(b.q[j], b.sc[j]) : bfrag<FMT, 1>(b.q[j], b.sc[j]);
         } else {
           bv = bfrag<FMT, 0>(b.q[j], b.sc[j]);
         }
@@ -643,7 +659,7 @@ typedef void (*GemvKernel)(FfnParams, GemvArgs);
 // Sub-item size: the largest of 16 (only when it is all of K, and not for
 // NVFP4, whose decode needs more registers), 8, 6, 4, 2, 1 K-tiles dividing nk.
 template <int FMT>
-constexpr int kSubMax = FMT == MOE_FMT_NVFP4 ? 8 : 16;
+constexpr int kSubMax = (FMT == MOE_FMT_NVFP4 || FMT == MOE_FMT_FP8) ? 8 : 16;
 
 template <int FMT, bool DOWN, bool XALL>
 static GemvKernel gemv_kernel(int nk) {
@@ -727,6 +743,7 @@ static hipError_t set_gemv_lds_limits() {
     if ((e = set_lds_limits_fmt<MOE_FMT_BF16>()) != hipSuccess) return e;
     if ((e = set_lds_limits_fmt<MOE_FMT_MXFP4>()) != hipSuccess) return e;
     if ((e = set_lds_limits_fmt<MOE_FMT_NVFP4>()) != hipSuccess) return e;
+    if ((e = set_lds_limits_fmt<MOE_FMT_FP8>()) != hipSuccess) return e;
     done = true;
   }
   return hipSuccess;
@@ -739,6 +756,7 @@ hipError_t launch_gemv(const FfnParams& P, const GemvArgs& G, hipStream_t s) {
     case MOE_FMT_BF16: return launch_fmt<MOE_FMT_BF16>(P, G, s);
     case MOE_FMT_MXFP4: return launch_fmt<MOE_FMT_MXFP4>(P, G, s);
     case MOE_FMT_NVFP4: return launch_fmt<MOE_FMT_NVFP4>(P, G, s);
+    case MOE_FMT_FP8: return launch_fmt<MOE_FMT_FP8>(P, G, s);
   }
   return hipErrorInvalidValue;
 }

@@ -198,8 +198,39 @@ __device__ inline TileJob find_tile(const FfnParams& P, int NT) {
 
 enum { kGateUp = 0, kDown = 1 };
 
-template <bool FP4, int MODE, int D>
+// Weights decoded to bf16 as they are stored to LDS (bf16 activations, the
+// bf16 MFMA): E2M1 times its block scale (NVFP4: E4M3, MXFP4: E8M0) or an
+// E4M3 value (FP8) has at most 6 significant bits and a magnitude inside
+// bf16's range, so each decoded weight is exact; NVFP4 and FP8 per-tensor
+// multipliers scale the fp32 sums in the epilogue.
+__device__ __forceinline__ uint32_t bf16_pair_scaled(float a, float b, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a * sc, b * sc}, bf16x2_t));
+}
+
+// 8 bf16 values (16 bytes) of E2M1 codes `d` (8 nibbles, element 2i low) times sc.
+__device__ __forceinline__ uint4 e2m1x8_to_bf16(uint32_t d, float sc) {
+  const f32x2_t v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2),
+                        __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3)};
+  return make_uint4(bf16_pair_scaled(v[0].x, v[0].y, sc), bf16_pair_scaled(v[1].x, v[1].y, sc),
+                    bf16_pair_scaled(v[2].x, v[2].y, sc), bf16_pair_scaled(v[3].x, v[3].y, sc));
+}
+
+// 8 bf16 values of 8 E4M3 codes (two dwords), exact.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true)));
+}
+
+// WQ: with FP4 false, the weight format: MOE_FMT_BF16 (copied), or NVFP4,
+// MXFP4 or FP8 (decoded to bf16 at the LDS store).
+template <bool FP4, int MODE, int D, int WQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_mfma_ffn(FfnParams P, MfmaBufs B) {
+  constexpr bool DEC = !FP4 && WQ != MOE_FMT_BF16;  // weights decoded at the LDS store
+  constexpr bool Q4 = DEC && WQ != MOE_FMT_FP8;     // E2M1 weights with block scales
   const int K = MODE == kGateUp ? P.H : P.I;
   const int NT = MODE == kGateUp ? (2 * P.I) / kBN : P.H / kBN;
   const TileJob tj = find_tile(P, NT);
@@ -220,7 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wm = wave >> 1, wn = wave & 1;
   const uint8_t* wt = tj.blob + (MODE == kGateUp ? P.L.off_w13 : P.L.off_w2);
   const uint8_t* st = tj.blob + (MODE == kGateUp ? P.L.off_s13 : P.L.off_s2);
-  const int nk_w = K / (FP4 ? 128 : 32);  // weight K-tiles per row-group
+  const int nk_w = K / (FP4 ? 128 : k_per_tile(WQ));  // weight K-tiles per row-group
   const int rg0 = tj.nt * 8;              // first 16-row group of the column tile
 
   // Operand A: thread t stages 16-byte segment t % 8 of rows t / 8 + 32 i
@@ -263,6 +294,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     uint4 a[4], b[4];
     uint32_t sa, sb;
   };
+  // per-tensor multipliers of the decoded formats (gate, up, down)
+  float gq = 1.f, uq = 1.f, dq = 1.f;
+  if constexpr (DEC) {
+    const BlobHeader* hd = reinterpret_cast<const BlobHeader*>(tj.blob);
+    gq = hd->g[0];
+    uq = hd->g[1];
+    dq = hd->g[2];
+  }
   const int nsteps = (K + KSTEP - 1) / KSTEP;
   // FP4 with K % 256 == 128: the last step holds one K-tile; its second
   // half re-reads the first half's addresses (in bounds, finite) and is
@@ -273,8 +312,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       S.a[i] = *reinterpret_cast<const uint4*>(abase + mfma_step_off(aoff[i], ks, 128u, mfma_a_back(tid, tail)));
-      S.b[i] = *reinterpret_cast<const uint4*>(
-          wt + mfma_step_off(mfma_b_base(rg0, nk_w, tid, i), ks, 2u * kTileBytes, mfma_b_back(tid, tail)));
+      if constexpr (!DEC)
+        S.b[i] = *reinterpret_cast<const uint4*>(
+            wt + mfma_step_off(mfma_b_base(rg0, nk_w, tid, i), ks, 2u * kTileBytes, mfma_b_back(tid, tail)));
+    }
+    if constexpr (Q4) {
+      S.b[0] = *reinterpret_cast<const uint4*>(wt + mfma_q4_b_off(rg0, nk_w, tid, ks));
+      constexpr uint32_t lsb = WQ == MOE_FMT_NVFP4 ? 2 : 1;
+      const uint8_t* sp = st + mfma_q4_s_off(rg0, nk_w, tid, ks, lsb);
+      S.sb = WQ == MOE_FMT_NVFP4 ? (uint32_t)*reinterpret_cast<const uint16_t*>(sp) : (uint32_t)*sp;
+    } else if constexpr (DEC) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) S.b[i] = *reinterpret_cast<const uint4*>(wt + mfma_f8_b_off(rg0, nk_w, tid, i, ks));
     }
     if (FP4) {
       S.sa = *reinterpret_cast<const uint32_t*>(asbase + mfma_step_off(as_off, ks, 8u, mfma_sa_back(tid, tail)));
@@ -289,7 +338,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const uint32_t k = (0u - ((avalid >> i) & 1u)) & lk & ((tail && seg >= 4) ? 0u : 0xFFFFFFFFu);  // bit masks
       *reinterpret_cast<uint4*>(buf + ((tid >> 3) + 32 * i) * kArow + seg * 16) =
           make_uint4(S.a[i].x & k, S.a[i].y & k, S.a[i].z & k, S.a[i].w & k);
-      reinterpret_cast<uint4*>(buf + kBoff)[tid + 256 * i] = S.b[i];
+      if constexpr (!DEC) reinterpret_cast<uint4*>(buf + kBoff)[tid + 256 * i] = S.b[i];
+    }
+    // decoded weights, in the bf16 layout: chunk (row group g, K-tile kt of
+    // the step, lane l) at index (2 g + kt) * 64 + l, lane l = row l % 16,
+    // values 8 (l / 16) .. + 8 of the 32-value K-tile
+    uint4* bl = reinterpret_cast<uint4*>(buf + kBoff);
+    if constexpr (Q4) {
+      // tile lane 32 (ks % 2) + tid % 32: row r, values 32 j .. 32 j + 31 of the step
+      const int g = tid >> 5, r = tid & 15, j = (tid >> 4) & 1;
+      float s0, s1;
+      if constexpr (WQ == MOE_FMT_NVFP4) {
+        s0 = __builtin_amdgcn_cvt_f32_fp8((int)S.sb, 0);  // E4M3 of values 0..15
+        s1 = __builtin_amdgcn_cvt_f32_fp8((int)S.sb, 1);  // and 16..31
+      } else {
+        s0 = s1 = e8m0_to_f32(S.sb);
+      }
+      bl[(2 * g + j) * 64 + r] = e2m1x8_to_bf16(S.b[0].x, s0);
+      bl[(2 * g + j) * 64 + r + 16] = e2m1x8_to_bf16(S.b[0].y, s0);
+      bl[(2 * g + j) * 64 + r + 32] = e2m1x8_to_bf16(S.b[0].z, s1);
+      bl[(2 * g + j) * 64 + r + 48] = e2m1x8_to_bf16(S.b[0].w, s1);
+    } else if constexpr (DEC) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // chunk tid + 256 i: row group c / 64, tile lane l = c % 64: row l % 16,
+        // values 16 (l / 16) .. + 16 = K-tile l / 32, chunks 2 ((l / 16) % 2) and + 1
+        const int c = tid + 256 * i, g = c >> 6, l = c & 63, r = l & 15, kt = l >> 5, q = 2 * ((l >> 4) & 1);
+        bl[(2 * g + kt) * 64 + r + 16 * q] = e4m3x8_to_bf16(S.b[i].x, S.b[i].y);
+        bl[(2 * g + kt) * 64 + r + 16 * (q + 1)] = e4m3x8_to_bf16(S.b[i].z, S.b[i].w);
+      }
     }
     if (FP4) {
       const uint32_t k = askeep & lk & ((tail && (tid & 1)) ? 0u : 0xFFFFFFFFu);
@@ -400,10 +477,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const size_t o = ((size_t)tj.p0 + tj.m0 + row) * P.H + tj.nt * kBN + (4 * wn) * 16 + col;
           if (B.yb) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) B.yb[o + 16 * j] = f32_to_bf16_rne(acc[i][j][v]);
+            for (int j = 0; j < 4; ++j) B.yb[o + 16 * j] = f32_to_bf16_rne(acc[i][j][v] * dq);
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) B.y[o + 16 * j] = acc[i][j][v];
+            for (int j = 0; j < 4; ++j) B.y[o + 16 * j] = acc[i][j][v] * dq;
           }
         }
       }
@@ -418,7 +495,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int row = (4 * wm + i) * 16 + rq + v;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        const float g = acc[i][2 * jj][v], u = acc[i][2 * jj + 1][v];
+        const float g = acc[i][2 * jj][v] * gq, u = acc[i][2 * jj + 1][v] * uq;
         ht[row * 64 + (2 * wn + jj) * 16 + col] = silu_f32(g) * u;
       }
     }
@@ -464,12 +541,13 @@ static int max_tiles(const FfnParams& P, int NT) {
 typedef void (*MfmaKernel)(FfnParams, MfmaBufs);
 
 // Pipeline depth: 2 register stages for FP4 (its operands and scales leave
-// no room for a third), 3 for BF16 when the K-steps divide by 3.
-template <bool FP4, int MODE>
+// no room for a third) and the decoded formats, 3 for BF16 when the K-steps
+// divide by 3.
+template <bool FP4, int MODE, int WQ = MOE_FMT_BF16>
 static MfmaKernel mfma_kernel(int nsteps) {
-  if constexpr (!FP4)
-    if (nsteps % 3 == 0) return k_mfma_ffn<FP4, MODE, 3>;
-  return k_mfma_ffn<FP4, MODE, 2>;
+  if constexpr (!FP4 && WQ == MOE_FMT_BF16)
+    if (nsteps % 3 == 0) return k_mfma_ffn<FP4, MODE, 3, WQ>;
+  return k_mfma_ffn<FP4, MODE, 2, WQ>;
 }
 
 bool fp4_gemm_fits(const FfnParams& P, int N, int K, bool gateup);
@@ -550,6 +628,26 @@ hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStrea
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     launch(mfma_kernel<true, kDown>((P.I + 255) / 256), dim3(max_tiles(P, P.H / kBN)), dim3(256), 0, s, P, B);
+    return hipGetLastError();
+  }
+  if (P.fmt != MOE_FMT_BF16) {
+    // NVFP4, MXFP4 or FP8 weights with bf16 activations: decoded at the LDS store
+    const int nt_gu = (2 * P.I) / kBN, nt_dn = P.H / kBN;
+    MfmaKernel gu, dn;
+    if (P.fmt == MOE_FMT_NVFP4) {
+      gu = mfma_kernel<false, kGateUp, MOE_FMT_NVFP4>(P.H / 64);
+      dn = mfma_kernel<false, kDown, MOE_FMT_NVFP4>(P.I / 64);
+    } else if (P.fmt == MOE_FMT_MXFP4) {
+      gu = mfma_kernel<false, kGateUp, MOE_FMT_MXFP4>(P.H / 64);
+      dn = mfma_kernel<false, kDown, MOE_FMT_MXFP4>(P.I / 64);
+    } else {
+      gu = mfma_kernel<false, kGateUp, MOE_FMT_FP8>(P.H / 64);
+      dn = mfma_kernel<false, kDown, MOE_FMT_FP8>(P.I / 64);
+    }
+    launch(gu, dim3(max_tiles(P, nt_gu)), dim3(256), 0, s, P, B);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch(dn, dim3(max_tiles(P, nt_dn)), dim3(256), 0, s, P, B);
     return hipGetLastError();
   }
   if (bf16_gemm_fits(P, 2 * P.I, P.H) && bf16_gemm_fits(P, P.H, P.I)) {

@@ -37,6 +37,8 @@ void pack_codes_tile(const uint8_t* src_row0, size_t src_row_bytes, int kt_idx, 
     const uint8_t* s;
     if (fmt == MOE_FMT_BF16)
       s = src_row0 + (size_t)r * src_row_bytes + ((size_t)kt_idx * kt + kb * 8) * 2;
+    else if (fmt == MOE_FMT_FP8)
+      s = src_row0 + (size_t)r * src_row_bytes + (size_t)kt_idx * kt + kb * 16;
     else
       s = src_row0 + (size_t)r * src_row_bytes + ((size_t)kt_idx * kt + kb * 32) / 2;
     memcpy(tile + l * 16, s, 16);
@@ -67,7 +69,7 @@ extern "C" moe_status moe_prepack_expert(const moe_expert_canonical* src, void* 
   MOE_CHECK_ARG(blob_bytes >= L.total, "moe_prepack_expert: blob_bytes %zu < %llu", blob_bytes,
                 (unsigned long long)L.total);
   const int fmt = src->fmt, H = src->H, I = src->I, kt = moe::k_per_tile(fmt);
-  const bool fp4 = fmt != MOE_FMT_BF16;
+  const bool fp4 = fmt == MOE_FMT_MXFP4 || fmt == MOE_FMT_NVFP4;  // block scales present
   MOE_CHECK_ARG(src->gate_q && src->up_q && src->down_q, "moe_prepack_expert: null weight tensor");
   MOE_CHECK_ARG(!fp4 || (src->gate_s && src->up_s && src->down_s), "moe_prepack_expert: null scale tensor");
 
@@ -79,7 +81,7 @@ extern "C" moe_status moe_prepack_expert(const moe_expert_canonical* src, void* 
   h->fmt = fmt;
   h->H = H;
   h->I = I;
-  const bool nv = fmt == MOE_FMT_NVFP4;
+  const bool nv = fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_FP8;  // per-tensor multipliers
   h->g[0] = nv ? src->gate_g : 1.0f;
   h->g[1] = nv ? src->up_g : 1.0f;
   h->g[2] = nv ? src->down_g : 1.0f;
@@ -90,7 +92,9 @@ extern "C" moe_status moe_prepack_expert(const moe_expert_canonical* src, void* 
   h->total = L.total;
 
   // bytes per row of the canonical code / scale tensors
-  auto row_bytes = [&](int cols) -> size_t { return fp4 ? (size_t)cols / 2 : (size_t)cols * 2; };
+  auto row_bytes = [&](int cols) -> size_t {
+    return fp4 ? (size_t)cols / 2 : (fmt == MOE_FMT_FP8 ? (size_t)cols : (size_t)cols * 2);
+  };
   auto srow_bytes = [&](int cols) -> size_t { return fmt == MOE_FMT_MXFP4 ? (size_t)cols / 32 : (size_t)cols / 16; };
   const int sb = moe::scale_bytes_per_tile(fmt);
 

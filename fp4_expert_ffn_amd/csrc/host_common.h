@@ -42,9 +42,9 @@ inline moe_status ok() { return MOE_OK; }
 //
 // Every section is a sequence of 1 KiB tiles, ordered (row-group, K-tile)
 // with K fastest.  A tile covers 16 rows x KT columns, KT = 128 for the 4-bit
-// formats and 32 for BF16, and lists 64 lanes' 16-byte fragments in lane
+// formats, 64 for FP8 and 32 for BF16, and lists 64 lanes' 16-byte fragments in lane
 // order: lane l holds row (l % 16) and the K-chunk (l / 16) of the tile
-// (32 E2M1 codes, or 8 bf16 values).  This is the operand layout of the
+// (32 E2M1 codes, 16 E4M3 codes, or 8 bf16 values).  This is the operand layout of the
 // gfx950 16x16x128 (FP4) and 16x16x32 (BF16) MFMA B-fragments, and it makes
 // every wave-wide 16-byte load one contiguous 1 KiB transaction.
 //
@@ -67,7 +67,9 @@ struct BlobHeader {
 };
 static_assert(sizeof(BlobHeader) == kHeaderBytes, "header size");
 
-__host__ __device__ inline int k_per_tile(int fmt) { return fmt == MOE_FMT_BF16 ? 32 : 128; }
+__host__ __device__ inline int k_per_tile(int fmt) {
+  return fmt == MOE_FMT_BF16 ? 32 : (fmt == MOE_FMT_FP8 ? 64 : 128);
+}
 __host__ __device__ inline int scale_bytes_per_tile(int fmt) {
   return fmt == MOE_FMT_MXFP4 ? 64 : (fmt == MOE_FMT_NVFP4 ? 128 : 0);
 }
@@ -79,7 +81,7 @@ struct BlobLayout {
 };
 
 inline bool layout_of(int fmt, int H, int I, BlobLayout* L) {
-  if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_NVFP4) return false;
+  if (fmt != MOE_FMT_BF16 && fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_FP8) return false;
   if (H <= 0 || I <= 0 || H % 128 || I % 128) return false;
   const int kt = k_per_tile(fmt), sb = scale_bytes_per_tile(fmt);
   L->tiles13 = (2 * I / 16) * (H / kt);

@@ -59,4 +59,27 @@ __host__ __device__ inline uint32_t mfma_sb_back(int tid, bool tail) {
   return (tail && ((tid >> 4) & 1)) ? 64u : 0u;
 }
 
+// ---- weights decoded to bf16 as they are stored to LDS (bf16 activations).
+// A K-step covers 64 values.  E2M1 tiles (NVFP4, MXFP4) hold 128 values, so
+// a step reads half of a tile of each of the column tile's 8 row groups:
+// thread tid takes lane 32 (ks % 2) + tid % 32 of the tile of row group
+// rg0 + tid / 32, 16 bytes (32 values), and its scale bytes (lane_sb each:
+// 2 for NVFP4, 1 for MXFP4).
+__host__ __device__ inline uint32_t mfma_q4_tile(int rg0, int nk_w, int tid, int ks) {
+  return (uint32_t)(rg0 + (tid >> 5)) * (uint32_t)nk_w + (uint32_t)(ks >> 1);
+}
+__host__ __device__ inline uint32_t mfma_q4_lane(int tid, int ks) { return 32u * (uint32_t)(ks & 1) + (uint32_t)(tid & 31); }
+__host__ __device__ inline uint32_t mfma_q4_b_off(int rg0, int nk_w, int tid, int ks) {
+  return mfma_q4_tile(rg0, nk_w, tid, ks) * 1024u + mfma_q4_lane(tid, ks) * 16u;
+}
+__host__ __device__ inline uint32_t mfma_q4_s_off(int rg0, int nk_w, int tid, int ks, uint32_t lane_sb) {
+  return mfma_q4_tile(rg0, nk_w, tid, ks) * 64u * lane_sb + mfma_q4_lane(tid, ks) * lane_sb;
+}
+// FP8 tiles hold 64 values: a step reads the whole tile of each row group,
+// chunk c = tid + 256 i (i < 2) being lane c % 64 of row group rg0 + c / 64.
+__host__ __device__ inline uint32_t mfma_f8_b_off(int rg0, int nk_w, int tid, int i, int ks) {
+  const uint32_t c = (uint32_t)tid + 256u * (uint32_t)i;
+  return ((uint32_t)(rg0 + (int)(c >> 6)) * (uint32_t)nk_w + (uint32_t)ks) * 1024u + (c & 63u) * 16u;
+}
+
 }  // namespace moe

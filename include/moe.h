@@ -52,7 +52,7 @@ typedef enum {
   MOE_ECACHE = 5         /* a step needs more distinct experts than slots    */
 } moe_status;
 
-typedef enum { MOE_FMT_BF16 = 0, MOE_FMT_MXFP4 = 1, MOE_FMT_NVFP4 = 2 } moe_wfmt;
+typedef enum { MOE_FMT_BF16 = 0, MOE_FMT_MXFP4 = 1, MOE_FMT_NVFP4 = 2, MOE_FMT_FP8 = 3 } moe_wfmt;
 typedef enum { MOE_ACT_BF16 = 0, MOE_ACT_MXFP4 = 1 } moe_amode;
 
 /* Thread-local description of the last non-OK status of this thread. */
@@ -116,7 +116,9 @@ typedef struct {
    *   MXFP4: q_* = E2M1 codes [rows, cols/2] (element 2i in the low nibble),
    *          s_* = E8M0 codes [rows, cols/32]
    *   NVFP4: q_* as MXFP4, s_* = E4M3FN codes [rows, cols/16],
-   *          g_* = per-tensor dequant multiplier (w = E2M1 * E4M3 * g)     */
+   *          g_* = per-tensor dequant multiplier (w = E2M1 * E4M3 * g)
+   *   FP8  : q_* = E4M3FN codes [rows, cols], s_* unused,
+   *          g_* = per-tensor dequant multiplier (w = E4M3 * g)            */
   const void* gate_q; const uint8_t* gate_s; float gate_g;
   const void* up_q;   const uint8_t* up_s;   float up_g;
   const void* down_q; const uint8_t* down_s; float down_g;
@@ -124,7 +126,8 @@ typedef struct {
 
 /* Bytes of one expert blob for (fmt, H, I); 0 if the shape is unsupported.
  * [page "FreeToken量子化：...", 3rd paragraph: MXFP4, NVFP4 and BF16 expert
- *  checkpoints; paragraph on the two-tier expert memory hierarchy: every
+ *  checkpoints; bhrtaym-blog page, section on models and quantisation
+ *  formats: MXFP4, NVFP4, FP8 and BF16; paragraph on the two-tier expert memory hierarchy: every
  *  routed expert is held in host RAM and copied whole into a GPU cache slot,
  *  so one expert is one fixed-size blob.]  H and I must be multiples of 128
  *  (this library's tile width; every shape the pages name satisfies it). */

@@ -14,9 +14,14 @@ The bit layouts are the public specifications:
 * MXFP4: 32 E2M1 elements share one E8M0 scale.
 * NVFP4: 16 E2M1 elements share one E4M3 scale, times one fp32 per-tensor
   multiplier g.
+* FP8 (page "「8GBのGPUで35Bモデルが動く」…" on the bhrtaym blog, section on
+  models and quantisation formats, names FP8 without its scaling; this is
+  the plainest reading): E4M3FN elements times one fp32 per-tensor
+  multiplier g.
 
 Packing (canonical layout produced by ``synth``): [rows, cols/2] bytes, element
 2i in the low nibble of byte i; scales [rows, cols/B] with B = 32 or 16.
+FP8: one E4M3FN code per byte, [rows, cols].
 """
 from __future__ import annotations
 
@@ -68,10 +73,12 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 def dequant(proj, fmt: str) -> np.ndarray:
     """Exact dequantised weights [rows, cols] in float64.
 
-    MXFP4: E2M1 * E8M0.  NVFP4: (E2M1 * E4M3) * g.  BF16: the bf16 value.
-    Every product is exact in float64."""
+    MXFP4: E2M1 * E8M0.  NVFP4: (E2M1 * E4M3) * g.  FP8: E4M3 * g.  BF16:
+    the bf16 value.  Every product is exact in float64."""
     if fmt == "bf16":
         return bf16_to_f64(proj.w)
+    if fmt == "fp8":
+        return E4M3[np.asarray(proj.q, dtype=np.uint8)] * float(np.float32(proj.g))
     vals = E2M1[unpack_e2m1(proj.q)]
     if fmt == "mxfp4":
         return vals * np.repeat(E8M0[proj.s], 32, axis=1)

@@ -50,6 +50,7 @@ def _load():
         lib.synth_weight_bf16.argtypes = [u64, u64, f32, i32, i32, vp]
         lib.synth_weight_mxfp4.argtypes = [u64, u64, f32, i32, i32, vp, vp]
         lib.synth_weight_nvfp4.argtypes = [u64, u64, f32, i32, i32, vp, vp, vp]
+        lib.synth_weight_fp8.argtypes = [u64, u64, f32, i32, i32, vp, vp]
         _lib = lib
     return _lib
 
@@ -78,7 +79,7 @@ def stream_id(config: int, layer: int, expert: int, tensor: int) -> int:
     return ((config & 0xFF) << 56) | ((layer & 0xFFFF) << 40) | ((expert & 0xFFFFFF) << 16) | (tensor & 0xFFFF)
 
 
-FMTS = ("bf16", "mxfp4", "nvfp4")
+FMTS = ("bf16", "mxfp4", "nvfp4", "fp8")
 SHARED_EXPERT = 0xFFFFFF  # expert id used in stream_id() for the always-on shared expert
 
 
@@ -88,9 +89,9 @@ class Proj:
     rows: int
     cols: int
     w: np.ndarray | None = None   # bf16 bits, uint16 [rows, cols]
-    q: np.ndarray | None = None   # packed E2M1 codes, uint8 [rows, cols/2]
+    q: np.ndarray | None = None   # packed E2M1 codes, uint8 [rows, cols/2] (FP8: E4M3 codes [rows, cols])
     s: np.ndarray | None = None   # block scales: E8M0 [rows, cols/32] or E4M3 [rows, cols/16]
-    g: float = 1.0                # NVFP4 per-tensor dequant multiplier
+    g: float = 1.0                # NVFP4 / FP8 per-tensor dequant multiplier
 
 
 @dataclass
@@ -112,7 +113,7 @@ class Expert:
             for a in (p.w, p.q, p.s):
                 if a is not None:
                     n += a.nbytes
-            if self.fmt == "nvfp4":
+            if self.fmt in ("nvfp4", "fp8"):
                 n += 4
         return n
 
@@ -134,6 +135,11 @@ def _proj(fmt, seed, stream, rows, cols, std) -> Proj:
         p.s = np.empty((rows, cols // 16), np.uint8)
         g = np.zeros(1, np.float32)
         lib.synth_weight_nvfp4(seed, stream, std, rows, cols, _p(p.q), _p(p.s), _p(g))
+        p.g = float(g[0])
+    elif fmt == "fp8":
+        p.q = np.empty((rows, cols), np.uint8)
+        g = np.zeros(1, np.float32)
+        lib.synth_weight_fp8(seed, stream, std, rows, cols, _p(p.q), _p(g))
         p.g = float(g[0])
     else:
         raise ValueError(fmt)

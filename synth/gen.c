@@ -214,3 +214,21 @@ void synth_weight_nvfp4(uint64_t seed, uint64_t stream, float std, int rows, int
   }
   free(tmp);
 }
+
+/* q: [rows, cols] E4M3FN codes of w / g (round to nearest even, saturating at
+   448, sign from w); *g: the per-tensor dequant multiplier amax / 448 (1 if 0). */
+void synth_weight_fp8(uint64_t seed, uint64_t stream, float std, int rows, int cols, uint8_t* q, float* g_out) {
+  int64_t n = (int64_t)rows * cols;
+  float* tmp = (float*)malloc(sizeof(float) * (size_t)n);
+  fill_normal(seed, stream, std, tmp, n);
+  double amax_t = 0;
+  for (int64_t i = 0; i < n; ++i) amax_t = fmax(amax_t, fabs((double)tmp[i]));
+  float g = (amax_t == 0) ? 1.0f : (float)(amax_t / 448.0);
+  *g_out = g;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    double v = (double)tmp[i] / (double)g;
+    q[i] = (uint8_t)(e4m3_rne_pos(fabs(v)) | (v < 0 ? 0x80 : 0));
+  }
+  free(tmp);
+}

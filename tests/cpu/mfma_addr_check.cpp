@@ -86,6 +86,33 @@ int main(int argc, char** argv) {
       }
     }
   }
+  // ---- weights decoded at the LDS store (bf16 activations): every E2M1
+  // (NVFP4 / MXFP4) and FP8 fragment and scale of every step, for every
+  // column tile, must be the one the bf16 layout wants and stay in its section
+  if (!fp4) {
+    const int steps64 = K / 64, nk4 = K / 128, nk8 = K / 64;
+    const unsigned long long w4 = (unsigned long long)(N / 16) * nk4 * 1024, w8 = (unsigned long long)(N / 16) * nk8 * 1024;
+    for (int nt = 0; nt < N / 128; ++nt)
+      for (int ks = 0; ks < steps64; ++ks)
+        for (int tid = 0; tid < 256; ++tid) {
+          const uint32_t o = mfma_q4_b_off(nt * 8, nk4, tid, ks);
+          const long long rg = o / (1024LL * nk4), kt = (o % (1024LL * nk4)) / 1024, ln = (o % 1024) / 16;
+          if (rg != nt * 8 + tid / 32 || kt != ks / 2 || ln != 32 * (ks % 2) + tid % 32) fail("E2M1 fragment", o, tid);
+          if ((unsigned long long)o + 16 > w4) fail("E2M1 past the weights", o, w4);
+          for (uint32_t lsb : {1u, 2u}) {
+            const uint32_t so = mfma_q4_s_off(nt * 8, nk4, tid, ks, lsb);
+            if (so != (uint32_t)((rg * nk4 + kt) * 64 * lsb + ln * lsb)) fail("E2M1 scale", so, lsb);
+            if ((unsigned long long)so + lsb > (unsigned long long)(N / 16) * nk4 * 64 * lsb) fail("scale past", so, lsb);
+          }
+          for (int i = 0; i < 2; ++i) {
+            const uint32_t f = mfma_f8_b_off(nt * 8, nk8, tid, i, ks);
+            const int c = tid + 256 * i;
+            const long long frg = f / (1024LL * nk8), fkt = (f % (1024LL * nk8)) / 1024, fl = (f % 1024) / 16;
+            if (frg != nt * 8 + c / 64 || fkt != ks || fl != c % 64) fail("FP8 fragment", f, c);
+            if ((unsigned long long)f + 16 > w8) fail("FP8 past the weights", f, w8);
+          }
+        }
+  }
   printf("violations %lld wrapped_violations %lld\n", bad, wrapped_bad);
   return 0;
 }

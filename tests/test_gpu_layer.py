@@ -74,6 +74,12 @@ SMALL = [  # fmt, amode, T, E, k, H, I, shared
     ("mxfp4", "mxfp4", 300, 8, 2, 256, 128, False),  # 128 x 128 FP4 kernel, down K = 128: half K-step at step 0
     ("mxfp4", "mxfp4", 77, 8, 2, 128, 256, True),    # 128 x 128 FP4 kernel, gate/up K = 128
     ("mxfp4", "mxfp4", 40, 4, 2, 128, 128, True),    # both projections K = 128
+    ("fp8", "bf16", 37, 16, 4, 256, 384, True),      # FP8 on the GEMV
+    ("fp8", "bf16", 13, 8, 2, 384, 128, False),
+    ("fp8", "bf16", 600, 8, 1, 256, 128, False),     # FP8 decoded to bf16 on the matrix cores
+    ("nvfp4", "bf16", 300, 8, 2, 256, 384, True),    # NVFP4 decoded to bf16 on the matrix cores
+    ("nvfp4", "bf16", 700, 16, 1, 384, 256, False),
+    ("fp8", "bf16", 257, 6, 3, 512, 256, True),
 ]
 
 
@@ -92,7 +98,7 @@ def test_small_layers_every_path(fmt, amode, T, E, k, H, I, shared):
     _full_check(layer, x, experts, k, logits, shared=sh, amode=amode)
 
 
-@pytest.mark.parametrize("fmt,rows", [("nvfp4", "all"), ("mxfp4", "all"), ("nvfp4", "some")])
+@pytest.mark.parametrize("fmt,rows", [("nvfp4", "all"), ("mxfp4", "all"), ("nvfp4", "some"), ("fp8", "some")])
 def test_large_magnitude_activations(fmt, rows):
     """|x| up to about 2^21 (beyond fp16's range) in every token row, or in
     two of them: the NVFP4 path stages operand rows in fp16 with a per-row
@@ -176,6 +182,17 @@ def a3b_nvfp4():
     return synth.a3b_experts("nvfp4", config=1)
 
 
+@pytest.mark.parametrize("T", [1, 16])
+def test_decode_a3b_fp8(T):
+    experts = synth.a3b_experts("fp8", config=1)
+    b = synth.decode_batch(T)
+    layer = resident_layer(experts, k=8, T=T)
+    say(f"decode A3B FP8 T={T}")
+    layer.forward(_x(b["x"]), logits=torch.from_numpy(b["logits"]).to(DEV))
+    torch.cuda.synchronize()
+    _full_check(layer, b["x"], experts, 8, b["logits"])
+
+
 @pytest.mark.parametrize("T", [1, 4, 16])
 def test_decode_a3b_nvfp4(a3b_nvfp4, T):
     b = synth.decode_batch(T)
@@ -216,7 +233,7 @@ def _whole_check(layer, b, make_expert, k, amode, shared=None, logits=None, bf16
                 f"{oracle.moe.relative_error(out, ref16):.3e}")
 
 
-@pytest.mark.parametrize("fmt,amode", [("bf16", "bf16"), ("mxfp4", "mxfp4")])
+@pytest.mark.parametrize("fmt,amode", [("bf16", "bf16"), ("mxfp4", "mxfp4"), ("nvfp4", "bf16"), ("fp8", "bf16")])
 def test_prefill_a3b(fmt, amode):
     b = synth.prefill_batch(4096)
     experts = synth.a3b_experts(fmt, config=2)

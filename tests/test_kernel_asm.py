@@ -57,9 +57,9 @@ def _row_waits(body):
 
 def test_row_wait_counts_the_loads_behind_the_rows(gemv_asm):
     names = re.findall(r"^(_ZN3moe6k_gemvILi(\d)ELb(\d)ELi(\d+)ELb(\d)EEE\w+):", gemv_asm, re.M)
-    # 3 formats x (gate/up, gate/up with every token row staged, down) x 6
-    # sub-item sizes, less NVFP4's 16 (its largest is 8)
-    assert len(names) == 51, len(names)
+    # 4 formats x (gate/up, gate/up with every token row staged, down) x 6
+    # sub-item sizes, less NVFP4's and FP8's 16 (their largest is 8)
+    assert len(names) == 66, len(names)
     for full, fmt, _down, sub, _xall in names:
         fmt, sub = int(fmt), int(sub)
         body = gemv_asm[gemv_asm.index(full + ":"):gemv_asm.index(".Lfunc_end", gemv_asm.index(full + ":"))]
@@ -67,8 +67,8 @@ def test_row_wait_counts_the_loads_behind_the_rows(gemv_asm):
         assert k > 0, full
         waits = _row_waits(body[k:])
         assert waits, full
-        # tiles and scales (4-bit formats) of the bank issued behind the rows
-        expected = sub + (sub if fmt != 0 else 0)
+        # tiles and scales (the 4-bit formats) of the bank issued behind the rows
+        expected = sub + (sub if fmt in (1, 2) else 0)
         for wait, loads in waits:
             assert wait == expected and loads == expected, (full, loads, wait, expected)
 

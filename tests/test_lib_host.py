@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_blob_bytes(L):
     # 4.5 bits/param (NVFP4), 4.25 (MXFP4), 16 (BF16) plus header and 256 B section padding
-    for fmt, bits in (("nvfp4", 4.5), ("mxfp4", 4.25), ("bf16", 16)):
+    for fmt, bits in (("nvfp4", 4.5), ("mxfp4", 4.25), ("bf16", 16), ("fp8", 8)):
         n = L.moe_blob_bytes(fmt, 2048, 768)
         assert abs(n - (256 + 3 * 2048 * 768 * bits / 8)) < 4 * 256
     assert L.moe_blob_bytes("mxfp4", 100, 128) == 0 and L.moe_blob_bytes(7, 128, 128) == 0
@@ -48,7 +48,7 @@ def test_blob_bytes(L):
 
 def _tile_codes(q, rows, cols, fmt):
     """Independent numpy statement of the documented tile order: [row-group][K-tile][lane][16 B]."""
-    kt = 32 if fmt == "bf16" else 128
+    kt = {"bf16": 32, "fp8": 64}.get(fmt, 128)
     raw = q.view(np.uint8).reshape(rows, -1)
     bpr = raw.shape[1]
     out = []
@@ -58,6 +58,8 @@ def _tile_codes(q, rows, cols, fmt):
                 r, kb = rg * 16 + lane % 16, lane // 16
                 if fmt == "bf16":
                     b0 = (k * kt + kb * 8) * 2
+                elif fmt == "fp8":
+                    b0 = k * kt + kb * 16
                 else:
                     b0 = (k * kt + kb * 32) // 2
                 out.append(raw[r, b0:b0 + 16])
@@ -77,13 +79,15 @@ def test_prepack_layout(L, fmt):
     assert (fmt_id, h, i) == (L.FMT[fmt], H, I)
     g = np.frombuffer(hdr[20:32].tobytes(), np.float32)
     off = np.frombuffer(hdr[32:72].tobytes(), np.uint64)
-    if fmt == "nvfp4":
+    if fmt in ("nvfp4", "fp8"):
         assert list(g) == [np.float32(ex.gate.g), np.float32(ex.up.g), np.float32(ex.down.g)]
+    else:
+        assert list(g) == [1.0, 1.0, 1.0]
     # W13 = interleaved 16-row groups of gate and up
     src = lambda p: p.w if fmt == "bf16" else p.q
     gate, _ = _tile_codes(src(ex.gate), I, H, fmt)
     up, _ = _tile_codes(src(ex.up), I, H, fmt)
-    kt = 32 if fmt == "bf16" else 128
+    kt = {"bf16": 32, "fp8": 64}.get(fmt, 128)
     per_group = (H // kt) * 1024
     inter = np.concatenate([np.concatenate([gate[p * per_group:(p + 1) * per_group], up[p * per_group:(p + 1) * per_group]])
                             for p in range(I // 16)])

@@ -8,6 +8,7 @@ import math
 import numpy as np
 import torch
 
+import synth
 from oracle import formats as F
 
 
@@ -100,3 +101,34 @@ def test_bf16_decode_and_round():
     rnd = np.random.default_rng(3).standard_normal(10000).astype(np.float32) * 100
     assert np.array_equal(F.round_f32_to_bf16(rnd),
                           torch.from_numpy(rnd).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def test_dequant_every_fp8_code():
+    """FP8 weights: every E4M3FN code (a [1, 256] tensor of all codes, each
+    row scaled by its own per-tensor multiplier) against torch's
+    float8_e4m3fn decode times g in float64: exact, NaN at 0x7F / 0xFF."""
+    codes = np.arange(256, dtype=np.uint8)[None, :]
+    for g in (1.0, 0.000202275623, 3.5, 2.0 ** -20):
+        proj = synth.Proj(1, 256, q=codes.copy(), g=g)
+        got = F.dequant(proj, "fp8")[0]
+        ref = torch.from_numpy(codes[0]).view(torch.float8_e4m3fn).to(torch.float64).numpy() * float(np.float32(g))
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+        assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_fp8_generator_codes_round_to_nearest():
+    """The synthetic FP8 weights (input generation, gen.c) hold the E4M3 code
+    nearest to w / g for each drawn w (g = amax / 448): decoding them by
+    torch's float8_e4m3fn is within half a grid step of w / g."""
+    ex = synth.expert("fp8", 256, 128, config=5)
+    w = synth.normal_f32(0, synth.stream_id(5, 0, 0, 0), 128 * 256, 0.02).reshape(128, 256).astype(np.float64)
+    q = ex.gate.q
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    v = w / float(np.float32(ex.gate.g))
+    # g is rounded to float32, so |w / g| may pass 448 by a hair: the code saturates there
+    assert np.abs(v).max() <= 448.0 * (1 + 2.0 ** -22)
+    v = np.clip(v, -448.0, 448.0)
+    # grid step of E4M3 at |v|: 2^(floor(log2 |v|) - 3), 2^-9 below 2^-6
+    step = np.where(np.abs(v) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(v), 1e-300))) - 3))
+    assert np.all(np.abs(dec - v) <= step / 2 + 1e-12)
