@@ -405,6 +405,9 @@ def main():
     ap.add_argument("--no-prefill-leg", action="store_true", help="decode: skip the prefill_mxfp4 leg")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--stream-tokens", type=int, default=512, help="tokens of the stream workload")
+    ap.add_argument("--policy", default="offload", choices=["offload", "hybrid", "cpu"],
+                    help="stream: miss policy (offload: copy every miss; hybrid: the calibrated share copied, "
+                         "the rest on the host; cpu: every miss on the host)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="first run three plain device copies of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
@@ -611,8 +614,20 @@ def bench_stream(args):
     lg_d = torch.from_numpy(logits).to(dev)
     x_d = torch.from_numpy(xs.view(np.int16)).to(dev)
 
+    # one-time bandwidth calibration (pinned host -> HBM copy of a blob vs the
+    # host expert FFN on it), which sets the hybrid policy's copy share
+    from fp4_expert_ffn_amd import moe_calibrate_bw
+    host_threads = max(1, len(os.sched_getaffinity(0)) - 1)
+    scratch = torch.empty(stride, dtype=torch.uint8, device=dev)
+    cal = moe_calibrate_bw(blob_view(0), scratch, reps=8, threads=host_threads)
+    del scratch
+    ratio = {"offload": None, "hybrid": float(cal.copy_ratio), "cpu": 0.0}[args.policy]
+    log(f"[bench] calibration: copy {cal.copy_us:.1f} us/expert ({cal.h2d_gbs:.1f} GB/s), host FFN "
+        f"{cal.cpu_us:.1f} us/expert ({cal.host_gbs:.1f} GB/s of weights, {host_threads} threads): "
+        f"copy share {cal.copy_ratio:.3f}; policy {args.policy}")
     dec = CachedDecoder(num_layers=LAYERS, num_experts=E, k=k, H=H, I=I, fmt=FMT, num_slots=SLOTS,
-                        host_blob=lambda l, e: blob_view(l * E + e), device=dev)
+                        host_blob=lambda l, e: blob_view(l * E + e), device=dev, copy_ratio=ratio,
+                        host_threads=host_threads)
     sh = torch.cuda.current_stream().cuda_stream
 
     # measured pinned host -> device rate: 128 slots in one copy on the copy stream
@@ -660,6 +675,9 @@ def bench_stream(args):
     hits, misses, nbytes = dec.stats()
     value = TOKENS / wall
     trace = stream_trace_verdict(tr_n, tr_e, tr_h, tr_s, tr_v, E, TOKENS, LAYERS, SLOTS)
+    if args.policy != "offload":
+        trace["matches_oracle"] = None  # the stored oracle trace is the offload policy's
+        trace.pop("oracle_sha256", None)
     log(f"[bench] trace of {NS} steps: sha256 {trace['sha256'][:16]}..., matches the oracle's: "
         f"{trace['matches_oracle']}")
 
@@ -725,6 +743,12 @@ def bench_stream(args):
                      "kernel": "hipMemcpyAsync pinned host -> HBM slot (miss fills)",
                      "peak_source": f"measured: one {n_cp}-slot pinned copy on the copy stream"},
         "trace": trace,
+        "policy": {"name": args.policy, "copy_ratio": ratio, "host_threads": host_threads,
+                   "host_run_experts": int(dec.hybrid.cpu_experts) if dec.hybrid is not None else 0,
+                   "calibration": {"copy_us_per_expert": round(cal.copy_us, 2), "h2d_GBps": round(cal.h2d_gbs, 2),
+                                   "host_ffn_us_per_expert": round(cal.cpu_us, 2),
+                                   "host_weight_GBps": round(cal.host_gbs, 2),
+                                   "copy_share": round(float(cal.copy_ratio), 4)}},
         "cache": {"hits": hits, "misses": misses, "hit_rate": round(hit_rate, 4),
                   "hit_rate_tokens_64_511": round(hit_late, 4), "misses_per_token": round(misses / TOKENS, 2),
                   "bytes_filled": nbytes},

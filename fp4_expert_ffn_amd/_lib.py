@@ -57,6 +57,17 @@ class CachePrefill(ctypes.Structure):
     ]
 
 
+class BwCalib(ctypes.Structure):
+    _fields_ = [("copy_us", ctypes.c_double), ("cpu_us", ctypes.c_double), ("h2d_gbs", ctypes.c_double),
+                ("host_gbs", ctypes.c_double), ("copy_ratio", ctypes.c_float)]
+
+
+class Hybrid(ctypes.Structure):
+    _fields_ = [("copy_ratio", ctypes.c_float), ("threads", ctypes.c_int), ("host_x", ctypes.c_void_p),
+                ("host_perm", ctypes.c_void_p), ("host_offsets", ctypes.c_void_p), ("host_y", ctypes.c_void_p),
+                ("cpu_experts", ctypes.c_longlong)]
+
+
 class ExpertCanonical(ctypes.Structure):
     _fields_ = [
         ("fmt", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
@@ -98,6 +109,9 @@ SIGNATURES = {
     "moe_cache_resize": (_i, [_vp, _i, _vp, _vp]),
     "moe_cache_prefetch_layer": (_i, [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_cache_prefill_step": (_i, [_vp, ctypes.POINTER(CachePrefill), _vp]),
+    "moe_cpu_expert_ffn": (_i, [_vp, _vp, _i, _vp, _i]),
+    "moe_calibrate_bw": (_i, [_vp, _vp, _i, _i, _vp, ctypes.POINTER(BwCalib)]),
+    "moe_cache_decode_step_hybrid": (_i, [_vp, ctypes.POINTER(CacheStep), ctypes.POINTER(Hybrid), _vp, _vp]),
 }
 
 _lib = None
@@ -356,3 +370,21 @@ def moe_cache_prefetch_layer(cache: Cache, layer, host_blobs, host_map, dev_map,
 def moe_cache_prefill_step(cache: Cache, step: CachePrefill, compute_stream=None):
     _check(lib().moe_cache_prefill_step(cache.handle, ctypes.byref(step), stream_handle(compute_stream)),
            "moe_cache_prefill_step")
+
+
+def moe_cpu_expert_ffn(blob, x, n, y, threads=1):
+    """blob, x (bf16 bits [n,H]), y (fp32 [n,H]): host arrays."""
+    _check(lib().moe_cpu_expert_ffn(ptr(blob), ptr(x), int(n), ptr(y), int(threads)), "moe_cpu_expert_ffn")
+
+
+def moe_calibrate_bw(host_blob, dev_buf, reps=8, threads=1, copy_stream=None) -> BwCalib:
+    out = BwCalib()
+    _check(lib().moe_calibrate_bw(ptr(host_blob), ptr(dev_buf), int(reps), int(threads), stream_handle(copy_stream),
+                                  ctypes.byref(out)), "moe_calibrate_bw")
+    return out
+
+
+def moe_cache_decode_step_hybrid(cache: Cache, step: CacheStep, hybrid: Hybrid, copy_stream=None, compute_stream=None):
+    _check(lib().moe_cache_decode_step_hybrid(cache.handle, ctypes.byref(step), ctypes.byref(hybrid),
+                                              stream_handle(copy_stream), stream_handle(compute_stream)),
+           "moe_cache_decode_step_hybrid")

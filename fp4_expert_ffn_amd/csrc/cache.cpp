@@ -412,43 +412,66 @@ static void copy_trace(const moe_cache* c, int n, int32_t* te, int32_t* ts, uint
 
 // ------------------------------------------------------------ one decode step
 
-extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t copy_stream,
-                                            moe_stream_t compute_stream) {
-  MOE_CHECK_ARG(c && s, "moe_cache_decode_step: null pointer");
+// One decode step; hy null: every miss copied into the cache.
+static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, moe_stream_t copy_stream,
+                              moe_stream_t compute_stream, const char* who) {
+  MOE_CHECK_ARG(c && s, "%s: null pointer", who);
   const moe_ffn_args& f = s->ffn;
   const int E = f.E, T = f.T;
   s->n_experts = 0;
-  MOE_CHECK_ARG(c->pool, "moe_cache_decode_step: cache has no slot pool");
-  MOE_CHECK_ARG(E == c->num_experts, "moe_cache_decode_step: E=%d but the cache has %d experts per layer", E,
-                c->num_experts);
-  MOE_CHECK_ARG(s->layer >= 0 && s->layer < c->num_layers, "moe_cache_decode_step: layer %d out of range", s->layer);
-  MOE_CHECK_ARG(T >= 0 && f.k >= 1 && f.k <= E, "moe_cache_decode_step: bad T=%d k=%d", T, f.k);
+  MOE_CHECK_ARG(c->pool, "%s: cache has no slot pool", who);
+  MOE_CHECK_ARG(E == c->num_experts, "%s: E=%d but the cache has %d experts per layer", who, E, c->num_experts);
+  MOE_CHECK_ARG(s->layer >= 0 && s->layer < c->num_layers, "%s: layer %d out of range", who, s->layer);
+  MOE_CHECK_ARG(T >= 0 && f.k >= 1 && f.k <= E, "%s: bad T=%d k=%d", who, T, f.k);
   if (T == 0) return MOE_OK;
   MOE_CHECK_ARG(s->logits && s->topk_ids && s->host_counts && s->host_map && s->dev_map && s->host_blobs,
-                "moe_cache_decode_step: null step buffer");
+                "%s: null step buffer", who);
   MOE_CHECK_ARG(f.y && f.out && f.topk_w && f.inv && f.counts && f.offsets && f.perm,
-                "moe_cache_decode_step: ffn.y, out, topk_w, inv, counts, offsets and perm are required");
-  MOE_CHECK_ARG(((uintptr_t)s->dev_map & 255) == 0, "moe_cache_decode_step: dev_map must be 256-byte aligned");
-  MOE_CHECK_ARG(c->slot_bytes % 256 == 0, "moe_cache_decode_step: slot_bytes %zu is not a multiple of 256",
-                c->slot_bytes);
+                "%s: ffn.y, out, topk_w, inv, counts, offsets and perm are required", who);
+  MOE_CHECK_ARG(((uintptr_t)s->dev_map & 255) == 0, "%s: dev_map must be 256-byte aligned", who);
+  MOE_CHECK_ARG(c->slot_bytes % 256 == 0, "%s: slot_bytes %zu is not a multiple of 256", who, c->slot_bytes);
+  if (hy)
+    MOE_CHECK_ARG(hy->copy_ratio >= 0.f && hy->copy_ratio <= 1.f && hy->threads >= 1 && hy->host_x &&
+                      hy->host_perm && hy->host_offsets && hy->host_y,
+                  "%s: bad hybrid policy or host buffers", who);
   hipStream_t ks = reinterpret_cast<hipStream_t>(compute_stream);
   hipStream_t cs = reinterpret_cast<hipStream_t>(copy_stream);
   moe_status st = ensure_events(c);
   if (st != MOE_OK) return st;
 
-  // 1-2. routing, then the step's experts on the host
+  // 1-2. routing, then the step's experts on the host (and, for host-run
+  // misses, the rows they take)
   st = moe_route_permute(s->logits, T, E, f.k, s->renormalize, s->topk_ids, const_cast<float*>(f.topk_w),
                          const_cast<int32_t*>(f.counts), const_cast<int32_t*>(f.offsets), const_cast<int32_t*>(f.perm),
                          const_cast<int32_t*>(f.inv), compute_stream);
   if (st != MOE_OK) return st;
   MOE_HIP(hipMemcpyAsync(s->host_counts, f.counts, sizeof(int32_t) * (size_t)E, hipMemcpyDeviceToHost, ks));
+  if (hy) {
+    MOE_HIP(hipMemcpyAsync(hy->host_offsets, f.offsets, sizeof(int32_t) * (size_t)(E + 1), hipMemcpyDeviceToHost, ks));
+    MOE_HIP(hipMemcpyAsync(hy->host_perm, f.perm, sizeof(int32_t) * (size_t)T * f.k, hipMemcpyDeviceToHost, ks));
+    MOE_HIP(hipMemcpyAsync(hy->host_x, f.x, sizeof(uint16_t) * (size_t)T * f.H, hipMemcpyDeviceToHost, ks));
+  }
   MOE_HIP(hipStreamSynchronize(ks));
-  c->step_ids.clear();
+  std::vector<int32_t> all, host_run;  // the step's experts; those run on the host
   for (int e = 0; e < E; ++e)
     if (s->host_counts[e] > 0) {
-      MOE_CHECK_ARG(s->host_blobs[e], "moe_cache_decode_step: host blob of expert %d is null", e);
-      c->step_ids.push_back(e);
+      MOE_CHECK_ARG(s->host_blobs[e], "%s: host blob of expert %d is null", who, e);
+      all.push_back(e);
     }
+  c->step_ids.clear();
+  if (hy) {
+    int m = 0;
+    for (int e : all) m += c->key_slot[(size_t)s->layer * E + e] < 0;
+    const int ncopy = (int)(hy->copy_ratio * (float)m + 0.5f);
+    int seen = 0;
+    for (int e : all) {
+      const bool miss = c->key_slot[(size_t)s->layer * E + e] < 0;
+      if (miss && seen++ >= ncopy) host_run.push_back(e);
+      else c->step_ids.push_back(e);
+    }
+  } else {
+    c->step_ids = all;
+  }
   const int n = (int)c->step_ids.size();
   c->step_slot.resize(n);
   c->step_hit.resize(n);
@@ -471,13 +494,13 @@ extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe
   const uint8_t* dhm = reinterpret_cast<const uint8_t*>(dmap + E);
   const uint8_t* dmm = dhm + E;
 
-  // 6. hits now (after any fill of theirs still pending), misses after their fills
+  // 6. hits now (after any fill of theirs still pending)
   moe_ffn_args a = f;
   a.slot_of_expert = dmap;
   a.slot_pool = c->pool;
   a.slot_stride = c->slot_bytes;
   a.out = nullptr;
-  if (nh > 0) {
+  if (nh > 0 || (nm == 0 && f.shared_blob)) {
     for (int i = 0; i < n; ++i)
       if (c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], ks)) != MOE_OK) return st;
     a.expert_mask = dhm;
@@ -485,6 +508,27 @@ extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe
     if (st != MOE_OK) return st;
     a.shared_blob = nullptr;  // computed once
   }
+  // 6b. host-run misses while the GPU works: their rows' outputs into host_y
+  // (perm order), then into y
+  if (!host_run.empty()) {
+    hipEvent_t up = nullptr;
+    st = map_before_write(c, hy->host_y, &up);  // the previous upload from host_y has finished
+    if (st != MOE_OK) return st;
+    std::vector<uint16_t> xg;
+    for (int e : host_run) {
+      const int p0 = hy->host_offsets[e], cnt = hy->host_offsets[e + 1] - p0;
+      xg.resize((size_t)cnt * f.H);
+      for (int r = 0; r < cnt; ++r)
+        memcpy(&xg[(size_t)r * f.H], hy->host_x + (size_t)(hy->host_perm[p0 + r] / f.k) * f.H, 2 * (size_t)f.H);
+      st = moe_cpu_expert_ffn(s->host_blobs[e], xg.data(), cnt, hy->host_y + (size_t)p0 * f.H, hy->threads);
+      if (st != MOE_OK) return st;
+      MOE_HIP(hipMemcpyAsync(f.y + (size_t)p0 * f.H, hy->host_y + (size_t)p0 * f.H, sizeof(float) * (size_t)cnt * f.H,
+                             hipMemcpyHostToDevice, ks));
+    }
+    MOE_HIP(hipEventRecord(up, ks));
+    hy->cpu_experts += (long long)host_run.size();
+  }
+  // 6c. copied misses after their fills
   if (nm > 0) {
     for (int i = 0; i < n; ++i)
       if (!c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], ks)) != MOE_OK) return st;
@@ -500,10 +544,32 @@ extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe
   st = mark_readers(c, c->step_slot.data(), n, ks);
   if (st != MOE_OK) return st;
 
-  if (s->trace_slot && s->trace_hit && s->trace_evicted)
-    copy_trace(c, n, s->trace_expert, s->trace_slot, s->trace_hit, s->trace_evicted);
-  s->n_experts = n;
+  // trace: every expert of the step in ascending id (host-run misses: -1 slot)
+  if (s->trace_slot && s->trace_hit && s->trace_evicted) {
+    size_t i = 0, j = 0;
+    for (int e : all) {
+      const bool looked = i < c->step_ids.size() && c->step_ids[i] == e;
+      if (s->trace_expert) s->trace_expert[j] = e;
+      s->trace_slot[j] = looked ? c->step_slot[i] : -1;
+      s->trace_hit[j] = looked ? c->step_hit[i] : 0;
+      s->trace_evicted[j] = looked ? c->step_ev[i] : -1;
+      i += looked;
+      ++j;
+    }
+  }
+  s->n_experts = (int)all.size();
   return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_decode_step(moe_cache* c, moe_cache_step* s, moe_stream_t copy_stream,
+                                            moe_stream_t compute_stream) {
+  return decode_step(c, s, nullptr, copy_stream, compute_stream, "moe_cache_decode_step");
+}
+
+extern "C" moe_status moe_cache_decode_step_hybrid(moe_cache* c, moe_cache_step* s, moe_hybrid* hy,
+                                                   moe_stream_t copy_stream, moe_stream_t compute_stream) {
+  MOE_CHECK_ARG(hy, "moe_cache_decode_step_hybrid: null policy");
+  return decode_step(c, s, hy, copy_stream, compute_stream, "moe_cache_decode_step_hybrid");
 }
 
 // ------------------------------------------------------------ layer-ahead prefill

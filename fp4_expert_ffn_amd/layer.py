@@ -131,10 +131,13 @@ class CachedDecoder:
     by every layer under LRU, misses copied on a side stream.
 
     host_blob(layer, e) -> pinned uint8 tensor holding that expert's blob.
+    copy_ratio: None copies every miss into the cache; a value in [0, 1] runs
+    the hybrid policy (that share of a step's misses copied, the rest run on
+    the host with `host_threads` threads, not cached).
     """
 
     def __init__(self, *, num_layers, num_experts, k, H, I, fmt, num_slots, host_blob, max_tokens=1,
-                 device="cuda", renormalize=True):
+                 device="cuda", renormalize=True, copy_ratio=None, host_threads=8):
         self.L, self.E, self.k, self.H, self.I, self.fmt = num_layers, num_experts, k, H, I, fmt
         self.dev = torch.device(device)
         self.blob_bytes = L.moe_blob_bytes(fmt, H, I)
@@ -163,6 +166,14 @@ class CachedDecoder:
         self.y = torch.empty((T * k, H), dtype=torch.float32, device=self.dev)
         self.out = torch.empty((T, H), dtype=torch.int16, device=self.dev)
         self.trace = [np.empty(E, np.int32), np.empty(E, np.int32), np.empty(E, np.uint8), np.empty(E, np.int32)]
+        self.hybrid = None
+        if copy_ratio is not None:
+            self._hx = torch.empty((T, H), dtype=torch.int16, pin_memory=True)
+            self._hperm = torch.empty(T * k, dtype=torch.int32, pin_memory=True)
+            self._hoff = torch.empty(E + 1, dtype=torch.int32, pin_memory=True)
+            self._hy = torch.empty((T * k, H), dtype=torch.float32, pin_memory=True)
+            self.hybrid = L.Hybrid(float(copy_ratio), int(host_threads), self._hx.data_ptr(), self._hperm.data_ptr(),
+                                   self._hoff.data_ptr(), self._hy.data_ptr(), 0)
         self._trace_ptrs = tuple(t.ctypes.data for t in self.trace)
         self._steps = {}
         self._ws = None
@@ -204,7 +215,7 @@ class CachedDecoder:
         out = self.out[:T] if out is None else out
         st = self._step(layer, T, x, logits, out)
         st.trace_expert, st.trace_slot, st.trace_hit, st.trace_evicted = self._trace_ptrs
-        L.moe_cache_decode_step(self.cache, st, self.copy_stream, stream)
+        self._run_step(st, stream)
         n = st.n_experts
         return out, tuple(t[:n].copy() for t in self.trace)
 
@@ -216,8 +227,14 @@ class CachedDecoder:
         T = x.shape[0]
         st = self._step(layer, T, x, logits, self.out[:T])
         st.trace_expert, st.trace_slot, st.trace_hit, st.trace_evicted = trace or self._trace_ptrs
-        L.moe_cache_decode_step(self.cache, st, self.copy_stream, stream_handle)
+        self._run_step(st, stream_handle)
         return st.n_experts
+
+    def _run_step(self, st, stream):
+        if self.hybrid is None:
+            L.moe_cache_decode_step(self.cache, st, self.copy_stream, stream)
+        else:
+            L.moe_cache_decode_step_hybrid(self.cache, st, self.hybrid, self.copy_stream, stream)
 
     def stats(self):
         return L.moe_cache_stats(self.cache)
@@ -235,6 +252,8 @@ class CachedDecoder:
 
     def reset(self):
         L.moe_cache_reset(self.cache)
+        if self.hybrid is not None:
+            self.hybrid.cpu_experts = 0
 
     def close(self):
         self.cache.close()

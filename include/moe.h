@@ -395,6 +395,66 @@ typedef struct {
  * cached (its prefetch did not run, or a later one evicted it). */
 moe_status moe_cache_prefill_step(moe_cache* c, moe_cache_prefill* s, moe_stream_t compute_stream);
 
+/* ------------------------------------------------- hybrid miss policy
+ * [page "FreeToken量子化：MoE推論のセットアップガイド", decode paragraph: a
+ *  miss is either brought over PCIe into the cache or executed on the CPU,
+ *  by the host-memory and PCIe bandwidths measured on the machine; paragraph
+ *  on the bandwidth-adaptive policy; bhrtaym-blog page, section
+ *  "MoEバックエンドは4種類から選べる": backend rows "cpu" (misses computed on
+ *  the CPU, not fetched) and "hybrid" (part of the misses copied, the rest
+ *  computed on the CPU, overlapped), and the one-time bandwidth calibration
+ *  run before hybrid is used.] */
+
+/* The expert FFN of one blob on the host: y[t,:] = W_down (silu(W_gate x_t) *
+ * (W_up x_t)) for the n bf16 rows x [n,H] (host), y [n,H] fp32 (host); fp32
+ * accumulation, per-tensor multipliers applied to the sums, `threads` host
+ * threads (a pool kept until the process ends).  blob: host memory holding
+ * a prepacked blob (any format).  Synchronous; no GPU work. */
+moe_status moe_cpu_expert_ffn(const void* blob, const uint16_t* x, int n, float* y, int threads);
+
+/* Result of the one-time bandwidth calibration. */
+typedef struct {
+  double copy_us;    /* one blob, pinned host -> device                          */
+  double cpu_us;     /* moe_cpu_expert_ffn of that blob on one token row          */
+  double h2d_gbs;    /* blob bytes / copy_us                                      */
+  double host_gbs;   /* blob bytes / cpu_us: the host kernel's weight stream rate  */
+  float copy_ratio;  /* share of a step's misses to copy: cpu_us / (cpu_us + copy_us),
+                        which makes the copies and the host's run take equal time */
+} moe_bw_calib;
+
+/* Times `reps` copies of host_blob (pinned, a prepacked blob) into dev_buf
+ * (device, at least the blob's size) on copy_stream, and `reps` runs of
+ * moe_cpu_expert_ffn on it with `threads` threads; synchronises the host. */
+moe_status moe_calibrate_bw(const void* host_blob, void* dev_buf, int reps, int threads, moe_stream_t copy_stream,
+                            moe_bw_calib* out);
+
+/* Host buffers and policy of moe_cache_decode_step_hybrid. */
+typedef struct {
+  float copy_ratio;       /* in [0, 1]: of a step's m misses, the first
+                             floor(copy_ratio * m + 0.5) in ascending id are
+                             copied into the cache; the rest run on the host and
+                             are not cached (1: every miss copied; 0: none)      */
+  int threads;            /* host threads of moe_cpu_expert_ffn                  */
+  uint16_t* host_x;       /* pinned [T,H]: the step's token rows                 */
+  int32_t* host_perm;     /* pinned [T*k]                                        */
+  int32_t* host_offsets;  /* pinned [E+1]                                        */
+  float* host_y;          /* pinned [T*k][H]: expert outputs of host-run experts  */
+  long long cpu_experts;  /* in/out: incremented by the experts run on the host   */
+} moe_hybrid;
+
+/* moe_cache_decode_step with the hybrid miss policy: the step's routing,
+ * counts, offsets, permutation and token rows come to the host (its one
+ * synchronisation); hits and the looked-up misses are handled as in
+ * moe_cache_decode_step (lookups in ascending id, fills on copy_stream, the
+ * FFN on the GPU); each miss past the copied share runs on the host, after
+ * the GPU's hit FFN is enqueued, and its outputs are copied into ffn.y
+ * before the combine.  The trace lists every expert of the step in
+ * ascending id; a host-run miss has hit 0, slot -1 and evicted key -1 and
+ * leaves the cache unchanged.  s->host_blobs must point to prepacked blobs
+ * the host can read. */
+moe_status moe_cache_decode_step_hybrid(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, moe_stream_t copy_stream,
+                                        moe_stream_t compute_stream);
+
 /* Resize the cache at a safe point (between layer calls, no step in flight).
  * [page "FreeToken量子化：MoE推論のセットアップガイド", paragraph on resizing
  *  the expert cache at runtime at scheduler safe points.]

@@ -7,6 +7,7 @@
 //   cache_harness prefill L E C passes seed                      layer-ahead prefill passes
 //   cache_harness fault KIND NTH L E k T C steps seed            decode stream, the NTH call of KIND fails
 //                                                                (0 copy, 1 event create, 2 event record, 3 stream wait)
+//   cache_harness hybrid RATIO L E k T C steps seed              decode stream, hybrid miss policy
 // stdout, one line per call:
 //   D <layer> <status> e:h:s:v ...   a decode step's records
 //   P <layer> <status> h:s:v ...     a prefetch's lookups of experts 0..E-1
@@ -66,12 +67,17 @@ void* buffer(size_t n, int device) {
   return (void*)p;
 }
 
+constexpr int kH = 128, kI = 128;  // blob shape: valid MXFP4 blobs, so the host FFN can run them
+constexpr int kTagOffset = 200;
+
 struct World {
   int L, E, k, T, C;
-  size_t slot = 4096;
+  size_t slot = (moe_blob_bytes(MOE_FMT_MXFP4, kH, kI) + 255) / 256 * 256;
   std::vector<void*> blob_ptr;  // L * E host blobs, tagged (layer, expert)
   void* pool;
-  int32_t *counts, *offsets, *perm, *inv, *ids, *host_counts;
+  int32_t *counts, *offsets, *perm, *inv, *ids, *host_counts, *host_perm, *host_offsets;
+  uint16_t* host_x;
+  float* host_y;
   float *topk_w, *y, *logits;
   uint16_t *out, *x;
   std::vector<void*> host_map, dev_map;  // per layer
@@ -83,9 +89,18 @@ struct World {
     for (int l = 0; l < L; ++l)
       for (int e = 0; e < E; ++e) {
         uint8_t* b = bank + slot * ((size_t)l * E + e);
+        memset(b, (l * 31 + e) & 127, slot);  // codes; scales below 2^0
+        moe::BlobHeader hdr{};
+        moe::BlobLayout Ly;
+        moe::layout_of(MOE_FMT_MXFP4, kH, kI, &Ly);
+        hdr.magic = moe::kBlobMagic;
+        hdr.fmt = MOE_FMT_MXFP4; hdr.H = kH; hdr.I = kI;
+        hdr.g[0] = hdr.g[1] = hdr.g[2] = 1.f;
+        hdr.off_w13 = Ly.off_w13; hdr.off_s13 = Ly.off_s13; hdr.off_w2 = Ly.off_w2; hdr.off_s2 = Ly.off_s2;
+        hdr.total = Ly.total;
+        memcpy(b, &hdr, sizeof hdr);
         const int32_t tag[2] = {l, e};
-        memcpy(b, tag, sizeof tag);
-        memset(b + 8, (l * 31 + e) & 255, slot - 8);
+        memcpy(b + kTagOffset, tag, sizeof tag);
         blob_ptr.push_back(b);
       }
     pool = buffer(slot * C, 1);
@@ -97,10 +112,14 @@ struct World {
     ids = (int32_t*)buffer(4 * T * k, 1);
     host_counts = (int32_t*)buffer(4 * E, 2);
     topk_w = (float*)buffer(4 * T * k, 1);
-    y = (float*)buffer(4 * T * k * 256, 1);
+    y = (float*)buffer(4 * T * k * kH, 1);
     logits = (float*)buffer(4 * T * E, 1);
-    out = (uint16_t*)buffer(2 * T * 256, 1);
-    x = (uint16_t*)buffer(2 * T * 256, 1);
+    out = (uint16_t*)buffer(2 * T * kH, 1);
+    x = (uint16_t*)buffer(2 * T * kH, 1);
+    host_x = (uint16_t*)buffer(2 * T * kH, 2);
+    host_perm = (int32_t*)buffer(4 * T * k, 2);
+    host_offsets = (int32_t*)buffer(4 * (E + 1), 2);
+    host_y = (float*)buffer(4 * T * k * kH, 2);
     for (int l = 0; l < L; ++l) {
       host_map.push_back(buffer(moe_cache_map_bytes(E), 2));
       dev_map.push_back(buffer(moe_cache_map_bytes(E), 1));
@@ -111,7 +130,7 @@ struct World {
   }
   moe_ffn_args ffn() const {
     moe_ffn_args a{};
-    a.T = T; a.k = k; a.E = E; a.H = 256; a.I = 128; a.wfmt = MOE_FMT_NVFP4; a.amode = MOE_ACT_BF16;
+    a.T = T; a.k = k; a.E = E; a.H = kH; a.I = kI; a.wfmt = MOE_FMT_MXFP4; a.amode = MOE_ACT_BF16;
     a.x = x; a.counts = counts; a.offsets = offsets; a.perm = perm; a.inv = inv; a.topk_w = topk_w;
     a.y = y; a.out = out;
     return a;
@@ -128,7 +147,7 @@ void print_recs(char tag, int layer, int st, int n, const int32_t* e, const uint
   printf("\n");
 }
 
-int decode(int argc, char** argv, int fail_kind, int fail_nth) {
+int decode(int argc, char** argv, int fail_kind, int fail_nth, float ratio = -1.f) {
   const int L = atoi(argv[0]), E = atoi(argv[1]), k = atoi(argv[2]), T = atoi(argv[3]), C = atoi(argv[4]);
   const int steps = atoi(argv[5]);
   g_rng ^= (uint64_t)atoll(argv[6]) * 0x9E3779B97F4A7C15ull;
@@ -139,6 +158,7 @@ int decode(int argc, char** argv, int fail_kind, int fail_nth) {
   }
   World w(L, E, k, T, C);
   if (fail_kind >= 0) stub_fail(fail_kind, fail_nth);
+  moe_hybrid hy{ratio, 2, w.host_x, w.host_perm, w.host_offsets, w.host_y, 0};
   std::vector<std::vector<int>> prev(L);
   std::vector<int> sel;
   std::vector<int32_t> te(E), ts(E), tv(E), cnt(E);
@@ -172,8 +192,11 @@ int decode(int argc, char** argv, int fail_kind, int fail_nth) {
     s.host_blobs = (const void* const*)&w.blob_ptr[(size_t)l * E];
     s.ffn = w.ffn();
     s.trace_expert = te.data(); s.trace_slot = ts.data(); s.trace_hit = th.data(); s.trace_evicted = tv.data();
-    const moe_status st = moe_cache_decode_step(w.c, &s, reinterpret_cast<moe_stream_t>(w.cs),
-                                                reinterpret_cast<moe_stream_t>(w.ks));
+    const moe_status st =
+        ratio < 0.f ? moe_cache_decode_step(w.c, &s, reinterpret_cast<moe_stream_t>(w.cs),
+                                            reinterpret_cast<moe_stream_t>(w.ks))
+                    : moe_cache_decode_step_hybrid(w.c, &s, &hy, reinterpret_cast<moe_stream_t>(w.cs),
+                                                   reinterpret_cast<moe_stream_t>(w.ks));
     print_recs('D', l, (int)st, st == MOE_OK ? s.n_experts : 0, te.data(), th.data(), ts.data(), tv.data());
   }
   moe_cache_destroy(w.c);
@@ -240,5 +263,6 @@ int main(int argc, char** argv) {
   if (!strcmp(argv[1], "decode") && argc >= 9) return decode(argc - 2, argv + 2, -1, -1);
   if (!strcmp(argv[1], "prefill") && argc == 7 && atoi(argv[2]) >= 3) return prefill(argv + 2);
   if (!strcmp(argv[1], "fault") && argc == 11) return decode(7, argv + 4, atoi(argv[2]), atoi(argv[3]));
+  if (!strcmp(argv[1], "hybrid") && argc == 10) return decode(7, argv + 3, -1, -1, (float)atof(argv[2]));
   return 2;
 }

@@ -34,6 +34,7 @@ struct ihipEvent_t {
 
 namespace {
 constexpr int kMaxStreams = 16;
+constexpr int kTagOffset = 200;  // (layer, expert) tag of a test blob, inside its header padding
 typedef std::vector<int> VC;
 
 struct Op {
@@ -140,6 +141,15 @@ long long stub_bad() { return g_bad; }
 extern "C" {
 const char* hipGetErrorString(hipError_t e) { return e == hipSuccess ? "no error" : "injected failure"; }
 
+hipError_t hipEventCreate(hipEvent_t* e) {
+  if (inject(1)) return hipErrorOutOfMemory;
+  *e = new ihipEvent_t{VC(kMaxStreams, 0)};
+  return hipSuccess;
+}
+hipError_t hipEventElapsedTime(float* ms, hipEvent_t, hipEvent_t) {
+  *ms = 1.0f;
+  return hipSuccess;
+}
 hipError_t hipEventCreateWithFlags(hipEvent_t* e, unsigned) {
   if (inject(1)) return hipErrorOutOfMemory;
   *e = new ihipEvent_t{VC(kMaxStreams, 0)};
@@ -201,7 +211,7 @@ hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind ki
 
 // ------------------------------------------------------------ library stand-ins
 namespace {
-void route_counts(int E, int32_t* counts, int32_t* offsets) {
+void route_counts(int E, int32_t* counts, int32_t* offsets, int32_t* perm) {
   int run = 0;
   for (int e = 0; e < E; ++e) {
     counts[e] = e < (int)g_next_counts.size() ? g_next_counts[e] : 0;
@@ -209,23 +219,25 @@ void route_counts(int E, int32_t* counts, int32_t* offsets) {
     run += counts[e];
   }
   offsets[E] = run;
+  if (perm)
+    for (int p = 0; p < run; ++p) perm[p] = p;  // flat index p: token p / k
 }
 }  // namespace
 
 extern "C" moe_status moe_route_permute(const float*, int, int E, int, int, int32_t*, float*, int32_t* counts,
-                                        int32_t* offsets, int32_t*, int32_t*, moe_stream_t stream) {
+                                        int32_t* offsets, int32_t* perm, int32_t*, moe_stream_t stream) {
   tick(reinterpret_cast<hipStream_t>(stream));
-  route_counts(E, counts, offsets);
+  route_counts(E, counts, offsets, perm);
   return MOE_OK;
 }
 extern "C" moe_status moe_route(const float*, int, int, int, int, int32_t*, float*, moe_stream_t stream) {
   tick(reinterpret_cast<hipStream_t>(stream));
   return MOE_OK;
 }
-extern "C" moe_status moe_permute(const int32_t*, int, int, int E, int32_t* counts, int32_t* offsets, int32_t*,
+extern "C" moe_status moe_permute(const int32_t*, int, int, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                                   int32_t*, moe_stream_t stream) {
   tick(reinterpret_cast<hipStream_t>(stream));
-  route_counts(E, counts, offsets);
+  route_counts(E, counts, offsets, perm);
   return MOE_OK;
 }
 extern "C" moe_status moe_combine(const float*, const int32_t*, const float*, const float*, int, int, int, uint16_t*,
@@ -247,8 +259,8 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
       continue;
     }
     slot_read(addr, o);
-    int32_t tag[2];
-    memcpy(tag, reinterpret_cast<const void*>(addr), sizeof tag);
+    int32_t tag[2];  // in the blob header's padding
+    memcpy(tag, reinterpret_cast<const void*>(addr + kTagOffset), sizeof tag);
     if (tag[0] != g_layer || tag[1] != e) bad("slot holds another blob", tag[0] * 100000LL + tag[1], g_layer * 100000LL + e);
   }
   return MOE_OK;

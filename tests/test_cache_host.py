@@ -33,8 +33,8 @@ def harness(tmp_path_factory):
     exe = str(tmp_path_factory.mktemp("cache") / "cache_harness")
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
            "-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined",
-           os.path.join(CSRC, "cache.cpp"), os.path.join(CSRC, "host.cpp"), os.path.join(CPU, "hip_stub.cpp"),
-           os.path.join(CPU, "cache_harness.cpp"), "-o", exe]
+           os.path.join(CSRC, "cache.cpp"), os.path.join(CSRC, "host.cpp"), os.path.join(CSRC, "cpu_expert.cpp"),
+           os.path.join(CPU, "hip_stub.cpp"), os.path.join(CPU, "cache_harness.cpp"), "-o", exe, "-pthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         pytest.fail(f"build failed:\n{r.stderr}")
@@ -112,3 +112,33 @@ def test_injected_failures_leave_a_consistent_cache(harness, kind, nth):
     out = run(harness, "fault", kind, nth, 3, 16, 4, 2, 10, 60, nth)
     st = [int(ln[2]) for ln in out]
     assert st.count(MOE_EHIP) == 1 and all(s == MOE_OK for s in st if s != MOE_EHIP), st
+
+
+@pytest.mark.parametrize("ratio", ["0.5", "0", "1"])
+def test_hybrid_policy_protocol_and_trace(harness, ratio):
+    """The hybrid miss policy on the CPU harness (real host expert FFN on
+    the blobs): the copied share of each step's misses is looked up as by
+    the oracle LRU, the rest are reported as host-run (slot -1) and leave the
+    cache unchanged; the host's expert outputs are copied to the device
+    before the combine and its staging buffer is rewritten only after its
+    previous copy finished (no hazard)."""
+    import numpy as np
+    E = 16
+    out = run(harness, "hybrid", ratio, 3, E, 4, 2, 10, 200, 6)
+    lru = SlotLRU(10)
+    r = np.float32(float(ratio))
+    for ln in out:
+        assert ln[0] == "D" and int(ln[2]) == MOE_OK, ln
+        layer = int(ln[1])
+        recs = [tuple(map(int, x.split(":"))) for x in ln[3:]]
+        ids = [x[0] for x in recs]
+        misses = [e for e in ids if (layer, e) not in lru]
+        ncopy = int(r * np.float32(len(misses)) + np.float32(0.5))
+        host = set(misses[ncopy:])
+        want = {w[0]: w for w in lru.lookup(layer, [e for e in ids if e not in host])}
+        for e, h, s_, v in recs:
+            if e in host:
+                assert (h, s_, v) == (0, -1, -1)
+            else:
+                _, wh, ws, wv = want[e]
+                assert (h, s_, v) == (int(wh), ws, _ev(wv, E))

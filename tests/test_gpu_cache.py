@@ -50,7 +50,7 @@ def test_cache_fill_copies_the_blob_into_its_slot():
 
 
 def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=None, config=86, resize_at=None,
-                routing_seed=None, blob_key=None):
+                routing_seed=None, blob_key=None, copy_ratio=None):
     """Decode `tokens` single-token steps through `layers` layers; returns the
     number of steps checked against the oracle.  blob_key(l, e) names the
     pinned blob of an expert (experts with equal keys share one host copy;
@@ -68,7 +68,7 @@ def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=N
         return bank[key]
 
     dec = CachedDecoder(num_layers=layers, num_experts=E, k=k, H=H, I=I, fmt="nvfp4", num_slots=slots,
-                        host_blob=host_blob, device=DEV)
+                        host_blob=host_blob, device=DEV, copy_ratio=copy_ratio, host_threads=4)
     seed = config if routing_seed is None else routing_seed
     logits = synth.stream_routing(tokens, layers, E, seed=seed)
     xs = np.stack([np.stack([synth.stream_activations(t, l, H, seed=seed)[0] for l in range(layers)])
@@ -87,12 +87,12 @@ def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=N
         for l in range(layers):
             out, (te, ts, th, tv) = dec.step(l, x_d[t, l:l + 1], lg_d[t, l:l + 1])
             ids, w = oracle.moe.route(logits[t, l:l + 1], k)
-            want = lru.lookup(l, sorted(set(ids[0].tolist())))
+            want = _policy_lookup(lru, l, sorted(set(ids[0].tolist())), copy_ratio)
             assert te.tolist() == [r[0] for r in want], (t, l)
             assert th.tolist() == [int(r[1]) for r in want], (t, l)
             assert ts.tolist() == [r[2] for r in want], (t, l)
             assert tv.tolist() == [-1 if r[3] is None else r[3][0] * E + r[3][1] for r in want], (t, l)
-            misses += int(np.sum(th == 0))
+            misses += int(np.sum((th == 0) & (ts >= 0)))
             if check_steps is None or (t, l) in check_steps:
                 torch.cuda.synchronize()
                 got = synth.bf16_bits_to_f32(to_numpy_bf16(out))
@@ -108,6 +108,21 @@ def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=N
     return checked
 
 
+def _policy_lookup(lru, layer, ids, copy_ratio):
+    """The oracle LRU's records of one step under the hybrid miss policy: of
+    the step's m misses, the first floor(r m + 1/2) in ascending id (r and
+    the product in float32, as the library takes them) are looked up (and
+    cached); the others run on the host: (expert, False, -1, None), cache
+    unchanged.  copy_ratio None: every expert looked up."""
+    if copy_ratio is None:
+        return lru.lookup(layer, ids)
+    misses = [e for e in ids if (layer, e) not in lru]
+    ncopy = int(np.float32(copy_ratio) * np.float32(len(misses)) + np.float32(0.5))
+    host = set(misses[ncopy:])
+    recs = {r[0]: r for r in lru.lookup(layer, [e for e in ids if e not in host])}
+    return [recs[e] if e in recs else (e, False, -1, None) for e in ids]
+
+
 def test_cached_stream_small_every_step():
     """16 experts per layer, top-4, 10 slots for 3 layers: most steps miss and evict."""
     say("cached stream: 3 layers x 16 NVFP4 experts (hidden 256, inter 256), 10 slots, 20 tokens")
@@ -116,6 +131,22 @@ def test_cached_stream_small_every_step():
         return synth.expert("nvfp4", 256, 256, config=86, layer=l, expert_id=e)
 
     _run_stream(layers=3, E=16, k=4, H=256, I=256, tokens=20, slots=10, make_expert=make)
+
+
+@pytest.mark.parametrize("copy_ratio", [0.5, 0.0])
+def test_cached_stream_hybrid_policy(copy_ratio):
+    """The hybrid miss policy: a share of each step's misses copied into the
+    cache, the rest run on the host (copy_ratio 0: the cpu backend, every
+    miss on the host and nothing cached after the first lookups).  Every
+    step's trace equals the oracle LRU under the same split and every output
+    matches the oracle layer."""
+    say(f"cached stream, hybrid policy (copy ratio {copy_ratio}): 3 layers x 16 NVFP4 experts, 10 slots, 20 tokens")
+
+    def make(l, e):
+        return synth.expert("nvfp4", 256, 256, config=92, layer=l, expert_id=e)
+
+    _run_stream(layers=3, E=16, k=4, H=256, I=256, tokens=20, slots=10, make_expert=make, config=92,
+                copy_ratio=copy_ratio)
 
 
 def test_cached_stream_with_resizes():
