@@ -151,6 +151,7 @@ __device__ inline ActiveLds active_view(uint8_t* base, int na, int ntok) {
   return A;
 }
 
+template <int KPER>
 __device__ inline void build_active(const FfnParams& P, int rbs, const ActiveLds& A) {
   const int tid = threadIdx.x;
   const int N = P.T * P.k;
@@ -163,7 +164,7 @@ __device__ inline void build_active(const FfnParams& P, int rbs, const ActiveLds
       }
   } else {
     // every load first (one round trip), then the compaction
-    constexpr int kPer = 1024 / 64;
+    constexpr int kPer = KPER;
     int c[kPer], off[kPer], sl[kPer], mk[kPer];
     // unconditional loads (indices clamped to E - 1), so they all issue
     // before the first wait; lanes past E are zeroed afterwards
@@ -398,7 +399,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int rbs = DOWN ? G.rbs2 : G.rbs1, nchunk = DOWN ? G.nd : G.ng;
   const ActiveLds A = active_view(lds, G.na, P.T * P.k <= kTokCache ? P.T * P.k : 0);
   uint8_t* act = lds + G.act_off;  // operand rows (swizzled) + slack
-  build_active(P, rbs, A);
+  if (P.E <= 128) build_active<2>(P, rbs, A);
+  else if (P.E <= 256) build_active<4>(P, rbs, A);
+  else build_active<16>(P, rbs, A);
   const int nrb = A.rb[*A.n];
   // this workgroup's items: [i_beg, i_end) of nrb * nchunk, row block major.
   // With two workgroups per CU (workgroups b and b + ncu share a CU), each
