@@ -34,6 +34,9 @@
 namespace moe {
 hipError_t launch_move_slots(const int32_t* src_slots, int n, int dst0, const void* src_pool, void* dst_pool,
                              size_t slot_bytes, hipStream_t s);
+hipError_t launch_publish_counts(const int32_t* counts, int E, int32_t* host_counts_dev, uint32_t* flag_dev,
+                                 uint32_t seq, hipStream_t s);
+hipError_t launch_write_map(const StepMap& m, int E, void* dev_map, hipStream_t s);
 }
 
 struct moe_cache {
@@ -66,6 +69,14 @@ struct moe_cache {
   int has_resized = 0;
   // last upload from each host slot map: the map is rewritten only after it
   std::vector<std::pair<const void*, hipEvent_t>> map_upload;
+  // decode-step handoff: a host-mapped flag the GPU publishes each step's
+  // sequence number in (publish: -1 not tried yet, 0 unavailable, 1 ready),
+  // and the device addresses of the host-count buffers
+  int publish = -1;
+  uint32_t* flag_host = nullptr;
+  uint32_t* flag_dev = nullptr;
+  uint32_t seq = 0;
+  std::vector<std::pair<const void*, void*>> mapped;
 
   void unlink(int32_t k) {
     int32_t p = prev[k], n = next[k];
@@ -126,6 +137,7 @@ extern "C" void moe_cache_destroy(moe_cache* c) {
   for (auto& t : c->fill_tail) (void)hipEventDestroy(t.second);
   for (auto& m : c->map_upload) (void)hipEventDestroy(m.second);
   if (c->resized) (void)hipEventDestroy(c->resized);
+  if (c->flag_host) (void)hipHostFree(c->flag_host);
   delete c;
 }
 
@@ -410,6 +422,78 @@ static void copy_trace(const moe_cache* c, int n, int32_t* te, int32_t* ts, uint
   }
 }
 
+// ------------------------------------------------------------ decode-step handoffs
+
+// The device address of pinned host memory (null if it is not mapped for
+// the device; the failed query's error is cleared).
+static void* mapped_device_ptr(moe_cache* c, void* host) {
+  for (auto& m : c->mapped)
+    if (m.first == host) return m.second;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, host, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    d = nullptr;
+  }
+  c->mapped.emplace_back(host, d);
+  return d;
+}
+
+// The host-mapped, coherent flag of the count handoff (allocated on first
+// use; without it the steps copy the counts and synchronise the stream).
+static void ensure_flag(moe_cache* c) {
+  if (c->publish >= 0) return;
+  c->publish = 0;
+  void* h = nullptr;
+  if (hipHostMalloc(&h, 256, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess || !d) {
+    (void)hipGetLastError();
+    (void)hipHostFree(h);
+    return;
+  }
+  c->flag_host = static_cast<uint32_t*>(h);
+  c->flag_dev = static_cast<uint32_t*>(d);
+  __atomic_store_n(c->flag_host, 0u, __ATOMIC_RELEASE);
+  c->publish = 1;
+}
+
+// Waits (polling) until the GPU has published `seq`; checks the stream for
+// errors every few thousand polls.
+static moe_status wait_flag(moe_cache* c, uint32_t seq, hipStream_t ks, const char* who) {
+  for (unsigned long long spin = 1;; ++spin) {
+    if (__atomic_load_n(c->flag_host, __ATOMIC_ACQUIRE) == seq) return MOE_OK;
+    __builtin_ia32_pause();
+    if ((spin & 0xFFF) == 0) {
+      const hipError_t q = hipStreamQuery(ks);
+      if (q == hipSuccess) {
+        if (__atomic_load_n(c->flag_host, __ATOMIC_ACQUIRE) == seq) return MOE_OK;
+        return moe::set_error(MOE_EHIP, "%s: the stream finished without publishing the step's counts", who);
+      }
+      if (q != hipErrorNotReady) return moe::set_error(MOE_EHIP, "%s: %s", who, hipGetErrorString(q));
+    }
+  }
+}
+
+// The step's map (the lookups in step_ids / step_slot / step_hit) into
+// dev_map on ks: by a kernel that takes it by value, or for steps with more
+// than kStepMapMax experts through host_map.
+static moe_status write_map(moe_cache* c, void* host_map, void* dev_map, int E, int n, hipStream_t ks) {
+  if (n > moe::kStepMapMax) return upload_map(c, host_map, dev_map, E, n, ks);
+  moe::StepMap m;
+  m.n = n;
+  for (int i = 0; i < n; ++i) {
+    m.expert[i] = c->step_ids[i];
+    m.slot[i] = c->step_slot[i];
+    m.hit[i] = c->step_hit[i];
+  }
+  const hipError_t e = moe::launch_write_map(m, E, dev_map, ks);
+  if (e != hipSuccess) return moe::set_error(MOE_EHIP, "slot map launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
 // ------------------------------------------------------------ one decode step
 
 // One decode step; hy null: every miss copied into the cache.
@@ -445,13 +529,25 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
                          const_cast<int32_t*>(f.counts), const_cast<int32_t*>(f.offsets), const_cast<int32_t*>(f.perm),
                          const_cast<int32_t*>(f.inv), compute_stream);
   if (st != MOE_OK) return st;
-  MOE_HIP(hipMemcpyAsync(s->host_counts, f.counts, sizeof(int32_t) * (size_t)E, hipMemcpyDeviceToHost, ks));
-  if (hy) {
-    MOE_HIP(hipMemcpyAsync(hy->host_offsets, f.offsets, sizeof(int32_t) * (size_t)(E + 1), hipMemcpyDeviceToHost, ks));
-    MOE_HIP(hipMemcpyAsync(hy->host_perm, f.perm, sizeof(int32_t) * (size_t)T * f.k, hipMemcpyDeviceToHost, ks));
-    MOE_HIP(hipMemcpyAsync(hy->host_x, f.x, sizeof(uint16_t) * (size_t)T * f.H, hipMemcpyDeviceToHost, ks));
+  ensure_flag(c);
+  int32_t* counts_dev = (c->publish == 1 && !hy) ? static_cast<int32_t*>(mapped_device_ptr(c, s->host_counts)) : nullptr;
+  if (counts_dev) {
+    // the GPU writes the counts into the mapped host buffer and publishes the
+    // step's number; the host polls for it
+    const uint32_t seq = ++c->seq;
+    const hipError_t e = moe::launch_publish_counts(f.counts, E, counts_dev, c->flag_dev, seq, ks);
+    if (e != hipSuccess) return moe::set_error(MOE_EHIP, "%s: count handoff launch failed: %s", who, hipGetErrorString(e));
+    st = wait_flag(c, seq, ks, who);
+    if (st != MOE_OK) return st;
+  } else {
+    MOE_HIP(hipMemcpyAsync(s->host_counts, f.counts, sizeof(int32_t) * (size_t)E, hipMemcpyDeviceToHost, ks));
+    if (hy) {
+      MOE_HIP(hipMemcpyAsync(hy->host_offsets, f.offsets, sizeof(int32_t) * (size_t)(E + 1), hipMemcpyDeviceToHost, ks));
+      MOE_HIP(hipMemcpyAsync(hy->host_perm, f.perm, sizeof(int32_t) * (size_t)T * f.k, hipMemcpyDeviceToHost, ks));
+      MOE_HIP(hipMemcpyAsync(hy->host_x, f.x, sizeof(uint16_t) * (size_t)T * f.H, hipMemcpyDeviceToHost, ks));
+    }
+    MOE_HIP(hipStreamSynchronize(ks));
   }
-  MOE_HIP(hipStreamSynchronize(ks));
   std::vector<int32_t> all, host_run;  // the step's experts; those run on the host
   for (int e = 0; e < E; ++e)
     if (s->host_counts[e] > 0) {
@@ -488,7 +584,7 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
   const int nh = n - nm;
 
   // 5. slot map and masks
-  st = upload_map(c, s->host_map, s->dev_map, E, n, ks);
+  st = write_map(c, s->host_map, s->dev_map, E, n, ks);
   if (st != MOE_OK) return st;
   const int32_t* dmap = static_cast<const int32_t*>(s->dev_map);
   const uint8_t* dhm = reinterpret_cast<const uint8_t*>(dmap + E);
@@ -601,7 +697,7 @@ extern "C" moe_status moe_cache_prefetch_layer(moe_cache* c, int layer, const vo
   int nm = 0;
   st = fill_misses(c, layer, E, host_blobs, cs, &nm);
   if (st != MOE_OK) return st;
-  st = upload_map(c, host_map, dev_map, E, E, ks);
+  st = write_map(c, host_map, dev_map, E, E, ks);
   if (st != MOE_OK) return st;
   if (trace_slot && trace_hit && trace_evicted) copy_trace(c, E, nullptr, trace_slot, trace_hit, trace_evicted);
   return MOE_OK;

@@ -54,4 +54,49 @@ hipError_t launch_move_slots(const int32_t* src_slots, int n, int dst0, const vo
   return hipSuccess;
 }
 
+// ---------------------------------------------------------------- decode-step handoffs
+
+// Copies the step's per-expert row counts into a host-mapped buffer, then
+// publishes `seq` in the host-mapped flag (release at system scope): the host
+// waits for the flag by polling instead of a copy and a stream
+// synchronisation.
+__global__ __launch_bounds__(256) void k_publish_counts(const int32_t* __restrict__ counts, int E,
+                                                        int32_t* __restrict__ host_counts, uint32_t* flag,
+                                                        uint32_t seq) {
+  for (int e = threadIdx.x; e < E; e += 256) host_counts[e] = counts[e];
+  __threadfence_system();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+hipError_t launch_publish_counts(const int32_t* counts, int E, int32_t* host_counts_dev, uint32_t* flag_dev,
+                                 uint32_t seq, hipStream_t s) {
+  launch(k_publish_counts, dim3(1), dim3(256), 0, s, counts, E, host_counts_dev, flag_dev, seq);
+  return hipGetLastError();
+}
+
+// The step's slot map, passed by value: map layout int32 slot[E], uint8
+// hit[E], uint8 miss[E]; experts outside the step get slot 0 and no mask.
+__global__ __launch_bounds__(256) void k_write_map(StepMap m, int E, uint8_t* __restrict__ map) {
+  int32_t* slot = reinterpret_cast<int32_t*>(map);
+  uint8_t* hit = map + 4 * E;
+  uint8_t* miss = hit + E;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    slot[e] = 0;
+    hit[e] = 0;
+    miss[e] = 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < m.n; i += 256) {
+    const int e = m.expert[i];
+    slot[e] = m.slot[i];
+    (m.hit[i] ? hit : miss)[e] = 1;
+  }
+}
+
+hipError_t launch_write_map(const StepMap& m, int E, void* dev_map, hipStream_t s) {
+  launch(k_write_map, dim3(1), dim3(256), 0, s, m, E, static_cast<uint8_t*>(dev_map));
+  return hipGetLastError();
+}
+
 }  // namespace moe

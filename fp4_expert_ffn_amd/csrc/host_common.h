@@ -95,4 +95,14 @@ inline bool layout_of(int fmt, int H, int I, BlobLayout* L) {
   return true;
 }
 
+// The slot map of one decode step, passed to a kernel by value (the kernel
+// argument segment holds it; no host buffer).
+constexpr int kStepMapMax = 256;
+struct StepMap {
+  int32_t n;
+  int32_t expert[kStepMapMax];
+  int32_t slot[kStepMapMax];
+  uint8_t hit[kStepMapMax];
+};
+
 }  // namespace moe

@@ -183,6 +183,23 @@ hipError_t hipStreamWaitEvent(hipStream_t s, hipEvent_t e, unsigned int) {
   for (int i = 0; i < kMaxStreams; ++i) g_vc[id][i] = std::max(g_vc[id][i], e->vc[i]);
   return hipSuccess;
 }
+hipError_t hipGetLastError() { return hipSuccess; }
+hipError_t hipStreamQuery(hipStream_t) { return hipSuccess; }
+hipError_t hipHostMalloc(void** p, size_t n, unsigned int) {
+  static std::vector<std::unique_ptr<std::vector<uint8_t>>> bufs;
+  bufs.emplace_back(new std::vector<uint8_t>(n + 256));
+  *p = (void*)(((uintptr_t)bufs.back()->data() + 255) & ~(uintptr_t)255);
+  g_regions.push_back({(uintptr_t)*p, n, 2});
+  return hipSuccess;
+}
+hipError_t hipHostFree(void*) { return hipSuccess; }
+// host memory the test registered (or hipHostMalloc gave) is "mapped": same address
+hipError_t hipHostGetDevicePointer(void** d, void* h, unsigned int) {
+  const Region* r = region_of((uintptr_t)h, 1);
+  if (!r || r->device == 1) return hipErrorInvalidValue;
+  *d = h;
+  return hipSuccess;
+}
 hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind kind, hipStream_t s) {
   if (inject(0)) return hipErrorOutOfMemory;
   const Region* rd = region_of((uintptr_t)dst, n);
@@ -267,6 +284,28 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
 }
 
 namespace moe {
+// the count handoff: the stream writes the counts to host memory and the flag,
+// which the host has then observed (its clock joins the stream's)
+hipError_t launch_publish_counts(const int32_t* counts, int E, int32_t* host_counts, uint32_t* flag, uint32_t seq,
+                                 hipStream_t s) {
+  const Op o = tick(s);
+  memcpy(host_counts, counts, sizeof(int32_t) * (size_t)E);
+  __atomic_store_n(flag, seq, __ATOMIC_RELEASE);
+  for (int i = 0; i < kMaxStreams; ++i) g_host[i] = std::max(g_host[i], o.vc[i]);
+  return hipSuccess;
+}
+hipError_t launch_write_map(const StepMap& m, int E, void* dev_map, hipStream_t s) {
+  tick(s);
+  if (!region_of((uintptr_t)dev_map, 6 * (size_t)E)) bad("slot map outside the registered memory", E, 0);
+  int32_t* slot = static_cast<int32_t*>(dev_map);
+  uint8_t* hit = static_cast<uint8_t*>(dev_map) + 4 * E;
+  memset(dev_map, 0, 6 * (size_t)E);
+  for (int i = 0; i < m.n; ++i) {
+    slot[m.expert[i]] = m.slot[i];
+    (m.hit[i] ? hit : hit + E)[m.expert[i]] = 1;
+  }
+  return hipSuccess;
+}
 hipError_t launch_move_slots(const int32_t* src_slots, int n, int dst0, const void* src_pool, void* dst_pool,
                              size_t slot_bytes, hipStream_t s) {
   const Op o = tick(s);
