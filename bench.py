@@ -181,7 +181,7 @@ def layer_workload(wl, args, torch, dev, steps=None, warmup=None, cpu_baseline=T
             lg = torch.from_numpy(b["logits"]).to(dev) if "logits" in b else None
             wr = torch.from_numpy(b["w_router"]).to(dev) if "w_router" in b else None
             st = lay.new_state(T)
-            calls.append((T, x, lg, wr, st, st.args(T, x)))
+            calls.append((T, x, lg, wr, st, st.layer_args(T, x, lg if lg is not None else st.logits)))
         units.append(calls)
     # copies cycle with a period of ncopies calls: extend the unit list to a whole period
     while (len(units) * ncalls) % ncopies:
@@ -189,15 +189,15 @@ def layer_workload(wl, args, torch, dev, steps=None, warmup=None, cpu_baseline=T
         calls = []
         for j, (T, x, lg, wr, _, _) in enumerate(units[i % len(inputs)]):
             st = layers[(ncalls * i + j) % ncopies].new_state(T)
-            calls.append((T, x, lg, wr, st, st.args(T, x)))
+            calls.append((T, x, lg, wr, st, st.layer_args(T, x, lg if lg is not None else st.logits)))
         units.append(calls)
     U = len(units)
     toks_per_step = sum(c[0] for c in units[0])
 
     def run_call(c):
-        T, x, lg, wr, st, a = c
-        st.route(T, x=x, w_router=wr, logits=lg)
-        st.ffn(T, x, args=a)
+        # one layer call: router logits (large-expert layer), then moe_layer
+        T, x, lg, wr, st, la = c
+        st.call(T, x, logits=lg, w_router=wr, la=la)
 
     def capture(call_lists):
         g = torch.cuda.CUDAGraph()
@@ -241,13 +241,13 @@ def layer_workload(wl, args, torch, dev, steps=None, warmup=None, cpu_baseline=T
         del g
 
     # Dominant kernel (the gate/up projection): launch durations from HIP events
-    # recorded at the kernel's own start and end (moe_expert_ffn_traced), over
-    # the unit's calls run eagerly.  Launch order: GEMV path gate/up, down,
-    # combine; FP4 path quantiser, gate/up, down, combine; BF16 matrix-core
-    # path gate/up, down, combine.  The calls are enqueued in batches behind a
-    # spin kernel on the same stream, so the GPU never waits for the host
-    # inside a timed launch.
-    from fp4_expert_ffn_amd import moe_expert_ffn_traced
+    # recorded at the kernel's own start and end (moe_layer_traced), over the
+    # unit's calls run eagerly.  Launch order: GEMV path gate/up (with the
+    # routing folded in for batches of up to 4 tokens), down, combine; FP4 path
+    # quantiser, gate/up, down, combine; BF16 matrix-core path gate/up, down,
+    # combine.  The calls are enqueued in batches behind a spin kernel on the
+    # same stream, so the GPU never waits for the host inside a timed launch.
+    from fp4_expert_ffn_amd import moe_layer_traced, moe_router_logits
     dom = 1 if amode == "mxfp4" else 0
     stream_now = torch.cuda.current_stream()
     reps = max(1, -(-64 // U))
@@ -257,12 +257,13 @@ def layer_workload(wl, args, torch, dev, steps=None, warmup=None, cpu_baseline=T
     for i in range(0, len(flat), 16):
         torch.cuda._sleep(int(0.012 * clock_hz))  # about 12 ms of backlog
         for c in flat[i:i + 16]:
-            T, x, lg, wr, st, a = c
-            st.route(T, x=x, w_router=wr, logits=lg)
+            T, x, lg, wr, st, la = c
+            if wr is not None:
+                moe_router_logits(x, wr, T, H, E, st.logits)
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
             for e in evs:
                 e.record(stream_now)  # creates the HIP events; re-recorded by the launches
-            n = moe_expert_ffn_traced(a, evs)
+            n = moe_layer_traced(la, evs)
             assert n >= 2 * (dom + 1), n
             recs.append((c, evs[2 * dom], evs[2 * dom + 1]))
     torch.cuda.synchronize()
@@ -302,9 +303,11 @@ def layer_workload(wl, args, torch, dev, steps=None, warmup=None, cpu_baseline=T
     elif amode == "mxfp4":
         kname = "k_fp4_gemm<0, true> (gate/up projection + SwiGLU, FP4 matrix cores)"
     elif fmt == "nvfp4":
-        kname = "k_gemv (gate/up projection + SwiGLU, NVFP4 weights on fp16 matrix cores)"
+        kname = "k_gemv (gate/up projection + SwiGLU, NVFP4 weights on fp16 matrix cores; " \
+                "the routing folded in at batches of at most 4 tokens)"
     else:
-        kname = "k_gemv (gate/up projection + SwiGLU, bf16 operands)"
+        kname = "k_gemv (gate/up projection + SwiGLU, bf16 operands; the routing folded in at batches of at most " \
+                "4 tokens)"
     # The large-expert prefill sits below the FP4 ridge (about 267 FLOP/B): HBM bounds it.
     if wl in ("prefill-nvfp4", "prefill-fp8"):
         # 4.5 / 8.5 bits per weight: compute-bound on the bf16 matrix cores

@@ -39,6 +39,11 @@ class FfnArgs(ctypes.Structure):
     ]
 
 
+class LayerArgs(ctypes.Structure):
+    _fields_ = [("logits", ctypes.c_void_p), ("renormalize", ctypes.c_int), ("topk_ids", ctypes.c_void_p),
+                ("ffn", FfnArgs)]
+
+
 class CacheStep(ctypes.Structure):
     _fields_ = [
         ("layer", ctypes.c_int), ("logits", ctypes.c_void_p), ("renormalize", ctypes.c_int),
@@ -91,6 +96,8 @@ SIGNATURES = {
     "moe_expert_ffn_workspace_size": (_sz, [ctypes.POINTER(FfnArgs)]),
     "moe_expert_ffn": (_i, [ctypes.POINTER(FfnArgs), _vp]),
     "moe_expert_ffn_noalloc": (_i, [ctypes.POINTER(FfnArgs), _vp]),
+    "moe_layer": (_i, [ctypes.POINTER(LayerArgs), _vp]),
+    "moe_layer_traced": (_i, [ctypes.POINTER(LayerArgs), _vp, _vp, _i, _vp]),
     "moe_expert_ffn_traced": (_i, [ctypes.POINTER(FfnArgs), _vp, _vp, _i, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "moe_quantize_mxfp4": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
@@ -239,6 +246,19 @@ def moe_expert_ffn_workspace_size(args: FfnArgs) -> int:
 
 def moe_expert_ffn(args: FfnArgs, stream=None):
     _check(lib().moe_expert_ffn(ctypes.byref(args), stream_handle(stream)), "moe_expert_ffn")
+
+
+def moe_layer(args: LayerArgs, stream=None):
+    """Routing, expert FFN and combine of one layer call (args.ffn.out required)."""
+    _check(lib().moe_layer(ctypes.byref(args), stream_handle(stream)), "moe_layer")
+
+
+def moe_layer_traced(args: LayerArgs, events, stream=None) -> int:
+    arr = (ctypes.c_void_p * max(len(events), 1))(*[e.cuda_event for e in events])
+    n = ctypes.c_int(0)
+    _check(lib().moe_layer_traced(ctypes.byref(args), stream_handle(stream), arr, len(events), ctypes.byref(n)),
+           "moe_layer_traced")
+    return n.value
 
 
 def moe_expert_ffn_noalloc(args: FfnArgs, stream=None):

@@ -12,6 +12,7 @@
 
 namespace moe {
 hipError_t launch_gemv(const FfnParams& P, const GemvArgs& G, hipStream_t s);
+bool gemv_route_fits(const FfnParams& P);
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s);
 hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st);
 hipError_t launch_fp4_codes_canon(const FfnParams& P, const MfmaBufs& B, int which, uint8_t* q, uint8_t* s,
@@ -258,10 +259,14 @@ FfnParams params_of(const moe_ffn_args* a) {
 }
 }  // namespace
 
-extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream) {
-  moe_status st = check_args(a);
-  if (st != MOE_OK || a->T == 0) return st;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+// Routing folded into the expert FFN's first launch (moe_layer).
+struct RouteFold {
+  const float* logits;
+  int renorm;
+  int32_t* ids;
+};
+
+static moe_status run_ffn(const moe_ffn_args* a, hipStream_t s, const RouteFold* rf) {
   FfnParams P = params_of(a);
 
   const WsLayout w = ws_layout(a);
@@ -279,6 +284,12 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     // an internal y read only by the combine below: written in flat order,
     // so the combine needs no row-index load
     G.yflat = (!a->y && a->out && (long long)a->T * a->k <= 1024) ? 1 : 0;
+    if (rf) {
+      G.logits = rf->logits;
+      G.renorm = rf->renorm;
+      G.ids_out = rf->ids;
+      G.w_out = const_cast<float*>(a->topk_w);
+    }
     e = launch_gemv(P, G, s);
   } else {
     MfmaBufs B{};
@@ -303,8 +314,42 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
     const bool yflat = path == kPathGemv && !a->y && (long long)a->T * a->k <= 1024;
     e = launch_combine(y, yflat ? nullptr : a->inv, a->topk_w, ysh, a->T, a->k, a->H, a->out, s);
     if (e != hipSuccess) return set_error(MOE_EHIP, "moe_expert_ffn: combine launch failed: %s", hipGetErrorString(e));
-    }
+  }
   return MOE_OK;
+}
+
+extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream) {
+  moe_status st = check_args(a);
+  if (st != MOE_OK || a->T == 0) return st;
+  return run_ffn(a, reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
+extern "C" moe_status moe_layer(const moe_layer_args* la, moe_stream_t stream) {
+  MOE_CHECK_ARG(la, "moe_layer: null args");
+  const moe_ffn_args* a = &la->ffn;
+  moe_status st = check_args(a);
+  if (st != MOE_OK) return st;
+  MOE_CHECK_ARG(a->out && !a->expert_mask, "moe_layer: out is required and expert_mask must be null");
+  MOE_CHECK_ARG(a->k <= a->E, "moe_layer: k=%d > E=%d", a->k, a->E);
+  if (a->T == 0) return MOE_OK;
+  MOE_CHECK_ARG(la->logits && la->topk_ids, "moe_layer: logits and topk_ids are required");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (choose_path(a) == kPathGemv && gemv_route_fits(params_of(a))) {
+    const RouteFold rf{la->logits, la->renormalize ? 1 : 0, la->topk_ids};
+    return run_ffn(a, s, &rf);
+  }
+  if ((long long)a->T * a->k <= 1024)
+    st = moe_route_permute(la->logits, a->T, a->E, a->k, la->renormalize, la->topk_ids, const_cast<float*>(a->topk_w),
+                           const_cast<int32_t*>(a->counts), const_cast<int32_t*>(a->offsets),
+                           const_cast<int32_t*>(a->perm), const_cast<int32_t*>(a->inv), stream);
+  else {
+    st = moe_route(la->logits, a->T, a->E, a->k, la->renormalize, la->topk_ids, const_cast<float*>(a->topk_w), stream);
+    if (st == MOE_OK)
+      st = moe_permute(la->topk_ids, a->T, a->k, a->E, const_cast<int32_t*>(a->counts), const_cast<int32_t*>(a->offsets),
+                       const_cast<int32_t*>(a->perm), const_cast<int32_t*>(a->inv), stream);
+  }
+  if (st != MOE_OK) return st;
+  return run_ffn(a, s, nullptr);
 }
 
 extern "C" moe_status moe_debug_fp4_codes(const moe_ffn_args* a, int which, uint8_t* q, uint8_t* s,
@@ -379,6 +424,17 @@ extern "C" moe_status moe_expert_ffn_traced(const moe_ffn_args* a, moe_stream_t 
   LaunchTrace t{events, n_events, 0};
   g_launch_trace = &t;
   const moe_status st = moe_expert_ffn(a, stream);
+  g_launch_trace = nullptr;
+  *n_recorded = t.used;
+  return st;
+}
+
+extern "C" moe_status moe_layer_traced(const moe_layer_args* a, moe_stream_t stream, void* const* events,
+                                       int n_events, int* n_recorded) {
+  MOE_CHECK_ARG(n_events >= 0 && (n_events == 0 || events) && n_recorded, "moe_layer_traced: bad event list");
+  LaunchTrace t{events, n_events, 0};
+  g_launch_trace = &t;
+  const moe_status st = moe_layer(a, stream);
   g_launch_trace = nullptr;
   *n_recorded = t.used;
   return st;

@@ -54,6 +54,14 @@ struct GemvArgs {
   int act_off;     // LDS byte offset of the staged operand rows
   int yflat;       // 1: y rows in flat order t * k + j (T*k <= 1024 only), 0: perm order
   int ncu;         // > 0: the grid is two workgroups per CU on ncu CUs (items dealt per CU)
+  // routing folded into the gate/up launch (logits non-null): every workgroup
+  // routes the call's few tokens itself; workgroup 0 writes topk ids /
+  // weights and the counts, offsets, permutation and its inverse (P's
+  // pointers) for the down projection and the combine
+  const float* logits;
+  int renorm;
+  int32_t* ids_out;
+  float* w_out;
 };
 
 // One unit of expert work: an expert (or the shared expert) and its rows.

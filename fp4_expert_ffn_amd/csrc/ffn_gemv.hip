@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "ffn_common.h"
+#include "topk.h"
 #include "wave.h"
 
 namespace moe {
@@ -220,6 +221,92 @@ __device__ inline void build_active(const FfnParams& P, int rbs, const ActiveLds
   lds_barrier();
 }
 
+// The routing of a call of at most kRouteFoldRows tokens (T * k <= 64),
+// computed by every workgroup of the gate/up launch in place of reading it:
+// wave t selects token t's experts (wave_topk, the routing kernels' own
+// selection), then the stable counting sort of the T * k pairs by expert
+// (rank = pairs with a lower expert id + pairs of the same expert and a
+// lower flat index) fills the active-expert table.  Each expert's rows fit
+// one row block (count <= T <= rbs).  Workgroup 0 also writes the routing
+// outputs for the later launches: ids, weights, counts (all E), offsets
+// (E + 1), perm and inv.  No expert mask.
+constexpr int kRouteFoldRows = 4;
+
+template <int NPER>
+__device__ inline void route_active(const FfnParams& P, const GemvArgs& G, const ActiveLds& A) {
+  __shared__ int32_t s_ids[64], s_rank[64], s_lower[64];
+  __shared__ float s_w[64];
+  __shared__ int32_t s_slot[256];
+  __shared__ uint8_t s_first[64];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int T = P.T, k = P.k, E = P.E, N = T * k;
+  for (int e = tid; e < E; e += 256) s_slot[e] = P.slot_of_expert[e];
+  if (wave < T) wave_topk<NPER>(G.logits + (size_t)wave * E, E, k, G.renorm, s_ids + wave * k, s_w + wave * k);
+  __syncthreads();
+  if (tid < N) {
+    const int e = s_ids[tid];
+    int lower = 0, same_before = 0;
+    for (int g = 0; g < N; ++g) {
+      const int eg = s_ids[g];
+      lower += eg < e;
+      same_before += (eg == e) & (g < tid);
+    }
+    s_rank[tid] = lower + same_before;
+    s_lower[tid] = lower;
+    s_first[tid] = same_before == 0;
+  }
+  __syncthreads();
+  if (tid < N) {
+    A.flat[s_rank[tid]] = tid;
+    A.tok[s_rank[tid]] = tid / k;
+    if (s_first[tid]) {
+      const int e = s_ids[tid];
+      int a = 0, cnt = 0;
+      for (int g = 0; g < N; ++g) {
+        a += s_first[g] && s_ids[g] < e;
+        cnt += s_ids[g] == e;
+      }
+      A.cnt[a] = cnt;
+      A.p0[a] = s_lower[tid];
+      A.slot[a] = s_slot[e];
+      A.rb[a + 1] = a + 1;
+    }
+  }
+  if (tid == 0) {
+    int n = 0;
+    for (int g = 0; g < N; ++g) n += s_first[g];
+    A.rb[0] = 0;
+    if (P.shared_blob) {
+      A.cnt[n] = T;
+      A.p0[n] = N;
+      A.slot[n] = -1;
+      A.rb[n + 1] = n + 1;
+      ++n;
+    }
+    *A.n = n;
+  }
+  if (blockIdx.x == 0) {
+    int32_t* counts = const_cast<int32_t*>(P.counts);
+    int32_t* offsets = const_cast<int32_t*>(P.offsets);
+    for (int e = tid; e <= E; e += 256) {
+      int below = 0, at = 0;
+      for (int g = 0; g < N; ++g) {
+        below += s_ids[g] < e;
+        at += s_ids[g] == e;
+      }
+      offsets[e] = below;
+      if (e < E) counts[e] = at;
+    }
+    if (tid < N) {
+      G.ids_out[tid] = s_ids[tid];
+      G.w_out[tid] = s_w[tid];
+      const_cast<int32_t*>(P.perm)[s_rank[tid]] = tid;
+      const_cast<int32_t*>(P.inv)[tid] = s_rank[tid];
+    }
+  }
+  lds_barrier();
+}
+
 // Work item of one row block: which expert, which rows.
 struct RowBlock {
   const uint8_t* blob;
@@ -383,10 +470,11 @@ constexpr int kTrashSlots = 256;         // 4 KiB scratch slots (workgroup index
 // current one's matrix instructions run.
 constexpr int kXallMaxT = 4;
 
-template <int FMT, bool DOWN, int SUB, bool XALL>
+template <int FMT, bool DOWN, int SUB, bool XALL, bool ROUTE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemv(FfnParams P, GemvArgs G) {
   using F = Fmt<FMT>;
   static_assert(!(XALL && DOWN), "the down projection stages its rows per task");
+  static_assert(!ROUTE || XALL, "the folded routing goes with every token row staged");
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int s_pexp[16];
   __shared__ float s_u[2][16][17];
@@ -399,9 +487,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int rbs = DOWN ? G.rbs2 : G.rbs1, nchunk = DOWN ? G.nd : G.ng;
   const ActiveLds A = active_view(lds, G.na, P.T * P.k <= kTokCache ? P.T * P.k : 0);
   uint8_t* act = lds + G.act_off;  // operand rows (swizzled) + slack
-  if (P.E <= 128) build_active<2>(P, rbs, A);
-  else if (P.E <= 256) build_active<4>(P, rbs, A);
-  else build_active<16>(P, rbs, A);
+  if constexpr (ROUTE) {
+    // the token rows do not depend on the routing: staged while it runs
+    dma_rows(act, P.x, K, P.T, [](int r) { return r; });
+    if (P.E <= 128) route_active<2>(P, G, A);
+    else route_active<4>(P, G, A);
+  } else if (P.E <= 128) {
+    build_active<2>(P, rbs, A);
+  } else if (P.E <= 256) {
+    build_active<4>(P, rbs, A);
+  } else {
+    build_active<16>(P, rbs, A);
+  }
   const int nrb = A.rb[*A.n];
   // this workgroup's items: [i_beg, i_end) of nrb * nchunk, row block major.
   // With two workgroups per CU (workgroups b and b + ncu share a CU), each
@@ -436,7 +533,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // XALL: every token row of x, in token order, before the first task (whose
   // first weights then go out behind them)
-  if (XALL && i_beg < i_end) dma_rows(act, P.x, K, P.T, [](int r) { return r; });
+  if (XALL && !ROUTE && i_beg < i_end) dma_rows(act, P.x, K, P.T, [](int r) { return r; });
   bool first = true;
 #pragma unroll 1
   for (long long it = i_beg; it < i_end;) {
@@ -675,6 +772,16 @@ static GemvKernel gemv_kernel(int nk) {
 }
 
 template <int FMT>
+static GemvKernel gemv_route_kernel(int nk) {
+  if (nk == 16) return k_gemv<FMT, false, kSubMax<FMT>, true, true>;
+  if (nk % 8 == 0) return k_gemv<FMT, false, 8, true, true>;
+  if (nk % 6 == 0) return k_gemv<FMT, false, 6, true, true>;
+  if (nk % 4 == 0) return k_gemv<FMT, false, 4, true, true>;
+  if (nk % 2 == 0) return k_gemv<FMT, false, 2, true, true>;
+  return k_gemv<FMT, false, 1, true, true>;
+}
+
+template <int FMT>
 static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   const long long rows = (long long)P.T * P.k;
   G.na = (int)std::min<long long>(P.E, rows) + (P.shared_blob ? 1 : 0);
@@ -699,8 +806,11 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
     if (P.shared_blob) n += (P.T + rbs - 1) / rbs;
     return n;
   };
-  const auto k1 = xall ? gemv_kernel<FMT, false, true>(P.H / Fmt<FMT>::KT)
-                       : gemv_kernel<FMT, false, false>(P.H / Fmt<FMT>::KT);
+  const bool route = G.logits != nullptr;  // the caller checked gemv_route_fits
+  if (route && !xall) return hipErrorInvalidValue;
+  const auto k1 = route ? gemv_route_kernel<FMT>(P.H / Fmt<FMT>::KT)
+                  : xall ? gemv_kernel<FMT, false, true>(P.H / Fmt<FMT>::KT)
+                         : gemv_kernel<FMT, false, false>(P.H / Fmt<FMT>::KT);
   const auto k2 = gemv_kernel<FMT, true, false>(P.I / Fmt<FMT>::KT);
   // The kernels are built for two resident workgroups per CU (their register
   // budget); more would start late, after the first ones finish.
@@ -719,10 +829,11 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   return e;
 }
 
-template <int FMT, bool DOWN, bool XALL>
+template <int FMT, bool DOWN, bool XALL, bool ROUTE = false>
 static hipError_t set_lds_limit_all() {
-  const GemvKernel ks[] = {k_gemv<FMT, DOWN, kSubMax<FMT>, XALL>, k_gemv<FMT, DOWN, 8, XALL>, k_gemv<FMT, DOWN, 6, XALL>,
-                           k_gemv<FMT, DOWN, 4, XALL>, k_gemv<FMT, DOWN, 2, XALL>, k_gemv<FMT, DOWN, 1, XALL>};
+  const GemvKernel ks[] = {k_gemv<FMT, DOWN, kSubMax<FMT>, XALL, ROUTE>, k_gemv<FMT, DOWN, 8, XALL, ROUTE>,
+                           k_gemv<FMT, DOWN, 6, XALL, ROUTE>, k_gemv<FMT, DOWN, 4, XALL, ROUTE>,
+                           k_gemv<FMT, DOWN, 2, XALL, ROUTE>, k_gemv<FMT, DOWN, 1, XALL, ROUTE>};
   for (GemvKernel f : ks) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)kDynLds);
@@ -736,6 +847,7 @@ static hipError_t set_lds_limits_fmt() {
   hipError_t e;
   if ((e = set_lds_limit_all<FMT, false, false>()) != hipSuccess) return e;
   if ((e = set_lds_limit_all<FMT, false, true>()) != hipSuccess) return e;
+  if ((e = set_lds_limit_all<FMT, false, true, true>()) != hipSuccess) return e;
   return set_lds_limit_all<FMT, true, false>();
 }
 
@@ -750,6 +862,13 @@ static hipError_t set_gemv_lds_limits() {
     done = true;
   }
   return hipSuccess;
+}
+
+// Whether a call can take the gate/up launch with the routing folded in.
+bool gemv_route_fits(const FfnParams& P) {
+  // every token row staged in LDS beside the tables (the launcher's XALL condition holds with room to spare)
+  return P.T >= 1 && P.T <= kRouteFoldRows && P.T * P.k <= 64 && P.E <= 256 && P.mask == nullptr &&
+         (size_t)P.T * row_bytes(P.H) + kRowSlack + 16384 <= kDynLds;
 }
 
 hipError_t launch_gemv(const FfnParams& P, const GemvArgs& G, hipStream_t s) {

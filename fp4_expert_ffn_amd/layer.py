@@ -80,11 +80,24 @@ class LayerState:
     def ffn(self, T, x, stream=None, args=None):
         L.moe_expert_ffn(args if args is not None else self.args(T, x), stream)
 
+    def layer_args(self, T, x, logits):
+        """moe_layer arguments: routing outputs into this state's buffers, the combined output in out."""
+        la = L.LayerArgs()
+        la.logits, la.renormalize, la.topk_ids = L.ptr(logits), 1 if self.layer.renormalize else 0, self.ids.data_ptr()
+        la.ffn = self.args(T, x)
+        return la
+
+    def call(self, T, x, *, logits=None, w_router=None, stream=None, la=None):
+        """One layer call: router logits (if w_router is given), then moe_layer."""
+        if logits is None:
+            L.moe_router_logits(x, w_router, T, self.layer.H, self.layer.E, self.logits, stream)
+            logits = self.logits
+        L.moe_layer(la if la is not None else self.layer_args(T, x, logits), stream)
+
     def forward(self, x, *, logits=None, w_router=None, stream=None):
         T = x.shape[0]
         assert T <= self.max_tokens
-        self.route(T, x=x, w_router=w_router, logits=logits, stream=stream)
-        self.ffn(T, x, stream)
+        self.call(T, x, logits=logits, w_router=w_router, stream=stream)
         self.last_x = x
         return self.out[:T]
 
@@ -120,7 +133,7 @@ class MoELayer:
     # ------------------------------------------------------------ default state
     def __getattr__(self, name):
         if name in ("logits", "ids", "w", "counts", "offsets", "perm", "inv", "out", "y", "args", "route", "ffn",
-                    "forward", "check"):
+                    "forward", "check", "call", "layer_args"):
             return getattr(self.__dict__["state"], name)
         raise AttributeError(name)
 

@@ -193,6 +193,30 @@ size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a);
  * MOE_EHIP (a launch failed); nothing is enqueued on an error. */
 moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream);
 
+/* One whole layer call: routing (moe_route + moe_permute), the expert FFN and
+ * the combine, with results equal to moe_route_permute(logits, ...)
+ * followed by moe_expert_ffn(&ffn), in as few launches as the batch
+ * allows: for decode batches of up to 4 tokens (T*k <= 64, E <= 256, the
+ * bf16-activation path) the routing runs inside the gate/up launch, which
+ * saves the routing kernel and its boundary.
+ * [pages as for moe_route and moe_expert_ffn.]
+ * ffn.counts, offsets, perm, inv and topk_w are outputs here (written by
+ * the call); ffn.out is required, ffn.expert_mask must be null.  logits:
+ * [T,E] fp32; topk_ids: [T,k] output. */
+typedef struct {
+  const float* logits;
+  int renormalize;
+  int32_t* topk_ids;
+  moe_ffn_args ffn;
+} moe_layer_args;
+moe_status moe_layer(const moe_layer_args* a, moe_stream_t stream);
+
+/* moe_layer timing its expert-FFN launches as moe_expert_ffn_traced does
+ * (a separate routing kernel, when one runs, records no events); with the
+ * routing folded in, launch 0 is the gate/up launch that routes. */
+moe_status moe_layer_traced(const moe_layer_args* a, moe_stream_t stream, void* const* events, int n_events,
+                            int* n_recorded);
+
 /* moe_expert_ffn without a caller workspace and without any allocation, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc).  a->workspace and

@@ -80,6 +80,10 @@ SMALL = [  # fmt, amode, T, E, k, H, I, shared
     ("nvfp4", "bf16", 300, 8, 2, 256, 384, True),    # NVFP4 decoded to bf16 on the matrix cores
     ("nvfp4", "bf16", 700, 16, 1, 384, 256, False),
     ("fp8", "bf16", 257, 6, 3, 512, 256, True),
+    ("mxfp4", "bf16", 3, 64, 8, 256, 256, True),     # routing folded into the gate/up launch
+    ("bf16", "bf16", 4, 256, 8, 256, 128, False),
+    ("fp8", "bf16", 2, 16, 4, 384, 256, True),
+    ("nvfp4", "bf16", 4, 128, 16, 256, 128, False),  # T * k = 64
 ]
 
 
@@ -116,6 +120,42 @@ def test_large_magnitude_activations(fmt, rows):
     layer.forward(_x(x), logits=torch.from_numpy(logits).to(DEV))
     torch.cuda.synchronize()
     _full_check(layer, x, experts, k, logits)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_folded_routing_edge_rows(T):
+    """The routing folded into the gate/up launch (moe_layer, T <= 4) on rows
+    with ties, -inf and NaN logits: ids, weights, counts, offsets, perm and
+    inv against the oracle's route and permute (ids and the permutation
+    bit-exact), and the output against the oracle layer."""
+    fmt, E, k, H, I = "nvfp4", 128, 8, 256, 256
+    experts = [synth.expert(fmt, H, I, config=93, expert_id=e) for e in range(E)]
+    rng = np.random.default_rng(T)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, [5, 9, 17, 40, 41, 100, 120, 127]] = 3.0                 # an 8-way tie at the top
+    logits[0, [60, 61]] = 3.0                                          # ... and beyond it
+    if T > 1:
+        logits[1, :] = -np.inf
+        logits[1, [7, 8, 90]] = [0.5, np.nan, 0.5]
+        logits[2, :] = 1.0                                             # all equal
+        logits[3, 10:20] = np.nan
+    x = synth.activations(T, H, 93, T)
+    layer = resident_layer(experts, k=k, T=T)
+    say(f"folded routing, edge rows, T={T}")
+    layer.forward(_x(x), logits=torch.from_numpy(logits).to(DEV))
+    torch.cuda.synchronize()
+    rid, rw = oracle.moe.route(logits, k)
+    counts, offsets, perm, inv = oracle.moe.permute(rid, E)
+    assert np.array_equal(layer.ids[:T].cpu().numpy(), rid)
+    np.testing.assert_allclose(layer.w[:T].cpu().numpy(), rw, rtol=2e-6, atol=1e-7)
+    assert np.array_equal(layer.counts.cpu().numpy(), counts)
+    assert np.array_equal(layer.offsets.cpu().numpy(), offsets)
+    assert np.array_equal(layer.perm[:T * k].cpu().numpy(), perm)
+    assert np.array_equal(layer.inv[:T * k].cpu().numpy(), inv)
+    ref = oracle.moe.layer(x, experts, k, logits=logits)
+    err = oracle.moe.relative_error(out_f32(layer, T), ref["out"])
+    say(f"    rel err {err:.3e}")
+    assert err <= TOL
 
 
 def test_zero_tokens_is_a_no_op():
