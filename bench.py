@@ -470,10 +470,18 @@ def main():
 
 # Kernel-name patterns of the dominant kernel (gate/up projection) per workload.
 DOMINANT = {"decode": "k_gemv<2, false", "large-decode": "k_gemv<1, false", "prefill-mxfp4": "k_fp4_gemm<0, true>",
-            "large-prefill": "k_fp4_gemm<0, true>", "prefill-bf16": "k_fp4_gemm<0, false>"}
-KERNEL_SOURCES = ["fp4_expert_ffn_amd/csrc/ffn_gemv.hip", "fp4_expert_ffn_amd/csrc/ffn_mfma.hip",
-                  "fp4_expert_ffn_amd/csrc/ffn_fp4gemm.hip", "fp4_expert_ffn_amd/csrc/ffn_common.h",
-                  "fp4_expert_ffn_amd/csrc/common.h"]
+            "large-prefill": "k_fp4_gemm<0, true>", "prefill-bf16": "k_fp4_gemm<0, false>",
+            "prefill-nvfp4": "k_mfma_ffn<false, 0", "prefill-fp8": "k_mfma_ffn<false, 0"}
+# The sources each workload's dominant kernel is built from: a committed
+# counter summary stands only while none of them has changed.
+_HEADERS = ["fp4_expert_ffn_amd/csrc/ffn_common.h", "fp4_expert_ffn_amd/csrc/common.h",
+            "fp4_expert_ffn_amd/csrc/host_common.h"]
+_GEMV = ["fp4_expert_ffn_amd/csrc/ffn_gemv.hip", "fp4_expert_ffn_amd/csrc/topk.h",
+         "fp4_expert_ffn_amd/csrc/wave.h"] + _HEADERS
+_FP4GEMM = ["fp4_expert_ffn_amd/csrc/ffn_fp4gemm.hip"] + _HEADERS
+_MFMA = ["fp4_expert_ffn_amd/csrc/ffn_mfma.hip", "fp4_expert_ffn_amd/csrc/mfma_addr.h"] + _HEADERS
+KERNEL_SOURCES = {"decode": _GEMV, "large-decode": _GEMV, "prefill-mxfp4": _FP4GEMM, "large-prefill": _FP4GEMM,
+                  "prefill-bf16": _FP4GEMM, "prefill-nvfp4": _MFMA, "prefill-fp8": _MFMA}
 
 
 def _pmc_rows(path, counter):
@@ -529,7 +537,7 @@ def summarize(args):
             res[name] = {"kib_per_dispatch": sum(dom) / len(dom), "dispatches": len(dom),
                          "copy_kib": sum(cal) / len(cal), "bytes_per_kib": copy_bytes / (sum(cal) / len(cal))}
         h = hashlib.sha256()
-        for src in KERNEL_SOURCES:
+        for src in KERNEL_SOURCES[wl]:
             with open(os.path.join(ROOT, src), "rb") as f:
                 h.update(f.read())
         fetch = res["FETCH_SIZE"]["kib_per_dispatch"] * res["FETCH_SIZE"]["bytes_per_kib"]
@@ -537,7 +545,7 @@ def summarize(args):
         t = {"workload": wl, "kernel_pattern": pat, "command": cmd, "counters": res,
              "fetch_bytes_per_launch": int(fetch), "write_bytes_per_launch": int(write),
              "bytes_per_launch": int(fetch + write), "copy_bytes": copy_bytes,
-             "sources": KERNEL_SOURCES, "sources_sha256": h.hexdigest()}
+             "sources": KERNEL_SOURCES[wl], "sources_sha256": h.hexdigest()}
         with open(out, "w") as f:
             json.dump(t, f, indent=1)
         print(f"wrote {out}: {int(fetch + write)} bytes per launch")

@@ -80,10 +80,16 @@ SMALL = [  # fmt, amode, T, E, k, H, I, shared
     ("nvfp4", "bf16", 300, 8, 2, 256, 384, True),    # NVFP4 decoded to bf16 on the matrix cores
     ("nvfp4", "bf16", 700, 16, 1, 384, 256, False),
     ("fp8", "bf16", 257, 6, 3, 512, 256, True),
-    ("mxfp4", "bf16", 3, 64, 8, 256, 256, True),     # routing folded into the gate/up launch
+    ("mxfp4", "bf16", 3, 64, 8, 256, 256, True),     # routing folded into the gate/up launch (T <= 4)
     ("bf16", "bf16", 4, 256, 8, 256, 128, False),
     ("fp8", "bf16", 2, 16, 4, 384, 256, True),
     ("nvfp4", "bf16", 4, 128, 16, 256, 128, False),  # T * k = 64
+    ("nvfp4", "bf16", 16, 128, 8, 256, 256, True),   # T * k = 128: routing kernel, then the GEMV launches
+    ("mxfp4", "bf16", 11, 256, 8, 512, 384, False),  # E = 256; down K-tiles 3 (sub-items of 1)
+    ("bf16", "bf16", 16, 32, 8, 256, 256, True),
+    ("fp8", "bf16", 9, 64, 8, 384, 768, True),       # gate/up K-tiles 6 (sub-items of 2), down 12
+    ("mxfp4", "bf16", 5, 8, 8, 256, 128, False),     # k = E: every expert in every token
+    ("nvfp4", "bf16", 7, 16, 8, 128, 256, True),     # one gate/up K-tile
 ]
 
 
@@ -122,12 +128,13 @@ def test_large_magnitude_activations(fmt, rows):
     _full_check(layer, x, experts, k, logits)
 
 
-@pytest.mark.parametrize("T", [1, 4])
+@pytest.mark.parametrize("T", [1, 4, 16])
 def test_folded_routing_edge_rows(T):
-    """The routing folded into the gate/up launch (moe_layer, T <= 4) on rows
-    with ties, -inf and NaN logits: ids, weights, counts, offsets, perm and
-    inv against the oracle's route and permute (ids and the permutation
-    bit-exact), and the output against the oracle layer."""
+    """moe_layer's routing (folded into the gate/up launch for T <= 4, the
+    routing kernel above) on rows with ties, -inf and NaN logits: ids,
+    weights, counts, offsets, perm and inv against the oracle's route and
+    permute (ids and the permutation bit-exact), and the output against the
+    oracle layer."""
     fmt, E, k, H, I = "nvfp4", 128, 8, 256, 256
     experts = [synth.expert(fmt, H, I, config=93, expert_id=e) for e in range(E)]
     rng = np.random.default_rng(T)
@@ -139,6 +146,11 @@ def test_folded_routing_edge_rows(T):
         logits[1, [7, 8, 90]] = [0.5, np.nan, 0.5]
         logits[2, :] = 1.0                                             # all equal
         logits[3, 10:20] = np.nan
+    if T > 4:
+        logits[5, :] = 0.0                                             # all zero (+0 and -0)
+        logits[5, 1::2] = -0.0
+        logits[9, [3, 4]] = np.inf                                     # two +inf
+        logits[T - 1] = logits[0]                                      # the first row again
     x = synth.activations(T, H, 93, T)
     layer = resident_layer(experts, k=k, T=T)
     say(f"folded routing, edge rows, T={T}")
@@ -156,6 +168,44 @@ def test_folded_routing_edge_rows(T):
     err = oracle.moe.relative_error(out_f32(layer, T), ref["out"])
     say(f"    rel err {err:.3e}")
     assert err <= TOL
+
+
+def test_layer_replays_over_a_dirty_workspace():
+    """A moe_layer call reads no workspace byte it has not written itself:
+    graph replays of one call, with the whole workspace overwritten by
+    garbage between them, and eager calls after that give the first call's
+    output bit for bit (the sums run in a fixed order, so the result is
+    deterministic)."""
+    fmt, E, k, H, I, T = "nvfp4", 128, 8, 256, 256, 16
+    experts = [synth.expert(fmt, H, I, config=95, expert_id=e) for e in range(E)]
+    sh = synth.expert(fmt, H, I, config=95, expert_id=synth.SHARED_EXPERT)
+    x = synth.activations(T, H, 95, T, E)
+    logits = np.random.default_rng(95).standard_normal((T, E)).astype(np.float32)
+    layer = resident_layer(experts, k=k, T=T, shared=sh)
+    xs, lg = _x(x), torch.from_numpy(logits).to(DEV)
+    say("moe_layer: graph replays over a dirty workspace")
+    layer.forward(xs, logits=lg)
+    torch.cuda.synchronize()
+    _full_check(layer, x, experts, k, logits, shared=sh)
+    st = layer.state
+    first = st.out[:T].clone()
+    la = st.layer_args(T, xs, lg)
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        st.call(T, xs, logits=lg, la=la)
+    torch.cuda.synchronize()
+    for i, junk in enumerate((0xFF, 0x5A, 0x01)):
+        st._ws.fill_(junk)
+        st.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out[:T], first), f"replay {i}"
+    st._ws.fill_(0x7F)
+    layer.forward(xs, logits=lg)
+    torch.cuda.synchronize()
+    assert torch.equal(st.out[:T], first)
 
 
 def test_zero_tokens_is_a_no_op():
