@@ -31,88 +31,71 @@ __device__ __forceinline__ float unnorm(float v, float m) {
   return expf(v - m);
 }
 
-// Rank of this lane among the set lanes of a wave-uniform mask m below it.
-__device__ __forceinline__ int lanes_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 // Lane l holds experts l + 64 i (i < NPER, NPER * 64 >= E), each as a 32-bit
-// rank key (0: no expert).  Selection:
-//  1. the k-th largest key value thr, counted with multiplicity, by a binary
-//     radix walk from the top bit: at bit b the keys that match the bits
-//     above b chosen so far and have bit b set are counted with ballots; if
-//     they are at least the number still needed, bit b of thr is set, else
-//     they are all selected and taken off the count;
-//  2. every key above thr is selected, and of the keys equal to thr the ones
-//     with the lowest expert ids, as many as are still needed;
-//  3. a selected key's output position is the number of selected keys that
-//     rank above it (larger key, or equal key and lower id), found by one
-//     pass over the selected keys with readlane.
-// All counts are ballots and scalar arithmetic: no cross-lane reduction
-// sits on the critical path except the softmax denominator.
+// rank key (0: no expert).  Selection in k rounds: round r takes the largest
+// remaining key (a wave-wide maximum: DPP row steps, then the cross-row
+// permlane swaps) and, of the keys equal to it, the one with the lowest
+// expert id (the lowest slot i holding one, then the lowest lane); that key
+// is output position r and leaves the remaining set.  The k keys are thus
+// the k largest in the order (key descending, id ascending), in that order.
+// Then the softmax over them (renormalised) or over all E.
 // Writes ids[pos], w[pos] for pos in [0, k) (global or LDS pointers).
+//
+// The logits of one row as the selection holds them: lane l, experts
+// l + 64 i (0 past E).  Separate from the selection so that a wave can load
+// several rows before it selects in any of them.
 template <int NPER>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm, int32_t* ids,
-                                          float* wout) {
+__device__ __forceinline__ void wave_topk_load(const float* __restrict__ row, int E, float (&val)[NPER]) {
   const int lane = threadIdx.x & 63;
-  uint32_t rk[NPER];
-  float val[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
-    val[i] = 0.f;
-    rk[i] = 0u;
-    if (e < E) {
-      val[i] = row[e];
-      rk[i] = rank_bits(val[i]) + 1u;  // 0 marks "no key"; NaN -> 1, below every number
-    }
+    val[i] = e < E ? row[e] : 0.f;
   }
-  // 1. threshold (wave-uniform)
-  uint32_t thr = 0u;
-  int need = k;
-#pragma unroll 4
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = thr | (1u << b);
-    const uint32_t hi = ~0u << b;
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) cnt += (int)__popcll(__ballot((rk[i] & hi) == cand));
-    if (cnt >= need) thr = cand;
-    else need -= cnt;
-  }
-  // 2. selection: `need` keys equal to thr remain to be taken, lowest ids first
+}
+
+template <int NPER>
+__device__ __forceinline__ void wave_topk_select(const float (&val)[NPER], int E, int k, int renorm, int32_t* ids,
+                                                 float* wout) {
+  const int lane = threadIdx.x & 63;
+  uint32_t rk[NPER];  // remaining keys (0: none, or taken)
   bool sel[NPER];
-  uint64_t selm[NPER];
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const bool eq = rk[i] == thr && rk[i] != 0u;
-    const uint64_t eqm = __ballot(eq);
-    sel[i] = (rk[i] > thr) || (eq && lanes_below(eqm) < need);
-    selm[i] = __ballot(sel[i]);
-    need = max(0, need - (int)__popcll(eqm));  // __popcll is unsigned: keep the difference signed
-  }
-  // 3. output positions
   int pos[NPER];
 #pragma unroll
-  for (int i = 0; i < NPER; ++i) pos[i] = 0;
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    uint64_t m = selm[j];
-    while (m) {
-      const int src = __builtin_ctzll(m);
-      m &= m - 1;
-      const uint32_t ks = (uint32_t)__builtin_amdgcn_readlane((int)rk[j], src);
-      const int id = 64 * j + src;
-#pragma unroll
-      for (int i = 0; i < NPER; ++i) pos[i] += (ks > rk[i] || (ks == rk[i] && id < lane + 64 * i)) ? 1 : 0;
-    }
-  }
-  // the top logit m (position 0), from the lane that holds it, and the softmax weights
-  float top = 0.f;
-#pragma unroll
   for (int i = 0; i < NPER; ++i) {
-    const uint64_t b = __ballot(sel[i] && pos[i] == 0);
-    if (b) top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[i]), __builtin_ctzll(b)));
+    rk[i] = lane + 64 * i < E ? rank_bits(val[i]) + 1u : 0u;  // NaN -> 1, below every number
+    sel[i] = false;
+    pos[i] = 0;
+  }
+  float top = 0.f;  // the logit at position 0
+  for (int r = 0; r < k; ++r) {
+    uint32_t lm = rk[0];
+#pragma unroll
+    for (int i = 1; i < NPER; ++i) lm = max(lm, rk[i]);
+    const uint32_t m = wave_max_u32(lm);
+    if (m == 0u) break;  // fewer than k keys (not reached: k <= E)
+    int ws = NPER, wl = 0;  // slot and lane of the key taken
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      if (ws == NPER) {
+        const uint64_t b = __ballot(rk[i] == m);
+        if (b) {
+          ws = i;
+          wl = __builtin_ctzll(b);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      if (i == ws) {
+        if (r == 0) top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[i]), wl));
+        if (lane == wl) {
+          sel[i] = true;
+          pos[i] = r;
+          rk[i] = 0u;
+        }
+      }
+    }
   }
   float part = 0.f;
 #pragma unroll
@@ -121,11 +104,19 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, 
   const float den = wave_sum(part);
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
-    if (sel[i] && pos[i] < k) {  // exactly k keys are selected; the bound keeps every store in the row
+    if (sel[i]) {
       ids[pos[i]] = lane + 64 * i;
       wout[pos[i]] = den > 0.f ? unnorm(val[i], top) / den : 1.0f / (float)k;
     }
   }
+}
+
+template <int NPER>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ row, int E, int k, int renorm, int32_t* ids,
+                                          float* wout) {
+  float val[NPER];
+  wave_topk_load<NPER>(row, E, val);
+  wave_topk_select<NPER>(val, E, k, renorm, ids, wout);
 }
 
 }  // namespace moe
