@@ -332,7 +332,9 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
     }
   };
 
-  // Epilogue of tile q (reads the accumulators).
+  // Epilogue of tile q (reads the accumulators); a tile of at most 64 rows
+  // (full false) skips row blocks 4-7.
+  bool full = true;
   auto epilogue = [&](int q) __attribute__((always_inline)) {
     const TileDesc d = uniform_desc(q);
     const int t16 = lane & 15, g = lane >> 4;
@@ -344,6 +346,7 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
         uint8_t* ws = g_stg + wave * 4096;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+        if (i >= 4 && !full) break;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
@@ -364,6 +367,7 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
     } else if constexpr (MODE == kG_DownF32) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        if (i >= 4 && !full) break;
         const int m = 16 * i + t16;
         if (m < d.rows) {
           const size_t o = (size_t)(d.row0 + m) * P.H + d.nt * kGBN + 128 * wave + 4 * g;
@@ -380,6 +384,7 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
       const int cb = d.nt * 256 + 64 * wave;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        if (i >= 4 && !full) break;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           uint32_t w2[2];
@@ -412,6 +417,7 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
       const int kt = wave >> 1, half = wave & 1;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
+        if (i >= 4 && !full) break;
         const int m = 16 * i + t16;
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
@@ -537,7 +543,11 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
   // live, and the next tile's first fragments are read after it.
   const std::true_type yes;
   const std::false_type no;
+  // A tile of at most 64 rows skips the epilogue work of its empty row
+  // blocks 4-7.  (Its matrix instructions for them still run: a branch
+  // around them splits the accumulator updates, and the kernel then spills.)
   for (int q = 0; q < ntile; ++q) {
+    full = __builtin_amdgcn_readfirstlane(desc[q].rows) > 64;
     step(yes, yes, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
     for (int ks = 1; ks < nsteps - 1; ks += 2) {
       step(no, yes, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
