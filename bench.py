@@ -411,6 +411,8 @@ def main():
     ap.add_argument("--policy", default="offload", choices=["offload", "hybrid", "cpu"],
                     help="stream: miss policy (offload: copy every miss; hybrid: the calibrated share copied, "
                          "the rest on the host; cpu: every miss on the host)")
+    ap.add_argument("--copy-engine", action="store_true",
+                    help="stream: fill misses through the copy engine instead of the fill kernel")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="first run three plain device copies of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
@@ -638,6 +640,7 @@ def bench_stream(args):
         f"copy share {cal.copy_ratio:.3f}; policy {args.policy}")
     dec = CachedDecoder(num_layers=LAYERS, num_experts=E, k=k, H=H, I=I, fmt=FMT, num_slots=SLOTS,
                         host_blob=lambda l, e: blob_view(l * E + e), device=dev, copy_ratio=ratio,
+                        copy_engine=args.copy_engine,
                         host_threads=host_threads)
     sh = torch.cuda.current_stream().cuda_stream
 
@@ -751,10 +754,14 @@ def bench_stream(args):
                    "layers": LAYERS, "slots": SLOTS, "tokens": TOKENS, "parallelism": "single GPU"},
         "roofline": {"bound": "h2d", "achieved": round(h2d, 2), "peak": round(h2d_peak, 2), "unit": "GB/s",
                      "frac": round(h2d / h2d_peak, 4), "traffic": None,
-                     "kernel": "hipMemcpyAsync pinned host -> HBM slot (miss fills)",
+                     "kernel": ("hipMemcpyAsync pinned host -> HBM slot on the copy stream (miss fills)"
+                                if args.copy_engine else
+                                "k_fill_slots: the step's miss blobs read from pinned host memory into their "
+                                "slots on the compute stream"),
                      "peak_source": f"measured: one {n_cp}-slot pinned copy on the copy stream"},
         "trace": trace,
         "policy": {"name": args.policy, "copy_ratio": ratio, "host_threads": host_threads,
+                   "fill": "copy engine" if args.copy_engine else "fill kernel on the compute stream",
                    "host_run_experts": int(dec.hybrid.cpu_experts) if dec.hybrid is not None else 0,
                    "calibration": {"copy_us_per_expert": round(cal.copy_us, 2), "h2d_GBps": round(cal.h2d_gbs, 2),
                                    "host_ffn_us_per_expert": round(cal.cpu_us, 2),

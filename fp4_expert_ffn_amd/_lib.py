@@ -109,6 +109,7 @@ SIGNATURES = {
     "cache_fill": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp]),
     "moe_cache_mark_used": (_i, [_vp, _vp, _i, _vp]),
     "moe_cache_reset": (_i, [_vp]),
+    "moe_cache_use_copy_engine": (_i, [_vp, _i]),
     "moe_cache_pin_resident": (_i, [_vp, _i, _i]),
     "moe_cache_stats": (_i, [_vp, _vp, _vp, _vp]),
     "moe_cache_map_bytes": (_sz, [_i]),
@@ -349,6 +350,10 @@ def moe_cache_mark_used(cache: Cache, slots, stream=None):
 
 def moe_cache_reset(cache: Cache):
     _check(lib().moe_cache_reset(cache.handle), "moe_cache_reset")
+
+
+def moe_cache_use_copy_engine(cache: Cache, on: bool):
+    _check(lib().moe_cache_use_copy_engine(cache.handle, 1 if on else 0), "moe_cache_use_copy_engine")
 
 
 def moe_cache_pin_resident(cache: Cache, layer, s0):

@@ -22,10 +22,19 @@
 //    reads the slot makes the compute stream wait for it (pending flag).
 //  - a resize copies kept blobs after every fill enqueued so far, through a
 //    tail event per copy stream recorded after its last fill.
+//  - a decode step on the decode GEMV may copy its misses with a fill kernel
+//    on the compute stream instead (pinned blobs read by the shader over
+//    PCIe): its miss FFN then follows the fills in stream order, and its hit
+//    FFN runs meanwhile on a side stream whose completion the compute stream
+//    waits for before the combine.  Such a step starts after the host has
+//    seen its counts, which the compute stream published after every earlier
+//    step's combine, so no earlier reader or fill of any slot is still
+//    running when it enqueues.
 #include <string.h>
 
 #include <algorithm>
 #include <set>
+#include <unordered_map>
 #include <utility>
 #include <vector>
 
@@ -37,6 +46,9 @@ hipError_t launch_move_slots(const int32_t* src_slots, int n, int dst0, const vo
 hipError_t launch_publish_counts(const int32_t* counts, int E, int32_t* host_counts_dev, uint32_t* flag_dev,
                                  uint32_t seq, hipStream_t s);
 hipError_t launch_write_map(const StepMap& m, int E, void* dev_map, hipStream_t s);
+hipError_t launch_fill_slots(const FillList& f, const StepMap& m, int E, void* dev_map, void* pool, size_t slot_bytes,
+                             hipStream_t s);
+bool ffn_takes_gemv(const moe_ffn_args* a);
 }
 
 struct moe_cache {
@@ -76,7 +88,16 @@ struct moe_cache {
   uint32_t* flag_host = nullptr;
   uint32_t* flag_dev = nullptr;
   uint32_t seq = 0;
-  std::vector<std::pair<const void*, void*>> mapped;
+  std::unordered_map<const void*, void*> mapped;  // host address -> device address (null: not mapped)
+  // decode steps whose misses a kernel copies on the compute stream: the
+  // hits run meanwhile on a side stream with their own slot map, and
+  // hit_done joins them back before the combine (copy_engine: 1 forces the
+  // copy-engine fills instead)
+  int copy_engine = 0;
+  hipStream_t side = nullptr;
+  hipEvent_t hit_done = nullptr;
+  void* side_map = nullptr;
+  size_t side_map_bytes = 0;
 
   void unlink(int32_t k) {
     int32_t p = prev[k], n = next[k];
@@ -138,6 +159,9 @@ extern "C" void moe_cache_destroy(moe_cache* c) {
   for (auto& m : c->map_upload) (void)hipEventDestroy(m.second);
   if (c->resized) (void)hipEventDestroy(c->resized);
   if (c->flag_host) (void)hipHostFree(c->flag_host);
+  if (c->hit_done) (void)hipEventDestroy(c->hit_done);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->side_map) (void)hipFree(c->side_map);
   delete c;
 }
 
@@ -351,6 +375,12 @@ extern "C" moe_status cache_fill(moe_cache* c, int layer, int expert, int slot, 
   return wait_fill(c, slot, ks);
 }
 
+extern "C" moe_status moe_cache_use_copy_engine(moe_cache* c, int on) {
+  MOE_CHECK_ARG(c, "moe_cache_use_copy_engine: null cache");
+  c->copy_engine = on ? 1 : 0;
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_cache_mark_used(moe_cache* c, const int32_t* slots, int n, moe_stream_t compute_stream) {
   MOE_CHECK_ARG(c && (n == 0 || slots), "moe_cache_mark_used: null pointer");
   for (int i = 0; i < n; ++i)
@@ -426,15 +456,15 @@ static void copy_trace(const moe_cache* c, int n, int32_t* te, int32_t* ts, uint
 
 // The device address of pinned host memory (null if it is not mapped for
 // the device; the failed query's error is cleared).
-static void* mapped_device_ptr(moe_cache* c, void* host) {
-  for (auto& m : c->mapped)
-    if (m.first == host) return m.second;
+static void* mapped_device_ptr(moe_cache* c, const void* host) {
+  const auto it = c->mapped.find(host);
+  if (it != c->mapped.end()) return it->second;
   void* d = nullptr;
-  if (hipHostGetDevicePointer(&d, host, 0) != hipSuccess) {
+  if (hipHostGetDevicePointer(&d, const_cast<void*>(host), 0) != hipSuccess) {
     (void)hipGetLastError();
     d = nullptr;
   }
-  c->mapped.emplace_back(host, d);
+  c->mapped.emplace(host, d);
   return d;
 }
 
@@ -480,21 +510,70 @@ static moe_status wait_flag(moe_cache* c, uint32_t seq, hipStream_t ks, const ch
 // The step's map (the lookups in step_ids / step_slot / step_hit) into
 // dev_map on ks: by a kernel that takes it by value, or for steps with more
 // than kStepMapMax experts through host_map.
+static void step_map(const moe_cache* c, int n, moe::StepMap* m) {
+  m->n = n;
+  for (int i = 0; i < n; ++i) {
+    m->expert[i] = c->step_ids[i];
+    m->slot[i] = c->step_slot[i];
+    m->hit[i] = c->step_hit[i];
+  }
+}
 static moe_status write_map(moe_cache* c, void* host_map, void* dev_map, int E, int n, hipStream_t ks) {
   if (n > moe::kStepMapMax) return upload_map(c, host_map, dev_map, E, n, ks);
   moe::StepMap m;
-  m.n = n;
-  for (int i = 0; i < n; ++i) {
-    m.expert[i] = c->step_ids[i];
-    m.slot[i] = c->step_slot[i];
-    m.hit[i] = c->step_hit[i];
-  }
+  step_map(c, n, &m);
   const hipError_t e = moe::launch_write_map(m, E, dev_map, ks);
   if (e != hipSuccess) return moe::set_error(MOE_EHIP, "slot map launch failed: %s", hipGetErrorString(e));
   return MOE_OK;
 }
 
+// The step's miss fills as one fill kernel's list; false when they go
+// through the copy engine instead: the FFN is off the GEMV path (the hit and
+// miss launches would share workspace, so they cannot run at once), too many
+// experts or misses for the kernel arguments, or a blob that is not mapped
+// pinned memory on a 16-byte boundary.
+static bool kernel_fill_list(moe_cache* c, const moe_ffn_args& f, const void* const* host_blobs, int n, int nm,
+                             moe::FillList* fl) {
+  if (c->copy_engine || nm == 0 || nm > moe::kFillMax || n > moe::kStepMapMax || !moe::ffn_takes_gemv(&f) ||
+      c->slot_bytes / 16 >= (1ull << 31))
+    return false;
+  fl->n = 0;
+  for (int i = 0; i < n; ++i) {
+    if (c->step_hit[i]) continue;
+    const void* d = mapped_device_ptr(c, host_blobs[c->step_ids[i]]);
+    if (!d || ((uintptr_t)d & 15)) return false;
+    fl->slot[fl->n] = c->step_slot[i];
+    fl->src[fl->n] = static_cast<const uint8_t*>(d);
+    ++fl->n;
+  }
+  return true;
+}
+
+// The side stream of the hit FFN, its join event and its slot map (created
+// on first use, kept until the cache is destroyed).
+static moe_status ensure_side(moe_cache* c) {
+  if (!c->side) MOE_HIP(hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking));
+  if (!c->hit_done) MOE_HIP(hipEventCreateWithFlags(&c->hit_done, hipEventDisableTiming));
+  if (!c->side_map) {
+    const size_t mb = moe_cache_map_bytes(c->num_experts);
+    MOE_HIP(hipMalloc(&c->side_map, mb));
+    c->side_map_bytes = mb;
+  }
+  return MOE_OK;
+}
+
 // ------------------------------------------------------------ one decode step
+
+// A step that returns early after enqueueing its hits on the side stream
+// waits for them on the host, so that no later fill overwrites a slot they
+// still read (the compute stream never joined them).
+struct SideJoin {
+  moe_cache* c;
+  bool pending;
+  ~SideJoin() {
+    if (pending && c->side) (void)hipStreamSynchronize(c->side);
+  }
+};
 
 // One decode step; hy null: every miss copied into the cache.
 static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, moe_stream_t copy_stream,
@@ -577,32 +656,84 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
   st = cache_lookup(c, s->layer, c->step_ids.data(), n, c->step_slot.data(), c->step_hit.data(), c->step_ev.data());
   if (st != MOE_OK) return st;
 
-  // 4. miss fills on the copy stream
+  // 4-6. miss fills, the slot map and the hit FFN.  With a fill kernel the
+  // misses are copied on the compute stream (their FFN follows in stream
+  // order) and the hits run meanwhile on the side stream; otherwise the copy
+  // engine fills them on the copy stream and the hits run first on the
+  // compute stream.
   int nm = 0;
-  st = fill_misses(c, s->layer, n, s->host_blobs, cs, &nm);
-  if (st != MOE_OK) return st;
+  for (int i = 0; i < n; ++i) nm += !c->step_hit[i];
   const int nh = n - nm;
-
-  // 5. slot map and masks
-  st = write_map(c, s->host_map, s->dev_map, E, n, ks);
-  if (st != MOE_OK) return st;
+  moe::FillList fl;
+  const bool kfill = kernel_fill_list(c, f, s->host_blobs, n, nm, &fl);
   const int32_t* dmap = static_cast<const int32_t*>(s->dev_map);
   const uint8_t* dhm = reinterpret_cast<const uint8_t*>(dmap + E);
   const uint8_t* dmm = dhm + E;
-
-  // 6. hits now (after any fill of theirs still pending)
   moe_ffn_args a = f;
   a.slot_of_expert = dmap;
   a.slot_pool = c->pool;
   a.slot_stride = c->slot_bytes;
   a.out = nullptr;
-  if (nh > 0 || (nm == 0 && f.shared_blob)) {
-    for (int i = 0; i < n; ++i)
-      if (c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], ks)) != MOE_OK) return st;
-    a.expert_mask = dhm;
-    st = moe_expert_ffn(&a, compute_stream);
+  SideJoin join{c, false};
+  if (kfill) {
+    // The fills first (the step's critical path).  Every earlier reader and
+    // kernel fill of the slots is behind the host already: this step's counts
+    // were published after them on the compute stream, and an earlier step's
+    // hits joined it before that step's combine.  A copy-engine fill of a
+    // slot that no step has waited for yet is waited for (write after
+    // write).  A failure before the fill launch drops the misses.
+    moe::StepMap m;
+    step_map(c, n, &m);
+    for (int i = 0; i < n && st == MOE_OK; ++i)
+      if (!c->step_hit[i]) {
+        st = wait_readers(c, c->step_slot[i], ks);
+        if (st == MOE_OK) st = wait_fill(c, c->step_slot[i], ks);
+      }
+    if (st == MOE_OK && c->has_resized) {
+      const hipError_t e = hipStreamWaitEvent(ks, c->resized, 0);
+      if (e != hipSuccess) st = moe::set_error(MOE_EHIP, "%s: %s", who, hipGetErrorString(e));
+    }
+    if (st == MOE_OK) {
+      const hipError_t e = moe::launch_fill_slots(fl, m, E, s->dev_map, c->pool, c->slot_bytes, ks);
+      if (e != hipSuccess) st = moe::set_error(MOE_EHIP, "%s: fill launch failed: %s", who, hipGetErrorString(e));
+    }
+    if (st != MOE_OK) {
+      drop_unfilled(c, s->layer, 0, n);
+      return st;
+    }
+    c->bytes_filled += (long long)nm * (long long)c->slot_bytes;
+    // the hits on the side stream, with their own copy of the map
+    if (nh > 0) {
+      join.pending = true;
+      st = ensure_side(c);
+      if (st != MOE_OK) return st;
+      const hipError_t e = moe::launch_write_map(m, E, c->side_map, c->side);
+      if (e != hipSuccess) return moe::set_error(MOE_EHIP, "%s: slot map launch failed: %s", who, hipGetErrorString(e));
+      for (int i = 0; i < n; ++i)
+        if (c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], c->side)) != MOE_OK) return st;
+      moe_ffn_args ah = a;
+      ah.slot_of_expert = static_cast<const int32_t*>(c->side_map);
+      ah.expert_mask = static_cast<const uint8_t*>(c->side_map) + 4 * (size_t)E;
+      st = moe_expert_ffn(&ah, reinterpret_cast<moe_stream_t>(c->side));
+      if (st != MOE_OK) return st;
+      a.shared_blob = nullptr;  // computed once
+      MOE_HIP(hipEventRecord(c->hit_done, c->side));
+    }
+  } else {
+    int nq = 0;
+    st = fill_misses(c, s->layer, n, s->host_blobs, cs, &nq);
     if (st != MOE_OK) return st;
-    a.shared_blob = nullptr;  // computed once
+    st = write_map(c, s->host_map, s->dev_map, E, n, ks);
+    if (st != MOE_OK) return st;
+    // hits now (after any fill of theirs still pending)
+    if (nh > 0 || (nm == 0 && f.shared_blob)) {
+      for (int i = 0; i < n; ++i)
+        if (c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], ks)) != MOE_OK) return st;
+      a.expert_mask = dhm;
+      st = moe_expert_ffn(&a, compute_stream);
+      if (st != MOE_OK) return st;
+      a.shared_blob = nullptr;  // computed once
+    }
   }
   // 6b. host-run misses while the GPU works: their rows' outputs into host_y
   // (perm order), then into y
@@ -624,13 +755,17 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
     MOE_HIP(hipEventRecord(up, ks));
     hy->cpu_experts += (long long)host_run.size();
   }
-  // 6c. copied misses after their fills
+  // 6c. copied misses after their fills (a fill kernel's are in stream order)
   if (nm > 0) {
     for (int i = 0; i < n; ++i)
       if (!c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], ks)) != MOE_OK) return st;
     a.expert_mask = dmm;
     st = moe_expert_ffn(&a, compute_stream);
     if (st != MOE_OK) return st;
+  }
+  if (join.pending) {
+    MOE_HIP(hipStreamWaitEvent(ks, c->hit_done, 0));
+    join.pending = false;
   }
 
   // 7. combine, then the slots' readers (one marking for the step)
@@ -781,9 +916,12 @@ extern "C" moe_status moe_cache_resize(moe_cache* c, int num_slots, void* slot_p
   std::vector<int32_t> keys;
   for (int32_t k = c->head; k >= 0; k = c->next[k]) keys.push_back(k);
   const int nkeep = std::min<int>((int)keys.size(), num_slots), ndrop = (int)keys.size() - nkeep;
-  // the copies start after every fill enqueued so far (one wait per copy stream)
+  // the copies start after every fill enqueued so far: one wait per copy
+  // stream, and one on the last marking of readers, which followed every
+  // fill kernel and side-stream hit FFN of the decode steps
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   for (auto& t : c->fill_tail) MOE_HIP(hipStreamWaitEvent(hs, t.second, 0));
+  if (c->gen > 0) MOE_HIP(hipStreamWaitEvent(hs, c->ring[(c->gen - 1) % moe_cache::kRing], 0));
   std::vector<int32_t> src(nkeep);
   for (int i = 0; i < nkeep; ++i) src[i] = c->key_slot[keys[ndrop + i]];
   const hipError_t e = moe::launch_move_slots(src.data(), nkeep, 0, c->pool, slot_pool, c->slot_bytes, hs);

@@ -77,7 +77,8 @@ hipError_t launch_publish_counts(const int32_t* counts, int E, int32_t* host_cou
 
 // The step's slot map, passed by value: map layout int32 slot[E], uint8
 // hit[E], uint8 miss[E]; experts outside the step get slot 0 and no mask.
-__global__ __launch_bounds__(256) void k_write_map(StepMap m, int E, uint8_t* __restrict__ map) {
+// One workgroup of 256 threads.
+__device__ __forceinline__ void write_step_map(const StepMap& m, int E, uint8_t* __restrict__ map) {
   int32_t* slot = reinterpret_cast<int32_t*>(map);
   uint8_t* hit = map + 4 * E;
   uint8_t* miss = hit + E;
@@ -94,8 +95,49 @@ __global__ __launch_bounds__(256) void k_write_map(StepMap m, int E, uint8_t* __
   }
 }
 
+__global__ __launch_bounds__(256) void k_write_map(StepMap m, int E, uint8_t* __restrict__ map) {
+  write_step_map(m, E, map);
+}
+
 hipError_t launch_write_map(const StepMap& m, int E, void* dev_map, hipStream_t s) {
   launch(k_write_map, dim3(1), dim3(256), 0, s, m, E, static_cast<uint8_t*>(dev_map));
+  return hipGetLastError();
+}
+
+// Miss fills of a decode step read straight from pinned host memory (PCIe
+// reads issued by the shader, no copy engine), so the step's miss FFN follows
+// them on the same stream with no cross-queue handoff.  Blob blockIdx.y of
+// the list (slot_vecs 16-byte vectors) goes to its slot; the x blocks below
+// kFillBlocks stride over its vectors with four loads in flight per thread,
+// and block kFillBlocks of row 0 writes the step's map.  PCIe-bound: the
+// link's read rate is the ceiling, which kFillBlocks workgroups per blob
+// reach.
+constexpr int kFillBlocks = 64;
+__global__ __launch_bounds__(256) void k_fill_slots(FillList f, StepMap m, int E, uint8_t* __restrict__ map,
+                                                    uint4* __restrict__ pool, uint32_t slot_vecs) {
+  if (blockIdx.x == kFillBlocks) {
+    if (blockIdx.y == 0) write_step_map(m, E, map);
+    return;
+  }
+  const uint4* src = reinterpret_cast<const uint4*>(f.src[blockIdx.y]);
+  uint4* dst = pool + (size_t)f.slot[blockIdx.y] * slot_vecs;
+  constexpr uint32_t step = kFillBlocks * 256u;
+  for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < slot_vecs; v += 4 * step) {
+    uint4 r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (v + j * step < slot_vecs) r[j] = src[v + j * step];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (v + j * step < slot_vecs) dst[v + j * step] = r[j];
+  }
+}
+
+// f.n in [1, kFillMax]; slot_bytes a multiple of 16, below 2^35.
+hipError_t launch_fill_slots(const FillList& f, const StepMap& m, int E, void* dev_map, void* pool, size_t slot_bytes,
+                             hipStream_t s) {
+  launch(k_fill_slots, dim3(kFillBlocks + 1, f.n), dim3(256), 0, s, f, m, E, static_cast<uint8_t*>(dev_map),
+         static_cast<uint4*>(pool), (uint32_t)(slot_bytes / 16));
   return hipGetLastError();
 }
 

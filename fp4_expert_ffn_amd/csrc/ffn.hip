@@ -13,6 +13,7 @@
 namespace moe {
 hipError_t launch_gemv(const FfnParams& P, const GemvArgs& G, hipStream_t s);
 bool gemv_route_fits(const FfnParams& P);
+bool ffn_takes_gemv(const moe_ffn_args* a);
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s);
 hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st);
 hipError_t launch_fp4_codes_canon(const FfnParams& P, const MfmaBufs& B, int which, uint8_t* q, uint8_t* s,
@@ -237,6 +238,11 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ blo
 }
 
 }  // namespace
+
+// Whether moe_expert_ffn runs `a` on the decode GEMV, whose launches write
+// only the h and y rows of their masked experts' permutation positions (so
+// two calls with disjoint masks may run at once on one workspace and y).
+bool moe::ffn_takes_gemv(const moe_ffn_args* a) { return choose_path(a) == kPathGemv; }
 
 extern "C" size_t moe_expert_ffn_workspace_size(const moe_ffn_args* a) {
   if (!a) return 0;

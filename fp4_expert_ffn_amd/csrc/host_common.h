@@ -105,4 +105,14 @@ struct StepMap {
   uint8_t hit[kStepMapMax];
 };
 
+// The blobs a decode step copies from pinned host memory into its miss
+// slots, passed by value beside the step's map: src[i] is the device address
+// of the host blob (16-byte aligned, slot_bytes long), slot[i] its slot.
+constexpr int kFillMax = 64;
+struct FillList {
+  int32_t n;
+  int32_t slot[kFillMax];
+  const uint8_t* src[kFillMax];
+};
+
 }  // namespace moe

@@ -141,22 +141,28 @@ class MoELayer:
 class CachedDecoder:
     """Decode through the expert-slot cache: `num_layers` layers of `num_experts`
     experts whose blobs sit in a pinned host bank, `num_slots` HBM slots shared
-    by every layer under LRU, misses copied on a side stream.
+    by every layer under LRU; misses copied from host memory by a fill kernel
+    on the compute stream while the hits run on a side stream (or by the copy
+    engine, see moe_cache_decode_step).
 
     host_blob(layer, e) -> pinned uint8 tensor holding that expert's blob.
     copy_ratio: None copies every miss into the cache; a value in [0, 1] runs
     the hybrid policy (that share of a step's misses copied, the rest run on
     the host with `host_threads` threads, not cached).
+    copy_engine: copy misses through the copy engine on the side stream even
+    where a fill kernel on the compute stream could copy them.
     """
 
     def __init__(self, *, num_layers, num_experts, k, H, I, fmt, num_slots, host_blob, max_tokens=1,
-                 device="cuda", renormalize=True, copy_ratio=None, host_threads=8):
+                 device="cuda", renormalize=True, copy_ratio=None, host_threads=8, copy_engine=False):
         self.L, self.E, self.k, self.H, self.I, self.fmt = num_layers, num_experts, k, H, I, fmt
         self.dev = torch.device(device)
         self.blob_bytes = L.moe_blob_bytes(fmt, H, I)
         self.stride = (self.blob_bytes + 255) // 256 * 256
         self.pool = torch.empty(num_slots * self.stride, dtype=torch.uint8, device=self.dev)
         self.cache = L.moe_cache_create(num_slots, self.stride, self.pool, num_layers, num_experts)
+        if copy_engine:
+            L.moe_cache_use_copy_engine(self.cache, True)
         self.copy_stream = torch.cuda.Stream(device=self.dev)
         T, E = max(max_tokens, 1), num_experts
         self.max_tokens = T

@@ -321,6 +321,11 @@ moe_status cache_fill(moe_cache* c, int layer, int expert, int slot, const void*
  * enqueued so far; a later cache_fill of one of them waits for that work. */
 moe_status moe_cache_mark_used(moe_cache* c, const int32_t* slots, int n, moe_stream_t compute_stream);
 
+/* Decode steps copy their misses through the copy engine (on != 0) even
+ * where the fill kernel of moe_cache_decode_step could (on == 0, the
+ * default).  Both orders give the same results and trace. */
+moe_status moe_cache_use_copy_engine(moe_cache* c, int on);
+
 /* Hits, misses and bytes copied by cache_fill since creation or reset (host). */
 moe_status moe_cache_stats(const moe_cache* c, long long* hits, long long* misses, long long* bytes_filled);
 
@@ -336,11 +341,19 @@ moe_status moe_cache_stats(const moe_cache* c, long long* hits, long long* misse
  *   2. a copy of counts to host_counts, and waits for it (the host must
  *      know the step's experts: this is the step's one host synchronisation);
  *   3. cache_lookup of the experts with rows, in ascending id (the trace);
- *   4. for every miss, a fill from host_blobs[expert] on copy_stream (after
- *      the slot's previous readers);
- *   5. the slot map and the hit / miss masks, host_map -> dev_map;
- *   6. the FFN over the hit experts (overlapping the fills), then a wait on
- *      each miss's fill, then the FFN over the missed experts;
+ *   4-6. the miss fills, the slot map and the two FFN calls, in one of two
+ *      orders.  Fill kernel (the FFN takes the decode GEMV, at most 64 misses
+ *      and 256 experts, every miss blob mapped pinned memory on a 16-byte
+ *      boundary, and moe_cache_use_copy_engine not set): one kernel on
+ *      compute_stream copies every miss blob from host memory into its slot
+ *      and writes dev_map, then the FFN over the missed experts follows;
+ *      meanwhile the FFN over the hit experts runs on a stream the cache
+ *      owns, with its own copy of the map, and compute_stream waits for it
+ *      before the combine.  Copy engine (otherwise): for every miss a fill
+ *      from host_blobs[expert] on copy_stream (after the slot's previous
+ *      readers), the slot map and masks host_map -> dev_map, the FFN over the
+ *      hit experts (overlapping the fills), a wait on each miss's fill, then
+ *      the FFN over the missed experts;
  *   7. moe_combine into ffn.out, and moe_cache_mark_used of the step's slots.
  * ffn.slot_of_expert, ffn.expert_mask are set by the call; ffn.y is
  * required; ffn.out, topk_w, inv receive the combine.  host_counts and

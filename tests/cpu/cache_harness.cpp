@@ -6,7 +6,10 @@
 //   cache_harness decode L E k T C steps seed [step:slots ...]   decode stream (optional resizes)
 //   cache_harness prefill L E C passes seed                      layer-ahead prefill passes
 //   cache_harness fault KIND NTH L E k T C steps seed            decode stream, the NTH call of KIND fails
-//                                                                (0 copy, 1 event create, 2 event record, 3 stream wait)
+//                                                                (0 copy, 1 event create, 2 event record, 3 stream wait,
+//                                                                4 fill-kernel launch)
+// HARNESS_COPY_ENGINE=1 in the environment: decode steps fill through the
+// copy engine (moe_cache_use_copy_engine), else through the fill kernel.
 //   cache_harness hybrid RATIO L E k T C steps seed              decode stream, hybrid miss policy
 // stdout, one line per call:
 //   D <layer> <status> e:h:s:v ...   a decode step's records
@@ -157,6 +160,8 @@ int decode(int argc, char** argv, int fail_kind, int fail_nth, float ratio = -1.
     if (sscanf(argv[i], "%d:%d", &st, &n) == 2) resize_at[st] = n;
   }
   World w(L, E, k, T, C);
+  const char* ce = getenv("HARNESS_COPY_ENGINE");
+  if (ce && atoi(ce)) moe_cache_use_copy_engine(w.c, 1);
   if (fail_kind >= 0) stub_fail(fail_kind, fail_nth);
   moe_hybrid hy{ratio, 2, w.host_x, w.host_perm, w.host_offsets, w.host_y, 0};
   std::vector<std::vector<int>> prev(L);

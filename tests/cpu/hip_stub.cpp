@@ -17,8 +17,10 @@
 // (the test writes a marker into every blob).  Failures can be injected
 // into the n-th call of a kind.
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <map>
 #include <memory>
 #include <vector>
@@ -75,9 +77,13 @@ void bad(const char* what, long long a, long long b) {
   if (g_bad++ < 10) fprintf(stderr, "bad: %s (%lld, %lld)\n", what, a, b);
 }
 int sid_of(hipStream_t s) { return s ? s->id : 0; }
+// An operation enqueued after the host has seen other work finish (a
+// synchronisation, or the count flag the stream publishes) runs after that
+// work: the stream's clock joins the host's.
 Op tick(hipStream_t s) {
   const int id = sid_of(s);
   if (g_vc[id].empty()) g_vc[id].assign(kMaxStreams, 0);
+  for (int i = 0; i < kMaxStreams; ++i) g_vc[id][i] = std::max(g_vc[id][i], g_host[i]);
   ++g_vc[id][id];
   ++g_ops;
   Op o;
@@ -115,6 +121,10 @@ uintptr_t slot_addr(uintptr_t p) {
 extern "C" {
 hipStream_t stub_stream_create() {
   static std::vector<std::unique_ptr<ihipStream_t>> streams;
+  if (g_nstreams >= kMaxStreams) {
+    fprintf(stderr, "stub: more than %d streams\n", kMaxStreams);
+    abort();
+  }
   streams.emplace_back(new ihipStream_t{g_nstreams++});
   ihipStream_t* s = streams.back().get();
   g_vc[s->id].assign(kMaxStreams, 0);
@@ -183,6 +193,20 @@ hipError_t hipStreamWaitEvent(hipStream_t s, hipEvent_t e, unsigned int) {
   for (int i = 0; i < kMaxStreams; ++i) g_vc[id][i] = std::max(g_vc[id][i], e->vc[i]);
   return hipSuccess;
 }
+hipError_t hipStreamCreateWithFlags(hipStream_t* s, unsigned int) {
+  *s = stub_stream_create();
+  return hipSuccess;
+}
+hipError_t hipStreamDestroy(hipStream_t) { return hipSuccess; }
+// device memory the library allocates itself (registered as device memory)
+hipError_t hipMalloc(void** p, size_t n) {
+  static std::vector<std::unique_ptr<std::vector<uint8_t>>> bufs;
+  bufs.emplace_back(new std::vector<uint8_t>(n + 256));
+  *p = (void*)(((uintptr_t)bufs.back()->data() + 255) & ~(uintptr_t)255);
+  g_regions.push_back({(uintptr_t)*p, n, 1});
+  return hipSuccess;
+}
+hipError_t hipFree(void*) { return hipSuccess; }
 hipError_t hipGetLastError() { return hipSuccess; }
 hipError_t hipStreamQuery(hipStream_t) { return hipSuccess; }
 hipError_t hipHostMalloc(void** p, size_t n, unsigned int) {
@@ -306,6 +330,38 @@ hipError_t launch_write_map(const StepMap& m, int E, void* dev_map, hipStream_t 
   }
   return hipSuccess;
 }
+// the fill kernel: writes the map like launch_write_map, then copies each
+// listed host blob (host memory, slot_bytes long) into its slot (kind 4 fails)
+hipError_t launch_fill_slots(const FillList& f, const StepMap& m, int E, void* dev_map, void* pool, size_t slot_bytes,
+                             hipStream_t s) {
+  if (inject(4)) return hipErrorLaunchFailure;
+  const Op o = tick(s);
+  if (!region_of((uintptr_t)dev_map, 6 * (size_t)E)) bad("slot map outside the registered memory", E, 0);
+  int32_t* slot = static_cast<int32_t*>(dev_map);
+  uint8_t* hit = static_cast<uint8_t*>(dev_map) + 4 * E;
+  memset(dev_map, 0, 6 * (size_t)E);
+  for (int i = 0; i < m.n; ++i) {
+    slot[m.expert[i]] = m.slot[i];
+    (m.hit[i] ? hit : hit + E)[m.expert[i]] = 1;
+  }
+  if (f.n < 1 || f.n > kFillMax) bad("fill list size", f.n, 0);
+  for (int i = 0; i < f.n; ++i) {
+    const uintptr_t to = (uintptr_t)pool + (uintptr_t)f.slot[i] * slot_bytes;
+    const Region* rs = region_of((uintptr_t)f.src[i], slot_bytes);
+    if (!rs || rs->device == 1 || ((uintptr_t)f.src[i] & 15)) {
+      bad("fill source not in host memory", f.slot[i], 0);
+      continue;
+    }
+    if (slot_addr(to) != to || slot_bytes != g_slot_bytes || (uintptr_t)pool != g_pool) {
+      bad("fill destination not a slot of the pool", f.slot[i], 0);
+      continue;
+    }
+    slot_write(to, o);
+    memcpy(reinterpret_cast<void*>(to), f.src[i], slot_bytes);
+  }
+  return hipSuccess;
+}
+bool ffn_takes_gemv(const moe_ffn_args* a) { return (long long)a->T * a->k < 512 && a->amode != MOE_ACT_MXFP4; }
 hipError_t launch_move_slots(const int32_t* src_slots, int n, int dst0, const void* src_pool, void* dst_pool,
                              size_t slot_bytes, hipStream_t s) {
   const Op o = tick(s);

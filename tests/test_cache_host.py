@@ -41,8 +41,9 @@ def harness(tmp_path_factory):
     return exe
 
 
-def run(exe, *args):
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1", UBSAN_OPTIONS="halt_on_error=1")
+def run(exe, *args, copy_engine=False):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=1", UBSAN_OPTIONS="halt_on_error=1",
+               HARNESS_COPY_ENGINE="1" if copy_engine else "0")
     r = subprocess.run([exe, *map(str, args)], capture_output=True, text=True, env=env, timeout=120)
     assert r.returncode == 0, r.stderr[-3000:]
     lines = r.stdout.split("\n")
@@ -61,8 +62,12 @@ def _ev(v, E):
     (2, 128, 8, 16, 80, 200, 3, []),       # 16-token steps, up to ~60 experts a step
     (3, 16, 4, 2, 10, 300, 4, ["100:8", "200:14"]),  # shrink, then grow
 ])
-def test_decode_stream_protocol_and_trace(harness, L, E, k, T, C, steps, seed, resizes):
-    out = run(harness, "decode", L, E, k, T, C, steps, seed, *resizes)
+@pytest.mark.parametrize("copy_engine", [False, True])
+def test_decode_stream_protocol_and_trace(harness, L, E, k, T, C, steps, seed, resizes, copy_engine):
+    """Decode streams, misses filled by the fill kernel on the compute stream
+    (hits on the side stream) or by the copy engine: the lookups equal the
+    oracle LRU's and the stand-in sees no ordering hazard."""
+    out = run(harness, "decode", L, E, k, T, C, steps, seed, *resizes, copy_engine=copy_engine)
     lru = SlotLRU(C)
     n = 0
     for ln in out:
@@ -102,20 +107,24 @@ def test_layer_ahead_prefill_protocol_and_trace(harness, L, E, passes, seed):
             assert all(r[0] == 1 for r in recs)
 
 
-@pytest.mark.parametrize("kind", [0, 1, 2, 3])
+@pytest.mark.parametrize("copy_engine,kind", [(True, 0), (True, 1), (True, 2), (True, 3),
+                                              (False, 1), (False, 2), (False, 3), (False, 4)])
 @pytest.mark.parametrize("nth", [1, 2, 5, 9])
-def test_injected_failures_leave_a_consistent_cache(harness, kind, nth):
-    """The n-th copy (0), event creation (1), event record (2) or stream wait
-    (3) fails: that step returns MOE_EHIP, every later step succeeds, no
-    ordering hazard appears, and no step ever reads a slot that does not hold
-    the blob it wants (a miss whose fill never started leaves the cache)."""
-    out = run(harness, "fault", kind, nth, 3, 16, 4, 2, 10, 60, nth)
+def test_injected_failures_leave_a_consistent_cache(harness, kind, nth, copy_engine):
+    """The n-th copy (0), event creation (1), event record (2), stream wait
+    (3) or fill-kernel launch (4) fails: that step returns MOE_EHIP, every
+    later step succeeds, no ordering hazard appears, and no step ever reads a
+    slot that does not hold the blob it wants (a miss whose fill never
+    started leaves the cache).  Copy-engine fills, or the fill kernel with
+    the hits on the side stream."""
+    out = run(harness, "fault", kind, nth, 3, 16, 4, 2, 10, 60, nth, copy_engine=copy_engine)
     st = [int(ln[2]) for ln in out]
     assert st.count(MOE_EHIP) == 1 and all(s == MOE_OK for s in st if s != MOE_EHIP), st
 
 
 @pytest.mark.parametrize("ratio", ["0.5", "0", "1"])
-def test_hybrid_policy_protocol_and_trace(harness, ratio):
+@pytest.mark.parametrize("copy_engine", [False, True])
+def test_hybrid_policy_protocol_and_trace(harness, ratio, copy_engine):
     """The hybrid miss policy on the CPU harness (real host expert FFN on
     the blobs): the copied share of each step's misses is looked up as by
     the oracle LRU, the rest are reported as host-run (slot -1) and leave the
@@ -124,7 +133,7 @@ def test_hybrid_policy_protocol_and_trace(harness, ratio):
     previous copy finished (no hazard)."""
     import numpy as np
     E = 16
-    out = run(harness, "hybrid", ratio, 3, E, 4, 2, 10, 200, 6)
+    out = run(harness, "hybrid", ratio, 3, E, 4, 2, 10, 200, 6, copy_engine=copy_engine)
     lru = SlotLRU(10)
     r = np.float32(float(ratio))
     for ln in out:

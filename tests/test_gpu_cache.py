@@ -50,7 +50,7 @@ def test_cache_fill_copies_the_blob_into_its_slot():
 
 
 def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=None, config=86, resize_at=None,
-                routing_seed=None, blob_key=None, copy_ratio=None):
+                routing_seed=None, blob_key=None, copy_ratio=None, copy_engine=False):
     """Decode `tokens` single-token steps through `layers` layers; returns the
     number of steps checked against the oracle.  blob_key(l, e) names the
     pinned blob of an expert (experts with equal keys share one host copy;
@@ -68,7 +68,8 @@ def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=N
         return bank[key]
 
     dec = CachedDecoder(num_layers=layers, num_experts=E, k=k, H=H, I=I, fmt="nvfp4", num_slots=slots,
-                        host_blob=host_blob, device=DEV, copy_ratio=copy_ratio, host_threads=4)
+                        host_blob=host_blob, device=DEV, copy_ratio=copy_ratio, host_threads=4,
+                        copy_engine=copy_engine)
     seed = config if routing_seed is None else routing_seed
     logits = synth.stream_routing(tokens, layers, E, seed=seed)
     xs = np.stack([np.stack([synth.stream_activations(t, l, H, seed=seed)[0] for l in range(layers)])
@@ -103,6 +104,11 @@ def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=N
     torch.cuda.synchronize()
     hits, m, nbytes = dec.stats()
     assert m == misses and nbytes == misses * stride
+    # the cached blobs are byte-equal to their host copies (up to 32 of them)
+    cached = [(l, e) for l in range(layers) for e in range(E) if (l, e) in lru][:32]
+    for l, e in cached:
+        sl = lru.slot_of((l, e))
+        assert torch.equal(dec.pool[sl * stride:(sl + 1) * stride].cpu(), host_blob(l, e)), (l, e, sl)
     say(f"    {tokens} tokens x {layers} layers: {hits} hits, {m} misses, {checked} outputs checked")
     dec.close()
     return checked
@@ -123,14 +129,18 @@ def _policy_lookup(lru, layer, ids, copy_ratio):
     return [recs[e] if e in recs else (e, False, -1, None) for e in ids]
 
 
-def test_cached_stream_small_every_step():
-    """16 experts per layer, top-4, 10 slots for 3 layers: most steps miss and evict."""
-    say("cached stream: 3 layers x 16 NVFP4 experts (hidden 256, inter 256), 10 slots, 20 tokens")
+@pytest.mark.parametrize("copy_engine", [False, True])
+def test_cached_stream_small_every_step(copy_engine):
+    """16 experts per layer, top-4, 10 slots for 3 layers: most steps miss and
+    evict.  Misses copied by the fill kernel (hits on the side stream) or by
+    the copy engine."""
+    say(f"cached stream: 3 layers x 16 NVFP4 experts (hidden 256, inter 256), 10 slots, 20 tokens, "
+        f"copy engine {copy_engine}")
 
     def make(l, e):
         return synth.expert("nvfp4", 256, 256, config=86, layer=l, expert_id=e)
 
-    _run_stream(layers=3, E=16, k=4, H=256, I=256, tokens=20, slots=10, make_expert=make)
+    _run_stream(layers=3, E=16, k=4, H=256, I=256, tokens=20, slots=10, make_expert=make, copy_engine=copy_engine)
 
 
 @pytest.mark.parametrize("copy_ratio", [0.5, 0.0])
