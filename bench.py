@@ -663,15 +663,18 @@ def bench_stream(args):
     tr_n = np.zeros(NS, np.int32)
     bases = (tr_e.ctypes.data, tr_s.ctypes.data, tr_h.ctypes.data, tr_v.ctypes.data)
 
+    # the step's inputs by address: x_d[t, l] and lg_d[t, l] rows
+    x0, lg0 = x_d.data_ptr(), lg_d.data_ptr()
+
     def run(t0_, t1_, record):
         for t in range(t0_, t1_):
             for l in range(LAYERS):
+                i = t * LAYERS + l
                 if record:
-                    i = t * LAYERS + l
                     ptrs = (bases[0] + 4 * E * i, bases[1] + 4 * E * i, bases[2] + E * i, bases[3] + 4 * E * i)
-                    tr_n[i] = dec.step_fast(l, x_d[t, l:l + 1], lg_d[t, l:l + 1], sh, ptrs)
+                    tr_n[i] = dec.step_raw(l, x0 + 2 * H * i, lg0 + 4 * E * i, sh, ptrs)
                 else:
-                    dec.step_fast(l, x_d[t, l:l + 1], lg_d[t, l:l + 1], sh)
+                    dec.step_raw(l, x0 + 2 * H * i, lg0 + 4 * E * i, sh)
 
     log(f"[bench] warmup {warm_tokens} tokens, then {TOKENS} tokens from a cold cache")
     run(0, warm_tokens, False)

@@ -43,12 +43,11 @@
 namespace moe {
 hipError_t launch_move_slots(const int32_t* src_slots, int n, int dst0, const void* src_pool, void* dst_pool,
                              size_t slot_bytes, hipStream_t s);
-hipError_t launch_publish_counts(const int32_t* counts, int E, int32_t* host_counts_dev, uint32_t* flag_dev,
-                                 uint32_t seq, hipStream_t s);
 hipError_t launch_write_map(const StepMap& m, int E, void* dev_map, hipStream_t s);
 hipError_t launch_fill_slots(const FillList& f, const StepMap& m, int E, void* dev_map, void* pool, size_t slot_bytes,
                              hipStream_t s);
 bool ffn_takes_gemv(const moe_ffn_args* a);
+moe_status expert_ffn_fill(const moe_ffn_args* a, const FillList& f, void* pool, size_t slot_bytes, hipStream_t s);
 }
 
 struct moe_cache {
@@ -527,25 +526,35 @@ static moe_status write_map(moe_cache* c, void* host_map, void* dev_map, int E, 
   return MOE_OK;
 }
 
-// The step's miss fills as one fill kernel's list; false when they go
-// through the copy engine instead: the FFN is off the GEMV path (the hit and
-// miss launches would share workspace, so they cannot run at once), too many
-// experts or misses for the kernel arguments, or a blob that is not mapped
-// pinned memory on a 16-byte boundary.
+// The step's miss fills as two kernel copy lists: `head` (the blob header
+// and the gate/up weights, bytes [0, off_w2)) for the fill kernel and `tail`
+// (the down weights to the slot's end) for the copy workgroups of the miss
+// FFN's gate/up launch, which copy them while the gate/up runs.  False when
+// the fills go through the copy engine instead: the FFN is off the GEMV path
+// (the hit and miss launches would share workspace, so they cannot run at
+// once), too many experts or misses for the kernel arguments, or a blob that
+// is not mapped pinned memory on a 16-byte boundary.
 static bool kernel_fill_list(moe_cache* c, const moe_ffn_args& f, const void* const* host_blobs, int n, int nm,
-                             moe::FillList* fl) {
+                             moe::FillList* head, moe::FillList* tail) {
+  moe::BlobLayout L;
   if (c->copy_engine || nm == 0 || nm > moe::kFillMax || n > moe::kStepMapMax || !moe::ffn_takes_gemv(&f) ||
-      c->slot_bytes / 16 >= (1ull << 31))
+      c->slot_bytes / 16 >= (1ull << 31) || !moe::layout_of(f.wfmt, f.H, f.I, &L) || L.total > c->slot_bytes)
     return false;
-  fl->n = 0;
+  head->n = 0;
   for (int i = 0; i < n; ++i) {
     if (c->step_hit[i]) continue;
     const void* d = mapped_device_ptr(c, host_blobs[c->step_ids[i]]);
     if (!d || ((uintptr_t)d & 15)) return false;
-    fl->slot[fl->n] = c->step_slot[i];
-    fl->src[fl->n] = static_cast<const uint8_t*>(d);
-    ++fl->n;
+    head->slot[head->n] = c->step_slot[i];
+    head->src[head->n] = static_cast<const uint8_t*>(d);
+    ++head->n;
   }
+  const uint32_t vecs = (uint32_t)(c->slot_bytes / 16), split = (uint32_t)(L.off_w2 / 16);
+  *tail = *head;
+  head->off16 = 0;
+  head->len16 = split;
+  tail->off16 = split;
+  tail->len16 = vecs - split;
   return true;
 }
 
@@ -604,21 +613,24 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
 
   // 1-2. routing, then the step's experts on the host (and, for host-run
   // misses, the rows they take)
-  st = moe_route_permute(s->logits, T, E, f.k, s->renormalize, s->topk_ids, const_cast<float*>(f.topk_w),
-                         const_cast<int32_t*>(f.counts), const_cast<int32_t*>(f.offsets), const_cast<int32_t*>(f.perm),
-                         const_cast<int32_t*>(f.inv), compute_stream);
-  if (st != MOE_OK) return st;
   ensure_flag(c);
   int32_t* counts_dev = (c->publish == 1 && !hy) ? static_cast<int32_t*>(mapped_device_ptr(c, s->host_counts)) : nullptr;
   if (counts_dev) {
-    // the GPU writes the counts into the mapped host buffer and publishes the
-    // step's number; the host polls for it
+    // the routing writes the counts into the mapped host buffer and then
+    // publishes the step's number; the host polls for it
     const uint32_t seq = ++c->seq;
-    const hipError_t e = moe::launch_publish_counts(f.counts, E, counts_dev, c->flag_dev, seq, ks);
-    if (e != hipSuccess) return moe::set_error(MOE_EHIP, "%s: count handoff launch failed: %s", who, hipGetErrorString(e));
+    st = moe::route_permute_publish(s->logits, T, E, f.k, s->renormalize, s->topk_ids, const_cast<float*>(f.topk_w),
+                                    const_cast<int32_t*>(f.counts), const_cast<int32_t*>(f.offsets),
+                                    const_cast<int32_t*>(f.perm), const_cast<int32_t*>(f.inv), counts_dev, c->flag_dev,
+                                    seq, ks);
+    if (st != MOE_OK) return st;
     st = wait_flag(c, seq, ks, who);
     if (st != MOE_OK) return st;
   } else {
+    st = moe_route_permute(s->logits, T, E, f.k, s->renormalize, s->topk_ids, const_cast<float*>(f.topk_w),
+                           const_cast<int32_t*>(f.counts), const_cast<int32_t*>(f.offsets), const_cast<int32_t*>(f.perm),
+                           const_cast<int32_t*>(f.inv), compute_stream);
+    if (st != MOE_OK) return st;
     MOE_HIP(hipMemcpyAsync(s->host_counts, f.counts, sizeof(int32_t) * (size_t)E, hipMemcpyDeviceToHost, ks));
     if (hy) {
       MOE_HIP(hipMemcpyAsync(hy->host_offsets, f.offsets, sizeof(int32_t) * (size_t)(E + 1), hipMemcpyDeviceToHost, ks));
@@ -664,8 +676,8 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
   int nm = 0;
   for (int i = 0; i < n; ++i) nm += !c->step_hit[i];
   const int nh = n - nm;
-  moe::FillList fl;
-  const bool kfill = kernel_fill_list(c, f, s->host_blobs, n, nm, &fl);
+  moe::FillList fl, fl_tail;
+  const bool kfill = kernel_fill_list(c, f, s->host_blobs, n, nm, &fl, &fl_tail);
   const int32_t* dmap = static_cast<const int32_t*>(s->dev_map);
   const uint8_t* dhm = reinterpret_cast<const uint8_t*>(dmap + E);
   const uint8_t* dmm = dhm + E;
@@ -755,13 +767,17 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
     MOE_HIP(hipEventRecord(up, ks));
     hy->cpu_experts += (long long)host_run.size();
   }
-  // 6c. copied misses after their fills (a fill kernel's are in stream order)
+  // 6c. copied misses after their fills (a fill kernel's are in stream order,
+  // and the gate/up launch copies the down weights while it runs)
   if (nm > 0) {
     for (int i = 0; i < n; ++i)
       if (!c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], ks)) != MOE_OK) return st;
     a.expert_mask = dmm;
-    st = moe_expert_ffn(&a, compute_stream);
-    if (st != MOE_OK) return st;
+    st = kfill ? moe::expert_ffn_fill(&a, fl_tail, c->pool, c->slot_bytes, ks) : moe_expert_ffn(&a, compute_stream);
+    if (st != MOE_OK) {
+      if (kfill) drop_unfilled(c, s->layer, 0, n);  // their down weights may never have arrived
+      return st;
+    }
   }
   if (join.pending) {
     MOE_HIP(hipStreamWaitEvent(ks, c->hit_done, 0));

@@ -106,37 +106,24 @@ hipError_t launch_write_map(const StepMap& m, int E, void* dev_map, hipStream_t 
 
 // Miss fills of a decode step read straight from pinned host memory (PCIe
 // reads issued by the shader, no copy engine), so the step's miss FFN follows
-// them on the same stream with no cross-queue handoff.  Blob blockIdx.y of
-// the list (slot_vecs 16-byte vectors) goes to its slot; the x blocks below
-// kFillBlocks stride over its vectors with four loads in flight per thread,
-// and block kFillBlocks of row 0 writes the step's map.  PCIe-bound: the
-// link's read rate is the ceiling, which kFillBlocks workgroups per blob
-// reach.
-constexpr int kFillBlocks = 64;
+// them on the same stream with no cross-queue handoff.  Workgroups below
+// kCopyWgs copy vectors [f.off16, f.off16 + f.len16) of every blob of the
+// list into its slot (of slot_vecs 16-byte vectors; copy_blob_list), and
+// workgroup kCopyWgs writes the step's map.  PCIe-bound.
 __global__ __launch_bounds__(256) void k_fill_slots(FillList f, StepMap m, int E, uint8_t* __restrict__ map,
                                                     uint4* __restrict__ pool, uint32_t slot_vecs) {
-  if (blockIdx.x == kFillBlocks) {
-    if (blockIdx.y == 0) write_step_map(m, E, map);
+  if (blockIdx.x == kCopyWgs) {
+    write_step_map(m, E, map);
     return;
   }
-  const uint4* src = reinterpret_cast<const uint4*>(f.src[blockIdx.y]);
-  uint4* dst = pool + (size_t)f.slot[blockIdx.y] * slot_vecs;
-  constexpr uint32_t step = kFillBlocks * 256u;
-  for (uint32_t v = blockIdx.x * 256u + threadIdx.x; v < slot_vecs; v += 4 * step) {
-    uint4 r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (v + j * step < slot_vecs) r[j] = src[v + j * step];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (v + j * step < slot_vecs) dst[v + j * step] = r[j];
-  }
+  copy_blob_list(f, pool, slot_vecs, blockIdx.x, kCopyWgs);
 }
 
-// f.n in [1, kFillMax]; slot_bytes a multiple of 16, below 2^35.
+// f.n in [1, kFillMax]; slot_bytes a multiple of 16, below 2^35; the range
+// inside the slot (f.off16 + f.len16 <= slot_bytes / 16, checked by the caller).
 hipError_t launch_fill_slots(const FillList& f, const StepMap& m, int E, void* dev_map, void* pool, size_t slot_bytes,
                              hipStream_t s) {
-  launch(k_fill_slots, dim3(kFillBlocks + 1, f.n), dim3(256), 0, s, f, m, E, static_cast<uint8_t*>(dev_map),
+  launch(k_fill_slots, dim3(kCopyWgs + 1), dim3(256), 0, s, f, m, E, static_cast<uint8_t*>(dev_map),
          static_cast<uint4*>(pool), (uint32_t)(slot_bytes / 16));
   return hipGetLastError();
 }

@@ -9,6 +9,31 @@
 
 namespace moe {
 
+// Copies vectors [f.off16, f.off16 + f.len16) of every blob of f from host
+// memory into its slot (slot_vecs 16-byte vectors a slot of pool): workgroup
+// w of nw takes every nw-th 256-vector chunk of each blob in turn, two loads
+// in flight per thread.  With nw = kCopyWgs that is 128 KiB in flight, which
+// keeps the host link at its read rate (about 51 GB/s on MI355X) without a
+// deep backlog: host-memory reads of other work (command packets, kernel
+// arguments, a concurrent kernel's launch) then wait about 2 us behind it
+// instead of about 13 us with 1 MiB in flight.
+constexpr int kCopyWgs = 16;
+__device__ __forceinline__ void copy_blob_list(const FillList& f, uint4* __restrict__ pool, uint32_t slot_vecs, int w,
+                                               int nw) {
+  const uint32_t n = f.len16, step = (uint32_t)nw * 256u;
+  for (int b = 0; b < f.n; ++b) {
+    const uint4* src = reinterpret_cast<const uint4*>(f.src[b]) + f.off16;
+    uint4* dst = pool + (size_t)f.slot[b] * slot_vecs + f.off16;
+    uint32_t v = (uint32_t)w * 256u + threadIdx.x;
+    for (; v + step < n; v += 2 * step) {  // named registers: no stack array
+      const uint4 r0 = src[v], r1 = src[v + step];
+      dst[v] = r0;
+      dst[v + step] = r1;
+    }
+    if (v < n) dst[v] = src[v];
+  }
+}
+
 // Device-side view of one expert blob.
 struct BlobView {
   const uint8_t* w13;

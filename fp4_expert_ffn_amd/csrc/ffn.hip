@@ -14,6 +14,7 @@ namespace moe {
 hipError_t launch_gemv(const FfnParams& P, const GemvArgs& G, hipStream_t s);
 bool gemv_route_fits(const FfnParams& P);
 bool ffn_takes_gemv(const moe_ffn_args* a);
+moe_status expert_ffn_fill(const moe_ffn_args* a, const FillList& f, void* pool, size_t slot_bytes, hipStream_t s);
 hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStream_t s);
 hipError_t launch_quant_mxfp4(const uint16_t* x, int rows, int cols, uint8_t* q, uint8_t* s, hipStream_t st);
 hipError_t launch_fp4_codes_canon(const FfnParams& P, const MfmaBufs& B, int which, uint8_t* q, uint8_t* s,
@@ -272,7 +273,14 @@ struct RouteFold {
   int32_t* ids;
 };
 
-static moe_status run_ffn(const moe_ffn_args* a, hipStream_t s, const RouteFold* rf) {
+// Blob copies for the gate/up launch of a GEMV-path call (GemvArgs::copy).
+struct CopyReq {
+  const FillList* f;
+  void* pool;
+  size_t slot_bytes;
+};
+
+static moe_status run_ffn(const moe_ffn_args* a, hipStream_t s, const RouteFold* rf, const CopyReq* cp = nullptr) {
   FfnParams P = params_of(a);
 
   const WsLayout w = ws_layout(a);
@@ -295,6 +303,12 @@ static moe_status run_ffn(const moe_ffn_args* a, hipStream_t s, const RouteFold*
       G.renorm = rf->renorm;
       G.ids_out = rf->ids;
       G.w_out = const_cast<float*>(a->topk_w);
+    }
+    if (cp) {
+      G.copy = *cp->f;
+      G.copy_wgs = kCopyWgs;
+      G.copy_pool = static_cast<uint4*>(cp->pool);
+      G.copy_slot_vecs = (uint32_t)(cp->slot_bytes / 16);
     }
     e = launch_gemv(P, G, s);
   } else {
@@ -328,6 +342,23 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
   moe_status st = check_args(a);
   if (st != MOE_OK || a->T == 0) return st;
   return run_ffn(a, reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
+// moe_expert_ffn on the decode GEMV whose gate/up launch also copies part of
+// some blobs from host memory into their slots (f: 1 to kFillMax blobs, the
+// range inside slot_bytes, slot_bytes a multiple of 16 below 2^35).  The
+// copies land before the down launch starts; none may touch a slot the call
+// reads in that range.
+moe_status moe::expert_ffn_fill(const moe_ffn_args* a, const FillList& f, void* pool, size_t slot_bytes,
+                                hipStream_t s) {
+  moe_status st = check_args(a);
+  if (st != MOE_OK) return st;
+  MOE_CHECK_ARG(a->T > 0 && choose_path(a) == kPathGemv, "expert_ffn_fill: the call must take the decode GEMV");
+  MOE_CHECK_ARG(f.n >= 1 && f.n <= kFillMax && pool && slot_bytes % 16 == 0 && slot_bytes / 16 < (1ull << 31) &&
+                    (uint64_t)f.off16 + f.len16 <= slot_bytes / 16,
+                "expert_ffn_fill: bad copy list");
+  const CopyReq cp{&f, pool, slot_bytes};
+  return run_ffn(a, s, nullptr, &cp);
 }
 
 extern "C" moe_status moe_layer(const moe_layer_args* la, moe_stream_t stream) {

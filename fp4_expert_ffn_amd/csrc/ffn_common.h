@@ -62,6 +62,15 @@ struct GemvArgs {
   int renorm;
   int32_t* ids_out;
   float* w_out;
+  // blob copies riding along a gate/up launch without folded routing
+  // (copy_wgs > 0): the last copy_wgs workgroups copy vectors [copy.off16,
+  // copy.off16 + copy.len16) of each listed blob from host memory into its
+  // slot of copy_pool (copy_slot_vecs vectors a slot; copy_blob_list); the
+  // others run the GEMV
+  int copy_wgs;
+  uint32_t copy_slot_vecs;
+  uint4* copy_pool;
+  FillList copy;
 };
 
 // One unit of expert work: an expert (or the shared expert) and its rows.

@@ -480,6 +480,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float s_u[2][16][17];
   __shared__ int s_rows[16];
   __shared__ int s_big;  // rows of the staged block that overflow fp16 (finish_rows)
+  // workgroups of the GEMV (the copy workgroups come after them)
+  int ngemv = (int)gridDim.x;
+  if constexpr (!DOWN && !ROUTE) {
+    ngemv -= G.copy_wgs;
+    if ((int)blockIdx.x >= ngemv) {
+      copy_blob_list(G.copy, G.copy_pool, G.copy_slot_vecs, (int)blockIdx.x - ngemv, G.copy_wgs);
+      return;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 15, grp = lane >> 4;
   if (tid == 0) s_big = 0;  // visible after the table's barrier
   const int H = P.H, I = P.I;
@@ -512,8 +521,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     i_beg = half ? mid : c0;
     i_end = half ? c1 : mid;
   } else {
-    i_beg = nitems * blockIdx.x / gridDim.x;
-    i_end = nitems * (blockIdx.x + 1) / gridDim.x;
+    i_beg = nitems * blockIdx.x / ngemv;
+    i_end = nitems * (blockIdx.x + 1) / ngemv;
   }
   const int nsub = nk / SUB;  // SUB divides nk: every sub-item loads exactly SUB tiles
   const size_t off_w = DOWN ? P.L.off_w2 : P.L.off_w13, off_s = DOWN ? P.L.off_s2 : P.L.off_s13;
@@ -807,7 +816,7 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
     return n;
   };
   const bool route = G.logits != nullptr;  // the caller checked gemv_route_fits
-  if (route && !xall) return hipErrorInvalidValue;
+  if ((route && !xall) || (route && G.copy_wgs > 0)) return hipErrorInvalidValue;
   const auto k1 = route ? gemv_route_kernel<FMT>(P.H / Fmt<FMT>::KT)
                   : xall ? gemv_kernel<FMT, false, true>(P.H / Fmt<FMT>::KT)
                          : gemv_kernel<FMT, false, false>(P.H / Fmt<FMT>::KT);
@@ -820,9 +829,10 @@ static hipError_t launch_fmt(const FfnParams& P, GemvArgs G, hipStream_t s) {
   const int g2 = (int)std::max<long long>(1, std::min<long long>(nrb(G.rbs2) * G.nd, cap2));
   // a full grid of two workgroups per CU deals its items per CU
   G.ncu = g1 == 2 * cu_count() ? cu_count() : 0;
-  launch(k1, dim3(g1), dim3(256), lds1, s, P, G);
+  launch(k1, dim3(g1 + G.copy_wgs), dim3(256), lds1, s, P, G);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  G.copy_wgs = 0;
   G.ncu = g2 == 2 * cu_count() ? cu_count() : 0;
   launch(k2, dim3(g2), dim3(256), lds2, s, P, G);
   e = hipGetLastError();

@@ -106,13 +106,26 @@ struct StepMap {
 };
 
 // The blobs a decode step copies from pinned host memory into its miss
-// slots, passed by value beside the step's map: src[i] is the device address
-// of the host blob (16-byte aligned, slot_bytes long), slot[i] its slot.
+// slots, passed by value: src[i] is the device address of the host blob
+// (16-byte aligned, slot_bytes long), slot[i] its slot; the 16-byte vectors
+// [off16, off16 + len16) of each blob are copied.
 constexpr int kFillMax = 64;
 struct FillList {
   int32_t n;
+  uint32_t off16, len16;
   int32_t slot[kFillMax];
   const uint8_t* src[kFillMax];
 };
+
+// The count handoff of a cache decode step: counts[0..E) copied into the
+// host-mapped host_counts, then `seq` stored in the host-mapped *flag with a
+// release at system scope (cache_kernels.hip).
+hipError_t launch_publish_counts(const int32_t* counts, int E, int32_t* host_counts, uint32_t* flag, uint32_t seq,
+                                 hipStream_t s);
+// moe_route_permute followed by that handoff, issued once every routing
+// output is written (route.hip).
+moe_status route_permute_publish(const float* logits, int T, int E, int k, int renormalize, int32_t* topk_ids,
+                                 float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                 int32_t* host_counts, uint32_t* flag, uint32_t seq, hipStream_t s);
 
 }  // namespace moe

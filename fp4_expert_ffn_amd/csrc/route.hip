@@ -436,12 +436,19 @@ __global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict_
 // expert is the popcount of the mask below t.  Every wave scans the counts
 // itself (no barrier between the scan and the placement), then places its
 // own tokens.  LDS: E 64-bit masks + E ints per wave.
+//
+// host_counts (null: none): a host-mapped copy of the counts, after which
+// the kernel publishes `seq` in the host-mapped *flag with a release at
+// system scope, once every output of the kernel is written: a host that sees
+// the flag may enqueue work on any stream that reads them.
 template <int NPER>
 __global__ __launch_bounds__(1024) void k_route_permute_small(const float* __restrict__ logits, int T, int E, int k,
                                                               int renorm, int32_t* __restrict__ ids,
                                                               float* __restrict__ wts, int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+                                                              int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                              int32_t* __restrict__ host_counts, uint32_t* flag,
+                                                              uint32_t seq) {
   extern __shared__ uint64_t tmask[];  // [E], then int off[nw][E]
   __shared__ int32_t ids_s[64 * kRouteMaxK];
   __shared__ float w_s[64 * kRouteMaxK];
@@ -481,6 +488,7 @@ __global__ __launch_bounds__(1024) void k_route_permute_small(const float* __res
       if (wave == 0) {
         counts[e] = c;
         offsets[e] = base;
+        if (host_counts) host_counts[e] = c;
       }
       base += c;
     }
@@ -496,6 +504,11 @@ __global__ __launch_bounds__(1024) void k_route_permute_small(const float* __res
         inv[f] = pos;
       }
     }
+  }
+  if (host_counts) {
+    __threadfence_system();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(flag, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
 
@@ -610,7 +623,7 @@ extern "C" moe_status moe_route_permute(const float* logits, int T, int E, int k
     const int ntw = 64 * std::min(T, kPermWaves);  // a wave per token, up to 16
     const size_t lds = sizeof(uint64_t) * (size_t)E + sizeof(int32_t) * (size_t)E * (ntw / 64);
 #define MOE_RPS(N) hipLaunchKernelGGL(k_route_permute_small<N>, dim3(1), dim3(ntw), lds, hs, logits, T, E, k, rn, \
-                                      topk_ids, topk_w, counts, offsets, perm, inv)
+                                      topk_ids, topk_w, counts, offsets, perm, inv, nullptr, nullptr, 0u)
     if (E <= 64) MOE_RPS(1);
     else if (E <= 128) MOE_RPS(2);
     else if (E <= 256) MOE_RPS(4);
@@ -626,6 +639,41 @@ extern "C" moe_status moe_route_permute(const float* logits, int T, int E, int k
     else MOE_RP(16);
 #undef MOE_RP
   }
+  MOE_LAUNCHED();
+  return MOE_OK;
+}
+
+// moe_route_permute, then the counts copied into host_counts (host-mapped)
+// and `seq` published in the host-mapped *flag (release at system scope)
+// after every routing output is written.  Steps of up to 64 tokens do all of
+// it in the one routing kernel; larger ones add the publishing kernel.
+moe_status moe::route_permute_publish(const float* logits, int T, int E, int k, int renormalize, int32_t* topk_ids,
+                                      float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                      int32_t* host_counts, uint32_t* flag, uint32_t seq, hipStream_t hs) {
+  MOE_CHECK_ARG(host_counts && flag, "route_permute_publish: null host pointer");
+  if (!(T >= 1 && T <= 64 && (long long)T * k <= kPermChunk && E >= 1 && E <= 1024 && k >= 1 && k <= E &&
+        k <= kRouteMaxK)) {
+    moe_status st = moe_route_permute(logits, T, E, k, renormalize, topk_ids, topk_w, counts, offsets, perm, inv,
+                                      reinterpret_cast<moe_stream_t>(hs));
+    if (st != MOE_OK) return st;
+    const hipError_t e = launch_publish_counts(counts, E, host_counts, flag, seq, hs);
+    if (e != hipSuccess) return set_error(MOE_EHIP, "count handoff launch failed: %s", hipGetErrorString(e));
+    return MOE_OK;
+  }
+  MOE_CHECK_ARG(logits && topk_ids && topk_w && counts && offsets && perm && inv,
+                "route_permute_publish: null pointer");
+  moe_status st = set_lds_limits();
+  if (st != MOE_OK) return st;
+  const int rn = renormalize ? 1 : 0;
+  const int ntw = 64 * std::min(T, kPermWaves);
+  const size_t lds = sizeof(uint64_t) * (size_t)E + sizeof(int32_t) * (size_t)E * (ntw / 64);
+#define MOE_RPS(N) hipLaunchKernelGGL(k_route_permute_small<N>, dim3(1), dim3(ntw), lds, hs, logits, T, E, k, rn, \
+                                      topk_ids, topk_w, counts, offsets, perm, inv, host_counts, flag, seq)
+  if (E <= 64) MOE_RPS(1);
+  else if (E <= 128) MOE_RPS(2);
+  else if (E <= 256) MOE_RPS(4);
+  else MOE_RPS(16);
+#undef MOE_RPS
   MOE_LAUNCHED();
   return MOE_OK;
 }

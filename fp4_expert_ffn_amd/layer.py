@@ -164,6 +164,7 @@ class CachedDecoder:
         if copy_engine:
             L.moe_cache_use_copy_engine(self.cache, True)
         self.copy_stream = torch.cuda.Stream(device=self.dev)
+        self._copy_handle = self.copy_stream.cuda_stream
         T, E = max(max_tokens, 1), num_experts
         self.max_tokens = T
         # host blob table per layer (pinned blobs must hold `stride` bytes: the copy moves whole slots)
@@ -247,6 +248,25 @@ class CachedDecoder:
         st = self._step(layer, T, x, logits, self.out[:T])
         st.trace_expert, st.trace_slot, st.trace_hit, st.trace_evicted = trace or self._trace_ptrs
         self._run_step(st, stream_handle)
+        return st.n_experts
+
+    def step_raw(self, layer, x_ptr, logits_ptr, stream_handle, trace=None, T=1):
+        """step_fast() on raw device addresses (x_ptr: [T,H] bf16, logits_ptr:
+        [T,E] fp32), with no tensor work on the host; the output lands in
+        self.out[:T].  Returns the step's number of distinct experts."""
+        st = self._steps.get((layer, T))
+        if st is None:
+            st = self._step(layer, T, self.out[:T], self.w[:T], self.out[:T])  # placeholders, replaced below
+        st.logits = logits_ptr
+        st.ffn.x = x_ptr
+        st.trace_expert, st.trace_slot, st.trace_hit, st.trace_evicted = trace or self._trace_ptrs
+        if self.hybrid is None:
+            r = L.lib().moe_cache_decode_step(self.cache.handle, ctypes.byref(st), self._copy_handle, stream_handle)
+        else:
+            r = L.lib().moe_cache_decode_step_hybrid(self.cache.handle, ctypes.byref(st), ctypes.byref(self.hybrid),
+                                                     self._copy_handle, stream_handle)
+        if r != L.MOE_OK:
+            raise L.MoeError(r, f"moe_cache_decode_step: {L.moe_last_error()}")
         return st.n_experts
 
     def _run_step(self, st, stream):

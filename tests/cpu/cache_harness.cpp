@@ -104,6 +104,7 @@ struct World {
         memcpy(b, &hdr, sizeof hdr);
         const int32_t tag[2] = {l, e};
         memcpy(b + kTagOffset, tag, sizeof tag);
+        memcpy(b + Ly.off_w2 + 16, tag, sizeof tag);  // a second tag among the down weights
         blob_ptr.push_back(b);
       }
     pool = buffer(slot * C, 1);

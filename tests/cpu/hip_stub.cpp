@@ -288,9 +288,11 @@ extern "C" moe_status moe_combine(const float*, const int32_t*, const float*, co
 }
 // Reads the blob of every expert with rows (and enabled by the mask): its
 // slot must be in the pool, ordered after its fill, and hold the blob of
-// (current layer, expert).
-extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream) {
-  const Op o = tick(reinterpret_cast<hipStream_t>(stream));
+// (current layer, expert), both in its header and among its down weights.
+namespace {
+void ffn_reads(const moe_ffn_args* a, const Op& o) {
+  moe::BlobLayout Ly;
+  if (!moe::layout_of(a->wfmt, a->H, a->I, &Ly)) bad("FFN blob layout", a->H, a->I);
   for (int e = 0; e < a->E; ++e) {
     if (a->counts[e] <= 0 || (a->expert_mask && !a->expert_mask[e])) continue;
     const int slot = a->slot_of_expert[e];
@@ -300,14 +302,42 @@ extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream)
       continue;
     }
     slot_read(addr, o);
-    int32_t tag[2];  // in the blob header's padding
+    int32_t tag[2], tag2[2];  // in the blob header's padding, and among the down weights
     memcpy(tag, reinterpret_cast<const void*>(addr + kTagOffset), sizeof tag);
+    memcpy(tag2, reinterpret_cast<const void*>(addr + Ly.off_w2 + 16), sizeof tag2);
     if (tag[0] != g_layer || tag[1] != e) bad("slot holds another blob", tag[0] * 100000LL + tag[1], g_layer * 100000LL + e);
+    if (tag2[0] != g_layer || tag2[1] != e) bad("slot holds another blob's down weights", tag2[0], tag2[1]);
   }
+}
+}  // namespace
+
+extern "C" moe_status moe_expert_ffn(const moe_ffn_args* a, moe_stream_t stream) {
+  const Op o = tick(reinterpret_cast<hipStream_t>(stream));
+  ffn_reads(a, o);
   return MOE_OK;
 }
 
 namespace moe {
+// copies of blob ranges into slots by a kernel (the fill kernel, or the copy
+// workgroups of a gate/up launch)
+static void copy_parts(const FillList& f, void* pool, size_t slot_bytes, const Op& o) {
+  if (f.n < 1 || f.n > kFillMax) bad("fill list size", f.n, 0);
+  if ((uint64_t)f.off16 + f.len16 > slot_bytes / 16) bad("fill range outside the slot", f.off16, f.len16);
+  for (int i = 0; i < f.n; ++i) {
+    const uintptr_t to = (uintptr_t)pool + (uintptr_t)f.slot[i] * slot_bytes;
+    const Region* rs = region_of((uintptr_t)f.src[i], slot_bytes);
+    if (!rs || rs->device == 1 || ((uintptr_t)f.src[i] & 15)) {
+      bad("fill source not in host memory", f.slot[i], 0);
+      continue;
+    }
+    if (slot_addr(to) != to || slot_bytes != g_slot_bytes || (uintptr_t)pool != g_pool) {
+      bad("fill destination not a slot of the pool", f.slot[i], 0);
+      continue;
+    }
+    slot_write(to, o);
+    memcpy(reinterpret_cast<void*>(to + 16 * (size_t)f.off16), f.src[i] + 16 * (size_t)f.off16, 16 * (size_t)f.len16);
+  }
+}
 // the count handoff: the stream writes the counts to host memory and the flag,
 // which the host has then observed (its clock joins the stream's)
 hipError_t launch_publish_counts(const int32_t* counts, int E, int32_t* host_counts, uint32_t* flag, uint32_t seq,
@@ -317,6 +347,18 @@ hipError_t launch_publish_counts(const int32_t* counts, int E, int32_t* host_cou
   __atomic_store_n(flag, seq, __ATOMIC_RELEASE);
   for (int i = 0; i < kMaxStreams; ++i) g_host[i] = std::max(g_host[i], o.vc[i]);
   return hipSuccess;
+}
+// routing with the handoff folded in: one stream operation that writes the
+// routing outputs, then the host copy of the counts and the flag
+moe_status route_permute_publish(const float*, int, int E, int, int, int32_t*, float*, int32_t* counts,
+                                 int32_t* offsets, int32_t* perm, int32_t*, int32_t* host_counts, uint32_t* flag,
+                                 uint32_t seq, hipStream_t s) {
+  const Op o = tick(s);
+  route_counts(E, counts, offsets, perm);
+  memcpy(host_counts, counts, sizeof(int32_t) * (size_t)E);
+  __atomic_store_n(flag, seq, __ATOMIC_RELEASE);
+  for (int i = 0; i < kMaxStreams; ++i) g_host[i] = std::max(g_host[i], o.vc[i]);
+  return MOE_OK;
 }
 hipError_t launch_write_map(const StepMap& m, int E, void* dev_map, hipStream_t s) {
   tick(s);
@@ -344,22 +386,18 @@ hipError_t launch_fill_slots(const FillList& f, const StepMap& m, int E, void* d
     slot[m.expert[i]] = m.slot[i];
     (m.hit[i] ? hit : hit + E)[m.expert[i]] = 1;
   }
-  if (f.n < 1 || f.n > kFillMax) bad("fill list size", f.n, 0);
-  for (int i = 0; i < f.n; ++i) {
-    const uintptr_t to = (uintptr_t)pool + (uintptr_t)f.slot[i] * slot_bytes;
-    const Region* rs = region_of((uintptr_t)f.src[i], slot_bytes);
-    if (!rs || rs->device == 1 || ((uintptr_t)f.src[i] & 15)) {
-      bad("fill source not in host memory", f.slot[i], 0);
-      continue;
-    }
-    if (slot_addr(to) != to || slot_bytes != g_slot_bytes || (uintptr_t)pool != g_pool) {
-      bad("fill destination not a slot of the pool", f.slot[i], 0);
-      continue;
-    }
-    slot_write(to, o);
-    memcpy(reinterpret_cast<void*>(to), f.src[i], slot_bytes);
-  }
+  copy_parts(f, pool, slot_bytes, o);
   return hipSuccess;
+}
+// the FFN whose gate/up launch copies the rest of the blobs: one operation
+// that writes the listed ranges and reads the masked experts' blobs (which
+// must hold both parts by then)
+moe_status expert_ffn_fill(const moe_ffn_args* a, const FillList& f, void* pool, size_t slot_bytes, hipStream_t s) {
+  if (inject(4)) return MOE_EHIP;
+  const Op o = tick(s);
+  copy_parts(f, pool, slot_bytes, o);
+  ffn_reads(a, o);
+  return MOE_OK;
 }
 bool ffn_takes_gemv(const moe_ffn_args* a) { return (long long)a->T * a->k < 512 && a->amode != MOE_ACT_MXFP4; }
 hipError_t launch_move_slots(const int32_t* src_slots, int n, int dst0, const void* src_pool, void* dst_pool,

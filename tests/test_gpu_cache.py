@@ -50,11 +50,12 @@ def test_cache_fill_copies_the_blob_into_its_slot():
 
 
 def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=None, config=86, resize_at=None,
-                routing_seed=None, blob_key=None, copy_ratio=None, copy_engine=False):
+                routing_seed=None, blob_key=None, copy_ratio=None, copy_engine=False, raw=False):
     """Decode `tokens` single-token steps through `layers` layers; returns the
     number of steps checked against the oracle.  blob_key(l, e) names the
     pinned blob of an expert (experts with equal keys share one host copy;
-    make_expert must give them equal weights)."""
+    make_expert must give them equal weights).  raw: steps through
+    CachedDecoder.step_raw (inputs by device address) instead of step."""
     from fp4_expert_ffn_amd.layer import CachedDecoder, to_numpy_bf16
     import fp4_expert_ffn_amd as F
     stride = (F.moe_blob_bytes("nvfp4", H, I) + 255) // 256 * 256
@@ -86,7 +87,14 @@ def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=N
             dec.resize(resize_at[t])
             lru.resize(resize_at[t])
         for l in range(layers):
-            out, (te, ts, th, tv) = dec.step(l, x_d[t, l:l + 1], lg_d[t, l:l + 1])
+            if raw:
+                i = t * layers + l
+                n = dec.step_raw(l, x_d.data_ptr() + 2 * H * i, lg_d.data_ptr() + 4 * E * i,
+                                 torch.cuda.current_stream().cuda_stream)
+                out = dec.out[:1]
+                te, ts, th, tv = (a[:n].copy() for a in dec.trace)
+            else:
+                out, (te, ts, th, tv) = dec.step(l, x_d[t, l:l + 1], lg_d[t, l:l + 1])
             ids, w = oracle.moe.route(logits[t, l:l + 1], k)
             want = _policy_lookup(lru, l, sorted(set(ids[0].tolist())), copy_ratio)
             assert te.tolist() == [r[0] for r in want], (t, l)
@@ -156,7 +164,7 @@ def test_cached_stream_hybrid_policy(copy_ratio):
         return synth.expert("nvfp4", 256, 256, config=92, layer=l, expert_id=e)
 
     _run_stream(layers=3, E=16, k=4, H=256, I=256, tokens=20, slots=10, make_expert=make, config=92,
-                copy_ratio=copy_ratio)
+                copy_ratio=copy_ratio, raw=True)
 
 
 def test_cached_stream_with_resizes():
@@ -186,7 +194,7 @@ def test_cached_stream_a3b_shape():
     rng = np.random.default_rng(0)
     steps = {(int(t), int(l)) for t, l in zip(rng.integers(0, 12, 6), rng.integers(0, 2, 6))} | {(11, 1)}
     n = _run_stream(layers=2, E=128, k=8, H=2048, I=768, tokens=12, slots=24, make_expert=make,
-                    check_steps=steps, config=87)
+                    check_steps=steps, config=87, raw=True)
     assert n == len(steps)
 
 
