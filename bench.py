@@ -417,7 +417,8 @@ def main():
                     help="first run three plain device copies of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
                     help="no GPU work: 'stats CSV OUT CMD' writes a kernel-time summary; "
-                         "'traffic FETCH_CSV WRITE_CSV COPY_MIB OUT CMD' writes the dominant kernel's HBM bytes")
+                         "'traffic FETCH_CSV WRITE_CSV COPY_MIB OUT CMD' writes the dominant kernel's HBM bytes; "
+                         "'timeline KERNEL_TRACE_CSV OUT CMD' summarises a stream run's layer steps")
     args = ap.parse_args()
     if args.summarize:
         return summarize(args)
@@ -552,7 +553,75 @@ def summarize(args):
             json.dump(t, f, indent=1)
         print(f"wrote {out}: {int(fetch + write)} bytes per launch")
         return
+    if kind == "timeline":
+        src, out, cmd = args.summarize[1:4]
+        print(f"wrote {out}: " + stream_timeline(src, out, cmd))
+        return
     raise SystemExit(f"unknown summary kind {kind}")
+
+
+def stream_timeline(src, out, cmd):
+    """Per-layer-step summary of a kernel trace of the stream workload: each
+    step starts at its routing kernel; steps with a fill kernel are split from
+    the rest; the overlap is the share of the side-stream hit kernels' time
+    that falls inside the step's fill kernel."""
+    import csv
+    import statistics as stx
+
+    def short(n):
+        n = n.replace("(anonymous namespace)::", "").split("(")[0]
+        return n.replace("void ", "").replace("moe::", "")[:44]
+
+    with open(src) as f:
+        ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), short(r["Kernel_Name"]), r["Queue_Id"])
+                    for r in csv.DictReader(f))
+    starts = [i for i, k in enumerate(ks) if k[2].startswith("k_route_permute_small")]
+    steps = [ks[a:b] for a, b in zip(starts, starts[1:])]
+    steps = steps[len(steps) // 2:]  # the second half: a warm cache, the steady state
+    fill_steps, plain = [], []
+    for st in steps:
+        t0 = st[0][0]
+        span = (st[-1][1] - t0) / 1e3
+        fills = [k for k in st if k[2] == "k_fill_slots"]
+        if not fills:
+            plain.append(span)
+            continue
+        fq, (f0, f1) = fills[0][3], (fills[0][0], fills[0][1])
+        side = [k for k in st if k[3] != fq]
+        busy = sum((k[1] - k[0]) for k in side)
+        inside = sum(max(0, min(k[1], f1) - max(k[0], f0)) for k in side)
+        fill_steps.append({"span": span, "fill_us": (f1 - f0) / 1e3, "react_us": (f0 - st[0][1]) / 1e3,
+                           "side_us": busy / 1e3, "overlap": inside / busy if busy else None})
+    per = {}
+    for st in steps:
+        for k in st:
+            per.setdefault(k[2], []).append((k[1] - k[0]) / 1e3)
+    L = [f"# kernel timeline of the cached decode stream (rocprofv3 kernel trace)", f"# command: {cmd}",
+         "# host-side gaps are inflated by the profiler's per-dispatch work; kernel durations are not", "",
+         f"layer steps summarised: {len(steps)} (second half of the run)",
+         f"steps without a miss: {len(plain)}, mean span {stx.mean(plain):.1f} us" if plain else "steps without a miss: 0"]
+    if fill_steps:
+        ov = [x["overlap"] for x in fill_steps if x["overlap"] is not None]
+        L += [f"steps with misses: {len(fill_steps)}, mean span {stx.mean(x['span'] for x in fill_steps):.1f} us",
+              f"  fill kernel {stx.mean(x['fill_us'] for x in fill_steps):.1f} us mean; routing end to fill start "
+              f"{stx.mean(x['react_us'] for x in fill_steps):.1f} us mean (host LRU and launch)",
+              f"  steps whose hits ran on the side stream: {len(ov)}; share of the hit kernels' time inside the "
+              f"fill: {stx.mean(ov):.3f} mean, {min(ov):.3f} min" if ov else "  no side-stream hits"]
+    L += ["", f"{'kernel':<46} {'n':>6} {'mean_us':>9}"]
+    for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        L.append(f"{name:<46} {len(v):>6} {stx.mean(v):>9.2f}")
+    # three steps with fills, as they ran (queue 1 is the compute stream's)
+    shown = 0
+    for st in steps:
+        if shown == 3 or not any(k[2] == "k_fill_slots" for k in st):
+            continue
+        t0 = st[0][0]
+        L += ["", f"step (span {(st[-1][1] - t0) / 1e3:.1f} us): start_us end_us kernel queue"]
+        L += [f"  {(k[0] - t0) / 1e3:7.1f} {(k[1] - t0) / 1e3:7.1f} {k[2]:<44} q{k[3]}" for k in st]
+        shown += 1
+    with open(out, "w") as f:
+        f.write("\n".join(L) + "\n")
+    return f"{len(steps)} steps"
 
 
 def stream_trace_verdict(n, e, h, s, v, E, tokens, layers, slots):

@@ -688,7 +688,8 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
   a.out = nullptr;
   SideJoin join{c, false};
   if (kfill) {
-    // The fills first (the step's critical path).  Every earlier reader and
+    // The fills first, then the missed experts' FFN: the step's critical
+    // path, enqueued before anything else.  Every earlier reader and
     // kernel fill of the slots is behind the host already: this step's counts
     // were published after them on the compute stream, and an earlier step's
     // hits joined it before that step's combine.  A copy-engine fill of a
@@ -714,7 +715,17 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
       return st;
     }
     c->bytes_filled += (long long)nm * (long long)c->slot_bytes;
-    // the hits on the side stream, with their own copy of the map
+    // the missed experts next (the gate/up launch copies their down weights
+    // while it runs); the shared expert goes with the hits when there are any
+    moe_ffn_args am = a;
+    am.expert_mask = dmm;
+    if (nh > 0) am.shared_blob = nullptr;
+    st = moe::expert_ffn_fill(&am, fl_tail, c->pool, c->slot_bytes, ks);
+    if (st != MOE_OK) {
+      drop_unfilled(c, s->layer, 0, n);  // their down weights may never have arrived
+      return st;
+    }
+    // then the hits on the side stream, with their own copy of the map
     if (nh > 0) {
       join.pending = true;
       st = ensure_side(c);
@@ -728,7 +739,6 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
       ah.expert_mask = static_cast<const uint8_t*>(c->side_map) + 4 * (size_t)E;
       st = moe_expert_ffn(&ah, reinterpret_cast<moe_stream_t>(c->side));
       if (st != MOE_OK) return st;
-      a.shared_blob = nullptr;  // computed once
       MOE_HIP(hipEventRecord(c->hit_done, c->side));
     }
   } else {
@@ -767,17 +777,13 @@ static moe_status decode_step(moe_cache* c, moe_cache_step* s, moe_hybrid* hy, m
     MOE_HIP(hipEventRecord(up, ks));
     hy->cpu_experts += (long long)host_run.size();
   }
-  // 6c. copied misses after their fills (a fill kernel's are in stream order,
-  // and the gate/up launch copies the down weights while it runs)
-  if (nm > 0) {
+  // 6c. copy-engine misses after their fills
+  if (nm > 0 && !kfill) {
     for (int i = 0; i < n; ++i)
       if (!c->step_hit[i] && (st = wait_fill(c, c->step_slot[i], ks)) != MOE_OK) return st;
     a.expert_mask = dmm;
-    st = kfill ? moe::expert_ffn_fill(&a, fl_tail, c->pool, c->slot_bytes, ks) : moe_expert_ffn(&a, compute_stream);
-    if (st != MOE_OK) {
-      if (kfill) drop_unfilled(c, s->layer, 0, n);  // their down weights may never have arrived
-      return st;
-    }
+    st = moe_expert_ffn(&a, compute_stream);
+    if (st != MOE_OK) return st;
   }
   if (join.pending) {
     MOE_HIP(hipStreamWaitEvent(ks, c->hit_done, 0));

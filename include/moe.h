@@ -345,11 +345,14 @@ moe_status moe_cache_stats(const moe_cache* c, long long* hits, long long* misse
  *      orders.  Fill kernel (the FFN takes the decode GEMV, at most 64 misses
  *      and 256 experts, every miss blob mapped pinned memory on a 16-byte
  *      boundary, and moe_cache_use_copy_engine not set): one kernel on
- *      compute_stream copies every miss blob from host memory into its slot
- *      and writes dev_map, then the FFN over the missed experts follows;
- *      meanwhile the FFN over the hit experts runs on a stream the cache
- *      owns, with its own copy of the map, and compute_stream waits for it
- *      before the combine.  Copy engine (otherwise): for every miss a fill
+ *      compute_stream copies the header and gate/up weights of every miss
+ *      blob from host memory into its slot and writes dev_map, then the FFN
+ *      over the missed experts follows, its gate/up launch copying the down
+ *      weights while it runs; meanwhile the FFN over the hit experts (and
+ *      the shared expert) runs on a stream the cache owns, with its own copy
+ *      of the map, and compute_stream waits for it before the combine.  A
+ *      failure after the lookups leaves no key mapped to a slot whose blob
+ *      did not arrive.  Copy engine (otherwise): for every miss a fill
  *      from host_blobs[expert] on copy_stream (after the slot's previous
  *      readers), the slot map and masks host_map -> dev_map, the FFN over the
  *      hit experts (overlapping the fills), a wait on each miss's fill, then
