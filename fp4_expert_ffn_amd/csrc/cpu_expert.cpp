@@ -28,6 +28,11 @@
 
 #include "host_common.h"
 
+namespace moe {
+hipError_t launch_fill_slots(const FillList& f, const StepMap& m, int E, void* dev_map, void* pool, size_t slot_bytes,
+                             hipStream_t s);
+}
+
 namespace {
 
 // ---------------------------------------------------------------- thread pool
@@ -218,11 +223,32 @@ extern "C" moe_status moe_calibrate_bw(const void* host_blob, void* dev_buf, int
   hipEvent_t e0 = nullptr, e1 = nullptr;
   MOE_HIP(hipEventCreate(&e0));
   MOE_HIP(hipEventCreate(&e1));
-  // host -> device: reps copies of the blob from pinned memory, after one untimed
-  hipError_t err = hipMemcpyAsync(dev_buf, host_blob, bytes, hipMemcpyHostToDevice, cs);
+  // host -> device: reps copies of the blob from pinned memory, after one
+  // untimed, by the path the decode steps take: the fill kernel when the blob
+  // is mapped pinned memory on a 16-byte boundary, else the copy engine
+  void* mapped = nullptr;
+  if (hipHostGetDevicePointer(&mapped, const_cast<void*>(host_blob), 0) != hipSuccess) {
+    (void)hipGetLastError();
+    mapped = nullptr;
+  }
+  const bool kernel = mapped && ((uintptr_t)mapped & 15) == 0 && ((uintptr_t)dev_buf & 15) == 0 && bytes % 16 == 0 &&
+                      bytes / 16 < (1ull << 31);
+  moe::FillList fl{};
+  moe::StepMap none{};
+  if (kernel) {
+    fl.n = 1;
+    fl.off16 = 0;
+    fl.len16 = (uint32_t)(bytes / 16);
+    fl.slot[0] = 0;
+    fl.src[0] = static_cast<const uint8_t*>(mapped);
+  }
+  auto copy_once = [&]() {
+    return kernel ? moe::launch_fill_slots(fl, none, 0, nullptr, dev_buf, bytes, cs)
+                  : hipMemcpyAsync(dev_buf, host_blob, bytes, hipMemcpyHostToDevice, cs);
+  };
+  hipError_t err = copy_once();
   if (err == hipSuccess) err = hipEventRecord(e0, cs);
-  for (int i = 0; i < reps && err == hipSuccess; ++i)
-    err = hipMemcpyAsync(dev_buf, host_blob, bytes, hipMemcpyHostToDevice, cs);
+  for (int i = 0; i < reps && err == hipSuccess; ++i) err = copy_once();
   if (err == hipSuccess) err = hipEventRecord(e1, cs);
   if (err == hipSuccess) err = hipEventSynchronize(e1);
   float ms = 0.f;

@@ -464,7 +464,10 @@ typedef struct {
 
 /* Times `reps` copies of host_blob (pinned, a prepacked blob) into dev_buf
  * (device, at least the blob's size) on copy_stream, and `reps` runs of
- * moe_cpu_expert_ffn on it with `threads` threads; synchronises the host. */
+ * moe_cpu_expert_ffn on it with `threads` threads; synchronises the host.
+ * The copies take the path of moe_cache_decode_step's misses: the fill
+ * kernel when host_blob is mapped pinned memory and both pointers are on
+ * 16-byte boundaries, else the copy engine. */
 moe_status moe_calibrate_bw(const void* host_blob, void* dev_buf, int reps, int threads, moe_stream_t copy_stream,
                             moe_bw_calib* out);
 

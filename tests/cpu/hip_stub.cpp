@@ -378,13 +378,15 @@ hipError_t launch_fill_slots(const FillList& f, const StepMap& m, int E, void* d
                              hipStream_t s) {
   if (inject(4)) return hipErrorLaunchFailure;
   const Op o = tick(s);
-  if (!region_of((uintptr_t)dev_map, 6 * (size_t)E)) bad("slot map outside the registered memory", E, 0);
-  int32_t* slot = static_cast<int32_t*>(dev_map);
-  uint8_t* hit = static_cast<uint8_t*>(dev_map) + 4 * E;
-  memset(dev_map, 0, 6 * (size_t)E);
-  for (int i = 0; i < m.n; ++i) {
-    slot[m.expert[i]] = m.slot[i];
-    (m.hit[i] ? hit : hit + E)[m.expert[i]] = 1;
+  if (E > 0) {  // E == 0: no map (a plain copy)
+    if (!region_of((uintptr_t)dev_map, 6 * (size_t)E)) bad("slot map outside the registered memory", E, 0);
+    int32_t* slot = static_cast<int32_t*>(dev_map);
+    uint8_t* hit = static_cast<uint8_t*>(dev_map) + 4 * E;
+    memset(dev_map, 0, 6 * (size_t)E);
+    for (int i = 0; i < m.n; ++i) {
+      slot[m.expert[i]] = m.slot[i];
+      (m.hit[i] ? hit : hit + E)[m.expert[i]] = 1;
+    }
   }
   copy_parts(f, pool, slot_bytes, o);
   return hipSuccess;

@@ -49,6 +49,24 @@ def test_cache_fill_copies_the_blob_into_its_slot():
     c.close()
 
 
+def test_calibration_copies_the_blob():
+    """moe_calibrate_bw times the decode steps' miss copy (the fill kernel on
+    a pinned blob) and the host expert FFN: the device buffer then holds the
+    blob byte for byte, and the figures are positive with a copy share in
+    (0, 1)."""
+    import fp4_expert_ffn_amd as F
+    ex = synth.expert("nvfp4", 256, 128, config=85, expert_id=1)
+    nbytes = F.moe_blob_bytes("nvfp4", 256, 128)
+    stride = (nbytes + 255) // 256 * 256
+    src = _pinned_blob(ex, stride)
+    dst = torch.zeros(stride, dtype=torch.uint8, device=DEV)
+    say("moe_calibrate_bw on one NVFP4 blob (hidden 256, inter 128)")
+    cal = F.moe_calibrate_bw(src, dst, reps=3, threads=2)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes].cpu(), src[:nbytes])
+    assert cal.copy_us > 0 and cal.cpu_us > 0 and cal.h2d_gbs > 0 and 0 < cal.copy_ratio < 1
+
+
 def _run_stream(*, layers, E, k, H, I, tokens, slots, make_expert, check_steps=None, config=86, resize_at=None,
                 routing_seed=None, blob_key=None, copy_ratio=None, copy_engine=False, raw=False):
     """Decode `tokens` single-token steps through `layers` layers; returns the
