@@ -185,6 +185,50 @@ def test_cached_stream_hybrid_policy(copy_ratio):
                 copy_ratio=copy_ratio, raw=True)
 
 
+@pytest.mark.parametrize("copy_engine", [False, True])
+def test_cached_stream_batched_steps(copy_engine):
+    """Decode steps of 4 tokens through the cache (3 layers x 16 NVFP4
+    experts, top-4, 14 slots): up to 16 distinct experts a step, so a step
+    has many misses in one fill list and hits on the side stream at once.
+    Every step's trace equals the oracle LRU's and every token's output
+    matches the oracle layer."""
+    from fp4_expert_ffn_amd.layer import CachedDecoder, to_numpy_bf16
+    import fp4_expert_ffn_amd as F
+    L_, E, k, H, I, T, slots, steps = 3, 16, 4, 256, 256, 4, 14, 12
+    say(f"cached stream, {T}-token steps: {L_} layers x {E} NVFP4 experts, {slots} slots, {steps} steps, "
+        f"copy engine {copy_engine}")
+
+    def make(l, e):
+        return synth.expert("nvfp4", H, I, config=93, layer=l, expert_id=e)
+
+    stride = (F.moe_blob_bytes("nvfp4", H, I) + 255) // 256 * 256
+    bank = {(l, e): _pinned_blob(make(l, e), stride) for l in range(L_) for e in range(E)}
+    dec = CachedDecoder(num_layers=L_, num_experts=E, k=k, H=H, I=I, fmt="nvfp4", num_slots=slots,
+                        host_blob=lambda l, e: bank[(l, e)], max_tokens=T, device=DEV, copy_engine=copy_engine)
+    rng = np.random.default_rng(93)
+    lru = oracle.lru.SlotLRU(slots)
+    wts = {l: DequantCache(lambda e, l=l: make(l, e), cap=E) for l in range(L_)}
+    for step in range(steps):
+        l = step % L_
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        xb = synth.activations(T, H, 93, 1, step)
+        out, (te, ts, th, tv) = dec.step(l, torch.from_numpy(xb.view(np.int16)).to(DEV),
+                                         torch.from_numpy(logits).to(DEV))
+        ids, w = oracle.moe.route(logits, k)
+        want = lru.lookup(l, sorted(set(ids.ravel().tolist())))
+        assert te.tolist() == [r[0] for r in want], step
+        assert th.tolist() == [int(r[1]) for r in want], step
+        assert ts.tolist() == [r[2] for r in want], step
+        assert tv.tolist() == [-1 if r[3] is None else r[3][0] * E + r[3][1] for r in want], step
+        torch.cuda.synchronize()
+        got = synth.bf16_bits_to_f32(to_numpy_bf16(out))
+        for t in range(T):
+            ref = oracle.moe.token_output(t, xb, ids[t], w[t], wts[l])
+            err = oracle.moe.relative_error(got[t], ref)
+            assert err <= TOL, (step, t, err)
+    dec.close()
+
+
 def test_cached_stream_with_resizes():
     """The 16-expert stream with the cache shrunk from 10 to 5 slots, then grown
     to 14, between steps: the traces after each resize (which keys stayed, in
