@@ -185,16 +185,18 @@ def test_cached_stream_hybrid_policy(copy_ratio):
                 copy_ratio=copy_ratio, raw=True)
 
 
-@pytest.mark.parametrize("copy_engine", [False, True])
-def test_cached_stream_batched_steps(copy_engine):
-    """Decode steps of 4 tokens through the cache (3 layers x 16 NVFP4
-    experts, top-4, 14 slots): up to 16 distinct experts a step, so a step
-    has many misses in one fill list and hits on the side stream at once.
-    Every step's trace equals the oracle LRU's and every token's output
-    matches the oracle layer."""
+@pytest.mark.parametrize("T,copy_engine", [(4, False), (4, True), (80, False)])
+def test_cached_stream_batched_steps(T, copy_engine):
+    """Decode steps of several tokens through the cache (3 layers x 16 NVFP4
+    experts, top-4, 16 slots): up to 16 distinct experts a step, so a step
+    has many misses in one fill list and hits on the side stream at once;
+    steps of 80 tokens publish their counts through the separate handoff
+    kernel (the routing kernel folds it in up to 64 tokens).  Every step's
+    trace equals the oracle LRU's and every token's output matches the
+    oracle layer."""
     from fp4_expert_ffn_amd.layer import CachedDecoder, to_numpy_bf16
     import fp4_expert_ffn_amd as F
-    L_, E, k, H, I, T, slots, steps = 3, 16, 4, 256, 256, 4, 14, 12
+    L_, E, k, H, I, slots, steps = 3, 16, 4, 256, 256, 16, 12
     say(f"cached stream, {T}-token steps: {L_} layers x {E} NVFP4 experts, {slots} slots, {steps} steps, "
         f"copy engine {copy_engine}")
 
