@@ -296,12 +296,12 @@ def layer_workload(wl, args, torch, dev, steps=None, warmup=None, cpu_baseline=T
             per_T[T]["gateup_fp4_frac"] = round(sum(f) / len(f) / ds / 1e12 / MFMA_PEAK_TFLOPS["fp4"], 4)
 
     if wl == "prefill-bf16":
-        kname = "k_fp4_gemm<0, false> (gate/up projection + SwiGLU, bf16 weights on bf16 matrix cores)"
+        kname = "k_bf16_gemm<0> (gate/up projection + SwiGLU, bf16 weights on bf16 matrix cores)"
     elif wl in ("prefill-nvfp4", "prefill-fp8"):
         kname = f"k_mfma_ffn<false, 0, *, {fmt}> (gate/up projection + SwiGLU, {fmt} weights decoded to bf16 " \
                 "in LDS, bf16 matrix cores)"
     elif amode == "mxfp4":
-        kname = "k_fp4_gemm<0, true> (gate/up projection + SwiGLU, FP4 matrix cores)"
+        kname = "k_fp4_gemm<0> (gate/up projection + SwiGLU, FP4 matrix cores, two workgroups per CU)"
     elif fmt == "nvfp4":
         kname = "k_gemv (gate/up projection + SwiGLU, NVFP4 weights on fp16 matrix cores; " \
                 "the routing folded in at batches of at most 4 tokens)"
@@ -472,8 +472,8 @@ def main():
 
 
 # Kernel-name patterns of the dominant kernel (gate/up projection) per workload.
-DOMINANT = {"decode": "k_gemv<2, false", "large-decode": "k_gemv<1, false", "prefill-mxfp4": "k_fp4_gemm<0, true>",
-            "large-prefill": "k_fp4_gemm<0, true>", "prefill-bf16": "k_fp4_gemm<0, false>",
+DOMINANT = {"decode": "k_gemv<2, false", "large-decode": "k_gemv<1, false", "prefill-mxfp4": "k_fp4_gemm<0>",
+            "large-prefill": "k_fp4_gemm<0>", "prefill-bf16": "k_bf16_gemm<0>",
             "prefill-nvfp4": "k_mfma_ffn<false, 0", "prefill-fp8": "k_mfma_ffn<false, 0"}
 # The sources each workload's dominant kernel is built from: a committed
 # counter summary stands only while none of them has changed.

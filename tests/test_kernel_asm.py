@@ -98,8 +98,9 @@ def test_prefill_gemm_owns_m0(fp4gemm_asm):
     """The prefill GEMM's direct-to-LDS loads set M0 in inline assembly; that is
     only sound while the compiler itself neither reads nor writes M0 in the
     kernel: every mention must be one of those `s_mov_b32 m0` + load pairs."""
-    names = re.findall(r"^(_ZN3moe10k_fp4_gemm\w+):", fp4gemm_asm, re.M)
-    assert len(names) == 6  # {FP4, BF16} x {gate/up, down (bf16 out), down (fp32 out)}
+    names = re.findall(r"^(_ZN3moe1[01]k_(?:fp4|bf16)_gemm\w+):", fp4gemm_asm, re.M)
+    # {FP4, BF16} x {gate/up, down (bf16 out), down (fp32 out)}
+    assert len(names) == 6, names
     for full in names:
         i = fp4gemm_asm.index(full + ":")
         body = fp4gemm_asm[i:fp4gemm_asm.index(".Lfunc_end", i)]
