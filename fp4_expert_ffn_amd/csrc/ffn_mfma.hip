@@ -76,6 +76,11 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int nb = cols / 32;  // a multiple of 4
+  // the token's destination rows, one per lane (k <= 16), loaded once ahead
+  // of x: the stores below take them by lane broadcast, so a wave waits for
+  // one memory latency here instead of one per destination row
+  const uint32_t dst_row =
+      lane < k ? (uint32_t)inv[(size_t)t * k + lane] : (lane == k ? (uint32_t)(T * k + t) : 0u);
   for (int c0 = 0; c0 < nb; c0 += 64) {
     const int c = c0 + lane;
     float v[32];
@@ -104,7 +109,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
     if (c < nb) {
       const size_t kt = (size_t)(c >> 2) * rtot;
       for (int j = 0; j < k + shared; ++j) {
-        const uint32_t row = j < k ? (uint32_t)inv[(size_t)t * k + j] : (uint32_t)(T * k + t);
+        const uint32_t row = (uint32_t)__builtin_amdgcn_readlane((int)dst_row, j);
         *reinterpret_cast<uint4*>(q + (kt + row) * 64 + (c & 3) * 16) = qq;
         if ((c & 3) == 0) *reinterpret_cast<uint32_t*>(s + (kt + row) * 4) = sd;
       }

@@ -69,6 +69,7 @@ SMALL = [  # fmt, amode, T, E, k, H, I, shared
     ("bf16", "bf16", 300, 8, 2, 256, 384, True),     # bf16 MFMA path (600 rows)
     ("mxfp4", "mxfp4", 300, 8, 2, 256, 384, False),  # FP4 MFMA path, several row tiles + ragged tails
     ("mxfp4", "mxfp4", 97, 6, 3, 512, 256, True),
+    ("mxfp4", "mxfp4", 300, 8, 2, 256, 768, True),   # persistent FP4 GEMM: 6 gate/up column blocks, down K 6 steps
     ("mxfp4", "bf16", 600, 8, 1, 256, 128, False),   # GEMV path at a prefill-like row count
     ("nvfp4", "bf16", 1, 1, 1, 128, 128, False),     # one expert, top-1
     ("mxfp4", "mxfp4", 300, 8, 2, 256, 128, False),  # 128 x 128 FP4 kernel, down K = 128: half K-step at step 0
