@@ -16,7 +16,9 @@ Other workloads (--workload):
                  2048 HBM slots under LRU, 512 single-token steps from a cold
                  cache; misses copied host->device on a side stream
 
-Prints one JSON line (see the design doc for the definitions of every field).
+Prints one JSON line: the metric and its value, the configuration, the
+dominant kernel's roofline (algorithmic bytes or FLOPs per launch over its
+measured launch time, against the MI355X peak) and the oracle's CPU rate.
 """
 from __future__ import annotations
 
@@ -423,8 +425,8 @@ def main():
     if args.summarize:
         return summarize(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md, 'How the path would shard').", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the layer would shard by expert, each GPU owning its experts' slots).", file=sys.stderr)
         sys.exit(2)
 
     if args.workload == "stream":
