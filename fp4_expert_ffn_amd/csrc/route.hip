@@ -173,7 +173,6 @@ __global__ __launch_bounds__(64) void k_router_mfma(const uint16_t* __restrict__
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int p = 0; p < 3; ++p) acc[i][p] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
   for (int k0 = 0; k0 < H; k0 += 32) {
     const rbf16x8_t a0 = __builtin_bit_cast(rbf16x8_t, *reinterpret_cast<const ru32x4_t*>(xa + k0));
     const rbf16x8_t a1 = __builtin_bit_cast(rbf16x8_t, *reinterpret_cast<const ru32x4_t*>(xb + k0));
