@@ -83,9 +83,15 @@ inline void launch(F kernel, dim3 grid, dim3 block, size_t shmem, hipStream_t s,
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);  // v_cvt_pk_bf16_f32: round to nearest even
+}
+
+// Two fp32 values as packed bf16 (a in the low half), round to nearest even:
+// one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }

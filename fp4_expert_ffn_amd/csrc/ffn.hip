@@ -168,7 +168,7 @@ __global__ __launch_bounds__(128) void k_combine(const YT* __restrict__ y, const
   for (int i = 0; i < 8; ++i) acc[i] += vs[i];
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (uint32_t)f32_to_bf16_rne(acc[2 * i]) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) o[i] = bf16x2_rne(acc[2 * i], acc[2 * i + 1]);
   *reinterpret_cast<uint4*>(out + (size_t)t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 

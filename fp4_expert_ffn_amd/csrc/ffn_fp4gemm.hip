@@ -318,8 +318,8 @@ void k_bf16_gemm(FfnParams P, MfmaBufs B) {
         if (i >= 4 && !full) break;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
-            const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16);
+            const uint32_t lo = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+            const uint32_t hi = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
             const int gr = 2 * j + (g >> 1);  // 16-byte granule of columns 16 j + 4 g
             *reinterpret_cast<uint2*>(ws + t16 * 256 + ((gr ^ t16) << 4) + (g & 1) * 8) = make_uint2(lo, hi);
           }
@@ -361,7 +361,7 @@ void k_bf16_gemm(FfnParams P, MfmaBufs B) {
           for (int v = 0; v < 2; ++v) {
             const float h0 = silu_fast(acc[i][2 * p][2 * v]) * acc[i][2 * p + 1][2 * v];
             const float h1 = silu_fast(acc[i][2 * p][2 * v + 1]) * acc[i][2 * p + 1][2 * v + 1];
-            w2[v] = f32_to_bf16_rne(h0) | ((uint32_t)f32_to_bf16_rne(h1) << 16);
+            w2[v] = bf16x2_rne(h0, h1);
           }
           // row t16, 16-byte granule 2p + g / 2 of the row's 128 bytes, XOR-swizzled by row
           const int gr = 2 * p + (g >> 1);
@@ -690,8 +690,8 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
         if (i >= 4 && !full) break;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16);
+          const uint32_t lo = bf16x2_rne(acc[i][j][0], acc[i][j][1]);
+          const uint32_t hi = bf16x2_rne(acc[i][j][2], acc[i][j][3]);
           const int gr = 2 * j + (g >> 1);  // 16-byte granule of columns 16 j + 4 g
           *reinterpret_cast<uint2*>(ws + t16 * 128 + (((gr ^ t16) & 7) << 4) + (g & 1) * 8) = make_uint2(lo, hi);
         }

@@ -526,7 +526,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          w[j] = (uint32_t)f32_to_bf16_rne(hv[8 * q + 2 * j]) | ((uint32_t)f32_to_bf16_rne(hv[8 * q + 2 * j + 1]) << 16);
+          w[j] = bf16x2_rne(hv[8 * q + 2 * j], hv[8 * q + 2 * j + 1]);
         reinterpret_cast<uint4*>(dst)[q] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
