@@ -187,18 +187,13 @@ __device__ __forceinline__ int ilog2_f32(float v) {
   return (31 - __clz(u)) - 149;  // subnormal: u * 2^-149
 }
 
-// |q| -> E2M1 magnitude code, round to nearest even, saturate at 6.
+// |q| -> E2M1 magnitude code, round to nearest even, saturate at 6: the
+// boundaries (ties to the even code: <= at 0.25, 1.25, 2.5, 5; < at 0.75,
+// 1.75, 3.5) are nested, so the code is the number of them a lies above,
+// counted without branches (a NaN lies above none and gets 7).
 __device__ __forceinline__ uint32_t e2m1_mag_rne(float a) {
-  uint32_t m;
-  if (a <= 0.25f) m = 0;
-  else if (a < 0.75f) m = 1;
-  else if (a <= 1.25f) m = 2;
-  else if (a < 1.75f) m = 3;
-  else if (a <= 2.5f) m = 4;
-  else if (a < 3.5f) m = 5;
-  else if (a <= 5.0f) m = 6;
-  else m = 7;
-  return m;
+  return (uint32_t)!(a <= 0.25f) + (uint32_t)!(a < 0.75f) + (uint32_t)!(a <= 1.25f) + (uint32_t)!(a < 1.75f) +
+         (uint32_t)!(a <= 2.5f) + (uint32_t)!(a < 3.5f) + (uint32_t)!(a <= 5.0f);
 }
 
 // Encode 32 fp32 values as MXFP4: 16 packed bytes (element 2i low nibble) + E8M0.
