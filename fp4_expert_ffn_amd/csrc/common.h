@@ -112,9 +112,10 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
 
 // E8M0 code -> float 2^(c-127) (c = 255 is NaN; c = 0 is the fp32 subnormal 2^-127).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
-  if (c == 0) return __uint_as_float(0x00400000u);
-  if (c == 255) return __uint_as_float(0x7FC00000u);
-  return __uint_as_float(c << 23);
+  // selects, not branches: this runs once per weight tile in the decode loops
+  const uint32_t n = c << 23;
+  const uint32_t u = c == 0u ? 0x00400000u : n;
+  return __uint_as_float(c == 255u ? 0x7FC00000u : u);
 }
 
 }  // namespace moe

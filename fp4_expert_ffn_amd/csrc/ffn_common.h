@@ -183,8 +183,8 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int ilog2_f32(float v) {
   const uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
   const int e = (int)(u >> 23);
-  if (e) return e - 127;
-  return (31 - __clz(u)) - 149;  // subnormal: u * 2^-149
+  const int sub = (31 - __clz(u)) - 149;  // subnormal: u * 2^-149
+  return e ? e - 127 : sub;               // a select, not a branch
 }
 
 // |q| -> E2M1 magnitude code, round to nearest even, saturate at 6: the
@@ -201,8 +201,7 @@ __device__ __forceinline__ void mxfp4_encode32(const float* v, uint4& q, uint32_
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  int ex = 0;
-  if (amax != 0.f) ex = min(127, max(-127, ilog2_f32(amax) - 2));
+  const int ex = amax != 0.f ? min(127, max(-127, ilog2_f32(amax) - 2)) : 0;
   s = (uint32_t)(ex + 127);
   // 2^-ex as an exact fp32 (normal for ex in [-127, 126]; subnormal 2^-127 for ex = 127)
   const float inv = ex == 127 ? __uint_as_float(0x00400000u) : __uint_as_float((uint32_t)(127 - ex) << 23);

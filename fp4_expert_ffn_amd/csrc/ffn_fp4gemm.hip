@@ -734,8 +734,7 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
 #pragma unroll
         for (int v = 0; v < 8; ++v) amax = fmaxf(amax, fabsf(h[v]));
         amax = max_rows4(amax);
-        int ex = 0;
-        if (amax != 0.f) ex = min(127, max(-127, ilog2_f32(amax) - 2));
+        const int ex = amax != 0.f ? min(127, max(-127, ilog2_f32(amax) - 2)) : 0;
         const float sc = __uint_as_float((uint32_t)(max(ex, -126) + 127) << 23);
         if (ex == -127) {
 #pragma unroll
