@@ -74,27 +74,31 @@ __device__ __forceinline__ void wave_topk_select(const float (&val)[NPER], int E
     for (int i = 1; i < NPER; ++i) lm = max(lm, rk[i]);
     const uint32_t m = wave_max_u32(lm);
     if (m == 0u) break;  // fewer than k keys (not reached: k <= E)
-    int ws = NPER, wl = 0;  // slot and lane of the key taken
+    // slot ws and lane wl of the key taken: the lowest slot holding m, its
+    // lowest lane (wave-uniform selects, no branches)
+    uint64_t bs[NPER];
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      if (ws == NPER) {
-        const uint64_t b = __ballot(rk[i] == m);
-        if (b) {
-          ws = i;
-          wl = __builtin_ctzll(b);
-        }
-      }
+    for (int i = 0; i < NPER; ++i) bs[i] = __ballot(rk[i] == m);
+    int ws = NPER - 1;
+    uint64_t bw = bs[NPER - 1];
+#pragma unroll
+    for (int i = NPER - 2; i >= 0; --i) {
+      ws = bs[i] ? i : ws;
+      bw = bs[i] ? bs[i] : bw;
+    }
+    const int wl = __builtin_ctzll(bw);
+    if (r == 0) {
+      float v = val[0];
+#pragma unroll
+      for (int i = 1; i < NPER; ++i) v = i == ws ? val[i] : v;
+      top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), wl));
     }
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
-      if (i == ws) {
-        if (r == 0) top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(val[i]), wl));
-        if (lane == wl) {
-          sel[i] = true;
-          pos[i] = r;
-          rk[i] = 0u;
-        }
-      }
+      const bool hit = i == ws && lane == wl;
+      sel[i] = sel[i] || hit;
+      pos[i] = hit ? r : pos[i];
+      rk[i] = hit ? 0u : rk[i];
     }
   }
   float part = 0.f;

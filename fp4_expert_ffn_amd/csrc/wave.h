@@ -12,18 +12,19 @@ constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
-constexpr int kDppRowShr2 = 0x112;      // row_shr:2 (lane l reads lane l - 2 of its 16-lane row)
-constexpr int kDppRowShr4 = 0x114;
-constexpr int kDppRowShr8 = 0x118;
 
+// Every control used here (quad permutations, row mirrors) gives each lane a
+// source lane, so no lane reads out of bounds: with old = 0 and bound_ctrl
+// set the compiler fuses the move into the consuming instruction
+// (v_max_u32_dpp, v_add_f32_dpp), with the same result.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 // v_permlane16_swap on (v, v) returns one copy holding rows {0,0,2,2} and one
