@@ -735,10 +735,14 @@ void k_fp4_gemm(FfnParams P, MfmaBufs B) {
         for (int v = 0; v < 8; ++v) amax = fmaxf(amax, fabsf(h[v]));
         amax = max_rows4(amax);
         const int ex = amax != 0.f ? min(127, max(-127, ilog2_f32(amax) - 2)) : 0;
+        // The block scale 2^ex as a normal fp32; for ex = -127 (every |h| <
+        // 2^-124) the scale 2^-126 with doubled values gives the same
+        // quotient, h / 2^-127 = 2h / 2^-126 (doubling such small values is
+        // exact).
         const float sc = __uint_as_float((uint32_t)(max(ex, -126) + 127) << 23);
         if (ex == -127) {
 #pragma unroll
-          for (int v = 0; v < 8; ++v) h[v] *= 0.5f;
+          for (int v = 0; v < 8; ++v) h[v] *= 2.0f;
         }
         const uint32_t lo = e2m1_pair(h[0], h[1], sc) | (e2m1_pair(h[2], h[3], sc) << 8);
         const uint32_t hi = e2m1_pair(h[4], h[5], sc) | (e2m1_pair(h[6], h[7], sc) << 8);

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from tests.gpu_util import (DEV, fp4_code_report, grouped_reference, need_gpu, out_f32, resident_layer, say,
+from tests.gpu_util import (DEV, fp4_code_report, gpu_fp4_codes, grouped_reference, need_gpu, out_f32, resident_layer, say,
                             torch)
 
 pytestmark = pytest.mark.gpu
@@ -107,6 +107,28 @@ def test_small_layers_every_path(fmt, amode, T, E, k, H, I, shared):
     layer.forward(_x(x), logits=torch.from_numpy(logits).to(DEV))
     torch.cuda.synchronize()
     _full_check(layer, x, experts, k, logits, shared=sh, amode=amode)
+
+
+def test_fp4_tiny_swiglu_blocks():
+    """x scaled by 2^-61, so that many 32-value blocks of the SwiGLU output lie
+    below 2^-124 and take the smallest block scale (E8M0 code 0, 2^-127): the
+    persistent FP4 kernel's encodings of them match the oracle's, as does the
+    (tiny) output."""
+    fmt, amode, T, E, k, H, I = "mxfp4", "mxfp4", 300, 8, 2, 256, 768
+    experts = [synth.expert(fmt, H, I, config=80, expert_id=e) for e in range(E)]
+    x = synth.activations(T, H, 80, T, E)
+    # an exact power-of-two scaling of the bf16 values (no underflow at 2^-61)
+    x = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x) * np.float32(2.0 ** -61))
+    logits = np.random.default_rng(7).standard_normal((T, E)).astype(np.float32)
+    layer = resident_layer(experts, k=k, T=T, amode=amode)
+    say(f"tiny SwiGLU blocks: {fmt}/{amode} T={T} E={E} k={k} H={H} I={I}, x * 2^-61")
+    layer.forward(_x(x), logits=torch.from_numpy(logits).to(DEV))
+    torch.cuda.synchronize()
+    _, hs = gpu_fp4_codes(layer, T, layer.state.last_x, 1)
+    frac0 = float(np.mean(hs == 0))
+    say(f"    blocks with scale 2^-127: {frac0:.2f}")
+    assert frac0 > 0.05, "the inputs no longer reach the smallest block scale"
+    _full_check(layer, x, experts, k, logits, amode=amode)
 
 
 @pytest.mark.parametrize("fmt,rows", [("nvfp4", "all"), ("mxfp4", "all"), ("nvfp4", "some"), ("fp8", "some")])
