@@ -367,8 +367,8 @@ __device__ __forceinline__ uint32_t bf16x8_absmax_bits(const uint4 v) {
   return max(m, max(max(v.z & 0x7FFFu, v.z >> 16 & 0x7FFFu), max(v.w & 0x7FFFu, v.w >> 16 & 0x7FFFu)));
 }
 
-// bf16 values of one 16-byte piece (8 values) as fp16 times 2^-p (p >= 0):
-// the power of two is applied exactly in fp32, then one rounding to fp16.
+// bf16 values of one 16-byte piece (8 values) as fp16 times sc = 2^-p: the
+// power of two is applied exactly in fp32, then one rounding to fp16.
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4 v, float sc) {
   auto cv = [&](uint32_t w) -> uint32_t {
     const f32x2_t f = {__uint_as_float(w << 16) * sc, __uint_as_float(w & 0xFFFF0000u) * sc};
@@ -379,15 +379,16 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4 v, float sc) {
 
 // After every wave's rows have landed (and a barrier): for the fp16 operand
 // path the rows are rewritten in place as fp16 of value * 2^-pexp[r].  A row
-// whose values are all below 2^16 in magnitude is finite in fp16 as it is:
-// pexp[r] = 0, one pass.  A row holding a larger value (or inf / NaN), which
-// the pass marks in *big, is converted again from its global copy src(r)
-// with pexp[r] >= 0 the smallest shift that keeps its largest magnitude below
-// 2^15 (the output rows are multiplied back by 2^pexp[r]).  bf16 -> fp16 is
-// exact for every value of magnitude >= 2^-14 * 2^pexp[r]; smaller ones
-// round at 2^-24 * 2^pexp[r], far below the row's largest product.  The
-// piece order does not matter for the pass.  For fp16, ends with a barrier;
-// bf16 rows need nothing more.  *big is zero on entry and on return.
+// whose largest magnitude lies in [2^-10, 2^16) converts as it is: pexp[r] =
+// 0, one pass.  A row holding a larger value (or inf / NaN), or a piece below
+// 2^-10, is marked in *big by the pass; if its largest magnitude (from its
+// global copy src(r)) is outside [2^-10, 2^16) it is converted again with the
+// shift pexp[r] (in [-126, 127]) that puts that magnitude in [2^14, 2^15)
+// (the output rows are multiplied back by 2^pexp[r]).  bf16 -> fp16 is exact
+// for every value of magnitude >= 2^-14 * 2^pexp[r]; smaller ones round at
+// 2^-24 * 2^pexp[r], far below the row's largest product (at most 2^-14 of
+// it).  The piece order does not matter for the pass.  For fp16, ends with a
+// barrier; bf16 rows need nothing more.  *big is zero on entry and on return.
 template <bool F16, class Src>
 __device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pexp, int* big, Src src) {
   if constexpr (F16) {
@@ -397,7 +398,10 @@ __device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pe
     for (int p = tid; p < total; p += 256) {
       uint4* q = reinterpret_cast<uint4*>(act) + p;
       const uint4 v = *q;
-      if (bf16x8_absmax_bits(v) >= 0x4780u) atomicOr(big, 1 << (p / spr));  // |value| >= 2^16, inf or NaN
+      // |value| >= 2^16, inf or NaN; or a piece below 2^-10, whose row may
+      // lie below fp16's normal range (decided from the whole row below)
+      const uint32_t am = bf16x8_absmax_bits(v);
+      if (am >= 0x4780u || am < 0x3A80u) atomicOr(big, 1 << (p / spr));
       *q = bf16x8_to_f16x8(v, 1.0f);
     }
     lds_barrier();
@@ -410,7 +414,10 @@ __device__ __forceinline__ void finish_rows(uint8_t* act, int K, int nr, int* pe
         for (int j = lane; j < ppr; j += 64) mx = max(mx, bf16x8_absmax_bits(g[j]));
         mx = wave_max_u32(mx);
         const int E = (int)(mx >> 7);  // biased exponent of the row's largest |value|: it is < 2^(E-126)
-        const int pe = (E == 0xFF) ? 0 : max(0, E - 141);
+        // rows in [2^-10, 2^16) stay as converted; others are shifted so that
+        // their largest |value| lies in [2^14, 2^15) (up by at most 2^126)
+        if (E != 0xFF && E >= 0x75 && E < 0x8F) continue;
+        const int pe = (E == 0xFF) ? 0 : max(-126, E - 141);
         if (lane == 0) pexp[r] = pe;
         const float sc = __uint_as_float((uint32_t)(127 - pe) << 23);
         uint4* row = reinterpret_cast<uint4*>(act) + (size_t)r * spr;
@@ -438,7 +445,7 @@ __device__ __forceinline__ void rows_landed() {
   asm volatile("" ::: "memory");
 }
 
-// 2^p as a float (0 <= p < 128)
+// 2^p as a float (-126 <= p < 128)
 __device__ __forceinline__ float pow2i(int p) { return __uint_as_float((uint32_t)(127 + p) << 23); }
 
 constexpr int kTrashSlots = 256;         // 4 KiB scratch slots (workgroup index modulo this)

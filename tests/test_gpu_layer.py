@@ -151,6 +151,32 @@ def test_large_magnitude_activations(fmt, rows):
     _full_check(layer, x, experts, k, logits)
 
 
+@pytest.mark.parametrize("fmt,T,rows", [("nvfp4", 1, "all"), ("nvfp4", 4, "all"), ("nvfp4", 16, "some"),
+                                         ("fp8", 16, "all")])
+def test_tiny_activation_rows(fmt, T, rows):
+    """Token rows whose largest |x| is about 2^-55 (fp16's subnormal range ends
+    at 2^-24): the NVFP4 / FP8 decode path stages operand rows in fp16, so such
+    rows are taken again from their global copy with a power-of-two up-shift.
+    Checked per token row, each against its own largest output."""
+    E, k, H, I = 8, 2, 256, 256
+    experts = [synth.expert(fmt, H, I, config=84, expert_id=e) for e in range(E)]
+    scale = np.full((T, 1), 2.0 ** -57, np.float32)
+    if rows == "some":
+        scale[[0, 2, 4]] = 1.0
+    x = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(synth.activations(T, H, 84)) * scale)
+    logits = np.random.default_rng(11).standard_normal((T, E)).astype(np.float32)
+    layer = resident_layer(experts, k=k, T=T)
+    say(f"tiny activation rows {fmt} T={T}, {rows} rows")
+    layer.forward(_x(x), logits=torch.from_numpy(logits).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.moe.layer(x, experts, k, logits=logits)
+    assert np.array_equal(layer.ids[:T].cpu().numpy(), ref["ids"])
+    out = out_f32(layer, T)
+    worst = max(oracle.moe.relative_error(out[t], ref["out"][t]) for t in range(T))
+    say(f"    worst per-row rel err {worst:.3e}")
+    assert worst <= TOL
+
+
 @pytest.mark.parametrize("T", [1, 4, 16])
 def test_folded_routing_edge_rows(T):
     """moe_layer's routing (folded into the gate/up launch for T <= 4, the
