@@ -73,7 +73,12 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
                                                     const int32_t* __restrict__ inv, int shared, uint32_t rtot,
                                                     uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // Workgroup b runs on XCD b % 8, and each XCD takes a contiguous eighth of
+  // the tokens: an expert's neighbouring rows (tokens close in order) are then
+  // written through one L2, which merges their 64-byte code and 4-byte scale
+  // pieces into whole lines.  The grid is 8 * ceil(T / 32) workgroups.
+  const int per = (int)gridDim.x / 8, b = blockIdx.x;
+  const int t = ((b % 8) * per + b / 8) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int nb = cols / 32;  // a multiple of 4
   // the token's destination rows, one per lane (k <= 16), loaded once ahead
@@ -619,7 +624,7 @@ hipError_t launch_mfma(const FfnParams& P, bool fp4, const MfmaBufs& B, hipStrea
         launch(k_invert, dim3((n + 255) / 256), dim3(256), 0, s, P.perm, n, P.inv_ws);
         inv = P.inv_ws;
       }
-      launch(k_quant_rows, dim3((P.T + 3) / 4), dim3(256), 0, s, P.x, P.T, P.H, P.k, inv, P.shared_blob ? 1 : 0, rtot,
+      launch(k_quant_rows, dim3(8 * ((P.T + 31) / 32)), dim3(256), 0, s, P.x, P.T, P.H, P.k, inv, P.shared_blob ? 1 : 0, rtot,
              const_cast<uint8_t*>(B.xq), const_cast<uint8_t*>(B.xs));
       e = hipGetLastError();
       if (e != hipSuccess) return e;

@@ -49,6 +49,8 @@ def _quant_cases():
     x[4, :32] = np.float32(3.0e38)                       # near the top of the range
     x[5, :32] = -0.0
     x[6, 5] = 7.9                                        # saturating element
+    x[7] *= np.float32(2.0**-124) / np.abs(x[7]).max()   # shared exponents -127..-128 clamped, mixed codes
+    x[8] *= np.float32(2.0**-120) / np.abs(x[8]).max()   # normal fp32 values, exponents near the bottom
     return synth.f32_to_bf16_bits(x)
 
 
