@@ -8,7 +8,8 @@
 //
 // Two launches of one kernel template (k_gemv), neither waits for another
 // workgroup: gate/up + SwiGLU (h in bf16), then the down projection (y in
-// fp32; for small batches it also performs the weighted combine).  Every
+// fp32; when only the combined output is wanted, y rows are written in token
+// order t * k + j, so the combine kernel after it needs no row index).  Every
 // workgroup first compacts the active experts from the per-expert row
 // counts, so the grid never carries work for experts without rows.
 //
