@@ -15,9 +15,10 @@
 // (4x4 MFMA 16x16 tiles).  K-steps of 256 (FP4) or 64 (BF16), i.e. 128 bytes
 // of every operand row, are staged global -> registers -> LDS
 // (double-buffered) with the next steps' loads in flight during the current
-// step's MFMAs.  Tiles are listed expert by expert, column tile by
-// column tile, row tile fastest, and each XCD takes a contiguous range of the
-// list, so row tiles of a hot expert that share weights run on one L2.
+// step's MFMAs.  Tiles are listed expert by expert, row tile by row tile,
+// column tile fastest, and each XCD takes a contiguous range of the list:
+// the workgroups running at once on an XCD then share one row tile's
+// operand rows and their expert's weights in its L2.
 #include <algorithm>
 
 #include "ffn_common.h"
@@ -178,11 +179,11 @@ __device__ inline TileJob find_tile(const FfnParams& P, int NT) {
   const int L = (b % 8) * per + b / 8;
   if (b / 8 >= per || L >= total) return tj;  // rows == 0
   if (L >= routed) {
-    const int local = L - routed, mtn = (P.T + kBM - 1) / kBM;
+    const int local = L - routed;
     tj.blob = P.shared_blob;
     tj.shared = 1;
-    tj.nt = local / mtn;
-    tj.m0 = (local % mtn) * kBM;
+    tj.nt = local % NT;
+    tj.m0 = (local / NT) * kBM;
     tj.p0 = P.T * P.k;
     tj.rows = min(kBM, P.T - tj.m0);
     return tj;
@@ -194,10 +195,10 @@ __device__ inline TileJob find_tile(const FfnParams& P, int NT) {
     if (pre[mid] <= L) lo = mid; else hi = mid - 1;
   }
   const int e = lo;
-  const int c = P.counts[e], mt_n = (c + kBM - 1) / kBM, local = L - pre[e];
+  const int c = P.counts[e], local = L - pre[e];
   tj.blob = P.slot_pool + (size_t)P.slot_of_expert[e] * P.slot_stride;
-  tj.nt = local / mt_n;
-  tj.m0 = (local % mt_n) * kBM;
+  tj.nt = local % NT;
+  tj.m0 = (local / NT) * kBM;
   tj.p0 = P.offsets[e];
   tj.rows = min(kBM, c - tj.m0);
   (void)s_info;
